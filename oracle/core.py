@@ -1,0 +1,223 @@
+"""E1-E6 for one sequence, float64, numpy. Test infrastructure only.
+
+Each function cites the passage it follows. The pages (FlashPrefill V2 news
+summaries) describe the method in prose only; equation numbers E1-E6 refer to
+the reading written out in this package's docstring.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Optional, Sequence, Tuple
+
+import numpy as np
+
+NEG_INF = -np.inf
+
+
+def nblocks(L: int, B: int) -> int:
+    """Key blocks of a sequence of L keys (blocks partition tokens into fixed-size
+    groups: stuffinsider.com page, "Technical Details")."""
+    return (L + B - 1) // B
+
+
+def query_blocks(P: int, L: int, B: int) -> Tuple[int, int]:
+    """(first, count) of the query blocks holding present rows [P, L)."""
+    i0 = P // B
+    i1 = (L - 1) // B
+    return i0, i1 - i0 + 1
+
+
+def pool_queries(q: np.ndarray, B: int, P: int, L: int) -> np.ndarray:
+    """E1 for queries: q [L-P, Hq, d] holds rows P..L-1.  Returns Qbar [Hq, nq, d],
+    the mean over the present rows of each query block (block-level estimate,
+    aipulsen.com article body)."""
+    i0, nq = query_blocks(P, L, B)
+    Hq, d = q.shape[1], q.shape[2]
+    out = np.empty((Hq, nq, d))
+    for il in range(nq):
+        i = i0 + il
+        lo, hi = max(i * B, P), min((i + 1) * B, L)
+        out[:, il, :] = q[lo - P:hi - P].mean(axis=0)
+    return out
+
+
+def pool_keys(k: np.ndarray, B: int) -> np.ndarray:
+    """E1 for keys or values: k [L, H, d] -> [H, nb, d], mean over each key block."""
+    L, H, d = k.shape
+    nb = nblocks(L, B)
+    out = np.empty((H, nb, d))
+    for j in range(nb):
+        out[:, j, :] = k[j * B:min((j + 1) * B, L)].mean(axis=0)
+    return out
+
+
+def block_scores(qbar: np.ndarray, kbar: np.ndarray, c: float, i0: int) -> np.ndarray:
+    """E2: S[h, il, j] = c <Qbar[h, il], Kbar[g(h), j]> for j <= i0 + il, -inf above.
+
+    One estimate per (query block, key block) pair (aipulsen.com article body;
+    the "small sample of attention scores" of the lode.cx page, "How It Works")."""
+    Hq, nq, d = qbar.shape
+    Hkv, nb, _ = kbar.shape
+    G = Hq // Hkv
+    S = np.full((Hq, nq, nb), NEG_INF)
+    for h in range(Hq):
+        g = h // G
+        full = c * (qbar[h] @ kbar[g].T)            # [nq, nb]
+        for il in range(nq):
+            i = i0 + il
+            S[h, il, :i + 1] = full[il, :i + 1]
+    return S
+
+
+def select(S: np.ndarray, G: int, tau: float, i0: int) -> Tuple[np.ndarray, np.ndarray]:
+    """E3-E5: max-based dynamic threshold (lode.cx page, "How It Works";
+    aimodeling.com page, "From Prototype to Production").
+
+    Returns (keep bool [Hkv, nq, nb], R float [Hkv, nq, nb]) with R = -inf and
+    keep = False for j > i.  Sink j = 0 and diagonal j = i are always kept."""
+    if isinstance(tau, float) and math.isnan(tau):
+        raise ValueError("tau is NaN")
+    Hq, nq, nb = S.shape
+    Hkv = Hq // G
+    M = S.max(axis=2)                                # E3, over visible j only (rest -inf)
+    R = np.full((Hkv, nq, nb), NEG_INF)
+    keep = np.zeros((Hkv, nq, nb), dtype=bool)
+    for g in range(Hkv):
+        for il in range(nq):
+            i = i0 + il
+            diff = S[g * G:(g + 1) * G, il, :i + 1] - M[g * G:(g + 1) * G, il, None]
+            R[g, il, :i + 1] = diff.max(axis=0)      # E4: union over the group's heads
+            keep[g, il, :i + 1] = R[g, il, :i + 1] >= -tau   # E5, inclusive
+            keep[g, il, 0] = True
+            keep[g, il, i] = True
+    return keep, R
+
+
+def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, keep: np.ndarray,
+           kbar: np.ndarray, vbar: np.ndarray, c: float, B: int, P: int,
+           rows: Optional[Sequence[Tuple[int, int]]] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """E6: sparse attention over kept blocks plus the mean-correction pseudo-tokens.
+
+    Sparse operator over kept blocks: lode.cx page, "How It Works" and the
+    operator bullet list; correction term for pruning bias: lode.cx page, "How
+    It Works", and aimodeling.com page, "Error correction" bullet.
+
+    q [L-P, Hq, d] (rows P..L-1), k/v [L, Hkv, d], keep [Hkv, nq, nb].
+    rows: optional list of (g, il) to evaluate; other outputs stay NaN.
+    Returns o [L-P, Hq, d] and lse [Hq, L-P]."""
+    L, Hkv, d = k.shape
+    Hq = q.shape[1]
+    G = Hq // Hkv
+    i0, nq = query_blocks(P, L, B)
+    o = np.full((L - P, Hq, d), np.nan)
+    lse = np.full((Hq, L - P), np.nan)
+    todo = rows if rows is not None else [(g, il) for g in range(Hkv) for il in range(nq)]
+    for (g, il) in todo:
+        i = i0 + il
+        lo, hi = max(i * B, P), min((i + 1) * B, L)
+        kept_j = [j for j in range(i + 1) if keep[g, il, j]]
+        pruned_j = [j for j in range(i + 1) if not keep[g, il, j]]
+        tok = np.concatenate([np.arange(j * B, min((j + 1) * B, L)) for j in kept_j])
+        Kx = k[tok, g, :]
+        Vx = v[tok, g, :]
+        Kp = kbar[g, pruned_j, :]
+        Vp = vbar[g, pruned_j, :]
+        bias = np.array([math.log(min((j + 1) * B, L) - j * B) for j in pruned_j])
+        t = np.arange(lo, hi)
+        future = tok[None, :] > t[:, None]           # causal inside kept blocks
+        for h in range(g * G, (g + 1) * G):
+            Q = q[lo - P:hi - P, h, :]               # [rows, d]
+            z = c * (Q @ Kx.T)
+            z[future] = NEG_INF
+            zp = c * (Q @ Kp.T) + bias[None, :]
+            m = np.maximum(z.max(axis=1), zp.max(axis=1) if len(pruned_j) else NEG_INF)
+            w = np.exp(z - m[:, None])
+            wp = np.exp(zp - m[:, None])
+            l = w.sum(axis=1) + wp.sum(axis=1)
+            o[lo - P:hi - P, h, :] = (w @ Vx + wp @ Vp) / l[:, None]
+            lse[h, lo - P:hi - P] = m + np.log(l)
+    return o, lse
+
+
+def prefill(q: np.ndarray, k: np.ndarray, v: np.ndarray, B: int, tau: float,
+            c: Optional[float] = None, P: int = 0,
+            keep: Optional[np.ndarray] = None,
+            rows: Optional[Sequence[Tuple[int, int]]] = None,
+            with_output: bool = True) -> Dict[str, np.ndarray]:
+    """E1-E6 for one sequence.  keep overrides the oracle's own mask (used to
+    evaluate E6 under another, validated mask)."""
+    L, Hkv, d = k.shape
+    Hq = q.shape[1]
+    assert q.shape[0] == L - P and Hq % Hkv == 0 and v.shape == k.shape
+    G = Hq // Hkv
+    if c is None:
+        c = 1.0 / math.sqrt(d)
+    i0, nq = query_blocks(P, L, B)
+    qbar = pool_queries(q, B, P, L)
+    kbar = pool_keys(k, B)
+    vbar = pool_keys(v, B)
+    S = block_scores(qbar, kbar, c, i0)
+    own_keep, R = select(S, G, tau, i0)
+    out = dict(qbar=qbar, kbar=kbar, vbar=vbar, S=S, R=R, keep=own_keep, i0=i0, nq=nq)
+    if with_output:
+        use = own_keep if keep is None else keep
+        out["o"], out["lse"] = attend(q, k, v, use, kbar, vbar, c, B, P, rows=rows)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# bookkeeping used by reports (counts of blocks and FLOPs)
+# ---------------------------------------------------------------------------
+
+def threshold_margin(R: np.ndarray, tau: float) -> np.ndarray:
+    """|R + tau|: distance of each block's estimate to the threshold."""
+    return np.abs(R + tau)
+
+
+def causal_block_pairs(P: int, L: int, B: int) -> int:
+    i0, nq = query_blocks(P, L, B)
+    return sum(i0 + il + 1 for il in range(nq))
+
+
+def kept_fraction(keep: np.ndarray, P: int, L: int, B: int) -> float:
+    """Kept (g, i, j) block pairs over all causal block pairs of all KV heads."""
+    return float(keep.sum()) / (keep.shape[0] * causal_block_pairs(P, L, B))
+
+
+def _pairs(i: int, j: int, P: int, L: int, B: int) -> int:
+    lo, hi = max(i * B, P), min((i + 1) * B, L)
+    klo, khi = j * B, min((j + 1) * B, L)
+    if j < i:
+        return (hi - lo) * (khi - klo)
+    # diagonal: count s <= t
+    return sum(min(t, khi - 1) - klo + 1 for t in range(lo, hi))
+
+
+def dense_flops(P: int, L: int, d: int, Hq: int) -> float:
+    """4 d Hq sum_{present t} (t + 1): dense causal QK^T plus PV."""
+    n = L - P
+    return 4.0 * d * Hq * (n * (P + 1) + n * (n - 1) / 2.0)
+
+
+def kept_flops(keep: np.ndarray, P: int, L: int, B: int, d: int, G: int) -> float:
+    """4 d G sum over kept (g, i, j) of the causal (t, s) pairs in the block pair."""
+    i0, nq = query_blocks(P, L, B)
+    tot = 0
+    for g in range(keep.shape[0]):
+        for il in range(nq):
+            i = i0 + il
+            for j in np.nonzero(keep[g, il])[0]:
+                tot += _pairs(i, int(j), P, L, B)
+    return 4.0 * d * G * tot
+
+
+def correction_flops(keep: np.ndarray, P: int, L: int, B: int, d: int, G: int) -> float:
+    """4 d G sum over (g, i) of |I_i| * |pruned_i|."""
+    i0, nq = query_blocks(P, L, B)
+    tot = 0
+    for il in range(nq):
+        i = i0 + il
+        rows = min((i + 1) * B, L) - max(i * B, P)
+        npr = (i + 1) - keep[:, il, :i + 1].sum(axis=1)
+        tot += rows * int(npr.sum())
+    return 4.0 * d * G * tot
