@@ -1,0 +1,210 @@
+"""Block-sparse causal GQA prefill attention for AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI of libfp_prefill.so (include/fp_prefill.h):
+it builds the problem descriptors from torch tensors, allocates outputs with
+torch, and passes raw device pointers plus torch's current HIP stream. Every
+step of the method runs in the library's HIP kernels; there is no fallback.
+
+Entry points (same names as the C ABI):
+  fp_block_scores          pooling + block scores (E1-E2)
+  fp_select_blocks         max-based dynamic threshold -> CSR kept lists (E3-E5)
+  fp_sparse_prefill        sparse attention + mean correction (E6)
+  fp_sparse_prefill_paged  all of it for a paged varlen batch
+and sparse_prefill(), which chains the first three.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+import numpy as np
+import torch
+
+from . import _native as N
+from ._native import FpError, FpProblem, FpVarlenProblem
+
+__all__ = [
+    "FpError", "Problem", "make_problem", "fp_block_scores", "fp_select_blocks",
+    "fp_sparse_prefill", "fp_sparse_prefill_paged", "sparse_prefill", "version",
+    "make_varlen_problem",
+]
+
+
+def version() -> str:
+    return N.load().fp_version().decode()
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+@dataclass
+class Problem:
+    c: FpProblem
+    nb: int
+    rows: int
+    max_nnz: int
+    fp8: bool
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+def make_problem(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block: int,
+                 softmax_scale: float = 0.0, o: Optional[torch.Tensor] = None) -> Problem:
+    """Descriptor of a fixed-shape batch: q [batch, S, Hq, 128], k/v [batch, S, Hkv, 128]
+    (bf16, or uint8 E4M3FN codes), last dim contiguous."""
+    fp8 = q.dtype == torch.uint8
+    c = FpProblem()
+    c.batch, c.seqlen, c.num_q_heads, c.head_dim = q.shape[0], q.shape[1], q.shape[2], q.shape[3]
+    c.num_kv_heads = k.shape[2]
+    c.block = block
+    c.dtype = N.FP_DTYPE_FP8_E4M3 if fp8 else N.FP_DTYPE_BF16
+    c.softmax_scale = softmax_scale
+    for name, t in (("q_stride", q), ("k_stride", k), ("v_stride", v), ("o_stride", o if o is not None else q)):
+        st = t.stride()
+        if t.stride(-1) != 1:
+            raise FpError(N.FP_ERR_INVALID, f"{name[0]}: last dim must be contiguous")
+        arr = getattr(c, name)
+        arr[0], arr[1], arr[2] = st[0], st[1], st[2]
+    if o is None:
+        # o is allocated contiguous [batch, S, Hq, 128]
+        S, Hq, d = q.shape[1], q.shape[2], q.shape[3]
+        c.o_stride[0], c.o_stride[1], c.o_stride[2] = S * Hq * d, Hq * d, d
+    lib = N.load()
+    rows = N.check_size(lib.fp_num_rows(ctypes.byref(c)))
+    nnz = N.check_size(lib.fp_max_nnz(ctypes.byref(c)))
+    return Problem(c, (q.shape[1] + block - 1) // block, rows, nnz, fp8)
+
+
+def fp_block_scores(p: Problem, q, k, v, q_scale=None, k_scale=None, v_scale=None):
+    """E1-E2 -> (qbar, kbar, vbar, scores), fp32 device tensors."""
+    c = p.c
+    dev = q.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    qbar = torch.empty((c.batch, c.num_q_heads, p.nb, 128), **f32)
+    kbar = torch.empty((c.batch, c.num_kv_heads, p.nb, 128), **f32)
+    vbar = torch.empty((c.batch, c.num_kv_heads, p.nb, 128), **f32)
+    scores = torch.empty((c.batch, c.num_q_heads, p.nb, p.nb), **f32)
+    N.check(N.load().fp_block_scores(p.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(q_scale), _ptr(k_scale),
+                                     _ptr(v_scale), _ptr(qbar), _ptr(kbar), _ptr(vbar), _ptr(scores),
+                                     _stream()))
+    return qbar, kbar, vbar, scores
+
+
+def fp_select_blocks(p: Problem, scores: torch.Tensor, tau: float, with_sched: bool = True,
+                     workspace: Optional[torch.Tensor] = None):
+    """E3-E5 -> (row_ptr, col_idx, sched) int32 device tensors (col_idx has
+    capacity max_nnz; its first row_ptr[-1] entries are valid)."""
+    dev = scores.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    row_ptr = torch.empty(p.rows + 1, **i32)
+    col_idx = torch.empty(p.max_nnz, **i32)
+    sched = torch.empty(p.rows, **i32) if with_sched else None
+    lib = N.load()
+    ws_bytes = N.check_size(lib.fp_workspace_size(p.ref))
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    N.check(lib.fp_select_blocks(p.ref, _ptr(scores), float(tau), _ptr(row_ptr), _ptr(col_idx),
+                                 p.max_nnz, _ptr(sched), _ptr(workspace), workspace.numel(),
+                                 _stream()))
+    return row_ptr, col_idx, sched
+
+
+def fp_sparse_prefill(p: Problem, q, k, v, kbar, vbar, row_ptr, col_idx, sched=None,
+                      q_scale=None, k_scale=None, v_scale=None, with_lse: bool = True,
+                      o: Optional[torch.Tensor] = None):
+    """E6 -> (o bf16 like q, lse fp32 [batch, Hq, S] or None)."""
+    c = p.c
+    if o is None:
+        o = torch.empty((c.batch, c.seqlen, c.num_q_heads, 128), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((c.batch, c.num_q_heads, c.seqlen), dtype=torch.float32,
+                      device=q.device) if with_lse else None
+    N.check(N.load().fp_sparse_prefill(p.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(q_scale), _ptr(k_scale),
+                                       _ptr(v_scale), _ptr(kbar), _ptr(vbar), _ptr(row_ptr),
+                                       _ptr(col_idx), _ptr(sched), _ptr(o), _ptr(lse), _stream()))
+    return o, lse
+
+
+def sparse_prefill(q, k, v, block: int, tau: float, softmax_scale: float = 0.0,
+                   q_scale=None, k_scale=None, v_scale=None, with_lse: bool = True):
+    """All three stages on the current stream. Returns a dict of device tensors."""
+    p = make_problem(q, k, v, block, softmax_scale)
+    qbar, kbar, vbar, scores = fp_block_scores(p, q, k, v, q_scale, k_scale, v_scale)
+    row_ptr, col_idx, sched = fp_select_blocks(p, scores, tau)
+    o, lse = fp_sparse_prefill(p, q, k, v, kbar, vbar, row_ptr, col_idx, sched,
+                               q_scale, k_scale, v_scale, with_lse)
+    return dict(problem=p, qbar=qbar, kbar=kbar, vbar=vbar, scores=scores, row_ptr=row_ptr,
+                col_idx=col_idx, sched=sched, o=o, lse=lse)
+
+
+# ---------------------------------------------------------------------------
+# paged varlen
+# ---------------------------------------------------------------------------
+@dataclass
+class VarlenProblem:
+    c: FpVarlenProblem
+    cu: np.ndarray
+    lk: np.ndarray
+    rows: int
+    max_nnz: int
+    ws_bytes: int
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.c)
+
+    def host_ptrs(self):
+        return (self.cu.ctypes.data_as(ctypes.c_void_p), self.lk.ctypes.data_as(ctypes.c_void_p))
+
+
+def make_varlen_problem(q: torch.Tensor, cu_seqlens_q, seqlens_k, k_cache: torch.Tensor,
+                        block_table: torch.Tensor, block: int = 128,
+                        softmax_scale: float = 0.0) -> VarlenProblem:
+    c = FpVarlenProblem()
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens_q, dtype=np.int32))
+    lk = np.ascontiguousarray(np.asarray(seqlens_k, dtype=np.int32))
+    c.num_seqs = len(lk)
+    c.num_q_heads, c.head_dim = q.shape[1], q.shape[2]
+    c.num_kv_heads = k_cache.shape[2]
+    c.block = block
+    c.page_size = k_cache.shape[1]
+    c.dtype = N.FP_DTYPE_BF16
+    c.softmax_scale = softmax_scale
+    c.max_pages_per_seq = block_table.shape[1]
+    c.q_stride[0], c.q_stride[1] = q.stride(0), q.stride(1)
+    c.kv_stride[0], c.kv_stride[1], c.kv_stride[2] = k_cache.stride(0), k_cache.stride(1), k_cache.stride(2)
+    Hq = q.shape[1]
+    c.o_stride[0], c.o_stride[1] = Hq * 128, 128
+    lib = N.load()
+    cup, lkp = cu.ctypes.data_as(ctypes.c_void_p), lk.ctypes.data_as(ctypes.c_void_p)
+    rows = N.check_size(lib.fp_varlen_num_rows(ctypes.byref(c), cup, lkp))
+    nnz = N.check_size(lib.fp_varlen_max_nnz(ctypes.byref(c), cup, lkp))
+    ws = N.check_size(lib.fp_varlen_workspace_size(ctypes.byref(c), cup, lkp))
+    return VarlenProblem(c, cu, lk, rows, nnz, ws)
+
+
+def fp_sparse_prefill_paged(vp: VarlenProblem, q, k_cache, v_cache, block_table, tau: float,
+                            with_lse: bool = True, workspace: Optional[torch.Tensor] = None):
+    """E1-E6 on a paged varlen batch -> (o, lse, row_ptr, col_idx)."""
+    dev = q.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    row_ptr = torch.empty(vp.rows + 1, **i32)
+    col_idx = torch.empty(max(vp.max_nnz, 1), **i32)
+    o = torch.empty((q.shape[0], q.shape[1], 128), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=dev) if with_lse else None
+    if workspace is None:
+        workspace = torch.empty(vp.ws_bytes, dtype=torch.uint8, device=dev)
+    cup, lkp = vp.host_ptrs()
+    N.check(N.load().fp_sparse_prefill_paged(vp.ref, _ptr(q), cup, lkp, _ptr(k_cache), _ptr(v_cache),
+                                             _ptr(block_table), float(tau), _ptr(row_ptr),
+                                             _ptr(col_idx), vp.max_nnz, _ptr(o), _ptr(lse),
+                                             _ptr(workspace), workspace.numel(), _stream()))
+    return o, lse, row_ptr, col_idx

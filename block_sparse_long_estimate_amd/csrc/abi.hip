@@ -1,0 +1,473 @@
+// C ABI of the block-sparse prefill library (declared in include/fp_prefill.h).
+//
+// Host side only: argument validation (always before the first HIP call),
+// workspace sizing and carving, and launch sequencing on the caller's stream.
+// Nothing here allocates, frees or synchronises.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "../../include/fp_prefill.h"
+#include "fp_internal.h"
+
+using namespace fp;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = 0;
+    return FP_OK;
+}
+
+constexpr size_t ALIGN = 256;
+size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+float default_scale(float sc, int d) { return sc == 0.f ? 1.f / sqrtf((float)d) : sc; }
+
+int check_heads(int Hq, int Hkv, int d, int blk) {
+    if (Hq <= 0 || Hkv <= 0) return fail(FP_ERR_INVALID, "head counts must be positive (Hq=%d, Hkv=%d)", Hq, Hkv);
+    if (Hq % Hkv) return fail(FP_ERR_INVALID, "num_q_heads %% num_kv_heads != 0 (%d, %d)", Hq, Hkv);
+    if (Hq / Hkv > MAX_G) return fail(FP_ERR_UNSUPPORTED, "Hq/Hkv = %d exceeds %d", Hq / Hkv, MAX_G);
+    if (d != D) return fail(FP_ERR_UNSUPPORTED, "head_dim %d unsupported (only 128)", d);
+    if (blk != 64 && blk != 128) return fail(FP_ERR_UNSUPPORTED, "block %d unsupported (64 or 128)", blk);
+    return FP_OK;
+}
+
+int check_fixed(const fp_problem* p) {
+    if (!p) return fail(FP_ERR_INVALID, "problem is NULL");
+    int rc = check_heads(p->num_q_heads, p->num_kv_heads, p->head_dim, p->block);
+    if (rc) return rc;
+    if (p->batch <= 0 || p->seqlen <= 0) return fail(FP_ERR_INVALID, "batch and seqlen must be positive");
+    if (p->dtype != FP_DTYPE_BF16 && p->dtype != FP_DTYPE_FP8_E4M3)
+        return fail(FP_ERR_UNSUPPORTED, "dtype %d unsupported", p->dtype);
+    if (!(p->softmax_scale >= 0.f) || isinf(p->softmax_scale))
+        return fail(FP_ERR_INVALID, "softmax_scale must be finite and >= 0");
+    const int nb = cdiv(p->seqlen, p->block);
+    if (nb > MAX_NB) return fail(FP_ERR_UNSUPPORTED, "%d blocks per sequence exceed %d", nb, MAX_NB);
+    const long long rows = (long long)p->batch * p->num_kv_heads * nb;
+    if ((long long)p->batch * nb * p->num_q_heads * nb > (1LL << 40) || rows > (1LL << 30))
+        return fail(FP_ERR_UNSUPPORTED, "problem too large");
+    const int64_t* st[4] = {p->q_stride, p->k_stride, p->v_stride, p->o_stride};
+    for (int t = 0; t < 4; ++t)
+        for (int e = 0; e < 3; ++e)
+            if (st[t][e] < 0) return fail(FP_ERR_INVALID, "negative stride");
+    const int esz = p->dtype == FP_DTYPE_BF16 ? 2 : 1;
+    // 16-byte vector loads of whole rows need 16-byte aligned row starts
+    for (int t = 0; t < 3; ++t)
+        for (int e = 0; e < 3; ++e)
+            if ((st[t][e] * esz) % 16) return fail(FP_ERR_INVALID, "strides must be multiples of 16 bytes");
+    for (int e = 0; e < 3; ++e)
+        if ((p->o_stride[e] * 2) % 8) return fail(FP_ERR_INVALID, "o strides must be multiples of 8 bytes");
+    return FP_OK;
+}
+
+GeoFixed geo_fixed(const fp_problem* p) {
+    GeoFixed g;
+    g.nseq = p->batch;
+    g.S = p->seqlen;
+    g.Hq = p->num_q_heads;
+    g.Hkv = p->num_kv_heads;
+    g.blk = p->block;
+    g.nb = cdiv(p->seqlen, p->block);
+    g.ntile = score_tiles(g.nb, g.nb);
+    return g;
+}
+
+bool misaligned(const void* ptr, size_t a) { return ((uintptr_t)ptr) % a != 0; }
+
+struct SelectWs {
+    size_t counts, bits, total;
+    int nbw;
+};
+
+SelectWs select_ws(long long rows, int max_nbk) {
+    SelectWs w;
+    w.nbw = cdiv(max_nbk, 32) + 1;
+    w.counts = 0;
+    w.bits = align_up((size_t)rows * 4);
+    w.total = w.bits + align_up((size_t)rows * w.nbw * 4);
+    return w;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// descriptor-table copy: the table rides in kernel arguments (by value), so no
+// host buffer has to outlive the call and no memcpy is queued
+// ---------------------------------------------------------------------------
+namespace fp {
+constexpr int TABLE_CHUNK = 64;
+struct TableChunk {
+    SeqDesc e[TABLE_CHUNK];
+};
+__global__ void table_copy_kernel(TableChunk c, int n, SeqDesc* dst) {
+    const int t = threadIdx.x;
+    if (t < n) dst[t] = c.e[t];
+}
+hipError_t launch_table_copy(const SeqDesc* host, int n, SeqDesc* dev, hipStream_t st) {
+    for (int base = 0; base < n; base += TABLE_CHUNK) {
+        TableChunk c;
+        const int m = std::min(TABLE_CHUNK, n - base);
+        memcpy(c.e, host + base, sizeof(SeqDesc) * m);
+        table_copy_kernel<<<1, TABLE_CHUNK, 0, st>>>(c, m, dev + base);
+    }
+    return hipGetLastError();
+}
+}  // namespace fp
+
+extern "C" {
+
+const char* fp_version(void) { return "fp_prefill 0.1.0 (gfx950)"; }
+const char* fp_last_error(void) { return g_err; }
+
+int64_t fp_num_rows(const fp_problem* p) {
+    int rc = check_fixed(p);
+    if (rc) return rc;
+    return (int64_t)p->batch * p->num_kv_heads * cdiv(p->seqlen, p->block);
+}
+
+int64_t fp_max_nnz(const fp_problem* p) {
+    int rc = check_fixed(p);
+    if (rc) return rc;
+    const int64_t nb = cdiv(p->seqlen, p->block);
+    return (int64_t)p->batch * p->num_kv_heads * nb * (nb + 1) / 2;
+}
+
+int64_t fp_workspace_size(const fp_problem* p) {
+    int rc = check_fixed(p);
+    if (rc) return rc;
+    const int nb = cdiv(p->seqlen, p->block);
+    return (int64_t)select_ws((long long)p->batch * p->num_kv_heads * nb, nb).total;
+}
+
+int fp_block_scores(const fp_problem* p, const void* q, const void* k, const void* v,
+                    const float* q_scale, const float* k_scale, const float* v_scale,
+                    float* qbar, float* kbar, float* vbar, float* scores, void* stream) {
+    int rc = check_fixed(p);
+    if (rc) return rc;
+    if (!q || !k || !v || !qbar || !kbar || !vbar || !scores)
+        return fail(FP_ERR_INVALID, "fp_block_scores: NULL tensor pointer");
+    const bool fp8 = p->dtype == FP_DTYPE_FP8_E4M3;
+    if (fp8 && (!q_scale || !k_scale || !v_scale))
+        return fail(FP_ERR_INVALID, "fp_block_scores: fp8 needs q_scale, k_scale and v_scale");
+    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(qbar, 16) ||
+        misaligned(kbar, 16) || misaligned(vbar, 16))
+        return fail(FP_ERR_INVALID, "fp_block_scores: tensors must be 16-byte aligned");
+    GeoFixed geo = geo_fixed(p);
+    const int nsb = cdiv(p->seqlen, SCALE_TOK);
+    PoolArgs a;
+    a.q = q; a.k = k; a.v = v;
+    a.qa = RowAddr{p->q_stride[0], p->q_stride[1], p->q_stride[2]};
+    a.ka = KVAddr{p->k_stride[0], p->k_stride[1], p->k_stride[2], 0, nullptr, 0, 0};
+    a.va = KVAddr{p->v_stride[0], p->v_stride[1], p->v_stride[2], 0, nullptr, 0, 0};
+    a.qs = ScaleAddr{q_scale, (long long)p->num_q_heads * nsb, nsb};
+    a.ks = ScaleAddr{k_scale, (long long)p->num_kv_heads * nsb, nsb};
+    a.vs = ScaleAddr{v_scale, (long long)p->num_kv_heads * nsb, nsb};
+    a.qbar = qbar; a.kbar = kbar; a.vbar = vbar;
+    a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads; a.blk = p->block;
+    a.fp8 = fp8; a.paged = 0;
+    a.total_qblocks = a.total_kblocks = p->batch * geo.nb;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = launch_pool(&geo, nullptr, a, st);
+    if (e != hipSuccess) return fail(FP_ERR_HIP, "pool launch: %s", hipGetErrorString(e));
+    ScoreArgs sa;
+    sa.qbar = qbar; sa.kbar = kbar; sa.scores = scores;
+    sa.Hq = p->num_q_heads; sa.Hkv = p->num_kv_heads;
+    sa.total_tiles = p->batch * geo.ntile;
+    sa.scale = default_scale(p->softmax_scale, p->head_dim);
+    e = launch_scores(&geo, nullptr, sa, st);
+    if (e != hipSuccess) return fail(FP_ERR_HIP, "scores launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int fp_select_blocks(const fp_problem* p, const float* scores, float tau, int32_t* row_ptr,
+                     int32_t* col_idx, int64_t capacity, int32_t* sched, void* workspace,
+                     size_t ws_bytes, void* stream) {
+    int rc = check_fixed(p);
+    if (rc) return rc;
+    if (!scores || !row_ptr || !col_idx || !workspace)
+        return fail(FP_ERR_INVALID, "fp_select_blocks: NULL pointer");
+    if (isnan(tau)) return fail(FP_ERR_INVALID, "fp_select_blocks: tau is NaN");
+    const int nb = cdiv(p->seqlen, p->block);
+    const long long rows = (long long)p->batch * p->num_kv_heads * nb;
+    const long long need = rows * (nb + 1) / 2;
+    if (capacity < need)
+        return fail(FP_ERR_CAPACITY, "fp_select_blocks: capacity %lld < max nnz %lld", (long long)capacity, need);
+    const SelectWs w = select_ws(rows, nb);
+    if (ws_bytes < w.total)
+        return fail(FP_ERR_CAPACITY, "fp_select_blocks: workspace %zu < %zu bytes", ws_bytes, w.total);
+    if (misaligned(workspace, ALIGN)) return fail(FP_ERR_INVALID, "workspace must be 256-byte aligned");
+    GeoFixed geo = geo_fixed(p);
+    SelectArgs a;
+    a.scores = scores;
+    a.counts = (int32_t*)((char*)workspace + w.counts);
+    a.bits = (uint32_t*)((char*)workspace + w.bits);
+    a.nbw = w.nbw;
+    a.row_ptr = row_ptr; a.col_idx = col_idx; a.sched = sched;
+    a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads;
+    a.rows = (int)rows; a.max_nbk = nb;
+    a.neg_tau = -tau;
+    hipError_t e = launch_select(&geo, nullptr, a, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(FP_ERR_HIP, "select launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int fp_sparse_prefill(const fp_problem* p, const void* q, const void* k, const void* v,
+                      const float* q_scale, const float* k_scale, const float* v_scale,
+                      const float* kbar, const float* vbar, const int32_t* row_ptr,
+                      const int32_t* col_idx, const int32_t* sched, void* o, float* lse,
+                      void* stream) {
+    int rc = check_fixed(p);
+    if (rc) return rc;
+    if (!q || !k || !v || !kbar || !vbar || !row_ptr || !col_idx || !o)
+        return fail(FP_ERR_INVALID, "fp_sparse_prefill: NULL pointer");
+    const bool fp8 = p->dtype == FP_DTYPE_FP8_E4M3;
+    if (fp8 && (!q_scale || !k_scale || !v_scale))
+        return fail(FP_ERR_INVALID, "fp_sparse_prefill: fp8 needs q_scale, k_scale and v_scale");
+    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(kbar, 16) ||
+        misaligned(vbar, 16) || misaligned(o, 8))
+        return fail(FP_ERR_INVALID, "fp_sparse_prefill: misaligned tensor");
+    GeoFixed geo = geo_fixed(p);
+    const int nsb = cdiv(p->seqlen, SCALE_TOK);
+    const int G = p->num_q_heads / p->num_kv_heads;
+    AttnArgs a;
+    a.q = q; a.k = k; a.v = v;
+    a.qa = RowAddr{p->q_stride[0], p->q_stride[1], p->q_stride[2]};
+    a.oa = RowAddr{p->o_stride[0], p->o_stride[1], p->o_stride[2]};
+    a.ka = KVAddr{p->k_stride[0], p->k_stride[1], p->k_stride[2], 0, nullptr, 0, 0};
+    a.va = KVAddr{p->v_stride[0], p->v_stride[1], p->v_stride[2], 0, nullptr, 0, 0};
+    a.qs = ScaleAddr{q_scale, (long long)p->num_q_heads * nsb, nsb};
+    a.ks = ScaleAddr{k_scale, (long long)p->num_kv_heads * nsb, nsb};
+    a.vs = ScaleAddr{v_scale, (long long)p->num_kv_heads * nsb, nsb};
+    a.kbar = kbar; a.vbar = vbar;
+    a.row_ptr = row_ptr; a.col_idx = col_idx; a.sched = sched;
+    a.o = o; a.lse = lse;
+    a.la = RowAddr{(long long)p->num_q_heads * p->seqlen, 1, p->seqlen};
+    a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads; a.G = G;
+    a.rows = p->batch * p->num_kv_heads * geo.nb;
+    a.slices = cdiv(G * p->block, 128);
+    a.scale_log2 = default_scale(p->softmax_scale, p->head_dim) * 1.4426950408889634f;
+    hipError_t e = launch_attn(&geo, nullptr, a, p->block, fp8, 0, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(FP_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+// ---------------------------------------------------------------------------
+// paged varlen
+// ---------------------------------------------------------------------------
+namespace {
+
+struct VarPlan {
+    std::vector<SeqDesc> table;      // nseq + 1 (last: totals)
+    long long rows = 0, max_nnz = 0, sum_q = 0;
+    int max_nbk = 0, total_qblocks = 0, total_kblocks = 0, total_tiles = 0;
+    long long total_scores = 0;
+    // workspace carve (byte offsets)
+    size_t o_table = 0, o_qbar = 0, o_kbar = 0, o_vbar = 0, o_scores = 0, o_sched = 0, o_sel = 0, total = 0;
+    SelectWs sel;
+};
+
+int check_varlen(const fp_varlen_problem* p, const int32_t* cu, const int32_t* lk, VarPlan& plan) {
+    if (!p) return fail(FP_ERR_INVALID, "problem is NULL");
+    int rc = check_heads(p->num_q_heads, p->num_kv_heads, p->head_dim, p->block);
+    if (rc) return rc;
+    if (p->num_seqs <= 0 || p->num_seqs > 4096) return fail(FP_ERR_INVALID, "num_seqs must be in [1, 4096]");
+    if (p->dtype != FP_DTYPE_BF16) return fail(FP_ERR_UNSUPPORTED, "paged path supports bf16 only");
+    if (p->page_size < 16 || p->page_size > 256 || (p->page_size & (p->page_size - 1)))
+        return fail(FP_ERR_UNSUPPORTED, "page_size %d unsupported (power of two in [16, 256])", p->page_size);
+    if (p->max_pages_per_seq <= 0) return fail(FP_ERR_INVALID, "max_pages_per_seq must be positive");
+    if (!(p->softmax_scale >= 0.f) || isinf(p->softmax_scale))
+        return fail(FP_ERR_INVALID, "softmax_scale must be finite and >= 0");
+    if (!cu || !lk) return fail(FP_ERR_INVALID, "cu_seqlens_q and seqlens_k (host arrays) are required");
+    if (cu[0] != 0) return fail(FP_ERR_INVALID, "cu_seqlens_q[0] must be 0");
+    for (int e = 0; e < 2; ++e)
+        if (p->q_stride[e] < 0 || p->o_stride[e] < 0) return fail(FP_ERR_INVALID, "negative stride");
+    for (int e = 0; e < 3; ++e)
+        if (p->kv_stride[e] < 0 || (p->kv_stride[e] * 2) % 16) return fail(FP_ERR_INVALID, "bad kv stride");
+    if ((p->q_stride[0] * 2) % 16 || (p->q_stride[1] * 2) % 16 || (p->o_stride[0] * 2) % 8 || (p->o_stride[1] * 2) % 8)
+        return fail(FP_ERR_INVALID, "q/o strides must be multiples of 16/8 bytes");
+    const int B = p->block;
+    plan.table.assign(p->num_seqs + 1, SeqDesc{});
+    long long qb = 0, kb = 0, tiles = 0, sc = 0;
+    for (int b = 0; b < p->num_seqs; ++b) {
+        const int ql = cu[b + 1] - cu[b];
+        const int L = lk[b];
+        if (ql < 0) return fail(FP_ERR_INVALID, "cu_seqlens_q not non-decreasing at %d", b);
+        if (L < ql) return fail(FP_ERR_INVALID, "seqlens_k[%d] = %d < q_len %d", b, L, ql);
+        const int nbk = cdiv(L, B);
+        if (nbk > MAX_NB) return fail(FP_ERR_UNSUPPORTED, "sequence %d has %d blocks (max %d)", b, nbk, MAX_NB);
+        if ((long long)cdiv(L, p->page_size) > p->max_pages_per_seq)
+            return fail(FP_ERR_INVALID, "sequence %d needs %d pages > max_pages_per_seq", b, cdiv(L, p->page_size));
+        SeqDesc& s = plan.table[b];
+        s.L = L;
+        s.P = L - ql;
+        s.i0 = ql ? s.P / B : 0;
+        s.nq = ql ? (L - 1) / B - s.i0 + 1 : 0;
+        s.nbk = ql ? nbk : 0;      // a sequence with no new rows needs no pooled keys
+        s.q0 = cu[b];
+        s.qb0 = (int)qb;
+        s.kb0 = (int)kb;
+        s.row0 = (int)(qb * p->num_kv_heads);
+        s.tile0 = (int)tiles;
+        s.sc0 = sc;
+        for (int il = 0; il < s.nq; ++il) plan.max_nnz += (long long)p->num_kv_heads * (s.i0 + il + 1);
+        plan.max_nbk = std::max(plan.max_nbk, s.nbk);
+        qb += s.nq;
+        kb += s.nbk;
+        tiles += ql ? score_tiles(s.nq, s.nbk) : 0;
+        sc += (long long)p->num_q_heads * s.nq * s.nbk;
+        plan.sum_q += ql;
+    }
+    SeqDesc& e = plan.table[p->num_seqs];
+    e.qb0 = (int)qb; e.kb0 = (int)kb; e.row0 = (int)(qb * p->num_kv_heads); e.tile0 = (int)tiles; e.sc0 = sc;
+    if (qb > (1 << 28) || kb > (1 << 28) || sc > (1LL << 40)) return fail(FP_ERR_UNSUPPORTED, "batch too large");
+    plan.rows = qb * p->num_kv_heads;
+    plan.total_qblocks = (int)qb;
+    plan.total_kblocks = (int)kb;
+    plan.total_tiles = (int)tiles;
+    plan.total_scores = sc;
+    size_t off = 0;
+    plan.o_table = off; off = align_up(off + sizeof(SeqDesc) * (p->num_seqs + 1));
+    plan.o_qbar = off; off = align_up(off + (size_t)qb * p->num_q_heads * D * 4);
+    plan.o_kbar = off; off = align_up(off + (size_t)kb * p->num_kv_heads * D * 4);
+    plan.o_vbar = off; off = align_up(off + (size_t)kb * p->num_kv_heads * D * 4);
+    plan.o_scores = off; off = align_up(off + (size_t)sc * 4);
+    plan.o_sched = off; off = align_up(off + (size_t)plan.rows * 4);
+    plan.sel = select_ws(plan.rows, std::max(plan.max_nbk, 1));
+    plan.o_sel = off; off += plan.sel.total;
+    plan.total = off;
+    return FP_OK;
+}
+
+}  // namespace
+
+int64_t fp_varlen_num_rows(const fp_varlen_problem* p, const int32_t* cu, const int32_t* lk) {
+    VarPlan plan;
+    int rc = check_varlen(p, cu, lk, plan);
+    return rc ? rc : plan.rows;
+}
+
+int64_t fp_varlen_max_nnz(const fp_varlen_problem* p, const int32_t* cu, const int32_t* lk) {
+    VarPlan plan;
+    int rc = check_varlen(p, cu, lk, plan);
+    return rc ? rc : plan.max_nnz;
+}
+
+int64_t fp_varlen_workspace_size(const fp_varlen_problem* p, const int32_t* cu, const int32_t* lk) {
+    VarPlan plan;
+    int rc = check_varlen(p, cu, lk, plan);
+    return rc ? rc : (int64_t)plan.total;
+}
+
+int fp_sparse_prefill_paged(const fp_varlen_problem* p, const void* q, const int32_t* cu,
+                            const int32_t* lk, const void* k_cache, const void* v_cache,
+                            const int32_t* block_table, float tau, int32_t* row_ptr,
+                            int32_t* col_idx, int64_t capacity, void* o, float* lse,
+                            void* workspace, size_t ws_bytes, void* stream) {
+    VarPlan plan;
+    int rc = check_varlen(p, cu, lk, plan);
+    if (rc) return rc;
+    if (!q || !k_cache || !v_cache || !block_table || !row_ptr || !col_idx || !o || !workspace)
+        return fail(FP_ERR_INVALID, "fp_sparse_prefill_paged: NULL pointer");
+    if (isnan(tau)) return fail(FP_ERR_INVALID, "fp_sparse_prefill_paged: tau is NaN");
+    if (capacity < plan.max_nnz)
+        return fail(FP_ERR_CAPACITY, "fp_sparse_prefill_paged: capacity %lld < max nnz %lld",
+                    (long long)capacity, plan.max_nnz);
+    if (ws_bytes < plan.total)
+        return fail(FP_ERR_CAPACITY, "fp_sparse_prefill_paged: workspace %zu < %zu bytes", ws_bytes, plan.total);
+    if (misaligned(workspace, ALIGN)) return fail(FP_ERR_INVALID, "workspace must be 256-byte aligned");
+    if (misaligned(q, 16) || misaligned(k_cache, 16) || misaligned(v_cache, 16) || misaligned(o, 8))
+        return fail(FP_ERR_INVALID, "fp_sparse_prefill_paged: misaligned tensor");
+    if (plan.rows == 0) return ok();
+
+    char* ws = (char*)workspace;
+    SeqDesc* dtable = (SeqDesc*)(ws + plan.o_table);
+    float* qbar = (float*)(ws + plan.o_qbar);
+    float* kbar = (float*)(ws + plan.o_kbar);
+    float* vbar = (float*)(ws + plan.o_vbar);
+    float* scores = (float*)(ws + plan.o_scores);
+    int32_t* sched = (int32_t*)(ws + plan.o_sched);
+    char* selws = ws + plan.o_sel;
+    hipStream_t st = (hipStream_t)stream;
+
+    GeoTable geo;
+    geo.t = dtable;
+    geo.nseq = p->num_seqs;
+    geo.Hq = p->num_q_heads;
+    geo.Hkv = p->num_kv_heads;
+    geo.blk = p->block;
+    int shift = 0;
+    while ((1 << shift) < p->page_size) ++shift;
+    const KVAddr kva{0, p->kv_stride[1], p->kv_stride[2], p->kv_stride[0], block_table,
+                     p->max_pages_per_seq, shift};
+
+    hipError_t e = launch_table_copy(plan.table.data(), p->num_seqs + 1, dtable, st);
+    if (e != hipSuccess) return fail(FP_ERR_HIP, "table copy: %s", hipGetErrorString(e));
+
+    PoolArgs pa;
+    pa.q = q; pa.k = k_cache; pa.v = v_cache;
+    pa.qa = RowAddr{0, p->q_stride[0], p->q_stride[1]};
+    pa.ka = kva; pa.va = kva;
+    pa.qs = pa.ks = pa.vs = ScaleAddr{nullptr, 0, 0};
+    pa.qbar = qbar; pa.kbar = kbar; pa.vbar = vbar;
+    pa.Hq = p->num_q_heads; pa.Hkv = p->num_kv_heads; pa.blk = p->block;
+    pa.fp8 = 0; pa.paged = 1;
+    pa.total_qblocks = plan.total_qblocks; pa.total_kblocks = plan.total_kblocks;
+    e = launch_pool(nullptr, &geo, pa, st);
+    if (e != hipSuccess) return fail(FP_ERR_HIP, "pool launch: %s", hipGetErrorString(e));
+
+    ScoreArgs sa;
+    sa.qbar = qbar; sa.kbar = kbar; sa.scores = scores;
+    sa.Hq = p->num_q_heads; sa.Hkv = p->num_kv_heads;
+    sa.total_tiles = plan.total_tiles;
+    sa.scale = default_scale(p->softmax_scale, p->head_dim);
+    e = launch_scores(nullptr, &geo, sa, st);
+    if (e != hipSuccess) return fail(FP_ERR_HIP, "scores launch: %s", hipGetErrorString(e));
+
+    SelectArgs se;
+    se.scores = scores;
+    se.counts = (int32_t*)(selws + plan.sel.counts);
+    se.bits = (uint32_t*)(selws + plan.sel.bits);
+    se.nbw = plan.sel.nbw;
+    se.row_ptr = row_ptr; se.col_idx = col_idx; se.sched = sched;
+    se.Hq = p->num_q_heads; se.Hkv = p->num_kv_heads;
+    se.rows = (int)plan.rows; se.max_nbk = std::max(plan.max_nbk, 1);
+    se.neg_tau = -tau;
+    e = launch_select(nullptr, &geo, se, st);
+    if (e != hipSuccess) return fail(FP_ERR_HIP, "select launch: %s", hipGetErrorString(e));
+
+    const int G = p->num_q_heads / p->num_kv_heads;
+    AttnArgs a;
+    a.q = q; a.k = k_cache; a.v = v_cache;
+    a.qa = RowAddr{0, p->q_stride[0], p->q_stride[1]};
+    a.oa = RowAddr{0, p->o_stride[0], p->o_stride[1]};
+    a.ka = kva; a.va = kva;
+    a.qs = a.ks = a.vs = ScaleAddr{nullptr, 0, 0};
+    a.kbar = kbar; a.vbar = vbar;
+    a.row_ptr = row_ptr; a.col_idx = col_idx; a.sched = sched;
+    a.o = o; a.lse = lse;
+    a.la = RowAddr{0, 1, plan.sum_q};
+    a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads; a.G = G;
+    a.rows = (int)plan.rows;
+    a.slices = cdiv(G * p->block, 128);
+    a.scale_log2 = default_scale(p->softmax_scale, p->head_dim) * 1.4426950408889634f;
+    e = launch_attn(nullptr, &geo, a, p->block, 0, 1, st);
+    if (e != hipSuccess) return fail(FP_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,171 @@
+// Internal declarations shared by the HIP kernels and the C-ABI host code.
+// gfx950 (CDNA4) only: wave64, MFMA, 160 KiB LDS per CU.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp {
+
+constexpr int D = 128;            // head dim
+constexpr int MAX_G = 16;         // query heads per KV head
+constexpr int MAX_NB = 16384;     // key blocks per sequence
+constexpr int SCALE_TOK = 128;    // tokens per fp8 scale
+
+// ---------------------------------------------------------------------------
+// Sequence geometry. Blocks live on the absolute-position grid of each
+// sequence: query block i covers present rows [max(iB, P), min((i+1)B, L)),
+// key block j covers [jB, min((j+1)B, L)).
+// ---------------------------------------------------------------------------
+struct SeqDesc {
+    int L;        // keys (cache + new chunk)
+    int P;        // cached prefix (first present query row)
+    int i0;       // first query block
+    int nq;       // query blocks
+    int nbk;      // key blocks
+    int q0;       // packed row of token P in q / o / lse (varlen); 0 for fixed
+    int qb0;      // query blocks of earlier sequences (pooled-Q offset)
+    int kb0;      // key blocks of earlier sequences (pooled-K/V offset)
+    int row0;     // kept-list rows of earlier sequences (= Hkv * qb0)
+    int tile0;    // score tiles of earlier sequences
+    long long sc0;  // score-matrix elements of earlier sequences
+};
+
+constexpr int SC_TILE = 64;       // score tile edge (query blocks x key blocks)
+
+__host__ __device__ inline int cdiv(int a, int b) { return (a + b - 1) / b; }
+__host__ __device__ inline int score_tiles(int nq, int nbk) {
+    return cdiv(nq, SC_TILE) * cdiv(nbk, SC_TILE);
+}
+
+// Fixed shape: every sequence has S tokens and no prefix. Everything is
+// arithmetic; no table in memory.
+struct GeoFixed {
+    int nseq, S, Hq, Hkv, blk, nb, ntile;
+    __device__ __forceinline__ SeqDesc seq(int b) const {
+        SeqDesc s;
+        s.L = S; s.P = 0; s.i0 = 0; s.nq = nb; s.nbk = nb; s.q0 = 0;
+        s.qb0 = b * nb; s.kb0 = b * nb; s.row0 = b * Hkv * nb; s.tile0 = b * ntile;
+        s.sc0 = (long long)b * Hq * nb * nb;
+        return s;
+    }
+    __device__ __forceinline__ int seq_of_qblock(int u) const { return u / nb; }
+    __device__ __forceinline__ int seq_of_kblock(int u) const { return u / nb; }
+    __device__ __forceinline__ int seq_of_row(int r) const { return r / (Hkv * nb); }
+    __device__ __forceinline__ int seq_of_tile(int u) const { return u / ntile; }
+};
+
+// Varlen: a table of nseq descriptors in device memory, entry nseq holding
+// the running totals (qb0, kb0, row0, tile0, sc0) past the last sequence.
+struct GeoTable {
+    const SeqDesc* t;
+    int nseq, Hq, Hkv, blk;
+    __device__ __forceinline__ SeqDesc seq(int b) const { return t[b]; }
+    // largest b in [0, nseq) with field(b) <= u (empty sequences share the
+    // next one's offset, so ties resolve to the last, non-empty, one)
+#define FP_SEARCH(FIELD)                                              \
+    int lo = 0, hi = nseq;                                            \
+    while (hi - lo > 1) {                                             \
+        int mid = (lo + hi) >> 1;                                     \
+        if (t[mid].FIELD <= u) lo = mid; else hi = mid;               \
+    }                                                                 \
+    return lo;
+    __device__ __forceinline__ int seq_of_qblock(int u) const { FP_SEARCH(qb0) }
+    __device__ __forceinline__ int seq_of_kblock(int u) const { FP_SEARCH(kb0) }
+    __device__ __forceinline__ int seq_of_row(int r) const { int u = r; FP_SEARCH(row0) }
+    __device__ __forceinline__ int seq_of_tile(int u) const { FP_SEARCH(tile0) }
+#undef FP_SEARCH
+};
+
+// Token addressing (element offsets; the head dim is contiguous).
+// q / o / lse rows: b * sb + (q0 + t - P) * st + h * sh   (varlen: sb = 0)
+struct RowAddr {
+    long long sb, st, sh;
+    __device__ __forceinline__ long long off(int b, const SeqDesc& s, int t, int h) const {
+        return (long long)b * sb + (long long)(s.q0 + t - s.P) * st + (long long)h * sh;
+    }
+};
+
+// k / v: contiguous  b * sb + s * st + g * sh
+//        paged       table[b * maxp + s / page] * spage + (s % page) * st + g * sh
+struct KVAddr {
+    long long sb, st, sh, spage;
+    const int* table;
+    int maxp, page_shift;
+    template <bool PAGED>
+    __device__ __forceinline__ long long off(int b, int s, int g) const {
+        if (PAGED) {
+            int pg = table[(long long)b * maxp + (s >> page_shift)];
+            return (long long)pg * spage + (long long)(s & ((1 << page_shift) - 1)) * st +
+                   (long long)g * sh;
+        }
+        return (long long)b * sb + (long long)s * st + (long long)g * sh;
+    }
+};
+
+// Pooled tensors: Qbar [qb0*Hq + h*nq + il], Kbar/Vbar [kb0*Hkv + g*nbk + j], rows of D floats.
+__device__ __forceinline__ long long qbar_row(const SeqDesc& s, int Hq, int h, int il) {
+    return (long long)s.qb0 * Hq + (long long)h * s.nq + il;
+}
+__device__ __forceinline__ long long kbar_row(const SeqDesc& s, int Hkv, int g, int j) {
+    return (long long)s.kb0 * Hkv + (long long)g * s.nbk + j;
+}
+// Scores: [sc0 + (h*nq + il) * nbk + j]
+__device__ __forceinline__ long long score_off(const SeqDesc& s, int h, int il, int j) {
+    return s.sc0 + ((long long)h * s.nq + il) * s.nbk + j;
+}
+
+// fp8 scales: [b][H][nsb] with nsb = scale_stride_h, b stride = scale_stride_b
+struct ScaleAddr {
+    const float* p;
+    long long sb, sh;
+    __device__ __forceinline__ float at(int b, int h, int t) const {
+        return p[(long long)b * sb + (long long)h * sh + (t >> 7)];
+    }
+};
+
+// ---------------------------------------------------------------------------
+// launchers (defined in the .hip files); all return hipError_t of the launch
+// ---------------------------------------------------------------------------
+struct PoolArgs {
+    const void* q; const void* k; const void* v;
+    RowAddr qa; KVAddr ka, va;
+    ScaleAddr qs, ks, vs;
+    float* qbar; float* kbar; float* vbar;
+    int Hq, Hkv, blk, fp8, paged;
+    int total_qblocks, total_kblocks;
+};
+
+struct ScoreArgs {
+    const float* qbar; const float* kbar; float* scores;
+    int Hq, Hkv, total_tiles;
+    float scale;
+};
+
+struct SelectArgs {
+    const float* scores;
+    int32_t* counts; uint32_t* bits; int nbw;   // bitmask row stride (u32 words)
+    int32_t* row_ptr; int32_t* col_idx; int32_t* sched;
+    int Hq, Hkv, rows, max_nbk;
+    float neg_tau;
+};
+
+struct AttnArgs {
+    const void* q; const void* k; const void* v;
+    RowAddr qa, oa; KVAddr ka, va;
+    ScaleAddr qs, ks, vs;
+    const float* kbar; const float* vbar;
+    const int32_t* row_ptr; const int32_t* col_idx; const int32_t* sched;
+    void* o; float* lse; RowAddr la;   // lse offset: b*sb + (q0+t-P)*st + h*sh
+    int Hq, Hkv, G, rows, slices;
+    float scale_log2;                  // c * log2(e)
+};
+
+hipError_t launch_pool(const GeoFixed* gf, const GeoTable* gt, const PoolArgs& a, hipStream_t st);
+hipError_t launch_scores(const GeoFixed* gf, const GeoTable* gt, const ScoreArgs& a, hipStream_t st);
+hipError_t launch_select(const GeoFixed* gf, const GeoTable* gt, const SelectArgs& a, hipStream_t st);
+hipError_t launch_attn(const GeoFixed* gf, const GeoTable* gt, const AttnArgs& a, int blk,
+                       int fp8, int paged, hipStream_t st);
+hipError_t launch_table_copy(const SeqDesc* host, int n, SeqDesc* dev, hipStream_t st);
+
+}  // namespace fp

@@ -1,0 +1,531 @@
+// Sparse attention over the kept blocks plus the mean-correction pseudo-tokens
+// (E6), bf16 and fp8-e4m3 inputs, contiguous or paged K/V.
+//
+// The pages describe a sparse flash-attention operator over the kept blocks
+// (lode.cx page, implementation paragraph; aimodeling.com page, "Operator
+// alignment" bullet) and a mean correction for the pruned blocks (lode.cx
+// page, "How It Works"; aimodeling.com page, "Error correction" bullet). The
+// H20 design they name (PackGQA, warp specialisation, pingpong) is prior art;
+// this is a gfx950 design:
+//
+//  * Work unit = (kept-list row, 128-row slice). A row is (sequence, KV head
+//    g, query block i); its G query heads share the row's list, so the slice
+//    packs token-major rows (token, head) of all G heads into one M tile
+//    (the PackGQA idea: one K/V tile load serves G heads).
+//  * 4 wavefronts x 32 packed query rows. S^T = K Q^T and O^T = V^T P^T on
+//    v_mfma_f32_32x32x16_bf16, so each lane owns one query row: row max and
+//    row sum are lane-local plus one exchange with lane^32, and the
+//    accumulator rescale is a per-lane scalar.
+//  * P never leaves registers: the PV contraction order over the 16 keys of
+//    each MFMA step is chosen to be exactly the order in which the QK^T
+//    accumulator already holds them, and V^T is written to LDS in that same
+//    key order (key bits 2 and 3 swapped) while it is transposed.
+//  * The kept-tile loop is followed by summary tiles: the pooled keys of the
+//    pruned blocks (fp32, split hi+lo into two bf16 MFMAs so the logit keeps
+//    ~16 mantissa bits) with bias ln|block|, pooled values in bf16. Kept,
+//    future and sink/diagonal pooled columns are masked out.
+//  * Units run heavy-row-first (sched), each row's slices on one XCD (unit
+//    u goes to XCD u % 8) so they share that XCD's L2 copy of the K/V tiles.
+#include "fp_internal.h"
+
+namespace fp {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+__device__ __forceinline__ int vt_slot(int key) {
+    // swap bits 2 and 3 of the key index: the order in which a lane's QK^T
+    // accumulator holds keys inside each 16-key MFMA step
+    return (key & ~0xC) | ((key >> 1) & 4) | ((key << 1) & 8);
+}
+
+__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+    bf16x2 r;
+    r[0] = (__bf16)lo;
+    r[1] = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ float bf16_round(float x) {
+    return __uint_as_float(pk_bf16(x, 0.f) << 16);
+}
+
+// Online-softmax update for one tile held as S^T accumulators (log2 domain).
+// Element value s maps to logit s * f + bias; masked elements are -inf.
+template <int NKB>
+__device__ __forceinline__ void online_update(f32x16 (&sacc)[NKB], float f, float bias, float lw,
+                                              float& m, float& lsum, f32x16 (&oacc)[4]) {
+    const float NEG_INF = -__builtin_inff();
+    float mx = NEG_INF;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb][v]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mnew = fmaxf(m, mx * f + bias);
+    const float muse = mnew == NEG_INF ? 0.f : mnew;
+    const float alpha = __builtin_amdgcn_exp2f(m - muse);
+    lsum *= alpha;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
+    m = mnew;
+    const float nb = bias - muse + lw;
+    float ts = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][v], f, nb));
+            sacc[kb][v] = p;
+            ts += p;
+        }
+    lsum += lw == 0.f ? ts : ts * __builtin_amdgcn_exp2f(-lw);
+}
+
+// O^T += V^T P^T with P taken straight from the S^T accumulators.
+template <int NKB, int VLD>
+__device__ __forceinline__ void pv_bf16(const f32x16 (&sacc)[NKB], const __bf16* Vt, int n, int lh,
+                                        f32x16 (&oacc)[4]) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            bf16x8 bop;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bop[e] = (__bf16)sacc[kb][8 * s2 + e];
+#pragma unroll
+            for (int db = 0; db < 4; ++db) {
+                const bf16x8 aop = *(const bf16x8*)&Vt[(db * 32 + n) * VLD + kb * 32 + 16 * s2 + 8 * lh];
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop, oacc[db], 0, 0, 0);
+            }
+        }
+}
+
+// DORD 0: step ks covers dims 16 ks + 8 lh .. +8 (bf16 fragment order);
+// DORD 1: dims 64 (ks / 4) + 32 lh + 8 (ks % 4) .. +8 (the fp8 fragment's order).
+template <int NKB, int KLD, int DORD>
+__device__ __forceinline__ void qk_bf16(const __bf16* Ks, const bf16x8 (&qf)[8], int n, int lh,
+                                        f32x16 (&sacc)[NKB], bool accumulate) {
+    if (!accumulate) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) sacc[kb][v] = 0.f;
+    }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            const int d0 = DORD ? 64 * (ks >> 2) + 32 * lh + 8 * (ks & 3) : ks * 16 + lh * 8;
+            const bf16x8 aop = *(const bf16x8*)&Ks[(kb * 32 + n) * KLD + d0];
+            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, qf[ks], sacc[kb], 0, 0, 0);
+        }
+}
+
+// Transposed, key-permuted store of 4 consecutive keys x 8 dims (bf16 bit
+// patterns in w[r]) into V^T: row d, column slot(key0) .. +3.
+template <int VLD>
+__device__ __forceinline__ void store_vt4x8(__bf16* Vt, int d0, int slot0, const uint4 (&w)[4]) {
+    const uint32_t* w0 = (const uint32_t*)&w[0];
+    const uint32_t* w1 = (const uint32_t*)&w[1];
+    const uint32_t* w2 = (const uint32_t*)&w[2];
+    const uint32_t* w3 = (const uint32_t*)&w[3];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        uint2 lo, hi;
+        lo.x = (w0[e] & 0xFFFFu) | (w1[e] << 16);
+        lo.y = (w2[e] & 0xFFFFu) | (w3[e] << 16);
+        hi.x = (w0[e] >> 16) | (w1[e] & 0xFFFF0000u);
+        hi.y = (w2[e] >> 16) | (w3[e] & 0xFFFF0000u);
+        *(uint2*)&Vt[(d0 + 2 * e) * VLD + slot0] = lo;
+        *(uint2*)&Vt[(d0 + 2 * e + 1) * VLD + slot0] = hi;
+    }
+}
+
+// fp8 P -> E4M3 codes, 4 per dword (round to nearest even)
+__device__ __forceinline__ uint32_t pk_fp8x4(float a, float b, float c, float d) {
+    uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0u, false);
+    return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+}
+
+// fp8 V^T slot of a key inside its 64-key MFMA step: the lane holding query n
+// (half lh) owns keys kb*32 + 8q + 4lh + r of kb in {2s, 2s+1}, in the order
+// (kb parity, q, r); store them contiguously per (s, lh).
+__device__ __forceinline__ int vt8_slot(int key) {
+    const int lh = (key >> 2) & 1, c = (key >> 5) & 1, q = (key >> 3) & 3, r = key & 3;
+    return (key & ~0x3F) | (lh << 5) | (c << 4) | (q << 2) | r;
+}
+
+// 4 keys x 16 dims of e4m3 codes (w[r] = 16 bytes of key r) -> V^T rows d0..d0+15,
+// 4 consecutive slots starting at slot0.
+template <int VLD8>
+__device__ __forceinline__ void store_vt8_4x16(uint8_t* Vt, int d0, int slot0, const uint4 (&w)[4]) {
+    const uint32_t* w0 = (const uint32_t*)&w[0];
+    const uint32_t* w1 = (const uint32_t*)&w[1];
+    const uint32_t* w2 = (const uint32_t*)&w[2];
+    const uint32_t* w3 = (const uint32_t*)&w[3];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+            const int sh = 8 * bb;
+            const uint32_t x = ((w0[e] >> sh) & 0xFFu) | (((w1[e] >> sh) & 0xFFu) << 8) |
+                               (((w2[e] >> sh) & 0xFFu) << 16) | (((w3[e] >> sh) & 0xFFu) << 24);
+            *(uint32_t*)&Vt[(d0 + 4 * e + bb) * VLD8 + slot0] = x;
+        }
+}
+
+__device__ __forceinline__ float e4m3_val(uint32_t c) {
+    const uint32_t sgn = (c & 0x80u) << 24, e = (c >> 3) & 0xFu, mm = c & 0x7u;
+    const float mag = e ? __uint_as_float(((e + 120u) << 23) | (mm << 20)) : (float)mm * 0.001953125f;
+    return __uint_as_float(__float_as_uint(mag) | sgn);
+}
+
+template <int BLK, bool FP8, bool PAGED, typename Geo>
+__global__ __launch_bounds__(256, 2) void attn_kernel(Geo geo, AttnArgs a) {
+    constexpr int NKB = BLK / 32;
+    constexpr int KLD = D + 8;         // bf16 K tile row, +16 B against bank conflicts
+    constexpr int VLD = BLK + 8;       // bf16 V^T tile row
+    constexpr int KLD8 = D + 16;       // fp8 K tile row (bytes)
+    constexpr int VLD8 = BLK + 16;     // fp8 V^T tile row (bytes)
+    constexpr int KS_BYTES = BLK * KLD * 2;
+    constexpr int VT_BYTES = D * VLD * 2;
+    __shared__ __align__(16) uint8_t smem[KS_BYTES + VT_BYTES];
+    __shared__ uint32_t kept[MAX_NB / 32];
+    __shared__ float svmax_sh;
+    __bf16* Ks = (__bf16*)smem;
+    __bf16* Vt = (__bf16*)(smem + KS_BYTES);
+    uint8_t* Ks8 = smem;
+    uint8_t* Vt8 = smem + KS_BYTES;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 31, lh = lane >> 5;
+    const float NEG_INF = -__builtin_inff();
+
+    // unit -> (row position, slice); a row's slices share one XCD
+    const int u = blockIdx.x;
+    const int xcd = u & 7, k8 = u >> 3;
+    const int pidx = 8 * (k8 / a.slices) + xcd;
+    const int slice = k8 % a.slices;
+    if (pidx >= a.rows) return;
+    const int r = a.sched ? a.sched[pidx] : pidx;
+    const int b = geo.seq_of_row(r);
+    const SeqDesc s = geo.seq(b);
+    const int rl = r - s.row0;
+    const int g = rl / s.nq, il = rl % s.nq;
+    const int i = s.i0 + il;
+    const int t_lo = max(i * BLK, s.P), t_hi = min((i + 1) * BLK, s.L);
+    const int G = a.G;
+    const int npk = G * (t_hi - t_lo);               // packed rows of this row
+    if (slice * 128 >= npk) return;                  // uniform over the workgroup
+
+    const int prow = slice * 128 + wave * 32 + n;
+    const bool valid = prow < npk;
+    const int tl = prow / G, hl = prow - tl * G;
+    const int t = t_lo + tl;
+    const int h = g * G + hl;
+
+    // query fragment. bf16: lane (n, lh) holds q[t, h, 16 ks + 8 lh .. + 8];
+    // fp8: q[t, h, 64 ks + 32 lh .. + 32] (codes).
+    bf16x8 qf[8];
+    i32x8 qf8[2];
+    float f_row = a.scale_log2;
+    if (FP8) {
+        const uint8_t* qp = (const uint8_t*)a.q + (valid ? a.qa.off(b, s, t, h) : 0);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const uint4 w0 = valid ? *(const uint4*)(qp + ks * 64 + lh * 32) : make_uint4(0u, 0u, 0u, 0u);
+            const uint4 w1 = valid ? *(const uint4*)(qp + ks * 64 + lh * 32 + 16) : make_uint4(0u, 0u, 0u, 0u);
+            qf8[ks][0] = w0.x; qf8[ks][1] = w0.y; qf8[ks][2] = w0.z; qf8[ks][3] = w0.w;
+            qf8[ks][4] = w1.x; qf8[ks][5] = w1.y; qf8[ks][6] = w1.z; qf8[ks][7] = w1.w;
+        }
+        if (valid) f_row *= a.qs.at(b, h, t);
+    } else {
+        const __bf16* qp = (const __bf16*)a.q + (valid ? a.qa.off(b, s, t, h) : 0);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            if (valid) qf[ks] = *(const bf16x8*)(qp + ks * 16 + lh * 8);
+            else
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qf[ks][e] = (__bf16)0.f;
+        }
+    }
+
+    // kept bitmap of this row (pooled columns that must not be corrected)
+    const int rp0 = a.row_ptr[r], nnz = a.row_ptr[r + 1] - rp0;
+    const int nw = (i >> 5) + 1;
+    for (int w = tid; w < nw; w += 256) kept[w] = 0u;
+    if (tid == 0) svmax_sh = 0.f;
+    __syncthreads();
+    float svm = 0.f;
+    for (int e = tid; e < nnz; e += 256) {
+        const int j = a.col_idx[rp0 + e];
+        atomicOr(&kept[j >> 5], 1u << (j & 31));
+        if (FP8) svm = fmaxf(svm, a.vs.at(b, g, j * BLK));
+    }
+    if (FP8) {
+        svm = fmaxf(svm, __shfl_xor(svm, 32, 64));
+        svm = fmaxf(svm, __shfl_xor(svm, 16, 64));
+        svm = fmaxf(svm, __shfl_xor(svm, 8, 64));
+        svm = fmaxf(svm, __shfl_xor(svm, 4, 64));
+        svm = fmaxf(svm, __shfl_xor(svm, 2, 64));
+        svm = fmaxf(svm, __shfl_xor(svm, 1, 64));
+        if (lane == 0) atomicMax((int*)&svmax_sh, __float_as_int(svm));   // positive floats
+    }
+    __syncthreads();
+    // fp8 PV accumulates P * 2^8 * sv_j / svmax times value codes; undone at the end
+    const float svmax = FP8 ? svmax_sh : 1.f;
+    const float lsvmax = FP8 ? __log2f(svmax) : 0.f;
+
+    float m = NEG_INF, lsum = 0.f;
+    f32x16 oacc[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oacc[db][v] = 0.f;
+    f32x16 sacc[NKB];
+
+    // ---------------- kept blocks: exact tokens ----------------
+    for (int e = 0; e < nnz; ++e) {
+        const int j = a.col_idx[rp0 + e];
+        __syncthreads();
+        if (FP8) {
+            const uint8_t* kbase = (const uint8_t*)a.k;
+            const uint8_t* vbase = (const uint8_t*)a.v;
+            for (int c = tid; c < BLK * 8; c += 256) {
+                const int key = c >> 3, ch = c & 7;
+                const int sk = j * BLK + key;
+                uint4 w = make_uint4(0u, 0u, 0u, 0u);
+                if (sk < s.L) w = *(const uint4*)(kbase + a.ka.template off<PAGED>(b, sk, g) + ch * 16);
+                *(uint4*)&Ks8[key * KLD8 + ch * 16] = w;
+            }
+            for (int c = tid; c < (BLK / 4) * 8; c += 256) {
+                const int kq = c >> 3, ch = c & 7;
+                uint4 w[4];
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int sk = j * BLK + 4 * kq + rr;
+                    w[rr] = make_uint4(0u, 0u, 0u, 0u);
+                    if (sk < s.L) w[rr] = *(const uint4*)(vbase + a.va.template off<PAGED>(b, sk, g) + ch * 16);
+                }
+                store_vt8_4x16<VLD8>(Vt8, ch * 16, vt8_slot(4 * kq), w);
+            }
+        } else {
+            const __bf16* kbase = (const __bf16*)a.k;
+            const __bf16* vbase = (const __bf16*)a.v;
+            for (int c = tid; c < BLK * 16; c += 256) {
+                const int key = c >> 4, ch = c & 15;
+                const int sk = j * BLK + key;
+                uint4 w = make_uint4(0u, 0u, 0u, 0u);
+                if (sk < s.L) w = *(const uint4*)(kbase + a.ka.template off<PAGED>(b, sk, g) + ch * 8);
+                *(uint4*)&Ks[key * KLD + ch * 8] = w;
+            }
+            for (int c = tid; c < (BLK / 4) * 16; c += 256) {
+                const int kq = c >> 4, ch = c & 15;
+                uint4 w[4];
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int sk = j * BLK + 4 * kq + rr;
+                    w[rr] = make_uint4(0u, 0u, 0u, 0u);
+                    if (sk < s.L) w[rr] = *(const uint4*)(vbase + a.va.template off<PAGED>(b, sk, g) + ch * 8);
+                }
+                store_vt4x8<VLD>(Vt, ch * 8, vt_slot(4 * kq), w);
+            }
+        }
+        __syncthreads();
+        float f = f_row, lw = 0.f;
+        if (FP8) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) sacc[kb][v] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+                    const uint8_t* ap = &Ks8[(kb * 32 + n) * KLD8 + ks * 64 + lh * 32];
+                    const uint4 w0 = *(const uint4*)ap, w1 = *(const uint4*)(ap + 16);
+                    i32x8 aop;
+                    aop[0] = w0.x; aop[1] = w0.y; aop[2] = w0.z; aop[3] = w0.w;
+                    aop[4] = w1.x; aop[5] = w1.y; aop[6] = w1.z; aop[7] = w1.w;
+                    sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, qf8[ks], sacc[kb],
+                                                                              0, 0, 0, 127, 0, 127);
+                }
+            const float sk = a.ks.at(b, g, j * BLK);
+            f *= sk;
+            lw = 8.f + __log2f(a.vs.at(b, g, j * BLK)) - lsvmax;   // P scale 2^8 sv_j / svmax
+        } else {
+            qk_bf16<NKB, KLD, 0>(Ks, qf, n, lh, sacc, false);
+        }
+        if (j == i) {                                  // causal mask inside the diagonal block
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int sk = j * BLK + kb * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
+                    if (sk > t) sacc[kb][v] = NEG_INF;
+                }
+        }
+        online_update<NKB>(sacc, f, 0.f, lw, m, lsum, oacc);
+        if (FP8) {
+#pragma unroll
+            for (int s2 = 0; s2 < NKB / 2; ++s2) {
+                i32x8 bop;
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const f32x16& sv = sacc[2 * s2 + c];
+                        bop[4 * c + q4] = (int)pk_fp8x4(sv[4 * q4], sv[4 * q4 + 1], sv[4 * q4 + 2], sv[4 * q4 + 3]);
+                    }
+#pragma unroll
+                for (int db = 0; db < 4; ++db) {
+                    const uint8_t* ap = &Vt8[(db * 32 + n) * VLD8 + s2 * 64 + lh * 32];
+                    const uint4 w0 = *(const uint4*)ap, w1 = *(const uint4*)(ap + 16);
+                    i32x8 aop;
+                    aop[0] = w0.x; aop[1] = w0.y; aop[2] = w0.z; aop[3] = w0.w;
+                    aop[4] = w1.x; aop[5] = w1.y; aop[6] = w1.z; aop[7] = w1.w;
+                    oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, bop, oacc[db],
+                                                                              0, 0, 0, 127, 0, 127);
+                }
+            }
+        } else {
+            pv_bf16<NKB, VLD>(sacc, Vt, n, lh, oacc);
+        }
+    }
+
+    // ---------------- pruned blocks: pooled pseudo-tokens ----------------
+    const float lnb2 = (BLK == 128) ? 7.f : 6.f;       // log2 |block|
+    // fp8: the pseudo-token weights join the accumulator in its 2^8 / svmax units
+    const float lw_sum = FP8 ? 8.f - lsvmax : 0.f;
+    bool have_qbf = false;
+    for (int jt = 0; jt * BLK <= i - 1; ++jt) {
+        // any pruned column in [max(1, jt*BLK), min(i-1, jt*BLK + BLK - 1)] ?
+        const int c_lo = max(1, jt * BLK), c_hi = min(i - 1, jt * BLK + BLK - 1);
+        bool any = false;
+        for (int wd = c_lo >> 5; wd <= (c_hi >> 5); ++wd) {
+            uint32_t want = 0xFFFFFFFFu;
+            const int w0 = wd * 32;
+            if (w0 < c_lo) want &= 0xFFFFFFFFu << (c_lo - w0);
+            if (w0 + 31 > c_hi) want &= 0xFFFFFFFFu >> (w0 + 31 - c_hi);
+            if (~kept[wd] & want) { any = true; break; }
+        }
+        if (!any) continue;
+        if (FP8 && !have_qbf) {
+            // widen the query codes to bf16 (exact) in the fp8 fragment's d order
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int byte = (ks & 3) * 8 + e;              // within the 32-byte half
+                    const uint32_t w = (uint32_t)qf8[ks >> 2][byte >> 2];
+                    qf[ks][e] = (__bf16)e4m3_val((w >> ((byte & 3) * 8)) & 0xFFu);
+                }
+            have_qbf = true;
+        }
+        __syncthreads();
+        for (int c = tid; c < BLK * 32; c += 256) {     // Kbar hi
+            const int key = c >> 5, c4 = c & 31;
+            const int jp = jt * BLK + key;
+            float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (jp < s.nbk) x = *(const float4*)(a.kbar + kbar_row(s, a.Hkv, g, jp) * D + c4 * 4);
+            uint2 hv;
+            hv.x = pk_bf16(x.x, x.y);
+            hv.y = pk_bf16(x.z, x.w);
+            *(uint2*)&Ks[key * KLD + c4 * 4] = hv;
+        }
+        for (int c = tid; c < (BLK / 4) * 16; c += 256) {   // Vbar, transposed
+            const int kq = c >> 4, ch = c & 15;
+            uint4 w[4];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int jp = jt * BLK + 4 * kq + rr;
+                float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
+                if (jp < s.nbk) {
+                    const float* vp = a.vbar + kbar_row(s, a.Hkv, g, jp) * D + ch * 8;
+                    x0 = *(const float4*)vp;
+                    x1 = *(const float4*)(vp + 4);
+                }
+                w[rr] = make_uint4(pk_bf16(x0.x, x0.y), pk_bf16(x0.z, x0.w),
+                                   pk_bf16(x1.x, x1.y), pk_bf16(x1.z, x1.w));
+            }
+            store_vt4x8<VLD>(Vt, ch * 8, vt_slot(4 * kq), w);
+        }
+        __syncthreads();
+        qk_bf16<NKB, KLD, FP8 ? 1 : 0>(Ks, qf, n, lh, sacc, false);
+        __syncthreads();
+        for (int c = tid; c < BLK * 32; c += 256) {     // Kbar lo = bf16(x - hi)
+            const int key = c >> 5, c4 = c & 31;
+            const int jp = jt * BLK + key;
+            float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (jp < s.nbk) x = *(const float4*)(a.kbar + kbar_row(s, a.Hkv, g, jp) * D + c4 * 4);
+            uint2 lv;
+            lv.x = pk_bf16(x.x - bf16_round(x.x), x.y - bf16_round(x.y));
+            lv.y = pk_bf16(x.z - bf16_round(x.z), x.w - bf16_round(x.w));
+            *(uint2*)&Ks[key * KLD + c4 * 4] = lv;
+        }
+        __syncthreads();
+        qk_bf16<NKB, KLD, FP8 ? 1 : 0>(Ks, qf, n, lh, sacc, true);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int jp = jt * BLK + kb * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
+                const bool pruned = jp >= 1 && jp <= i - 1 && !((kept[jp >> 5] >> (jp & 31)) & 1u);
+                if (!pruned) sacc[kb][v] = NEG_INF;
+            }
+        online_update<NKB>(sacc, f_row, lnb2, lw_sum, m, lsum, oacc);
+        pv_bf16<NKB, VLD>(sacc, Vt, n, lh, oacc);
+    }
+
+    // ---------------- epilogue ----------------
+    const float ltot = lsum + __shfl_xor(lsum, 32, 64);
+    if (!valid) return;
+    const float inv = (FP8 ? svmax * 0.00390625f : 1.f) / ltot;
+    __bf16* op = (__bf16*)a.o + a.oa.off(b, s, t, h);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            uint2 w;
+            w.x = pk_bf16(oacc[db][4 * q4] * inv, oacc[db][4 * q4 + 1] * inv);
+            w.y = pk_bf16(oacc[db][4 * q4 + 2] * inv, oacc[db][4 * q4 + 3] * inv);
+            *(uint2*)(op + db * 32 + q4 * 8 + lh * 4) = w;
+        }
+    if (a.lse && lh == 0) a.lse[a.la.off(b, s, t, h)] = (m + __log2f(ltot)) * LN2;
+}
+
+template <int BLK, typename Geo>
+static void attn_launch(const Geo& geo, const AttnArgs& a, int fp8, int paged, int units, hipStream_t st) {
+    if (fp8) {
+        if (paged) attn_kernel<BLK, true, true, Geo><<<units, 256, 0, st>>>(geo, a);
+        else attn_kernel<BLK, true, false, Geo><<<units, 256, 0, st>>>(geo, a);
+    } else {
+        if (paged) attn_kernel<BLK, false, true, Geo><<<units, 256, 0, st>>>(geo, a);
+        else attn_kernel<BLK, false, false, Geo><<<units, 256, 0, st>>>(geo, a);
+    }
+}
+
+template <typename Geo>
+static hipError_t attn_dispatch(const Geo& geo, const AttnArgs& a, int blk, int fp8, int paged,
+                                hipStream_t st) {
+    const int units = cdiv(a.rows, 8) * 8 * a.slices;
+    if (blk == 128) attn_launch<128>(geo, a, fp8, paged, units, st);
+    else attn_launch<64>(geo, a, fp8, paged, units, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn(const GeoFixed* gf, const GeoTable* gt, const AttnArgs& a, int blk,
+                       int fp8, int paged, hipStream_t st) {
+    if (a.rows == 0) return hipSuccess;
+    return gf ? attn_dispatch(*gf, a, blk, fp8, paged, st) : attn_dispatch(*gt, a, blk, fp8, paged, st);
+}
+
+}  // namespace fp

@@ -1,0 +1,216 @@
+// Block-level estimate: pooling (E1) and block scores (E2).
+//
+// The estimate is one score per (query block, key block) pair (aipulsen.com
+// article body: scores estimated at the block level; lode.cx page, "How It
+// Works": a small sample of attention scores). Here it is the mean-pooled
+// query of the block against the mean-pooled key, which equals the mean token
+// logit of the block pair.
+//
+// Both kernels are HBM-bound streaming passes: pooling reads every Q/K/V byte
+// once with 16-byte coalesced loads, scores read the small pooled tensors
+// (L2-resident) and write one fp32 per block pair.
+#include "fp_internal.h"
+
+namespace fp {
+
+// OCP E4M3FN decode by bit assembly (sign, 4-bit exponent with bias 7, 3-bit
+// mantissa; exponent 0 is subnormal m * 2^-9). Codes are finite by contract.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+    uint32_t s = (c & 0x80u) << 24;
+    uint32_t e = (c >> 3) & 0xFu;
+    uint32_t m = c & 0x7u;
+    float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+    return __uint_as_float(__float_as_uint(mag) | s);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// ---------------------------------------------------------------------------
+// E1: one workgroup per (block, tensor-head). blockIdx.y < Hq: query head;
+// then Hkv key heads; then Hkv value heads. 256 threads = TL token lanes x
+// CH 16-byte column chunks; token lanes stride over the block's tokens and
+// are summed through LDS at the end. fp32 accumulation.
+// ---------------------------------------------------------------------------
+template <bool FP8, bool PAGED, typename Geo>
+__global__ __launch_bounds__(256) void pool_kernel(Geo geo, PoolArgs a) {
+    constexpr int EPC = FP8 ? 16 : 8;        // elements per 16-byte chunk
+    constexpr int CH = D / EPC;              // chunks per row
+    constexpr int TL = 256 / CH;             // token lanes
+    __shared__ float red[TL][D + 4];
+
+    const int tid = threadIdx.x;
+    const int ch = tid % CH, tl = tid / CH;
+    const int y = blockIdx.y;
+    const int u = blockIdx.x;
+    const bool isq = y < a.Hq;
+    if (isq ? (u >= a.total_qblocks) : (u >= a.total_kblocks)) return;
+
+    const int b = isq ? geo.seq_of_qblock(u) : geo.seq_of_kblock(u);
+    const SeqDesc s = geo.seq(b);
+    const int B = a.blk;
+    int lo, hi, blk;
+    if (isq) {
+        blk = u - s.qb0;                      // local query block
+        const int i = s.i0 + blk;
+        lo = max(i * B, s.P);
+        hi = min((i + 1) * B, s.L);
+    } else {
+        blk = u - s.kb0;
+        lo = blk * B;
+        hi = min((blk + 1) * B, s.L);
+    }
+
+    float acc[EPC];
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
+
+    const int head = isq ? y : (y < a.Hq + a.Hkv ? y - a.Hq : y - a.Hq - a.Hkv);
+    const bool isv = !isq && y >= a.Hq + a.Hkv;
+    const char* base = (const char*)(isq ? a.q : (isv ? a.v : a.k));
+    const ScaleAddr& sa = isq ? a.qs : (isv ? a.vs : a.ks);
+    constexpr int ESZ = FP8 ? 1 : 2;
+
+    for (int t = lo + tl; t < hi; t += TL) {
+        long long off;
+        if (isq) off = a.qa.off(b, s, t, head);
+        else off = (isv ? a.va : a.ka).template off<PAGED>(b, t, head);
+        const uint4 w = *(const uint4*)(base + (off + (long long)ch * EPC) * ESZ);
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+        if (FP8) {
+            const float sc = sa.at(b, head, t);
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                acc[e] += e4m3_to_f32((ws[e >> 2] >> ((e & 3) * 8)) & 0xFFu) * sc;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[2 * e] += bf16_lo(ws[e]);
+                acc[2 * e + 1] += bf16_hi(ws[e]);
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) red[tl][ch * EPC + e] = acc[e];
+    __syncthreads();
+    if (tid < D) {
+        float sum = 0.f;
+#pragma unroll 8
+        for (int r = 0; r < TL; ++r) sum += red[r][tid];
+        const float mean = sum / (float)(hi - lo);
+        if (isq) a.qbar[qbar_row(s, a.Hq, head, blk) * D + tid] = mean;
+        else (isv ? a.vbar : a.kbar)[kbar_row(s, a.Hkv, head, blk) * D + tid] = mean;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// E2: 64 x 64 tiles of (query block, key block) per workgroup, one query head
+// per blockIdx.y. Tiles entirely above the diagonal only write -inf. fp32
+// FMA on 4 x 4 register blocks from LDS; the pooled rows stay L2-resident.
+// ---------------------------------------------------------------------------
+template <typename Geo>
+__global__ __launch_bounds__(256) void scores_kernel(Geo geo, ScoreArgs a) {
+    constexpr int T = SC_TILE;
+    constexpr int LD = D + 4;
+    __shared__ __align__(16) float Qs[T][LD];
+    __shared__ __align__(16) float Ks[T][LD];
+
+    const int u = blockIdx.x;
+    if (u >= a.total_tiles) return;
+    const int h = blockIdx.y;
+    const int G = a.Hq / a.Hkv;
+    const int g = h / G;
+    const int b = geo.seq_of_tile(u);
+    const SeqDesc s = geo.seq(b);
+    const int lt = u - s.tile0;
+    const int ntk = cdiv(s.nbk, T);
+    const int tq = lt / ntk, tk = lt % ntk;
+    const int il0 = tq * T, j0 = tk * T;
+    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+    const float NEG_INF = -__builtin_inff();
+
+    // highest absolute query block in this tile
+    const int imax = s.i0 + min(il0 + T, s.nq) - 1;
+    if (j0 > imax) {
+        for (int e = tid; e < T * T; e += 256) {
+            const int r = e / T, c = e % T;
+            if (il0 + r < s.nq && j0 + c < s.nbk) a.scores[score_off(s, h, il0 + r, j0 + c)] = NEG_INF;
+        }
+        return;
+    }
+    // stage pooled rows (zero outside the sequence)
+    for (int e = tid; e < T * (D / 4); e += 256) {
+        const int r = e / (D / 4), c4 = e % (D / 4);
+        float4 qv = make_float4(0.f, 0.f, 0.f, 0.f), kv = qv;
+        if (il0 + r < s.nq) qv = *(const float4*)(a.qbar + qbar_row(s, a.Hq, h, il0 + r) * D + c4 * 4);
+        if (j0 + r < s.nbk) kv = *(const float4*)(a.kbar + kbar_row(s, a.Hkv, g, j0 + r) * D + c4 * 4);
+        *(float4*)&Qs[r][c4 * 4] = qv;
+        *(float4*)&Ks[r][c4 * 4] = kv;
+    }
+    __syncthreads();
+
+    float acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+#pragma unroll 4
+    for (int dd = 0; dd < D; dd += 4) {
+        float4 qv[4], kv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qv[i] = *(const float4*)&Qs[ty + 16 * i][dd];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) kv[j] = *(const float4*)&Ks[tx + 16 * j][dd];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                acc[i][j] = fmaf(qv[i].x, kv[j].x, acc[i][j]);
+                acc[i][j] = fmaf(qv[i].y, kv[j].y, acc[i][j]);
+                acc[i][j] = fmaf(qv[i].z, kv[j].z, acc[i][j]);
+                acc[i][j] = fmaf(qv[i].w, kv[j].w, acc[i][j]);
+            }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int il = il0 + ty + 16 * i;
+        if (il >= s.nq) continue;
+        const int iabs = s.i0 + il;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int jj = j0 + tx + 16 * j;
+            if (jj >= s.nbk) continue;
+            a.scores[score_off(s, h, il, jj)] = jj <= iabs ? acc[i][j] * a.scale : NEG_INF;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+template <typename Geo>
+static hipError_t pool_dispatch(const Geo& geo, const PoolArgs& a, hipStream_t st) {
+    dim3 grid(max(a.total_qblocks, a.total_kblocks), a.Hq + 2 * a.Hkv);
+    if (a.fp8) {
+        if (a.paged) return hipErrorInvalidValue;
+        pool_kernel<true, false, Geo><<<grid, 256, 0, st>>>(geo, a);
+    } else if (a.paged) {
+        pool_kernel<false, true, Geo><<<grid, 256, 0, st>>>(geo, a);
+    } else {
+        pool_kernel<false, false, Geo><<<grid, 256, 0, st>>>(geo, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_pool(const GeoFixed* gf, const GeoTable* gt, const PoolArgs& a, hipStream_t st) {
+    if (a.total_qblocks == 0 && a.total_kblocks == 0) return hipSuccess;
+    return gf ? pool_dispatch(*gf, a, st) : pool_dispatch(*gt, a, st);
+}
+
+hipError_t launch_scores(const GeoFixed* gf, const GeoTable* gt, const ScoreArgs& a, hipStream_t st) {
+    if (a.total_tiles == 0) return hipSuccess;
+    dim3 grid(a.total_tiles, a.Hq);
+    if (gf) scores_kernel<GeoFixed><<<grid, 256, 0, st>>>(*gf, a);
+    else scores_kernel<GeoTable><<<grid, 256, 0, st>>>(*gt, a);
+    return hipGetLastError();
+}
+
+}  // namespace fp

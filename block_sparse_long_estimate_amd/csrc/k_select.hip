@@ -1,0 +1,191 @@
+// Max-based dynamic threshold (E3-E5) and compaction of the kept blocks into
+// CSR lists plus a heavy-row-first schedule.
+//
+// The threshold keeps a key block when its estimate lies within tau of the
+// query block's row maximum (lode.cx page, "How It Works"; aimodeling.com
+// page, "From Prototype to Production"); with grouped-query attention the G
+// query heads of a KV head share one list (the union over the heads), which
+// is what lets the attention pass pack those heads into one tile (lode.cx
+// page, PackGQA bullet). Sink and diagonal blocks are always kept.
+//
+// select_rows: one wavefront per row (b, g, i). Pass 1 reduces the G row
+//   maxima, pass 2 forms R = max_h (S - M_h) per key block, tests it and
+//   compacts the decisions with a 64-lane ballot into a bit row + count.
+// scan_rows:   single workgroup exclusive scan of the counts -> row_ptr.
+// expand_rows: one wavefront per row, ballot + lane-prefix popcount writes the
+//   ascending column list at row_ptr.
+// sort_rows:   single workgroup stable counting sort of the rows by count
+//   (descending), ties by row id -> sched.
+#include "fp_internal.h"
+
+namespace fp {
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+template <typename Geo>
+__global__ __launch_bounds__(256) void select_rows_kernel(Geo geo, SelectArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= a.rows) return;
+    const int b = geo.seq_of_row(r);
+    const SeqDesc s = geo.seq(b);
+    const int rl = r - s.row0;
+    const int g = rl / s.nq, il = rl % s.nq;
+    const int i = s.i0 + il;
+    const int G = a.Hq / a.Hkv;
+    const float NEG_INF = -__builtin_inff();
+
+    float M[MAX_G];
+#pragma unroll
+    for (int hh = 0; hh < MAX_G; ++hh) {
+        M[hh] = NEG_INF;
+        if (hh < G) {
+            const float* row = a.scores + score_off(s, g * G + hh, il, 0);
+            float m = NEG_INF;
+            for (int j = lane; j <= i; j += 64) m = fmaxf(m, row[j]);
+            M[hh] = wave_max(m);
+        }
+    }
+    int count = 0;
+    uint32_t* bits = a.bits + (long long)r * a.nbw;
+    for (int jc = 0; jc <= i; jc += 64) {
+        const int j = jc + lane;
+        bool keep = false;
+        if (j <= i) {
+            float R = NEG_INF;
+#pragma unroll
+            for (int hh = 0; hh < MAX_G; ++hh)
+                if (hh < G) R = fmaxf(R, a.scores[score_off(s, g * G + hh, il, j)] - M[hh]);
+            keep = (R >= a.neg_tau) || j == 0 || j == i;
+        }
+        const unsigned long long bal = __ballot(keep);
+        count += __popcll(bal);
+        if (lane == 0) bits[jc >> 5] = (uint32_t)bal;
+        if (lane == 1 && (jc >> 5) + 1 < a.nbw) bits[(jc >> 5) + 1] = (uint32_t)(bal >> 32);
+    }
+    if (lane == 0) a.counts[r] = count;
+}
+
+// Exclusive scan of counts into row_ptr[0..rows]; one workgroup of 1024.
+__global__ __launch_bounds__(1024) void scan_rows_kernel(SelectArgs a) {
+    __shared__ int part[1024];
+    const int tid = threadIdx.x;
+    const int per = cdiv(a.rows, 1024);
+    const int lo = min(tid * per, a.rows), hi = min(lo + per, a.rows);
+    int sum = 0;
+    for (int r = lo; r < hi; ++r) sum += a.counts[r];
+    part[tid] = sum;
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {           // Hillis-Steele inclusive scan
+        const int v = tid >= o ? part[tid - o] : 0;
+        __syncthreads();
+        part[tid] += v;
+        __syncthreads();
+    }
+    int run = part[tid] - sum;                      // exclusive prefix of this chunk
+    if (tid == 0) a.row_ptr[0] = 0;
+    for (int r = lo; r < hi; ++r) {
+        run += a.counts[r];
+        a.row_ptr[r + 1] = run;
+    }
+}
+
+template <typename Geo>
+__global__ __launch_bounds__(256) void expand_rows_kernel(Geo geo, SelectArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= a.rows) return;
+    const int b = geo.seq_of_row(r);
+    const SeqDesc s = geo.seq(b);
+    const int il = (r - s.row0) % s.nq;
+    const int i = s.i0 + il;
+    const uint32_t* bits = a.bits + (long long)r * a.nbw;
+    int pos = a.row_ptr[r];
+    for (int jc = 0; jc <= i; jc += 64) {
+        const uint32_t lo = bits[jc >> 5];
+        const uint32_t hi = (jc + 32 <= i) ? bits[(jc >> 5) + 1] : 0u;
+        const unsigned long long m = ((unsigned long long)hi << 32) | lo;
+        const unsigned long long below = lane ? (m & ((~0ull) >> (64 - lane))) : 0ull;
+        if ((m >> lane) & 1ull) a.col_idx[pos + __popcll(below)] = jc + lane;
+        pos += __popcll(m);
+    }
+}
+
+// Stable counting sort, keys = counts in [1, max_nbk], descending. One
+// workgroup of 1024 threads; bins in dynamic LDS.
+__global__ __launch_bounds__(1024) void sort_rows_kernel(SelectArgs a) {
+    extern __shared__ int sm[];
+    const int nbin = a.max_nbk + 1;
+    int* cur = sm;                 // [nbin] bin cursor
+    int* keys = sm + nbin;         // [1024] keys of the current chunk
+    __shared__ int part[1024];
+    const int tid = threadIdx.x;
+    for (int k = tid; k < nbin; k += 1024) cur[k] = 0;
+    __syncthreads();
+    for (int r = tid; r < a.rows; r += 1024) atomicAdd(&cur[a.counts[r]], 1);
+    __syncthreads();
+    // cursor[k] = number of rows with a larger count (descending order)
+    const int per = cdiv(nbin, 1024);
+    const int lo = min(tid * per, nbin), hi = min(lo + per, nbin);
+    int sum = 0;
+    for (int k = lo; k < hi; ++k) sum += cur[k];
+    part[tid] = sum;
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {           // inclusive suffix scan over threads
+        const int v = tid + o < 1024 ? part[tid + o] : 0;
+        __syncthreads();
+        part[tid] += v;
+        __syncthreads();
+    }
+    int run = part[tid] - sum;                      // rows in bins above this chunk
+    for (int k = hi - 1; k >= lo; --k) {
+        const int c = cur[k];
+        cur[k] = run;
+        run += c;
+    }
+    __syncthreads();
+    for (int base = 0; base < a.rows; base += 1024) {
+        const int r = base + tid;
+        const int key = r < a.rows ? a.counts[r] : -1;
+        keys[tid] = key;
+        __syncthreads();
+        int rank = 0;
+        for (int t = 0; t < tid; ++t) rank += keys[t] == key;
+        const int pos = key >= 0 ? cur[key] + rank : 0;
+        __syncthreads();
+        if (key >= 0) {
+            a.sched[pos] = r;
+            atomicAdd(&cur[key], 1);
+        }
+        __syncthreads();
+    }
+}
+
+template <typename Geo>
+static hipError_t select_dispatch(const Geo& geo, const SelectArgs& a, hipStream_t st) {
+    const int wg = cdiv(a.rows, 4);
+    select_rows_kernel<Geo><<<wg, 256, 0, st>>>(geo, a);
+    scan_rows_kernel<<<1, 1024, 0, st>>>(a);
+    expand_rows_kernel<Geo><<<wg, 256, 0, st>>>(geo, a);
+    if (a.sched) {
+        const size_t shm = (size_t)(a.max_nbk + 1 + 1024) * sizeof(int);
+        if (shm > 65536) {
+            hipError_t e = hipFuncSetAttribute((const void*)sort_rows_kernel,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+            if (e != hipSuccess) return e;
+        }
+        sort_rows_kernel<<<1, 1024, shm, st>>>(a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_select(const GeoFixed* gf, const GeoTable* gt, const SelectArgs& a, hipStream_t st) {
+    if (a.rows == 0) return hipSuccess;
+    return gf ? select_dispatch(*gf, a, st) : select_dispatch(*gt, a, st);
+}
+
+}  // namespace fp

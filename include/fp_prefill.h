@@ -1,0 +1,178 @@
+/*
+ * fp_prefill.h -- C ABI of a block-sparse causal GQA prefill-attention library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The method is FlashPrefill V2's prefill path as the pages describe it:
+ *   - a block-level score estimate per (query block, key block) pair
+ *     (aipulsen.com article body; lode.cx page, "How It Works");
+ *   - a max-based dynamic threshold that keeps the key blocks whose estimate
+ *     lies within tau of the query block's row maximum (lode.cx page, "How It
+ *     Works"; aimodeling.com page, "From Prototype to Production");
+ *   - a sparse flash-attention pass over the kept blocks with online softmax
+ *     (lode.cx page, implementation paragraph and bullet list);
+ *   - a mean-correction term standing in for the pruned blocks (lode.cx page,
+ *     "How It Works"; aimodeling.com page, "Error correction" bullet);
+ *   - FP8 inputs, paged KV cache and continuous (varlen) batching (lode.cx
+ *     page, implementation paragraph; aimodeling.com page, "Operator alignment"
+ *     and "Framework integration" bullets).
+ * The pages print no formulas. This library computes exactly these equations
+ * (B = block size, c = softmax scale, G = Hq/Hkv, g(h) = h / G):
+ *   E1  Qbar[h,i] = mean of q over the present rows of query block i;
+ *       Kbar[g,j], Vbar[g,j] = mean of k, v over key block j.
+ *   E2  S[h,i,j] = c <Qbar[h,i], Kbar[g(h),j]>, j <= i   (-inf for j > i).
+ *   E3  M[h,i] = max_{j<=i} S[h,i,j].
+ *   E4  R[g,i,j] = max over the G heads h of group g of (S[h,i,j] - M[h,i]).
+ *   E5  kept(g,i) = {0, i} U { j <= i : R[g,i,j] >= -tau }.
+ *   E6  row t of query block i, head h: softmax over (a) the causal tokens
+ *       s <= t of the kept blocks with logit c<q_t,k_s> and (b) one
+ *       pseudo-token per pruned block j with key Kbar[g,j], value Vbar[g,j]
+ *       and logit c<q_t,Kbar[g,j]> + ln|block j|; o = weighted value sum,
+ *       lse = natural log of the softmax denominator.
+ *
+ * Conventions (every entry point):
+ *   - Pointers marked (device) are HIP device pointers, (host) host pointers.
+ *     Every buffer is owned by the caller. The library allocates, frees and
+ *     synchronises nothing and keeps no state between calls.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = default stream) and
+ *     the call returns without waiting. Device faults surface at the caller's
+ *     next synchronisation.
+ *   - Return value: FP_OK, or a negative FP_ERR_* code with a message in
+ *     fp_last_error() (thread-local). Arguments are validated before any HIP
+ *     call, so an error return means nothing was enqueued (FP_ERR_HIP aside).
+ *   - head_dim must be 128; block must be 64 or 128; Hq % Hkv == 0 and
+ *     Hq / Hkv <= 16; block count per sequence <= 16384.
+ *   - Strides are in elements; the last (head_dim) dimension is contiguous.
+ *   - Inputs are post-RoPE and finite (non-finite inputs: undefined results).
+ *   - Kept-block lists are CSR over rows ordered (sequence b, KV head g, query
+ *     block i ascending); columns ascending, absolute key-block indices.
+ */
+#ifndef FP_PREFILL_H
+#define FP_PREFILL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP_OK 0
+#define FP_ERR_INVALID (-1)      /* null pointer, bad size, NaN tau, ...        */
+#define FP_ERR_UNSUPPORTED (-2)  /* head_dim != 128, block not 64/128, ...      */
+#define FP_ERR_CAPACITY (-3)     /* col_idx capacity or workspace too small      */
+#define FP_ERR_HIP (-4)          /* a HIP launch reported an error              */
+
+#define FP_DTYPE_BF16 0          /* bfloat16 Q/K/V                               */
+#define FP_DTYPE_FP8_E4M3 1      /* OCP E4M3FN codes (uint8) + fp32 scales       */
+
+/* Fixed-shape batch: `batch` sequences of `seqlen` tokens each, one-shot
+ * prefill (no cached prefix). q [batch, seqlen, Hq, 128], k and v
+ * [batch, seqlen, Hkv, 128], o like q; strides given per tensor. */
+typedef struct fp_problem {
+    int32_t batch;
+    int32_t seqlen;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;        /* 128 */
+    int32_t block;           /* 64 or 128 (square blocks) */
+    int32_t dtype;           /* FP_DTYPE_* */
+    float softmax_scale;     /* c; 0 means 1/sqrt(head_dim) */
+    int64_t q_stride[3];     /* batch, token, head */
+    int64_t k_stride[3];
+    int64_t v_stride[3];
+    int64_t o_stride[3];
+} fp_problem;
+
+/* Paged varlen batch (continuous batching with cached prefixes). Sequence b
+ * has L_b = seqlens_k[b] keys in the cache (new chunk included) and
+ * q_len_b = cu_seqlens_q[b+1] - cu_seqlens_q[b] present query rows, the
+ * positions [L_b - q_len_b, L_b). Blocks sit on the absolute-position grid. */
+typedef struct fp_varlen_problem {
+    int32_t num_seqs;        /* 1 .. 4096 */
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;        /* 128 */
+    int32_t block;           /* 128 */
+    int32_t page_size;       /* 64 or 128; block must be a multiple */
+    int32_t dtype;           /* FP_DTYPE_BF16 */
+    float softmax_scale;     /* 0 means 1/sqrt(head_dim) */
+    int32_t max_pages_per_seq;  /* row length of block_table */
+    int32_t pad_;
+    int64_t q_stride[2];     /* packed q: token, head */
+    int64_t kv_stride[3];    /* k_cache / v_cache: page, token-in-page, head */
+    int64_t o_stride[2];     /* packed o: token, head */
+} fp_varlen_problem;
+
+const char* fp_version(void);
+const char* fp_last_error(void);
+
+/* Sizing (host only, no HIP call). Return < 0 with fp_last_error() set on an
+ * invalid problem. */
+int64_t fp_num_rows(const fp_problem* p);       /* batch * Hkv * nb           */
+int64_t fp_max_nnz(const fp_problem* p);        /* batch * Hkv * nb(nb+1)/2   */
+int64_t fp_workspace_size(const fp_problem* p); /* bytes for fp_select_blocks */
+
+/* E1-E2. Pools Q, K, V per block (float32 accumulation) and writes the block
+ * scores. q, k, v (device, read-only): bf16, or E4M3FN codes with q_scale,
+ * k_scale, v_scale (device, fp32 [batch, H, ceil(seqlen/128)], one scale per
+ * 128-token block; NULL for bf16). Outputs (device, fp32, fully overwritten):
+ * qbar [batch, Hq, nb, 128], kbar and vbar [batch, Hkv, nb, 128],
+ * scores [batch, Hq, nb, nb] with -inf above the diagonal. */
+int fp_block_scores(const fp_problem* p, const void* q, const void* k, const void* v,
+                    const float* q_scale, const float* k_scale, const float* v_scale,
+                    float* qbar, float* kbar, float* vbar, float* scores, void* stream);
+
+/* E3-E5 plus compaction. scores (device) as written by fp_block_scores.
+ * tau: +inf keeps everything, tau < 0 keeps only the sink and diagonal
+ * blocks, NaN is an error. Outputs (device): row_ptr int32 [rows + 1],
+ * col_idx int32 [capacity] (capacity >= fp_max_nnz checked on the host),
+ * sched int32 [rows] or NULL: the rows ordered by kept count descending,
+ * ties by row id ascending (heavy-row-first order for fp_sparse_prefill).
+ * workspace (device) of ws_bytes >= fp_workspace_size(p). */
+int fp_select_blocks(const fp_problem* p, const float* scores, float tau,
+                     int32_t* row_ptr, int32_t* col_idx, int64_t capacity,
+                     int32_t* sched, void* workspace, size_t ws_bytes, void* stream);
+
+/* E6. Sparse attention over the kept blocks of (row_ptr, col_idx) -- any
+ * valid kept list whose rows contain the sink and diagonal blocks, e.g. the
+ * one fp_select_blocks wrote -- plus the mean-correction pseudo-tokens of the
+ * pruned blocks, taken from kbar and vbar (device, as fp_block_scores wrote
+ * them). sched (device, NULL = row order) only orders the work. Outputs
+ * (device): o bf16 (o_stride), lse fp32 [batch, Hq, seqlen] or NULL. */
+int fp_sparse_prefill(const fp_problem* p, const void* q, const void* k, const void* v,
+                      const float* q_scale, const float* k_scale, const float* v_scale,
+                      const float* kbar, const float* vbar,
+                      const int32_t* row_ptr, const int32_t* col_idx, const int32_t* sched,
+                      void* o, float* lse, void* stream);
+
+/* Sizing of a paged varlen call (host only). cu_seqlens_q int32 [num_seqs+1]
+ * and seqlens_k int32 [num_seqs] are HOST arrays. */
+int64_t fp_varlen_num_rows(const fp_varlen_problem* p, const int32_t* cu_seqlens_q,
+                           const int32_t* seqlens_k);
+int64_t fp_varlen_max_nnz(const fp_varlen_problem* p, const int32_t* cu_seqlens_q,
+                          const int32_t* seqlens_k);
+int64_t fp_varlen_workspace_size(const fp_varlen_problem* p, const int32_t* cu_seqlens_q,
+                                 const int32_t* seqlens_k);
+
+/* E1-E6 for a paged varlen batch in one call. q (device) packed
+ * [sum q_len, Hq, 128] bf16; k_cache, v_cache (device) [pages, page_size,
+ * Hkv, 128] bf16; block_table (device) int32 [num_seqs, max_pages_per_seq]
+ * (token s of sequence b lives in page block_table[b][s / page_size], slot
+ * s % page_size; the new chunk's keys must already be in the cache).
+ * cu_seqlens_q, seqlens_k: HOST arrays, read during the call only.
+ * Outputs (device): row_ptr [rows+1] and col_idx [capacity] (the kept lists,
+ * capacity >= fp_varlen_max_nnz), o packed like q, lse fp32 [Hq, sum q_len]
+ * or NULL. workspace (device) >= fp_varlen_workspace_size bytes. */
+int fp_sparse_prefill_paged(const fp_varlen_problem* p, const void* q,
+                            const int32_t* cu_seqlens_q, const int32_t* seqlens_k,
+                            const void* k_cache, const void* v_cache,
+                            const int32_t* block_table, float tau,
+                            int32_t* row_ptr, int32_t* col_idx, int64_t capacity,
+                            void* o, float* lse, void* workspace, size_t ws_bytes,
+                            void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP_PREFILL_H */

@@ -1,0 +1,53 @@
+"""Shared helpers of the GPU parity tests: kept-list decoding and the
+comparison rules (kept lists exact except inside the 1e-3 threshold band;
+outputs within the stated tolerances, evaluated under the GPU's validated
+kept lists)."""
+from __future__ import annotations
+
+import numpy as np
+
+BAND = 1e-3
+TOL = {"bf16": (2e-2, 2e-3), "fp8": (6e-2, 6e-3)}   # (max-abs, mean-abs)
+
+
+def csr_to_keep(row_ptr: np.ndarray, col_idx: np.ndarray, row0: int, Hkv: int, nq: int, nb: int) -> np.ndarray:
+    keep = np.zeros((Hkv, nq, nb), dtype=bool)
+    for g in range(Hkv):
+        for il in range(nq):
+            r = row0 + g * nq + il
+            cols = col_idx[row_ptr[r]:row_ptr[r + 1]]
+            keep[g, il, cols] = True
+    return keep
+
+
+def check_csr_wellformed(row_ptr: np.ndarray, col_idx: np.ndarray, i_of_row) -> None:
+    assert row_ptr[0] == 0
+    assert np.all(np.diff(row_ptr) >= 1)
+    for r in range(len(row_ptr) - 1):
+        cols = col_idx[row_ptr[r]:row_ptr[r + 1]]
+        i = i_of_row(r)
+        assert np.all(np.diff(cols) > 0), f"row {r}: columns not strictly ascending"
+        assert cols[0] == 0 and cols[-1] == i, f"row {r}: sink/diagonal missing"
+
+
+def compare_masks(gpu_keep: np.ndarray, ref_keep: np.ndarray, R: np.ndarray, tau: float):
+    diff = gpu_keep != ref_keep
+    band = np.abs(R + tau) <= BAND
+    out_band = int((diff & ~band).sum())
+    assert out_band == 0, f"{out_band} kept-block mismatches outside the threshold band"
+    return int(diff.sum()), int(band.sum())
+
+
+def compare_outputs(o_gpu: np.ndarray, o_ref: np.ndarray, kind: str):
+    mask = ~np.isnan(o_ref)
+    err = np.abs(o_gpu[mask] - o_ref[mask])
+    mx, mean = float(err.max()), float(err.mean())
+    tmax, tmean = TOL[kind]
+    assert mx <= tmax and mean <= tmean, f"{kind}: max|err| {mx:.3e} (<= {tmax}), mean|err| {mean:.3e} (<= {tmean})"
+    return mx, mean
+
+
+def check_sched(sched: np.ndarray, counts: np.ndarray) -> None:
+    assert sorted(sched.tolist()) == list(range(len(counts)))
+    order = sorted(range(len(counts)), key=lambda r: (-counts[r], r))
+    assert sched.tolist() == order

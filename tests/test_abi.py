@@ -1,0 +1,196 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, sizes problems, and rejects bad arguments before any HIP call."""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import block_sparse_long_estimate_amd._native as N
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp_prefill.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z0-9_]+\s*\*?\s*(fp_[a-z_]+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = N.load()
+    names = header_functions()
+    assert len(names) >= 12
+    assert set(names) == set(N.EXPORTS)
+    for name in names:
+        assert hasattr(lib, name), name
+    assert b"gfx950" in lib.fp_version()
+
+
+def problem(**kw):
+    c = N.FpProblem()
+    c.batch, c.seqlen, c.num_q_heads, c.num_kv_heads = 1, 1024, 8, 2
+    c.head_dim, c.block, c.dtype, c.softmax_scale = 128, 128, 0, 0.0
+    for name, H in (("q_stride", 8), ("k_stride", 2), ("v_stride", 2), ("o_stride", 8)):
+        arr = getattr(c, name)
+        arr[0], arr[1], arr[2] = 1024 * H * 128, H * 128, 128
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_sizes():
+    lib = N.load()
+    p = problem()
+    nb = 8
+    assert lib.fp_num_rows(ctypes.byref(p)) == 2 * nb
+    assert lib.fp_max_nnz(ctypes.byref(p)) == 2 * nb * (nb + 1) // 2
+    assert lib.fp_workspace_size(ctypes.byref(p)) > 0
+    p = problem(seqlen=1000, block=64)
+    assert lib.fp_num_rows(ctypes.byref(p)) == 2 * 16
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("num_q_heads", 7, N.FP_ERR_INVALID),          # Hq % Hkv != 0
+    ("head_dim", 64, N.FP_ERR_UNSUPPORTED),
+    ("block", 32, N.FP_ERR_UNSUPPORTED),
+    ("block", 96, N.FP_ERR_UNSUPPORTED),
+    ("dtype", 7, N.FP_ERR_UNSUPPORTED),
+    ("batch", 0, N.FP_ERR_INVALID),
+    ("seqlen", -5, N.FP_ERR_INVALID),
+    ("softmax_scale", float("nan"), N.FP_ERR_INVALID),
+    ("num_kv_heads", 0, N.FP_ERR_INVALID),
+])
+def test_invalid_problems(field, value, code):
+    lib = N.load()
+    p = problem(**{field: value})
+    assert lib.fp_num_rows(ctypes.byref(p)) == code
+    assert len(lib.fp_last_error()) > 0
+    fake = ctypes.c_void_p(1 << 20)
+    assert lib.fp_block_scores(ctypes.byref(p), fake, fake, fake, None, None, None,
+                               fake, fake, fake, fake, None) == code
+
+
+def test_group_limit_and_block_count_limit():
+    lib = N.load()
+    p = problem(num_q_heads=34, num_kv_heads=2)       # G = 17
+    assert lib.fp_num_rows(ctypes.byref(p)) == N.FP_ERR_UNSUPPORTED
+    p = problem(seqlen=16385 * 128)
+    assert lib.fp_num_rows(ctypes.byref(p)) == N.FP_ERR_UNSUPPORTED
+
+
+def test_null_pointers_and_fp8_scales():
+    lib = N.load()
+    p = problem()
+    fake = ctypes.c_void_p(1 << 20)
+    assert lib.fp_block_scores(ctypes.byref(p), None, fake, fake, None, None, None,
+                               fake, fake, fake, fake, None) == N.FP_ERR_INVALID
+    assert b"NULL" in lib.fp_last_error()
+    p8 = problem(dtype=1)
+    for name, H in (("q_stride", 8), ("k_stride", 2), ("v_stride", 2)):
+        arr = getattr(p8, name)
+        arr[0], arr[1], arr[2] = 1024 * H * 128, H * 128, 128
+    assert lib.fp_block_scores(ctypes.byref(p8), fake, fake, fake, None, None, None,
+                               fake, fake, fake, fake, None) == N.FP_ERR_INVALID
+    assert b"scale" in lib.fp_last_error()
+    assert lib.fp_sparse_prefill(ctypes.byref(p), fake, fake, fake, None, None, None, fake, fake,
+                                 None, fake, None, fake, None, None) == N.FP_ERR_INVALID
+
+
+def test_misaligned_strides_rejected():
+    lib = N.load()
+    p = problem()
+    p.q_stride[1] = 8 * 128 + 4                      # 8-byte aligned only
+    assert lib.fp_num_rows(ctypes.byref(p)) == N.FP_ERR_INVALID
+
+
+def test_select_rejects_nan_tau_capacity_and_workspace():
+    lib = N.load()
+    p = problem()
+    fake = ctypes.c_void_p(1 << 20)
+    need = lib.fp_max_nnz(ctypes.byref(p))
+    ws = lib.fp_workspace_size(ctypes.byref(p))
+    assert lib.fp_select_blocks(ctypes.byref(p), fake, float("nan"), fake, fake, need, None,
+                                fake, ws, None) == N.FP_ERR_INVALID
+    assert b"NaN" in lib.fp_last_error()
+    assert lib.fp_select_blocks(ctypes.byref(p), fake, 4.0, fake, fake, need - 1, None,
+                                fake, ws, None) == N.FP_ERR_CAPACITY
+    assert lib.fp_select_blocks(ctypes.byref(p), fake, 4.0, fake, fake, need, None,
+                                fake, ws - 1, None) == N.FP_ERR_CAPACITY
+    assert lib.fp_select_blocks(ctypes.byref(p), fake, 4.0, fake, fake, need, None,
+                                ctypes.c_void_p((1 << 20) + 8), ws, None) == N.FP_ERR_INVALID
+
+
+def vproblem(**kw):
+    c = N.FpVarlenProblem()
+    c.num_seqs, c.num_q_heads, c.num_kv_heads, c.head_dim = 3, 8, 2, 128
+    c.block, c.page_size, c.dtype, c.softmax_scale = 128, 64, 0, 0.0
+    c.max_pages_per_seq = 64
+    c.q_stride[0], c.q_stride[1] = 8 * 128, 128
+    c.kv_stride[0], c.kv_stride[1], c.kv_stride[2] = 64 * 2 * 128, 2 * 128, 128
+    c.o_stride[0], c.o_stride[1] = 8 * 128, 128
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def arr(x):
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+    return a, a.ctypes.data_as(ctypes.c_void_p)
+
+
+def test_varlen_sizes_match_a_direct_count():
+    lib = N.load()
+    p = vproblem()
+    cu, cup = arr([0, 300, 300, 1000])        # middle sequence has no new rows
+    lk, lkp = arr([500, 200, 1000])
+    rows = lib.fp_varlen_num_rows(ctypes.byref(p), cup, lkp)
+    nnz = lib.fp_varlen_max_nnz(ctypes.byref(p), cup, lkp)
+    exp_rows, exp_nnz = 0, 0
+    for b in range(3):
+        ql = cu[b + 1] - cu[b]
+        if ql == 0:
+            continue
+        P = lk[b] - ql
+        for i in range(P // 128, (lk[b] - 1) // 128 + 1):
+            exp_rows += 2
+            exp_nnz += 2 * (i + 1)
+    assert rows == exp_rows and nnz == exp_nnz
+    assert lib.fp_varlen_workspace_size(ctypes.byref(p), cup, lkp) > 0
+
+
+@pytest.mark.parametrize("cu,lk,kw,code", [
+    ([0, 300, 200, 1000], [500, 200, 1000], {}, N.FP_ERR_INVALID),     # cu not monotone
+    ([0, 300, 400, 1000], [200, 200, 1000], {}, N.FP_ERR_INVALID),     # L < q_len
+    ([1, 300, 400, 1000], [500, 200, 1000], {}, N.FP_ERR_INVALID),     # cu[0] != 0
+    ([0, 300, 400, 1000], [500, 200, 1000], {"page_size": 48}, N.FP_ERR_UNSUPPORTED),
+    ([0, 300, 400, 1000], [500, 200, 1000], {"dtype": 1}, N.FP_ERR_UNSUPPORTED),
+    ([0, 300, 400, 1000], [500, 200, 1000], {"max_pages_per_seq": 8}, N.FP_ERR_INVALID),
+    ([0, 300, 400, 1000], [500, 200, 1000], {"num_seqs": 0}, N.FP_ERR_INVALID),
+])
+def test_varlen_invalid(cu, lk, kw, code):
+    lib = N.load()
+    p = vproblem(**kw)
+    _, cup = arr(cu)
+    _, lkp = arr(lk)
+    assert lib.fp_varlen_num_rows(ctypes.byref(p), cup, lkp) == code
+    fake = ctypes.c_void_p(1 << 20)
+    assert lib.fp_sparse_prefill_paged(ctypes.byref(p), fake, cup, lkp, fake, fake, fake, 4.0,
+                                       fake, fake, 1 << 30, fake, None, fake, 1 << 40, None) == code
+
+
+def test_paged_rejects_nan_tau_capacity_workspace():
+    lib = N.load()
+    p = vproblem()
+    _, cup = arr([0, 300, 400, 1000])
+    _, lkp = arr([500, 200, 1000])
+    fake = ctypes.c_void_p(1 << 20)
+    nnz = lib.fp_varlen_max_nnz(ctypes.byref(p), cup, lkp)
+    ws = lib.fp_varlen_workspace_size(ctypes.byref(p), cup, lkp)
+    call = lambda tau, cap, wsb: lib.fp_sparse_prefill_paged(
+        ctypes.byref(p), fake, cup, lkp, fake, fake, fake, tau, fake, fake, cap, fake, None, fake, wsb, None)
+    assert call(float("nan"), nnz, ws) == N.FP_ERR_INVALID
+    assert call(4.0, nnz - 1, ws) == N.FP_ERR_CAPACITY
+    assert call(4.0, nnz, ws - 1) == N.FP_ERR_CAPACITY

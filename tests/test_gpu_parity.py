@@ -1,0 +1,266 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 CPU oracle.
+
+Kept lists must match bit-exactly except blocks whose oracle estimate lies
+within 1e-3 of the threshold; outputs (evaluated by the oracle under the
+GPU's validated kept lists) within max-abs 2e-2 / mean-abs 2e-3 for bf16 and
+6e-2 / 6e-3 for fp8; lse within 2e-3."""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from fp_testutil import (TOL, check_csr_wellformed, check_sched, compare_masks, compare_outputs,
+                         csr_to_keep)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fp():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_sparse_long_estimate_amd as m
+    m._native.load()
+    return m
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def to_dev(inp):
+    dev = torch.device("cuda:0")
+    mv = lambda t: None if t is None else t.to(dev)
+    return mv(inp.q), mv(inp.k), mv(inp.v), mv(inp.q_scale), mv(inp.k_scale), mv(inp.v_scale)
+
+
+def run_fixed(fp, inp, tau, block):
+    q, k, v, qs, ks, vs = to_dev(inp)
+    out = fp.sparse_prefill(q, k, v, block, tau, q_scale=qs, k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    return {kk: (vv.cpu() if isinstance(vv, torch.Tensor) else vv) for kk, vv in out.items()}
+
+
+def widen(inp, b):
+    if inp.q.dtype == torch.bfloat16:
+        return [oracle.widen_bf16(t[b]) for t in (inp.q, inp.k, inp.v)]
+    return [oracle.widen_fp8(t[b].numpy(), s[b].numpy())
+            for t, s in ((inp.q, inp.q_scale), (inp.k, inp.k_scale), (inp.v, inp.v_scale))]
+
+
+def check_fixed(fp, inp, tau, block, rows=None, kind="bf16", check_pooled=True):
+    """Full comparison of one fixed-shape run. rows: per-sequence list of
+    (g, il) to evaluate E6 on (None = all)."""
+    out = run_fixed(fp, inp, tau, block)
+    B, S, Hq = inp.q.shape[0], inp.q.shape[1], inp.q.shape[2]
+    Hkv = inp.k.shape[2]
+    nb = -(-S // block)
+    c = 1 / math.sqrt(128)
+    rp, ci = out["row_ptr"].numpy(), out["col_idx"].numpy()
+    check_csr_wellformed(rp, ci, lambda r: r % nb)
+    counts = np.diff(rp)
+    check_sched(out["sched"].numpy(), counts)
+    stats = []
+    for b in range(B):
+        q, k, v = widen(inp, b)
+        ref = oracle.prefill(q, k, v, block, tau, c, with_output=False)
+        if check_pooled:
+            for name in ("qbar", "kbar", "vbar"):
+                g = out[name][b].numpy()
+                r = ref[name]
+                assert np.abs(g - r).max() <= 1e-5 * max(1.0, np.abs(r).max()), name
+            sg, sr = out["scores"][b].numpy(), ref["S"]
+            fin = np.isfinite(sr)
+            assert np.array_equal(fin, np.isfinite(sg))
+            assert np.abs(sg[fin] - sr[fin]).max() <= 2e-4 * max(1.0, np.abs(sr[fin]).max())
+        keep = csr_to_keep(rp, ci, b * Hkv * nb, Hkv, nb, nb)
+        ndiff, nband = compare_masks(keep, ref["keep"], ref["R"], tau)
+        o_ref, lse_ref = oracle.attend(q, k, v, keep, ref["kbar"], ref["vbar"], c, block, 0,
+                                       rows=None if rows is None else rows[b])
+        mx, mean = compare_outputs(out["o"][b].float().numpy(), o_ref, kind)
+        lg = out["lse"][b].numpy()
+        okl = ~np.isnan(lse_ref)
+        assert np.abs(lg[okl] - lse_ref[okl]).max() <= 2e-3
+        frac = keep.sum() / (Hkv * nb * (nb + 1) / 2)
+        stats.append((frac, ndiff, nband, mx, mean))
+        say(f"  seq {b}: kept {frac:.3%}, mask diffs {ndiff} (band {nband}), max|err| {mx:.2e}, mean {mean:.2e}")
+    return out, stats
+
+
+# ---------------------------------------------------------------------------
+def test_config1_full(fp):
+    """S=2048, GQA 4:1, iid N(0,1), 64x64 blocks, tau=4 (every block expected kept)."""
+    cfg = synth.config(1)
+    say("config 1")
+    _, stats = check_fixed(fp, synth.gen_fixed(cfg), cfg.tau, cfg.block)
+    assert stats[0][0] == 1.0
+
+
+@pytest.mark.parametrize("tau", [0.01, 0.05])
+def test_config1_shape_low_tau(fp, tau):
+    """Config 1's shape at tau values that actually prune."""
+    cfg = synth.config(1, tau=tau)
+    say(f"config 1 shape, tau={tau}")
+    _, stats = check_fixed(fp, synth.gen_fixed(cfg), tau, cfg.block)
+    assert stats[0][0] < 1.0
+
+
+@pytest.mark.parametrize("S,block,tau", [(4096 + 77, 128, 2.0), (4096 + 77, 128, 4.0),
+                                         (3000, 64, 2.0), (1024, 128, 1.0)])
+def test_walk_pruning(fp, S, block, tau):
+    """Random-walk keys with sink and planted blocks: real pruning, the
+    correction path, a ragged last block."""
+    cfg = synth.config(2, S=S, Hq=8, Hkv=2, block=block, tau=tau)
+    say(f"walk S={S} block={block} tau={tau}")
+    _, stats = check_fixed(fp, synth.gen_fixed(cfg), tau, block)
+    assert stats[0][0] < 1.0
+
+
+def test_batch_of_two_equals_single_runs(fp):
+    cfg = synth.config(2, S=2048 + 5, Hq=8, Hkv=2, batch=2, tau=2.0)
+    inp = synth.gen_fixed(cfg)
+    out, _ = check_fixed(fp, inp, cfg.tau, cfg.block)
+    for b in range(2):
+        one = synth.FixedInputs(cfg, inp.q[b:b + 1], inp.k[b:b + 1], inp.v[b:b + 1])
+        o1 = run_fixed(fp, one, cfg.tau, cfg.block)
+        assert torch.equal(o1["o"][0], out["o"][b])
+        assert torch.equal(o1["lse"][0], out["lse"][b])
+
+
+@pytest.mark.parametrize("tau", [float("inf"), -1.0])
+def test_tau_limits(fp, tau):
+    """tau=inf keeps every block (dense causal attention); tau<0 keeps only
+    the sink and diagonal blocks (everything else through the correction)."""
+    cfg = synth.config(2, S=2048 + 64 + 3, Hq=8, Hkv=2, tau=tau)
+    inp = synth.gen_fixed(cfg)
+    say(f"tau limit {tau}")
+    out, stats = check_fixed(fp, inp, tau, cfg.block)
+    nb = -(-cfg.S // cfg.block)
+    counts = np.diff(out["row_ptr"].numpy())
+    if tau == float("inf"):
+        assert stats[0][0] == 1.0
+        # dense causal attention, float32 on the CPU
+        q = inp.q[0].float().permute(1, 0, 2)
+        k = inp.k[0].float().repeat_interleave(4, dim=1).permute(1, 0, 2)
+        v = inp.v[0].float().repeat_interleave(4, dim=1).permute(1, 0, 2)
+        ref = torch.nn.functional.scaled_dot_product_attention(q[None], k[None], v[None], is_causal=True)
+        err = (out["o"][0].float().permute(1, 0, 2) - ref[0]).abs()
+        assert err.max() <= TOL["bf16"][0] and err.mean() <= TOL["bf16"][1]
+    else:
+        exp = np.array([min(i, 1) + 1 for i in range(nb)] * cfg.Hkv)
+        assert np.array_equal(counts, exp)
+
+
+def test_caller_supplied_oracle_mask(fp):
+    """fp_sparse_prefill accepts any valid kept list: feed the oracle's."""
+    cfg = synth.config(2, S=3072 + 11, Hq=8, Hkv=2, tau=2.0)
+    inp = synth.gen_fixed(cfg)
+    q, k, v, _, _, _ = to_dev(inp)
+    p = fp.make_problem(q, k, v, cfg.block)
+    qbar, kbar, vbar, scores = fp.fp_block_scores(p, q, k, v)
+    qn, kn, vn = widen(inp, 0)
+    ref = oracle.prefill(qn, kn, vn, cfg.block, cfg.tau)
+    Hkv, nq, nb = ref["keep"].shape
+    rows = [np.nonzero(ref["keep"][g, il])[0] for g in range(Hkv) for il in range(nq)]
+    row_ptr = np.concatenate([[0], np.cumsum([len(r) for r in rows])]).astype(np.int32)
+    col_idx = np.concatenate(rows).astype(np.int32)
+    o, lse = fp.fp_sparse_prefill(p, q, k, v, kbar, vbar, torch.from_numpy(row_ptr).cuda(),
+                                  torch.from_numpy(col_idx).cuda(), None)
+    torch.cuda.synchronize()
+    compare_outputs(o[0].float().cpu().numpy(), ref["o"], "bf16")
+
+
+def test_run_twice_is_bit_identical(fp):
+    cfg = synth.config(2, S=4096, Hq=8, Hkv=2, tau=2.0)
+    inp = synth.gen_fixed(cfg)
+    a = run_fixed(fp, inp, cfg.tau, cfg.block)
+    b = run_fixed(fp, inp, cfg.tau, cfg.block)
+    for key in ("scores", "row_ptr", "sched", "o", "lse"):
+        assert torch.equal(a[key], b[key]), key
+    n = int(a["row_ptr"][-1])
+    assert torch.equal(a["col_idx"][:n], b["col_idx"][:n])
+
+
+# ---------------------------------------------------------------------------
+# fp8
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("S,tau", [(2048 + 40, 2.0), (4096, 4.0)])
+def test_fp8_walk(fp, S, tau):
+    cfg = synth.config(4, S=S, Hq=8, Hkv=2, tau=tau)
+    say(f"fp8 walk S={S} tau={tau}")
+    check_fixed(fp, synth.gen_fixed(cfg), tau, cfg.block, kind="fp8")
+
+
+def test_fp8_block64_iid(fp):
+    cfg = synth.config(1, S=1024 + 9, dtype="fp8", tau=0.05)
+    say("fp8 iid block 64")
+    check_fixed(fp, synth.gen_fixed(cfg), cfg.tau, cfg.block, kind="fp8")
+
+
+# ---------------------------------------------------------------------------
+# paged varlen
+# ---------------------------------------------------------------------------
+def run_paged(fp, inp, tau):
+    dev = torch.device("cuda:0")
+    q, kc, vc, bt = inp.q.to(dev), inp.k_cache.to(dev), inp.v_cache.to(dev), inp.block_table.to(dev)
+    vp = fp.make_varlen_problem(q, inp.cu_seqlens_q, inp.seqlens_k, kc, bt, inp.cfg.block)
+    o, lse, rp, ci = fp.fp_sparse_prefill_paged(vp, q, kc, vc, bt, tau)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu(), rp.cpu().numpy(), ci.cpu().numpy()
+
+
+def check_paged(fp, inp, tau, sample_rows=None):
+    o, lse, rp, ci = run_paged(fp, inp, tau)
+    cfg = inp.cfg
+    c = 1 / math.sqrt(128)
+    refs = oracle.prefill_varlen(inp.q, inp.cu_seqlens_q, inp.seqlens_k, inp.k_cache, inp.v_cache,
+                                 inp.block_table.numpy(), cfg.block, tau, with_output=False)
+    row0 = 0
+    for b, ref in enumerate(refs):
+        L, P = int(inp.seqlens_k[b]), int(inp.prefix[b])
+        Hkv, nq, nb = ref["keep"].shape
+        keep = csr_to_keep(rp, ci, row0, Hkv, nq, nb)
+        for r in range(Hkv * nq):
+            cols = ci[rp[row0 + r]:rp[row0 + r + 1]]
+            assert cols[0] == 0 and cols[-1] == ref["i0"] + r % nq and np.all(np.diff(cols) > 0)
+        ndiff, nband = compare_masks(keep, ref["keep"], ref["R"], tau)
+        lo, hi = int(inp.cu_seqlens_q[b]), int(inp.cu_seqlens_q[b + 1])
+        kb = oracle.batch.gather_pages(inp.k_cache, inp.block_table[b].numpy(), L)
+        vb = oracle.batch.gather_pages(inp.v_cache, inp.block_table[b].numpy(), L)
+        rows = None if sample_rows is None else sample_rows(Hkv, nq)
+        o_ref, lse_ref = oracle.attend(oracle.widen_bf16(inp.q[lo:hi]), oracle.widen_bf16(kb),
+                                       oracle.widen_bf16(vb), keep, ref["kbar"], ref["vbar"], c,
+                                       cfg.block, P, rows=rows)
+        mx, mean = compare_outputs(o[lo:hi].float().numpy(), o_ref, "bf16")
+        okl = ~np.isnan(lse_ref)
+        assert np.abs(lse[:, lo:hi].numpy()[okl] - lse_ref[okl]).max() <= 2e-3
+        say(f"  seq {b}: L={L} P={P} kept {keep.sum() / max(1, (np.tril(np.ones((nq, nb)), ref['i0']).sum()) * Hkv):.2%} "
+            f"diffs {ndiff} (band {nband}) max|err| {mx:.2e} mean {mean:.2e}")
+        row0 += Hkv * nq
+    assert row0 == len(rp) - 1
+
+
+@pytest.mark.parametrize("page", [64, 16])
+def test_paged_varlen_small(fp, page):
+    cfg = synth.config(5, Hq=8, Hkv=2, n_seqs=4, len_range=(300, 3500), page_size=page, tau=2.0)
+    L, P = synth.paged_lengths(cfg)
+    P[0] = 0                                    # one sequence without a cached prefix
+    say(f"paged varlen page={page}: L={L.tolist()} P={P.tolist()}")
+    check_paged(fp, synth.gen_paged(cfg, (L, P)), cfg.tau)
+
+
+def test_paged_equals_contiguous(fp):
+    """A shuffled block table gives bit-identical results to contiguous storage."""
+    cfg = synth.config(5, Hq=8, Hkv=2, n_seqs=1, tau=2.0)
+    inp = synth.gen_paged(cfg, (np.array([3000]), np.array([0])))
+    o, lse, rp, ci = run_paged(fp, inp, cfg.tau)
+    k, v = synth.unpage(inp, 0)
+    fixed = synth.FixedInputs(cfg, inp.q[None], k[None], v[None])
+    out = run_fixed(fp, fixed, cfg.tau, cfg.block)
+    assert np.array_equal(rp, out["row_ptr"].numpy())
+    assert torch.equal(o, out["o"][0])
+    assert torch.equal(lse, out["lse"][0])
