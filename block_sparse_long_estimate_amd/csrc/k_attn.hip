@@ -149,6 +149,13 @@ __device__ __forceinline__ void store_vt4x8(__bf16* Vt, int d0, int slot0, const
     }
 }
 
+// Bits b of a 32-column word starting at column c0 with lo <= c0 + b <= hi.
+__device__ __forceinline__ uint32_t range_bits(int c0, int lo, int hi) {
+    const int a = max(lo - c0, 0), z = min(hi - c0, 31);
+    if (a > z) return 0u;
+    return (0xFFFFFFFFu >> (31 - z)) & (0xFFFFFFFFu << a);
+}
+
 // fp8 P -> E4M3 codes, 4 per dword (round to nearest even)
 __device__ __forceinline__ uint32_t pk_fp8x4(float a, float b, float c, float d) {
     uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0u, false);
@@ -370,7 +377,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(Geo geo, AttnArgs a) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int sk = j * BLK + kb * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
-                    if (sk > t) sacc[kb][v] = NEG_INF;
+                    sacc[kb][v] = sk > t ? NEG_INF : sacc[kb][v];
                 }
         }
         online_update<NKB>(sacc, f, 0.f, lw, m, lsum, oacc);
@@ -409,14 +416,9 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(Geo geo, AttnArgs a) {
     for (int jt = 0; jt * BLK <= i - 1; ++jt) {
         // any pruned column in [max(1, jt*BLK), min(i-1, jt*BLK + BLK - 1)] ?
         const int c_lo = max(1, jt * BLK), c_hi = min(i - 1, jt * BLK + BLK - 1);
-        bool any = false;
-        for (int wd = c_lo >> 5; wd <= (c_hi >> 5); ++wd) {
-            uint32_t want = 0xFFFFFFFFu;
-            const int w0 = wd * 32;
-            if (w0 < c_lo) want &= 0xFFFFFFFFu << (c_lo - w0);
-            if (w0 + 31 > c_hi) want &= 0xFFFFFFFFu >> (w0 + 31 - c_hi);
-            if (~kept[wd] & want) { any = true; break; }
-        }
+        uint32_t anyw = 0u;
+        for (int wd = c_lo >> 5; wd <= (c_hi >> 5); ++wd) anyw |= ~kept[wd] & range_bits(wd * 32, c_lo, c_hi);
+        const bool any = anyw != 0u;
         if (!any) continue;
         if (FP8 && !have_qbf) {
             // widen the query codes to bf16 (exact) in the fp8 fragment's d order
@@ -473,14 +475,18 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(Geo geo, AttnArgs a) {
         }
         __syncthreads();
         qk_bf16<NKB, KLD, FP8 ? 1 : 0>(Ks, qf, n, lh, sacc, true);
+        // Branch-free mask: each 32-column group of the tile is one bitmap word;
+        // a column stays iff it lies in [1, i-1] and is not kept.
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+        for (int kb = 0; kb < NKB; ++kb) {
+            const int c0 = jt * BLK + kb * 32;
+            const uint32_t pw = ~kept[min(c0 >> 5, MAX_NB / 32 - 1)] & range_bits(c0, 1, i - 1);
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int jp = jt * BLK + kb * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
-                const bool pruned = jp >= 1 && jp <= i - 1 && !((kept[jp >> 5] >> (jp & 31)) & 1u);
-                if (!pruned) sacc[kb][v] = NEG_INF;
+                const int bit = 8 * (v >> 2) + 4 * lh + (v & 3);
+                sacc[kb][v] = ((pw >> bit) & 1u) ? sacc[kb][v] : NEG_INF;
             }
+        }
         online_update<NKB>(sacc, f_row, lnb2, lw_sum, m, lsum, oacc);
         pv_bf16<NKB, VLD>(sacc, Vt, n, lh, oacc);
     }
