@@ -1,0 +1,264 @@
+"""Benchmark of the block-sparse prefill hot path on one MI355X.
+
+One step = the whole path on one layer: fp_block_scores (pooling + block
+scores), fp_select_blocks (threshold + CSR + schedule) and fp_sparse_prefill
+(sparse attention + mean correction), on the S=131072, 32 query / 8 KV head,
+head dim 128, 128x128-block, tau=4 bf16 workload (synthetic, seeded; inputs
+resident in HBM before timing). The same path is also timed on the fp8-e4m3
+version of the same tensors.
+
+    python bench.py [--gpus 1] [--steps 10] [--warmup 3]
+
+Prints one JSON line: dense-equivalent TFLOP/s of the bf16 step as `value`,
+ms per layer, kept-block fraction, the attention kernel's MFMA roofline
+fraction over the FLOPs of the kept blocks, and the single-threaded CPU
+oracle's throughput on a bounded sample as `cpu_baseline`.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}   # MI355X dense MFMA peaks
+HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kept_flops_from_csr(row_ptr, col_idx, nb, S, B, G, d, Hkv, batch):
+    """4 d G x causal (t, s) pairs inside the kept block pairs; rows (b, g, i)."""
+    counts = np.diff(row_ptr)
+    rows = np.arange(len(counts))
+    i_of_row = np.repeat(rows % nb, counts)
+    j = col_idx[:row_ptr[-1]]
+    ni = np.minimum((i_of_row + 1) * B, S) - i_of_row * B
+    mj = np.minimum((j + 1) * B, S) - j * B
+    pairs = np.where(j < i_of_row, ni * mj, ni * (ni + 1) // 2)
+    kept = 4.0 * d * G * pairs.astype(np.float64).sum()
+    # correction work: each row's pruned blocks are pseudo-tokens for its |I_i| rows
+    i_all = rows % nb
+    n_all = np.minimum((i_all + 1) * B, S) - i_all * B
+    npr = (i_all + 1) - counts
+    corr = 4.0 * d * G * float((n_all * npr).sum())
+    return kept, corr
+
+
+def time_path(fp, N, inp, tau, steps, warmup, label):
+    """Run the path `warmup` + `steps` times; HIP events per stage on the
+    current stream (the library launches on it)."""
+    import torch
+    dev = torch.device("cuda:0")
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    sc = [None if t is None else t.to(dev) for t in (inp.q_scale, inp.k_scale, inp.v_scale)]
+    block = inp.cfg.block
+    p = fp.make_problem(q, k, v, block)
+    c = p.c
+    f32 = dict(dtype=torch.float32, device=dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    qbar = torch.empty((c.batch, c.num_q_heads, p.nb, 128), **f32)
+    kbar = torch.empty((c.batch, c.num_kv_heads, p.nb, 128), **f32)
+    vbar = torch.empty((c.batch, c.num_kv_heads, p.nb, 128), **f32)
+    scores = torch.empty((c.batch, c.num_q_heads, p.nb, p.nb), **f32)
+    row_ptr = torch.empty(p.rows + 1, **i32)
+    col_idx = torch.empty(p.max_nnz, **i32)
+    sched = torch.empty(p.rows, **i32)
+    lib = N.load()
+    ws = torch.empty(N.check_size(lib.fp_workspace_size(p.ref)), dtype=torch.uint8, device=dev)
+    o = torch.empty((c.batch, c.seqlen, c.num_q_heads, 128), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((c.batch, c.num_q_heads, c.seqlen), **f32)
+    P = lambda t: None if t is None else t.data_ptr()
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def step():
+        N.check(lib.fp_block_scores(p.ref, P(q), P(k), P(v), P(sc[0]), P(sc[1]), P(sc[2]), P(qbar),
+                                    P(kbar), P(vbar), P(scores), sh))
+        ev[1].record(stream)
+        N.check(lib.fp_select_blocks(p.ref, P(scores), float(tau), P(row_ptr), P(col_idx), p.max_nnz,
+                                     P(sched), P(ws), ws.numel(), sh))
+        ev[2].record(stream)
+        N.check(lib.fp_sparse_prefill(p.ref, P(q), P(k), P(v), P(sc[0]), P(sc[1]), P(sc[2]), P(kbar),
+                                      P(vbar), P(row_ptr), P(col_idx), P(sched), P(o), P(lse), sh))
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t_est, t_sel, t_att = [], [], []
+    all0 = torch.cuda.Event(enable_timing=True)
+    all1 = torch.cuda.Event(enable_timing=True)
+    per = []
+    all0.record(stream)
+    for _ in range(steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        ev = e
+        e[0].record(stream)
+        step()
+        e[3].record(stream)
+        per.append(e)
+    all1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = all0.elapsed_time(all1)
+    for e in per:
+        t_est.append(e[0].elapsed_time(e[1]))
+        t_sel.append(e[1].elapsed_time(e[2]))
+        t_att.append(e[2].elapsed_time(e[3]))
+    rp = row_ptr.cpu().numpy()
+    ci = col_idx[:int(rp[-1])].cpu().numpy()
+    G = c.num_q_heads // c.num_kv_heads
+    kept, corr = kept_flops_from_csr(rp, ci, p.nb, c.seqlen, block, G, 128, c.num_kv_heads, c.batch)
+    dense = 4.0 * 128 * c.num_q_heads * c.batch * c.seqlen * (c.seqlen + 1) / 2.0
+    nblk = c.batch * c.num_kv_heads * p.nb * (p.nb + 1) / 2.0
+    res = dict(
+        label=label,
+        ms_per_step=total_ms / steps,
+        ms_estimate=float(np.mean(t_est)), ms_select=float(np.mean(t_sel)),
+        ms_attention=float(np.mean(t_att)),
+        kept_fraction=float(len(ci) / nblk),
+        kept_tflop=kept / 1e12, correction_tflop=corr / 1e12, dense_tflop=dense / 1e12,
+    )
+    res["dense_equiv_tflops"] = dense / (res["ms_per_step"] * 1e-3) / 1e12
+    res["attn_kept_tflops"] = kept / (res["ms_attention"] * 1e-3) / 1e12
+    res["attn_executed_tflops"] = (kept + corr) / (res["ms_attention"] * 1e-3) / 1e12
+    # estimator: reads Q, K, V once and writes pooled rows + full score matrix
+    esz = 1 if inp.q.dtype == torch.uint8 else 2
+    est_bytes = (q.numel() + k.numel() + v.numel()) * esz + (qbar.numel() + kbar.numel() + vbar.numel()
+                                                             + scores.numel()) * 4
+    res["estimate_gbs"] = est_bytes / (res["ms_estimate"] * 1e-3) / 1e9
+    sel_bytes = scores.numel() * 4 // 2 + (len(ci) + 3 * p.rows) * 4
+    res["select_gbs"] = sel_bytes / (res["ms_select"] * 1e-3) / 1e9
+    del q, k, v, qbar, kbar, vbar, scores, o, lse, ws
+    torch.cuda.empty_cache()
+    return res, (rp, ci)
+
+
+def cpu_baseline(inp, tau, rows_sample=256):
+    """The fp64 oracle, as it stands, single-threaded, on a bounded sample of
+    the same workload: E1-E5 for one KV head group (all query blocks) and E6
+    for `rows_sample` (KV head, query block) rows spread over the sequence;
+    projected to the whole layer in dense-equivalent TFLOP/s."""
+    from threadpoolctl import threadpool_limits
+    import oracle
+    from oracle.core import pool_queries, pool_keys, block_scores, select, attend
+    cfg = inp.cfg
+    S, B, Hq, Hkv = cfg.S, cfg.block, cfg.Hq, cfg.Hkv
+    G = Hq // Hkv
+    c = 1 / math.sqrt(128)
+    nb = -(-S // B)
+    with threadpool_limits(limits=1):
+        g = 0
+        q = oracle.widen_bf16(inp.q[0, :, g * G:(g + 1) * G])
+        k = oracle.widen_bf16(inp.k[0, :, g:g + 1])
+        v = oracle.widen_bf16(inp.v[0, :, g:g + 1])
+        t0 = time.perf_counter()
+        qb = pool_queries(q, B, 0, S)
+        kb, vb = pool_keys(k, B), pool_keys(v, B)
+        Sc = block_scores(qb, kb, c, 0)
+        keep, _ = select(Sc, G, tau, 0)
+        t_est = time.perf_counter() - t0
+        il_list = np.linspace(0, nb - 1, rows_sample).round().astype(int)
+        t0 = time.perf_counter()
+        attend(q, k, v, keep, kb, vb, c, B, 0, rows=[(0, int(il)) for il in il_list])
+        t_att = time.perf_counter() - t0
+    # projection: estimator time per group x Hkv; E6 time per row (evenly spaced
+    # rows average the linear growth of row cost in i) x all rows
+    t_layer = t_est * Hkv + t_att / rows_sample * (Hkv * nb)
+    dense = 4.0 * 128 * Hq * S * (S + 1) / 2.0
+    return dict(value=dense / t_layer / 1e12, unit="TFLOP/s (dense-equivalent)", cores=1,
+                kind="oracle",
+                sample=(f"E1-E5 for KV head 0 (4 query heads, all {nb} query blocks): {t_est:.2f} s; "
+                        f"E6 for {rows_sample} evenly spaced query blocks of KV head 0: {t_att:.2f} s; "
+                        f"projected layer time {t_layer:.0f} s (x{Hkv} heads, x{nb} rows)"),
+                measured_s=t_est + t_att, projected_layer_s=t_layer)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--tau", type=float, default=4.0)
+    ap.add_argument("--seqlen", type=int, default=131072)
+    ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by KV head with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import block_sparse_long_estimate_amd as fp
+    import block_sparse_long_estimate_amd._native as N
+    N.load()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    cfg = synth.config(3, S=args.seqlen, tau=args.tau)
+    t0 = time.time()
+    inputs = synth.gen_fixed_multi(cfg, ("bf16",) if args.no_fp8 else ("bf16", "fp8"))
+    log(f"generated S={cfg.S} inputs in {time.time() - t0:.1f} s")
+    bf, _ = time_path(fp, N, inputs["bf16"], args.tau, args.steps, args.warmup, "bf16")
+    log(f"bf16: {json.dumps(bf)}")
+    f8 = None
+    if not args.no_fp8:
+        f8, _ = time_path(fp, N, inputs["fp8"], args.tau, args.steps, args.warmup, "fp8")
+        log(f"fp8: {json.dumps(f8)}")
+    cpu = None
+    if not args.no_cpu_baseline:
+        t0 = time.time()
+        cpu = cpu_baseline(inputs["bf16"], args.tau)
+        log(f"cpu baseline ({time.time() - t0:.1f} s): {json.dumps(cpu)}")
+
+    att_peak = PEAK_TFLOPS["bf16"]
+    line = {
+        "metric": "prefill attn ms/layer + dense-equiv TFLOP/s at 128K GQA bf16/fp8; MFMA util",
+        "value": round(bf["dense_equiv_tflops"], 2),
+        "unit": "TFLOP/s (dense-equivalent)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(bf["ms_per_step"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"one layer, S={cfg.S}, 32 query / 8 KV heads, head dim 128, "
+                               f"128x128 blocks, tau={args.tau}, random-walk K/V with sink and "
+                               f"16 planted blocks per KV head, seed {cfg.seed}",
+                   "seq_len": cfg.S, "batch": 1, "tau": args.tau, "block": 128},
+        "kept_fraction": round(bf["kept_fraction"], 5),
+        "ms_per_layer": {"total": round(bf["ms_per_step"], 4), "estimate": round(bf["ms_estimate"], 4),
+                         "select": round(bf["ms_select"], 4), "attention": round(bf["ms_attention"], 4)},
+        "mfma_util_kept": round(bf["attn_kept_tflops"] / att_peak, 4),
+        "mfma_util_executed": round(bf["attn_executed_tflops"] / att_peak, 4),
+        "estimator_gbs": round(bf["estimate_gbs"], 1), "select_gbs": round(bf["select_gbs"], 1),
+        "roofline": {"bound": "mfma", "kernel": "attn_kernel (fp_sparse_prefill)",
+                     "achieved": round(bf["attn_kept_tflops"], 2), "peak": att_peak,
+                     "unit": "TFLOP/s", "frac": round(bf["attn_kept_tflops"] / att_peak, 4),
+                     "traffic": None},
+    }
+    if f8 is not None:
+        line["fp8"] = {"ms_per_layer": round(f8["ms_per_step"], 4),
+                       "dense_equiv_tflops": round(f8["dense_equiv_tflops"], 2),
+                       "ms_attention": round(f8["ms_attention"], 4),
+                       "kept_fraction": round(f8["kept_fraction"], 5),
+                       "attn_kept_tflops": round(f8["attn_kept_tflops"], 2),
+                       "mfma_util_kept": round(f8["attn_kept_tflops"] / PEAK_TFLOPS["fp8"], 4),
+                       "estimator_gbs": round(f8["estimate_gbs"], 1)}
+    if cpu is not None:
+        line["cpu_baseline"] = {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")}
+        line["cpu_baseline"]["value"] = round(cpu["value"], 6)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -269,29 +269,56 @@ class FixedInputs:
 
 def gen_fixed(cfg: Config) -> FixedInputs:
     """Inputs for a fixed-shape configuration (every sequence has S tokens)."""
-    S, d = cfg.S, cfg.d
-    fp8 = cfg.dtype == "fp8"
-    tdt = torch.uint8 if fp8 else torch.bfloat16
-    q = torch.empty((cfg.batch, S, cfg.Hq, d), dtype=tdt)
-    k = torch.empty((cfg.batch, S, cfg.Hkv, d), dtype=tdt)
-    v = torch.empty((cfg.batch, S, cfg.Hkv, d), dtype=tdt)
-    nsb = (S + SCALE_BLOCK - 1) // SCALE_BLOCK
-    scales = {}
-    if fp8:
-        scales = {n: torch.empty((cfg.batch, H, nsb), dtype=torch.float32)
-                  for n, H in (("q", cfg.Hq), ("k", cfg.Hkv), ("v", cfg.Hkv))}
-    dst = {"q": q, "k": k, "v": v}
+    return gen_fixed_multi(cfg, (cfg.dtype,))[cfg.dtype]
+
+
+def gen_fixed_multi(cfg: Config, dtypes=("bf16", "fp8")):
+    """One draw of a fixed-shape configuration stored in several formats
+    ({"bf16": FixedInputs, "fp8": FixedInputs}); the fp8 codes come from the
+    same float64 values as the bf16 tensors."""
+    outs = {}
+    for dt in dtypes:
+        outs[dt] = _alloc_fixed(replace(cfg, dtype=dt))
     metas = []
     for b, ss in enumerate(np.random.SeedSequence(cfg.seed).spawn(cfg.batch)):
         def store(kind, h, x, b=b):
-            if fp8:
-                codes, sc = quantize_fp8(x)
-                dst[kind][b, :, h, :] = codes
-                scales[kind][b, h, :] = torch.from_numpy(sc)
-            else:
-                dst[kind][b, :, h, :] = _to_bf16(x)
-        metas.append(_gen_sequence(cfg, S, ss, store, fp8))
-    return FixedInputs(cfg, q, k, v, scales.get("q"), scales.get("k"), scales.get("v"), metas)
+            for o in outs.values():
+                o.store(kind, b, h, x)
+        metas.append(_gen_sequence(cfg, cfg.S, ss, store, False))
+    res = {}
+    for dt, o in outs.items():
+        fi = o.finish()
+        fi.meta = metas
+        res[dt] = fi
+    return res
+
+
+class _alloc_fixed:
+    def __init__(self, cfg: Config):
+        S, d = cfg.S, cfg.d
+        self.cfg = cfg
+        self.fp8 = cfg.dtype == "fp8"
+        tdt = torch.uint8 if self.fp8 else torch.bfloat16
+        self.t = {"q": torch.empty((cfg.batch, S, cfg.Hq, d), dtype=tdt),
+                  "k": torch.empty((cfg.batch, S, cfg.Hkv, d), dtype=tdt),
+                  "v": torch.empty((cfg.batch, S, cfg.Hkv, d), dtype=tdt)}
+        nsb = (S + SCALE_BLOCK - 1) // SCALE_BLOCK
+        self.sc = {}
+        if self.fp8:
+            self.sc = {n: torch.empty((cfg.batch, H, nsb), dtype=torch.float32)
+                       for n, H in (("q", cfg.Hq), ("k", cfg.Hkv), ("v", cfg.Hkv))}
+
+    def store(self, kind, b, h, x):
+        if self.fp8:
+            codes, sc = quantize_fp8(x)
+            self.t[kind][b, :, h, :] = codes
+            self.sc[kind][b, h, :] = torch.from_numpy(sc)
+        else:
+            self.t[kind][b, :, h, :] = _to_bf16(x)
+
+    def finish(self) -> "FixedInputs":
+        return FixedInputs(self.cfg, self.t["q"], self.t["k"], self.t["v"], self.sc.get("q"),
+                           self.sc.get("k"), self.sc.get("v"), [])
 
 
 # --------------------------------------------------------------------------
