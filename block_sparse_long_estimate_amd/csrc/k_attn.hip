@@ -508,23 +508,282 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(Geo geo, AttnArgs a) {
     if (a.lse && lh == 0) a.lse[a.la.off(b, s, t, h)] = (m + __log2f(ltot)) * LN2;
 }
 
+// ===========================================================================
+// bf16 kernel: 8 wavefronts x 32 packed query rows (M = 256 per workgroup).
+// K and V tiles live row-major in LDS (256-byte rows, 16-byte chunks XOR-
+// swizzled by row) and are filled one tile ahead by direct global->LDS loads
+// (no VGPR staging); the V^T operand of PV comes from ds_read_b64_tr_b16.
+// ===========================================================================
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// byte offset of 16-byte chunk c of row r in a swizzled 256-byte-row tile
+__device__ __forceinline__ int swz(int r, int c) { return (r << 8) | (((c ^ r) & 15) << 4); }
+
+template <int BLK, bool PAGED>
+__device__ __forceinline__ void issue_kv(const AttnArgs& a, int b, int L, int g, int j,
+                                         uint8_t* kbuf, uint8_t* vbuf, int wave, int lane) {
+    constexpr int KBS = BLK * 256 / 1024;            // 1-KiB pieces per tile
+    const int rmax = L - 1 - j * BLK;                 // rows past the sequence repeat its last key
+    const int pos = lane & 15;
+#pragma unroll
+    for (int t0 = 0; t0 < KBS; t0 += 8) {
+        const int t = t0 + wave;
+        const int r = 4 * t + (lane >> 4);
+        const int c = (pos ^ r) & 15;
+        const int sk = j * BLK + min(r, rmax);
+        const __bf16* kp = (const __bf16*)a.k + a.ka.template off<PAGED>(b, sk, g) + c * 8;
+        const __bf16* vp = (const __bf16*)a.v + a.va.template off<PAGED>(b, sk, g) + c * 8;
+        __builtin_amdgcn_global_load_lds((const void*)kp, (lds_void*)(kbuf + t * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)vp, (lds_void*)(vbuf + t * 1024), 16, 0, 0);
+    }
+}
+
+template <int NKB>
+__device__ __forceinline__ void qk_swz(const uint8_t* kt, const bf16x8 (&qf)[8], int n, int lh,
+                                       f32x16 (&sacc)[NKB], bool accumulate) {
+    if (!accumulate) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) sacc[kb][v] = 0.f;
+    }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            const bf16x8 aop = *(const bf16x8*)(kt + swz(kb * 32 + n, 2 * ks + lh));
+            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, qf[ks], sacc[kb], 0, 0, 0);
+        }
+}
+
+// O^T += V^T P^T: A operand = V^T fragment gathered by two transpose reads
+// (16-lane group: lane 4e + r addresses V[k0 + e][d0 + 4r .. +4], lane i
+// receives V[k0 + e][d0 + i] for e = 0..3); B operand = P from registers.
+template <int NKB>
+__device__ __forceinline__ void pv_tr(const f32x16 (&sacc)[NKB], const uint8_t* vt, int lane,
+                                      f32x16 (&oacc)[4]) {
+    const int jj = lane & 15, q = lane >> 4;
+    const int rsub = 4 * (q >> 1) + (jj >> 2);
+    const int dsub = 16 * (q & 1) + 4 * (jj & 3);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            bf16x8 bop;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bop[e] = (__bf16)sacc[kb][8 * s2 + e];
+#pragma unroll
+            for (int db = 0; db < 4; ++db) {
+                s16x4 h[2];
+#pragma unroll
+                for (int aa = 0; aa < 2; ++aa) {
+                    const int row = kb * 32 + 16 * s2 + 8 * aa + rsub;
+                    const int d = 32 * db + dsub;
+                    const uint8_t* ptr = vt + swz(row, d >> 3) + (d & 7) * 2;
+                    h[aa] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) s16x4*)(ptr));
+                }
+                const s16x4 h0 = h[0], h1 = h[1];
+                typedef short s16x8 __attribute__((ext_vector_type(8)));
+                const s16x8 cat = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+                const bf16x8 aop = __builtin_bit_cast(bf16x8, cat);
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop, oacc[db], 0, 0, 0);
+            }
+        }
+}
+
+template <int BLK, bool PAGED, typename Geo>
+__global__ __launch_bounds__(512, 1) void attn_bf16_kernel(Geo geo, AttnArgs a) {
+    constexpr int NKB = BLK / 32;
+    constexpr int TILE = BLK * 256;                 // bytes of one K (or V) tile
+    // two distinct buffers per operand (not one indexed array), so the
+    // compiler can tell the tile being read from the tile being loaded
+    __shared__ __align__(1024) uint8_t kA[TILE];
+    __shared__ __align__(1024) uint8_t kB[TILE];
+    __shared__ __align__(1024) uint8_t vA[TILE];
+    __shared__ __align__(1024) uint8_t vB[TILE];
+    __shared__ uint32_t kept[MAX_NB / 32];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 31, lh = lane >> 5;
+    const float NEG_INF = -__builtin_inff();
+
+    const int u = blockIdx.x;
+    const int xcd = u & 7, k8 = u >> 3;
+    const int pidx = 8 * (k8 / a.slices) + xcd;
+    const int slice = k8 % a.slices;
+    if (pidx >= a.rows) return;
+    const int r = a.sched ? a.sched[pidx] : pidx;
+    const int b = geo.seq_of_row(r);
+    const SeqDesc s = geo.seq(b);
+    const int rl = r - s.row0;
+    const int g = rl / s.nq, il = rl % s.nq;
+    const int i = s.i0 + il;
+    const int t_lo = max(i * BLK, s.P), t_hi = min((i + 1) * BLK, s.L);
+    const int G = a.G;
+    const int npk = G * (t_hi - t_lo);
+    if (slice * 256 >= npk) return;                  // uniform over the workgroup
+
+    const int prow = slice * 256 + wave * 32 + n;
+    const bool valid = prow < npk;
+    const int tl = prow / G, hl = prow - tl * G;
+    const int t = t_lo + tl;
+    const int h = g * G + hl;
+
+    const int rp0 = a.row_ptr[r], nnz = a.row_ptr[r + 1] - rp0;
+    // first kept tile starts loading before anything else
+    const int j0 = a.col_idx[rp0];
+    issue_kv<BLK, PAGED>(a, b, s.L, g, j0, kA, vA, wave, lane);
+
+    bf16x8 qf[8];
+    {
+        const __bf16* qp = (const __bf16*)a.q + (valid ? a.qa.off(b, s, t, h) : 0);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            if (valid) qf[ks] = *(const bf16x8*)(qp + ks * 16 + lh * 8);
+            else
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qf[ks][e] = (__bf16)0.f;
+        }
+    }
+    const int nw = (i >> 5) + 1;
+    for (int w = tid; w < nw; w += 512) kept[w] = 0u;
+    __syncthreads();
+    for (int e = tid; e < nnz; e += 512) {
+        const int j = a.col_idx[rp0 + e];
+        atomicOr(&kept[j >> 5], 1u << (j & 31));
+    }
+
+    float m = NEG_INF, lsum = 0.f;
+    f32x16 oacc[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oacc[db][v] = 0.f;
+    f32x16 sacc[NKB];
+    const float f = a.scale_log2;
+    __syncthreads();                                  // tile 0 landed (barrier waits for loads)
+
+    // ---------------- kept blocks: exact tokens, one tile in flight ahead ----------------
+    // The column of the next tile is read before its loads are issued, so no
+    // vector-memory wait inside a tile's compute drains the prefetch.
+    auto kept_tile = [&](int j, const uint8_t* kc, const uint8_t* vc) __attribute__((always_inline)) {
+        qk_swz<NKB>(kc, qf, n, lh, sacc, false);
+        if (j == i) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int sk = j * BLK + kb * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
+                    sacc[kb][v] = sk > t ? NEG_INF : sacc[kb][v];
+                }
+        }
+        online_update<NKB>(sacc, f, 0.f, 0.f, m, lsum, oacc);
+        pv_tr<NKB>(sacc, vc, lane, oacc);
+    };
+    int jc = j0;
+    for (int e = 0; e < nnz; e += 2) {
+        const int jn = e + 1 < nnz ? a.col_idx[rp0 + e + 1] : 0;
+        if (e + 1 < nnz) issue_kv<BLK, PAGED>(a, b, s.L, g, jn, kB, vB, wave, lane);
+        kept_tile(jc, kA, vA);
+        __syncthreads();                              // tile e+1 landed; A is free
+        if (e + 1 >= nnz) break;
+        const int jn2 = e + 2 < nnz ? a.col_idx[rp0 + e + 2] : 0;
+        if (e + 2 < nnz) issue_kv<BLK, PAGED>(a, b, s.L, g, jn2, kA, vA, wave, lane);
+        kept_tile(jn, kB, vB);
+        __syncthreads();
+        jc = jn2;
+    }
+
+    // ---------------- pruned blocks: pooled pseudo-tokens ----------------
+    const float lnb2 = (BLK == 128) ? 7.f : 6.f;
+    for (int jt = 0; jt * BLK <= i - 1; ++jt) {
+        const int c_lo = max(1, jt * BLK), c_hi = min(i - 1, jt * BLK + BLK - 1);
+        uint32_t anyw = 0u;
+        for (int wd = c_lo >> 5; wd <= (c_hi >> 5); ++wd) anyw |= ~kept[wd] & range_bits(wd * 32, c_lo, c_hi);
+        if (anyw == 0u) continue;
+        // Kbar hi -> kbuf[0], Kbar lo -> kbuf[1], Vbar -> vbuf[0]; swizzled bf16 rows
+        for (int idx = tid; idx < BLK * 16; idx += 512) {
+            const int row = idx >> 4, c = idx & 15;
+            const int jp = jt * BLK + row;
+            float4 k0 = make_float4(0.f, 0.f, 0.f, 0.f), k1 = k0, v0 = k0, v1 = k0;
+            if (jp < s.nbk) {
+                const float* kp = a.kbar + kbar_row(s, a.Hkv, g, jp) * D + c * 8;
+                const float* vp = a.vbar + kbar_row(s, a.Hkv, g, jp) * D + c * 8;
+                k0 = *(const float4*)kp; k1 = *(const float4*)(kp + 4);
+                v0 = *(const float4*)vp; v1 = *(const float4*)(vp + 4);
+            }
+            const float kx[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+            uint4 hi, lo;
+            uint32_t* hp = (uint32_t*)&hi;
+            uint32_t* lp = (uint32_t*)&lo;
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                hp[e2] = pk_bf16(kx[2 * e2], kx[2 * e2 + 1]);
+                lp[e2] = pk_bf16(kx[2 * e2] - bf16_round(kx[2 * e2]), kx[2 * e2 + 1] - bf16_round(kx[2 * e2 + 1]));
+            }
+            const uint4 vv = make_uint4(pk_bf16(v0.x, v0.y), pk_bf16(v0.z, v0.w), pk_bf16(v1.x, v1.y),
+                                        pk_bf16(v1.z, v1.w));
+            *(uint4*)(kA + swz(row, c)) = hi;
+            *(uint4*)(kB + swz(row, c)) = lo;
+            *(uint4*)(vA + swz(row, c)) = vv;
+        }
+        __syncthreads();
+        qk_swz<NKB>(kA, qf, n, lh, sacc, false);
+        qk_swz<NKB>(kB, qf, n, lh, sacc, true);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            const int c0 = jt * BLK + kb * 32;
+            const uint32_t pw = ~kept[min(c0 >> 5, MAX_NB / 32 - 1)] & range_bits(c0, 1, i - 1);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int bit = 8 * (v >> 2) + 4 * lh + (v & 3);
+                sacc[kb][v] = ((pw >> bit) & 1u) ? sacc[kb][v] : NEG_INF;
+            }
+        }
+        online_update<NKB>(sacc, f, lnb2, 0.f, m, lsum, oacc);
+        pv_tr<NKB>(sacc, vA, lane, oacc);
+        __syncthreads();
+    }
+
+    // ---------------- epilogue ----------------
+    const float ltot = lsum + __shfl_xor(lsum, 32, 64);
+    if (!valid) return;
+    const float inv = 1.f / ltot;
+    __bf16* op = (__bf16*)a.o + a.oa.off(b, s, t, h);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            uint2 w;
+            w.x = pk_bf16(oacc[db][4 * q4] * inv, oacc[db][4 * q4 + 1] * inv);
+            w.y = pk_bf16(oacc[db][4 * q4 + 2] * inv, oacc[db][4 * q4 + 3] * inv);
+            *(uint2*)(op + db * 32 + q4 * 8 + lh * 4) = w;
+        }
+    if (a.lse && lh == 0) a.lse[a.la.off(b, s, t, h)] = (m + __log2f(ltot)) * LN2;
+}
+
 template <int BLK, typename Geo>
-static void attn_launch(const Geo& geo, const AttnArgs& a, int fp8, int paged, int units, hipStream_t st) {
+static void attn_launch(const Geo& geo, const AttnArgs& a, int fp8, int paged, hipStream_t st) {
     if (fp8) {
+        const int units = cdiv(a.rows, 8) * 8 * a.slices;
         if (paged) attn_kernel<BLK, true, true, Geo><<<units, 256, 0, st>>>(geo, a);
         else attn_kernel<BLK, true, false, Geo><<<units, 256, 0, st>>>(geo, a);
     } else {
-        if (paged) attn_kernel<BLK, false, true, Geo><<<units, 256, 0, st>>>(geo, a);
-        else attn_kernel<BLK, false, false, Geo><<<units, 256, 0, st>>>(geo, a);
+        AttnArgs b2 = a;
+        b2.slices = cdiv(a.G * BLK, 256);
+        const int units = cdiv(a.rows, 8) * 8 * b2.slices;
+        if (paged) attn_bf16_kernel<BLK, true, Geo><<<units, 512, 0, st>>>(geo, b2);
+        else attn_bf16_kernel<BLK, false, Geo><<<units, 512, 0, st>>>(geo, b2);
     }
 }
 
 template <typename Geo>
 static hipError_t attn_dispatch(const Geo& geo, const AttnArgs& a, int blk, int fp8, int paged,
                                 hipStream_t st) {
-    const int units = cdiv(a.rows, 8) * 8 * a.slices;
-    if (blk == 128) attn_launch<128>(geo, a, fp8, paged, units, st);
-    else attn_launch<64>(geo, a, fp8, paged, units, st);
+    if (blk == 128) attn_launch<128>(geo, a, fp8, paged, st);
+    else attn_launch<64>(geo, a, fp8, paged, st);
     return hipGetLastError();
 }
 
