@@ -57,7 +57,13 @@ __device__ __forceinline__ float bf16_round(float x) {
 
 // Online-softmax update for one tile held as S^T accumulators (log2 domain).
 // Element value s maps to logit s * f + bias; masked elements are -inf.
-template <int NKB>
+// value of x held by lane l ^ 32 (permlane32 swap, no LDS traffic)
+__device__ __forceinline__ float other_half(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(__lane_id() < 32 ? r[1] : r[0]);
+}
+
+template <int NKB, int LAZY = 0>
 __device__ __forceinline__ void online_update(f32x16 (&sacc)[NKB], float f, float bias, float lw,
                                               float& m, float& lsum, f32x16 (&oacc)[4]) {
     const float NEG_INF = -__builtin_inff();
@@ -66,16 +72,23 @@ __device__ __forceinline__ void online_update(f32x16 (&sacc)[NKB], float f, floa
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb][v]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mnew = fmaxf(m, mx * f + bias);
-    const float muse = mnew == NEG_INF ? 0.f : mnew;
-    const float alpha = __builtin_amdgcn_exp2f(m - muse);
-    lsum *= alpha;
+    mx = fmaxf(mx, other_half(mx));
+    const float mcand = fmaxf(m, mx * f + bias);
+    // Lazy rescale: keep the running reference m while the tile maximum stays
+    // within 2^LAZY of it (probabilities then reach at most 2^LAZY, harmless
+    // in fp32 sums and bf16 P); rescale only when some lane of the wave needs to.
+    const bool need = LAZY == 0 ? true : (mcand > m + (float)LAZY);
+    if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
+        const float mnew = need ? mcand : m;
+        const float alpha = __builtin_amdgcn_exp2f(m - (mnew == NEG_INF ? 0.f : mnew));
+        lsum *= alpha;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
-    m = mnew;
+            for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
+        m = mnew;
+    }
+    const float muse = m == NEG_INF ? 0.f : m;
     const float nb = bias - muse + lw;
     float ts = 0.f;
 #pragma unroll
@@ -492,7 +505,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(Geo geo, AttnArgs a) {
     }
 
     // ---------------- epilogue ----------------
-    const float ltot = lsum + __shfl_xor(lsum, 32, 64);
+    const float ltot = lsum + other_half(lsum);
     if (!valid) return;
     const float inv = (FP8 ? svmax * 0.00390625f : 1.f) / ltot;
     __bf16* op = (__bf16*)a.o + a.oa.off(b, s, t, h);
@@ -515,44 +528,67 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(Geo geo, AttnArgs a) {
 // (no VGPR staging); the V^T operand of PV comes from ds_read_b64_tr_b16.
 // ===========================================================================
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-// byte offset of 16-byte chunk c of row r in a swizzled 256-byte-row tile
-__device__ __forceinline__ int swz(int r, int c) { return (r << 8) | (((c ^ r) & 15) << 4); }
+// Tile layouts in LDS (bf16, 128 dims = 256 bytes of data per row):
+//   K rows every 272 bytes: the QK^T operand read (32 rows at one 16-byte
+//     chunk per lane half) hits row * 4 + chunk * 4 dwords mod 64, i.e. 16
+//     distinct bank groups per 16 lanes;
+//   V rows every 288 bytes: the transpose read (8 rows x 4 chunks x 2 halves)
+//     hits every 8-byte bank pair exactly twice.
+// Padding (not an XOR swizzle) keeps every operand address lane_base +
+// immediate, so no per-lane address table has to stay live in registers.
+constexpr int KSTR = 272;
+constexpr int VSTR = 288;
 
-template <int BLK, bool PAGED>
-__device__ __forceinline__ void issue_kv(const AttnArgs& a, int b, int L, int g, int j,
-                                         uint8_t* kbuf, uint8_t* vbuf, int wave, int lane) {
-    constexpr int KBS = BLK * 256 / 1024;            // 1-KiB pieces per tile
-    const int rmax = L - 1 - j * BLK;                 // rows past the sequence repeat its last key
-    const int pos = lane & 15;
+// Direct global->LDS loads of one K tile and one V tile: each wavefront
+// instruction fills 1 KiB of LDS (lane l -> bytes 16 l .. 16 l + 15), so a
+// lane works out which (row, chunk) its 16 bytes belong to; lanes that land on
+// row padding load a dummy chunk. Rows past the sequence repeat its last key.
+template <int STR, int BLK, bool PAGED>
+__device__ __forceinline__ void issue_tile(const __bf16* base, const KVAddr& ka, int b, int L, int g,
+                                           int j, lds_u8* buf, int wave, int lane) {
+    constexpr int PIECES = BLK * STR / 1024;
+    const int rmax = L - 1 - j * BLK;
 #pragma unroll
-    for (int t0 = 0; t0 < KBS; t0 += 8) {
+    for (int t0 = 0; t0 < PIECES; t0 += 8) {
         const int t = t0 + wave;
-        const int r = 4 * t + (lane >> 4);
-        const int c = (pos ^ r) & 15;
-        const int sk = j * BLK + min(r, rmax);
-        const __bf16* kp = (const __bf16*)a.k + a.ka.template off<PAGED>(b, sk, g) + c * 8;
-        const __bf16* vp = (const __bf16*)a.v + a.va.template off<PAGED>(b, sk, g) + c * 8;
-        __builtin_amdgcn_global_load_lds((const void*)kp, (lds_void*)(kbuf + t * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)vp, (lds_void*)(vbuf + t * 1024), 16, 0, 0);
+        if (t < PIECES) {
+            const int pb = t * 1024 + lane * 16;
+            const int row = pb / STR;
+            int ch = (pb - row * STR) >> 4;
+            ch = ch < 16 ? ch : 0;
+            const int sk = j * BLK + min(row, rmax);
+            const __bf16* src = base + ka.template off<PAGED>(b, sk, g) + ch * 8;
+            __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(buf + t * 1024), 16, 0, 0);
+        }
     }
 }
 
-template <int NKB>
-__device__ __forceinline__ void qk_swz(const uint8_t* kt, const bf16x8 (&qf)[8], int n, int lh,
-                                       f32x16 (&sacc)[NKB], bool accumulate) {
+template <int BLK, bool PAGED>
+__device__ __forceinline__ void issue_kv(const AttnArgs& a, int b, int L, int g, int j,
+                                         lds_u8* kbuf, lds_u8* vbuf, int wave, int lane) {
+    issue_tile<KSTR, BLK, PAGED>((const __bf16*)a.k, a.ka, b, L, g, j, kbuf, wave, lane);
+    issue_tile<VSTR, BLK, PAGED>((const __bf16*)a.v, a.va, b, L, g, j, vbuf, wave, lane);
+}
+
+// S^T for key blocks kb0 .. kb0 + NB - 1 (32 keys each) of the tile.
+template <int NB>
+__device__ __forceinline__ void qk_pad(const lds_u8* kt, const bf16x8 (&qf)[8], int n, int lh, int kb0,
+                                       f32x16 (&sacc)[NB], bool accumulate) {
     if (!accumulate) {
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+        for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
             for (int v = 0; v < 16; ++v) sacc[kb][v] = 0.f;
     }
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            const bf16x8 aop = *(const bf16x8*)(kt + swz(kb * 32 + n, 2 * ks + lh));
+        for (int kb = 0; kb < NB; ++kb) {
+            const bf16x8 aop = *(const lds_bf16x8*)(kt + ((kb0 + kb) * 32 + n) * KSTR + (2 * ks + lh) * 16);
             sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, qf[ks], sacc[kb], 0, 0, 0);
         }
 }
@@ -560,14 +596,14 @@ __device__ __forceinline__ void qk_swz(const uint8_t* kt, const bf16x8 (&qf)[8],
 // O^T += V^T P^T: A operand = V^T fragment gathered by two transpose reads
 // (16-lane group: lane 4e + r addresses V[k0 + e][d0 + 4r .. +4], lane i
 // receives V[k0 + e][d0 + i] for e = 0..3); B operand = P from registers.
-template <int NKB>
-__device__ __forceinline__ void pv_tr(const f32x16 (&sacc)[NKB], const uint8_t* vt, int lane,
+template <int NB>
+__device__ __forceinline__ void pv_tr(const f32x16 (&sacc)[NB], const lds_u8* vt, int lane, int kb0,
                                       f32x16 (&oacc)[4]) {
     const int jj = lane & 15, q = lane >> 4;
     const int rsub = 4 * (q >> 1) + (jj >> 2);
     const int dsub = 16 * (q & 1) + 4 * (jj & 3);
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
             bf16x8 bop;
@@ -578,9 +614,9 @@ __device__ __forceinline__ void pv_tr(const f32x16 (&sacc)[NKB], const uint8_t* 
                 s16x4 h[2];
 #pragma unroll
                 for (int aa = 0; aa < 2; ++aa) {
-                    const int row = kb * 32 + 16 * s2 + 8 * aa + rsub;
+                    const int row = (kb0 + kb) * 32 + 16 * s2 + 8 * aa + rsub;
                     const int d = 32 * db + dsub;
-                    const uint8_t* ptr = vt + swz(row, d >> 3) + (d & 7) * 2;
+                    const lds_u8* ptr = vt + row * VSTR + d * 2;
                     h[aa] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                         (__attribute__((address_space(3))) s16x4*)(ptr));
                 }
@@ -596,13 +632,18 @@ __device__ __forceinline__ void pv_tr(const f32x16 (&sacc)[NKB], const uint8_t* 
 template <int BLK, bool PAGED, typename Geo>
 __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(Geo geo, AttnArgs a) {
     constexpr int NKB = BLK / 32;
-    constexpr int TILE = BLK * 256;                 // bytes of one K (or V) tile
+    constexpr int KTILE = BLK * KSTR;
+    constexpr int VTILE = BLK * VSTR;
     // two distinct buffers per operand (not one indexed array), so the
     // compiler can tell the tile being read from the tile being loaded
-    __shared__ __align__(1024) uint8_t kA[TILE];
-    __shared__ __align__(1024) uint8_t kB[TILE];
-    __shared__ __align__(1024) uint8_t vA[TILE];
-    __shared__ __align__(1024) uint8_t vB[TILE];
+    __shared__ __align__(1024) uint8_t kA_[KTILE];
+    __shared__ __align__(1024) uint8_t kB_[KTILE];
+    __shared__ __align__(1024) uint8_t vA_[VTILE];
+    __shared__ __align__(1024) uint8_t vB_[VTILE];
+    lds_u8* const kA = (lds_u8*)kA_;
+    lds_u8* const kB = (lds_u8*)kB_;
+    lds_u8* const vA = (lds_u8*)vA_;
+    lds_u8* const vB = (lds_u8*)vB_;
     __shared__ uint32_t kept[MAX_NB / 32];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -661,26 +702,29 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(Geo geo, AttnArgs a) 
     for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int v = 0; v < 16; ++v) oacc[db][v] = 0.f;
-    f32x16 sacc[NKB];
     const float f = a.scale_log2;
     __syncthreads();                                  // tile 0 landed (barrier waits for loads)
 
     // ---------------- kept blocks: exact tokens, one tile in flight ahead ----------------
     // The column of the next tile is read before its loads are issued, so no
     // vector-memory wait inside a tile's compute drains the prefetch.
-    auto kept_tile = [&](int j, const uint8_t* kc, const uint8_t* vc) __attribute__((always_inline)) {
-        qk_swz<NKB>(kc, qf, n, lh, sacc, false);
-        if (j == i) {
+    auto kept_tile = [&](int j, const lds_u8* kc, const lds_u8* vc) __attribute__((always_inline)) {
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
+        for (int hf = 0; hf < NKB / 2; ++hf) {        // 64 keys at a time: 32 S registers live
+            f32x16 sh[2];
+            qk_pad<2>(kc, qf, n, lh, 2 * hf, sh, false);
+            if (j == i) {
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int sk = j * BLK + kb * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
-                    sacc[kb][v] = sk > t ? NEG_INF : sacc[kb][v];
-                }
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int sk = j * BLK + (2 * hf + kb) * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
+                        sh[kb][v] = sk > t ? NEG_INF : sh[kb][v];
+                    }
+            }
+            online_update<2, 8>(sh, f, 0.f, 0.f, m, lsum, oacc);
+            pv_tr<2>(sh, vc, lane, 2 * hf, oacc);
         }
-        online_update<NKB>(sacc, f, 0.f, 0.f, m, lsum, oacc);
-        pv_tr<NKB>(sacc, vc, lane, oacc);
     };
     int jc = j0;
     for (int e = 0; e < nnz; e += 2) {
@@ -725,30 +769,36 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(Geo geo, AttnArgs a) 
             }
             const uint4 vv = make_uint4(pk_bf16(v0.x, v0.y), pk_bf16(v0.z, v0.w), pk_bf16(v1.x, v1.y),
                                         pk_bf16(v1.z, v1.w));
-            *(uint4*)(kA + swz(row, c)) = hi;
-            *(uint4*)(kB + swz(row, c)) = lo;
-            *(uint4*)(vA + swz(row, c)) = vv;
+            typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+            typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+            *(lds_u32x4*)(kA + row * KSTR + c * 16) = u32x4{hi.x, hi.y, hi.z, hi.w};
+            *(lds_u32x4*)(kB + row * KSTR + c * 16) = u32x4{lo.x, lo.y, lo.z, lo.w};
+            *(lds_u32x4*)(vA + row * VSTR + c * 16) = u32x4{vv.x, vv.y, vv.z, vv.w};
         }
         __syncthreads();
-        qk_swz<NKB>(kA, qf, n, lh, sacc, false);
-        qk_swz<NKB>(kB, qf, n, lh, sacc, true);
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            const int c0 = jt * BLK + kb * 32;
-            const uint32_t pw = ~kept[min(c0 >> 5, MAX_NB / 32 - 1)] & range_bits(c0, 1, i - 1);
+        for (int hf = 0; hf < NKB / 2; ++hf) {
+            f32x16 sh[2];
+            qk_pad<2>(kA, qf, n, lh, 2 * hf, sh, false);
+            qk_pad<2>(kB, qf, n, lh, 2 * hf, sh, true);
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int bit = 8 * (v >> 2) + 4 * lh + (v & 3);
-                sacc[kb][v] = ((pw >> bit) & 1u) ? sacc[kb][v] : NEG_INF;
+            for (int kb = 0; kb < 2; ++kb) {
+                const int c0 = jt * BLK + (2 * hf + kb) * 32;
+                const uint32_t pw = ~kept[min(c0 >> 5, MAX_NB / 32 - 1)] & range_bits(c0, 1, i - 1);
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int bit = 8 * (v >> 2) + 4 * lh + (v & 3);
+                    sh[kb][v] = ((pw >> bit) & 1u) ? sh[kb][v] : NEG_INF;
+                }
             }
+            online_update<2, 8>(sh, f, lnb2, 0.f, m, lsum, oacc);
+            pv_tr<2>(sh, vA, lane, 2 * hf, oacc);
         }
-        online_update<NKB>(sacc, f, lnb2, 0.f, m, lsum, oacc);
-        pv_tr<NKB>(sacc, vA, lane, oacc);
         __syncthreads();
     }
 
     // ---------------- epilogue ----------------
-    const float ltot = lsum + __shfl_xor(lsum, 32, 64);
+    const float ltot = lsum + other_half(lsum);
     if (!valid) return;
     const float inv = 1.f / ltot;
     __bf16* op = (__bf16*)a.o + a.oa.off(b, s, t, h);
