@@ -567,9 +567,46 @@ __device__ __forceinline__ void issue_tile(const __bf16* base, const KVAddr& ka,
     }
 }
 
+// Lane offsets (elements, relative to the tile's first key row) of the
+// pieces this lane loads, for contiguous K/V; computed once per workgroup.
+template <int STR, int BLK>
+struct TileOffs {
+    static constexpr int PIECES = BLK * STR / 1024;
+    static constexpr int NP = (PIECES + 7) / 8;
+    int off[NP];
+    __device__ __forceinline__ void init(long long tok_stride, int wave, int lane) {
+#pragma unroll
+        for (int k = 0; k < NP; ++k) {
+            const int pb = (k * 8 + wave) * 1024 + lane * 16;
+            const int row = pb / STR;
+            int ch = (pb - row * STR) >> 4;
+            ch = ch < 16 ? ch : 0;
+            off[k] = (int)(row * tok_stride) + ch * 8;
+        }
+    }
+    // full tile (every row inside the sequence): one uniform base per tile
+    __device__ __forceinline__ void issue(const __bf16* tile_base, lds_u8* buf, int wave) const {
+#pragma unroll
+        for (int k = 0; k < NP; ++k) {
+            const int t = k * 8 + wave;
+            if (t < PIECES)
+                __builtin_amdgcn_global_load_lds((const void*)(tile_base + off[k]),
+                                                 (lds_void*)(buf + t * 1024), 16, 0, 0);
+        }
+    }
+};
+
 template <int BLK, bool PAGED>
 __device__ __forceinline__ void issue_kv(const AttnArgs& a, int b, int L, int g, int j,
-                                         lds_u8* kbuf, lds_u8* vbuf, int wave, int lane) {
+                                         lds_u8* kbuf, lds_u8* vbuf, int wave, int lane,
+                                         const TileOffs<KSTR, BLK>& ko, const TileOffs<VSTR, BLK>& vo) {
+    if (!PAGED && (j + 1) * BLK <= L) {
+        const long long k0 = a.ka.template off<false>(b, j * BLK, g);
+        const long long v0 = a.va.template off<false>(b, j * BLK, g);
+        ko.issue((const __bf16*)a.k + k0, kbuf, wave);
+        vo.issue((const __bf16*)a.v + v0, vbuf, wave);
+        return;
+    }
     issue_tile<KSTR, BLK, PAGED>((const __bf16*)a.k, a.ka, b, L, g, j, kbuf, wave, lane);
     issue_tile<VSTR, BLK, PAGED>((const __bf16*)a.v, a.va, b, L, g, j, vbuf, wave, lane);
 }
@@ -675,7 +712,13 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(Geo geo, AttnArgs a) 
     const int rp0 = a.row_ptr[r], nnz = a.row_ptr[r + 1] - rp0;
     // first kept tile starts loading before anything else
     const int j0 = a.col_idx[rp0];
-    issue_kv<BLK, PAGED>(a, b, s.L, g, j0, kA, vA, wave, lane);
+    TileOffs<KSTR, BLK> ko;
+    TileOffs<VSTR, BLK> vo;
+    if (!PAGED) {
+        ko.init(a.ka.st, wave, lane);
+        vo.init(a.va.st, wave, lane);
+    }
+    issue_kv<BLK, PAGED>(a, b, s.L, g, j0, kA, vA, wave, lane, ko, vo);
 
     bf16x8 qf[8];
     {
@@ -729,12 +772,12 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(Geo geo, AttnArgs a) 
     int jc = j0;
     for (int e = 0; e < nnz; e += 2) {
         const int jn = e + 1 < nnz ? a.col_idx[rp0 + e + 1] : 0;
-        if (e + 1 < nnz) issue_kv<BLK, PAGED>(a, b, s.L, g, jn, kB, vB, wave, lane);
+        if (e + 1 < nnz) issue_kv<BLK, PAGED>(a, b, s.L, g, jn, kB, vB, wave, lane, ko, vo);
         kept_tile(jc, kA, vA);
         __syncthreads();                              // tile e+1 landed; A is free
         if (e + 1 >= nnz) break;
         const int jn2 = e + 2 < nnz ? a.col_idx[rp0 + e + 2] : 0;
-        if (e + 2 < nnz) issue_kv<BLK, PAGED>(a, b, s.L, g, jn2, kA, vA, wave, lane);
+        if (e + 2 < nnz) issue_kv<BLK, PAGED>(a, b, s.L, g, jn2, kA, vA, wave, lane, ko, vo);
         kept_tile(jn, kB, vB);
         __syncthreads();
         jc = jn2;
