@@ -6,7 +6,8 @@ import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_NAME = "libfp_prefill.so"
-LIB_PATH = os.path.join(_HERE, LIB_NAME)
+# FP_PREFILL_LIB selects another build of the same library (same ABI).
+LIB_PATH = os.environ.get("FP_PREFILL_LIB") or os.path.join(_HERE, LIB_NAME)
 
 FP_OK = 0
 FP_ERR_INVALID = -1
