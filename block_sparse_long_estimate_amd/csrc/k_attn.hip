@@ -703,6 +703,11 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(Geo geo, AttnArgs a) 
     const int npk = G * (t_hi - t_lo);
     if (slice * 256 >= npk) return;                  // uniform over the workgroup
 
+    // The two wavefronts sharing a SIMD (w and w + 4) get different issue
+    // priorities, so after each barrier one runs its MFMA phase ahead and the
+    // other's softmax VALU work fills the MFMA pipe's shadow.
+    if (wave < 4) __builtin_amdgcn_s_setprio(1);
+
     const int prow = slice * 256 + wave * 32 + n;
     const bool valid = prow < npk;
     const int tl = prow / G, hl = prow - tl * G;

@@ -264,3 +264,4 @@ def test_paged_equals_contiguous(fp):
     assert np.array_equal(rp, out["row_ptr"].numpy())
     assert torch.equal(o, out["o"][0])
     assert torch.equal(lse, out["lse"][0])
+
