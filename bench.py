@@ -76,6 +76,7 @@ def time_path(fp, N, inp, tau, steps, warmup, label):
     sched = torch.empty(p.rows, **i32)
     lib = N.load()
     ws = torch.empty(N.check_size(lib.fp_workspace_size(p.ref)), dtype=torch.uint8, device=dev)
+    ws2 = torch.empty(N.check_size(lib.fp_prefill_workspace_size(p.ref)), dtype=torch.uint8, device=dev)
     o = torch.empty((c.batch, c.seqlen, c.num_q_heads, 128), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((c.batch, c.num_q_heads, c.seqlen), **f32)
     P = lambda t: None if t is None else t.data_ptr()
@@ -90,7 +91,8 @@ def time_path(fp, N, inp, tau, steps, warmup, label):
                                      P(sched), P(ws), ws.numel(), sh))
         ev[2].record(stream)
         N.check(lib.fp_sparse_prefill(p.ref, P(q), P(k), P(v), P(sc[0]), P(sc[1]), P(sc[2]), P(kbar),
-                                      P(vbar), P(row_ptr), P(col_idx), P(sched), P(o), P(lse), sh))
+                                      P(vbar), P(row_ptr), P(col_idx), P(sched), P(o), P(lse), P(ws2),
+                                      ws2.numel(), sh))
 
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     for _ in range(warmup):
@@ -139,12 +141,12 @@ def time_path(fp, N, inp, tau, steps, warmup, label):
     res["estimate_gbs"] = est_bytes / (res["ms_estimate"] * 1e-3) / 1e9
     sel_bytes = scores.numel() * 4 // 2 + (len(ci) + 3 * p.rows) * 4
     res["select_gbs"] = sel_bytes / (res["ms_select"] * 1e-3) / 1e9
-    del q, k, v, qbar, kbar, vbar, scores, o, lse, ws
+    del q, k, v, qbar, kbar, vbar, scores, o, lse, ws, ws2
     torch.cuda.empty_cache()
     return res, (rp, ci)
 
 
-def cpu_baseline(inp, tau, rows_sample=256):
+def cpu_baseline(inp, tau, rows_sample=768):
     """The fp64 oracle, as it stands, single-threaded, on a bounded sample of
     the same workload: E1-E5 for one KV head group (all query blocks) and E6
     for `rows_sample` (KV head, query block) rows spread over the sequence;
@@ -184,6 +186,28 @@ def cpu_baseline(inp, tau, rows_sample=256):
                 measured_s=t_est + t_att, projected_layer_s=t_layer)
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_S131072_tau4_traffic.json")
+KERNEL_SOURCE = os.path.join(ROOT, "block_sparse_long_estimate_amd", "csrc", "k_attn.hip")
+
+
+def measured_traffic(S, tau):
+    """HBM bytes per attention launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE readings (scaled by a plain copy kernel's readings), or None
+    when they were taken on another workload or another version of the
+    kernel source."""
+    import hashlib
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        with open(KERNEL_SOURCE, "rb") as f:
+            digest = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    if rec.get("kernel_source_sha256") != digest or rec.get("seq_len") != S or rec.get("tau") != tau:
+        return None
+    return rec["hbm_bytes_per_launch"]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -193,6 +217,9 @@ def main():
     ap.add_argument("--seqlen", type=int, default=131072)
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (3 times): the reference "
+                         "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -200,6 +227,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": 3}), flush=True)
+        return
     import synth
     import block_sparse_long_estimate_amd as fp
     import block_sparse_long_estimate_amd._native as N
@@ -241,10 +277,10 @@ def main():
         "mfma_util_kept": round(bf["attn_kept_tflops"] / att_peak, 4),
         "mfma_util_executed": round(bf["attn_executed_tflops"] / att_peak, 4),
         "estimator_gbs": round(bf["estimate_gbs"], 1), "select_gbs": round(bf["select_gbs"], 1),
-        "roofline": {"bound": "mfma", "kernel": "attn_kernel (fp_sparse_prefill)",
+        "roofline": {"bound": "mfma", "kernel": "attn_bf16_kernel (fp_sparse_prefill)",
                      "achieved": round(bf["attn_kept_tflops"], 2), "peak": att_peak,
                      "unit": "TFLOP/s", "frac": round(bf["attn_kept_tflops"] / att_peak, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic(cfg.S, args.tau)},
     }
     if f8 is not None:
         line["fp8"] = {"ms_per_layer": round(f8["ms_per_step"], 4),

@@ -120,16 +120,21 @@ def fp_select_blocks(p: Problem, scores: torch.Tensor, tau: float, with_sched: b
 
 def fp_sparse_prefill(p: Problem, q, k, v, kbar, vbar, row_ptr, col_idx, sched=None,
                       q_scale=None, k_scale=None, v_scale=None, with_lse: bool = True,
-                      o: Optional[torch.Tensor] = None):
+                      o: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
     """E6 -> (o bf16 like q, lse fp32 [batch, Hq, S] or None)."""
     c = p.c
     if o is None:
         o = torch.empty((c.batch, c.seqlen, c.num_q_heads, 128), dtype=torch.bfloat16, device=q.device)
     lse = torch.empty((c.batch, c.num_q_heads, c.seqlen), dtype=torch.float32,
                       device=q.device) if with_lse else None
-    N.check(N.load().fp_sparse_prefill(p.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(q_scale), _ptr(k_scale),
-                                       _ptr(v_scale), _ptr(kbar), _ptr(vbar), _ptr(row_ptr),
-                                       _ptr(col_idx), _ptr(sched), _ptr(o), _ptr(lse), _stream()))
+    lib = N.load()
+    if workspace is None:
+        workspace = torch.empty(N.check_size(lib.fp_prefill_workspace_size(p.ref)), dtype=torch.uint8,
+                                device=q.device)
+    N.check(lib.fp_sparse_prefill(p.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(q_scale), _ptr(k_scale),
+                                  _ptr(v_scale), _ptr(kbar), _ptr(vbar), _ptr(row_ptr),
+                                  _ptr(col_idx), _ptr(sched), _ptr(o), _ptr(lse), _ptr(workspace),
+                                  workspace.numel(), _stream()))
     return o, lse
 
 

@@ -19,6 +19,7 @@ FP_DTYPE_FP8_E4M3 = 1
 
 EXPORTS = (
     "fp_version", "fp_last_error", "fp_num_rows", "fp_max_nnz", "fp_workspace_size",
+    "fp_prefill_workspace_size",
     "fp_block_scores", "fp_select_blocks", "fp_sparse_prefill",
     "fp_varlen_num_rows", "fp_varlen_max_nnz", "fp_varlen_workspace_size",
     "fp_sparse_prefill_paged",
@@ -65,7 +66,7 @@ def load() -> ctypes.CDLL:
     vp, i32p = ctypes.c_void_p, ctypes.c_void_p
     lib.fp_version.restype = ctypes.c_char_p
     lib.fp_last_error.restype = ctypes.c_char_p
-    for name in ("fp_num_rows", "fp_max_nnz", "fp_workspace_size"):
+    for name in ("fp_num_rows", "fp_max_nnz", "fp_workspace_size", "fp_prefill_workspace_size"):
         f = getattr(lib, name)
         f.restype, f.argtypes = ctypes.c_int64, [P]
     for name in ("fp_varlen_num_rows", "fp_varlen_max_nnz", "fp_varlen_workspace_size"):
@@ -77,7 +78,8 @@ def load() -> ctypes.CDLL:
     lib.fp_select_blocks.argtypes = [P, vp, ctypes.c_float, vp, vp, ctypes.c_int64, vp, vp,
                                      ctypes.c_size_t, vp]
     lib.fp_sparse_prefill.restype = ctypes.c_int
-    lib.fp_sparse_prefill.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.fp_sparse_prefill.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                      ctypes.c_size_t, vp]
     lib.fp_sparse_prefill_paged.restype = ctypes.c_int
     lib.fp_sparse_prefill_paged.argtypes = [VP, vp, i32p, i32p, vp, vp, vp, ctypes.c_float, vp,
                                             vp, ctypes.c_int64, vp, vp, vp, ctypes.c_size_t, vp]

@@ -72,6 +72,9 @@ int check_fixed(const fp_problem* p) {
             if ((st[t][e] * esz) % 16) return fail(FP_ERR_INVALID, "strides must be multiples of 16 bytes");
     for (int e = 0; e < 3; ++e)
         if ((p->o_stride[e] * 2) % 8) return fail(FP_ERR_INVALID, "o strides must be multiples of 8 bytes");
+    // a K/V tile's per-lane load offsets are 32-bit byte offsets
+    if (p->k_stride[1] * esz * p->block >= (1LL << 31) || p->v_stride[1] * esz * p->block >= (1LL << 31))
+        return fail(FP_ERR_UNSUPPORTED, "k/v token stride x block must stay below 2 GiB");
     return FP_OK;
 }
 
@@ -102,6 +105,9 @@ SelectWs select_ws(long long rows, int max_nbk) {
     w.total = w.bits + align_up((size_t)rows * w.nbw * 4);
     return w;
 }
+
+// bf16 copies of the pooled keys (hi, lo) and values used by the summary tiles
+size_t summary_ws_bytes(long long pooled_rows) { return 3 * align_up((size_t)pooled_rows * D * 2); }
 
 }  // namespace
 
@@ -145,6 +151,12 @@ int64_t fp_max_nnz(const fp_problem* p) {
     if (rc) return rc;
     const int64_t nb = cdiv(p->seqlen, p->block);
     return (int64_t)p->batch * p->num_kv_heads * nb * (nb + 1) / 2;
+}
+
+int64_t fp_prefill_workspace_size(const fp_problem* p) {
+    int rc = check_fixed(p);
+    if (rc) return rc;
+    return (int64_t)summary_ws_bytes((long long)p->batch * p->num_kv_heads * cdiv(p->seqlen, p->block));
 }
 
 int64_t fp_workspace_size(const fp_problem* p) {
@@ -230,11 +242,16 @@ int fp_sparse_prefill(const fp_problem* p, const void* q, const void* k, const v
                       const float* q_scale, const float* k_scale, const float* v_scale,
                       const float* kbar, const float* vbar, const int32_t* row_ptr,
                       const int32_t* col_idx, const int32_t* sched, void* o, float* lse,
-                      void* stream) {
+                      void* workspace, size_t ws_bytes, void* stream) {
     int rc = check_fixed(p);
     if (rc) return rc;
-    if (!q || !k || !v || !kbar || !vbar || !row_ptr || !col_idx || !o)
+    if (!q || !k || !v || !kbar || !vbar || !row_ptr || !col_idx || !o || !workspace)
         return fail(FP_ERR_INVALID, "fp_sparse_prefill: NULL pointer");
+    const long long prow = (long long)p->batch * p->num_kv_heads * cdiv(p->seqlen, p->block);
+    if (ws_bytes < summary_ws_bytes(prow))
+        return fail(FP_ERR_CAPACITY, "fp_sparse_prefill: workspace %zu < %zu bytes", ws_bytes,
+                    summary_ws_bytes(prow));
+    if (misaligned(workspace, ALIGN)) return fail(FP_ERR_INVALID, "workspace must be 256-byte aligned");
     const bool fp8 = p->dtype == FP_DTYPE_FP8_E4M3;
     if (fp8 && (!q_scale || !k_scale || !v_scale))
         return fail(FP_ERR_INVALID, "fp_sparse_prefill: fp8 needs q_scale, k_scale and v_scale");
@@ -254,6 +271,12 @@ int fp_sparse_prefill(const fp_problem* p, const void* q, const void* k, const v
     a.ks = ScaleAddr{k_scale, (long long)p->num_kv_heads * nsb, nsb};
     a.vs = ScaleAddr{v_scale, (long long)p->num_kv_heads * nsb, nsb};
     a.kbar = kbar; a.vbar = vbar;
+    {
+        const size_t part = align_up((size_t)prow * D * 2);
+        a.kbar_hi = (const __bf16*)workspace;
+        a.kbar_lo = (const __bf16*)((char*)workspace + part);
+        a.vbar_bf = (const __bf16*)((char*)workspace + 2 * part);
+    }
     a.row_ptr = row_ptr; a.col_idx = col_idx; a.sched = sched;
     a.o = o; a.lse = lse;
     a.la = RowAddr{(long long)p->num_q_heads * p->seqlen, 1, p->seqlen};
@@ -261,7 +284,10 @@ int fp_sparse_prefill(const fp_problem* p, const void* q, const void* k, const v
     a.rows = p->batch * p->num_kv_heads * geo.nb;
     a.slices = cdiv(G * p->block, 128);
     a.scale_log2 = default_scale(p->softmax_scale, p->head_dim) * 1.4426950408889634f;
-    hipError_t e = launch_attn(&geo, nullptr, a, p->block, fp8, 0, (hipStream_t)stream);
+    hipError_t e = launch_summary_prep(kbar, vbar, (__bf16*)a.kbar_hi, (__bf16*)a.kbar_lo,
+                                       (__bf16*)a.vbar_bf, prow * D, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(FP_ERR_HIP, "summary prep launch: %s", hipGetErrorString(e));
+    e = launch_attn(&geo, nullptr, a, p->block, fp8, 0, (hipStream_t)stream);
     if (e != hipSuccess) return fail(FP_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
     return ok();
 }
@@ -277,7 +303,8 @@ struct VarPlan {
     int max_nbk = 0, total_qblocks = 0, total_kblocks = 0, total_tiles = 0;
     long long total_scores = 0;
     // workspace carve (byte offsets)
-    size_t o_table = 0, o_qbar = 0, o_kbar = 0, o_vbar = 0, o_scores = 0, o_sched = 0, o_sel = 0, total = 0;
+    size_t o_table = 0, o_qbar = 0, o_kbar = 0, o_vbar = 0, o_scores = 0, o_sched = 0, o_sel = 0, o_sum = 0,
+           total = 0;
     SelectWs sel;
 };
 
@@ -348,7 +375,8 @@ int check_varlen(const fp_varlen_problem* p, const int32_t* cu, const int32_t* l
     plan.o_scores = off; off = align_up(off + (size_t)sc * 4);
     plan.o_sched = off; off = align_up(off + (size_t)plan.rows * 4);
     plan.sel = select_ws(plan.rows, std::max(plan.max_nbk, 1));
-    plan.o_sel = off; off += plan.sel.total;
+    plan.o_sel = off; off = align_up(off + plan.sel.total);
+    plan.o_sum = off; off += summary_ws_bytes(kb * p->num_kv_heads);
     plan.total = off;
     return FP_OK;
 }
@@ -458,6 +486,12 @@ int fp_sparse_prefill_paged(const fp_varlen_problem* p, const void* q, const int
     a.ka = kva; a.va = kva;
     a.qs = a.ks = a.vs = ScaleAddr{nullptr, 0, 0};
     a.kbar = kbar; a.vbar = vbar;
+    {
+        const size_t part = align_up((size_t)plan.total_kblocks * p->num_kv_heads * D * 2);
+        a.kbar_hi = (const __bf16*)(ws + plan.o_sum);
+        a.kbar_lo = (const __bf16*)(ws + plan.o_sum + part);
+        a.vbar_bf = (const __bf16*)(ws + plan.o_sum + 2 * part);
+    }
     a.row_ptr = row_ptr; a.col_idx = col_idx; a.sched = sched;
     a.o = o; a.lse = lse;
     a.la = RowAddr{0, 1, plan.sum_q};
@@ -465,6 +499,9 @@ int fp_sparse_prefill_paged(const fp_varlen_problem* p, const void* q, const int
     a.rows = (int)plan.rows;
     a.slices = cdiv(G * p->block, 128);
     a.scale_log2 = default_scale(p->softmax_scale, p->head_dim) * 1.4426950408889634f;
+    e = launch_summary_prep(kbar, vbar, (__bf16*)a.kbar_hi, (__bf16*)a.kbar_lo, (__bf16*)a.vbar_bf,
+                            (long long)plan.total_kblocks * p->num_kv_heads * D, st);
+    if (e != hipSuccess) return fail(FP_ERR_HIP, "summary prep launch: %s", hipGetErrorString(e));
     e = launch_attn(nullptr, &geo, a, p->block, 0, 1, st);
     if (e != hipSuccess) return fail(FP_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
     return ok();

@@ -155,6 +155,7 @@ struct AttnArgs {
     RowAddr qa, oa; KVAddr ka, va;
     ScaleAddr qs, ks, vs;
     const float* kbar; const float* vbar;
+    const __bf16* kbar_hi; const __bf16* kbar_lo; const __bf16* vbar_bf;   // summary operands
     const int32_t* row_ptr; const int32_t* col_idx; const int32_t* sched;
     void* o; float* lse; RowAddr la;   // lse offset: b*sb + (q0+t-P)*st + h*sh
     int Hq, Hkv, G, rows, slices;
@@ -166,6 +167,8 @@ hipError_t launch_scores(const GeoFixed* gf, const GeoTable* gt, const ScoreArgs
 hipError_t launch_select(const GeoFixed* gf, const GeoTable* gt, const SelectArgs& a, hipStream_t st);
 hipError_t launch_attn(const GeoFixed* gf, const GeoTable* gt, const AttnArgs& a, int blk,
                        int fp8, int paged, hipStream_t st);
+hipError_t launch_summary_prep(const float* kbar, const float* vbar, __bf16* hi, __bf16* lo,
+                               __bf16* vb, long long nfloats, hipStream_t st);
 hipError_t launch_table_copy(const SeqDesc* host, int n, SeqDesc* dev, hipStream_t st);
 
 }  // namespace fp

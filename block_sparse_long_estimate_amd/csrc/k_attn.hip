@@ -551,6 +551,7 @@ template <int STR, int BLK, bool PAGED>
 __device__ __forceinline__ void issue_tile(const __bf16* base, const KVAddr& ka, int b, int L, int g,
                                            int j, lds_u8* buf, int wave, int lane) {
     constexpr int PIECES = BLK * STR / 1024;
+    asm volatile("" : "+v"(lane));   // recompute addresses per call, keep none live
     const int rmax = L - 1 - j * BLK;
 #pragma unroll
     for (int t0 = 0; t0 < PIECES; t0 += 8) {
@@ -567,13 +568,15 @@ __device__ __forceinline__ void issue_tile(const __bf16* base, const KVAddr& ka,
     }
 }
 
-// Lane offsets (elements, relative to the tile's first key row) of the
-// pieces this lane loads, for contiguous K/V; computed once per workgroup.
+// Lane byte offsets (relative to the tile's first key row) of the pieces
+// this lane loads, for contiguous K/V; computed once per workgroup. Unsigned
+// 32-bit offsets from a uniform base let each load use the scalar-base
+// addressing form, so only one register per piece stays live.
 template <int STR, int BLK>
 struct TileOffs {
     static constexpr int PIECES = BLK * STR / 1024;
     static constexpr int NP = (PIECES + 7) / 8;
-    int off[NP];
+    uint32_t off[NP];
     __device__ __forceinline__ void init(long long tok_stride, int wave, int lane) {
 #pragma unroll
         for (int k = 0; k < NP; ++k) {
@@ -581,7 +584,7 @@ struct TileOffs {
             const int row = pb / STR;
             int ch = (pb - row * STR) >> 4;
             ch = ch < 16 ? ch : 0;
-            off[k] = (int)(row * tok_stride) + ch * 8;
+            off[k] = (uint32_t)(row * tok_stride + ch * 8) * 2u;
         }
     }
     // full tile (every row inside the sequence): one uniform base per tile
@@ -590,7 +593,7 @@ struct TileOffs {
         for (int k = 0; k < NP; ++k) {
             const int t = k * 8 + wave;
             if (t < PIECES)
-                __builtin_amdgcn_global_load_lds((const void*)(tile_base + off[k]),
+                __builtin_amdgcn_global_load_lds((const void*)((const char*)tile_base + off[k]),
                                                  (lds_void*)(buf + t * 1024), 16, 0, 0);
         }
     }
@@ -666,22 +669,61 @@ __device__ __forceinline__ void pv_tr(const f32x16 (&sacc)[NB], const lds_u8* vt
         }
 }
 
+// Summary sub-tile m covers pooled columns [SUMC m, SUMC m + SUMC) (SUMC =
+// BLK / 2): its K tile holds the bf16 hi parts of those pooled keys in rows
+// 0 .. SUMC-1 and the lo parts in rows SUMC .. BLK-1, so one ordinary tile
+// load brings both, and the two halves of QK^T accumulate into one logit.
+template <int BLK>
+__device__ __forceinline__ void issue_summary(const AttnArgs& a, const SeqDesc& s, int g, int m,
+                                              lds_u8* kbuf, lds_u8* vbuf, int wave, int lane) {
+    constexpr int SUMC = BLK / 2;
+    // recompute the per-lane piece addresses here instead of keeping them
+    // live across the tile loop (registers are the scarce resource)
+    asm volatile("" : "+v"(lane));
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+        constexpr int KP = BLK * KSTR / 1024, VP = BLK * VSTR / 1024;
+        const int STR = w == 0 ? KSTR : VSTR;
+        const int PIECES = w == 0 ? KP : VP;
+        lds_u8* buf = w == 0 ? kbuf : vbuf;
+#pragma unroll
+        for (int t0 = 0; t0 < (w == 0 ? KP : VP); t0 += 8) {
+            const int t = t0 + wave;
+            if (t < PIECES) {
+                const int pb = t * 1024 + lane * 16;
+                const int row = pb / STR;
+                int ch = (pb - row * STR) >> 4;
+                ch = ch < 16 ? ch : 0;
+                const int part = row >= SUMC;                       // 0 hi / 1 lo (K); V: upper rows unused
+                if (w == 1 && part) continue;
+                const int jp = min(SUMC * m + row - part * SUMC, s.nbk - 1);
+                const long long pr = kbar_row(s, a.Hkv, g, jp) * D + ch * 8;
+                const __bf16* src = w == 0 ? (part ? a.kbar_lo : a.kbar_hi) + pr : a.vbar_bf + pr;
+                __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(buf + t * 1024), 16, 0, 0);
+            }
+        }
+    }
+}
+
 template <int BLK, bool PAGED, typename Geo>
 __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(Geo geo, AttnArgs a) {
     constexpr int NKB = BLK / 32;
+    constexpr int SB = NKB / 2;                     // 32-column blocks per summary sub-tile
+    constexpr int SUMC = BLK / 2;
     constexpr int KTILE = BLK * KSTR;
     constexpr int VTILE = BLK * VSTR;
+    constexpr int NONE = -0x7fffffff;
     // two distinct buffers per operand (not one indexed array), so the
     // compiler can tell the tile being read from the tile being loaded
     __shared__ __align__(1024) uint8_t kA_[KTILE];
     __shared__ __align__(1024) uint8_t kB_[KTILE];
     __shared__ __align__(1024) uint8_t vA_[VTILE];
     __shared__ __align__(1024) uint8_t vB_[VTILE];
+    __shared__ uint32_t kept[MAX_NB / 32];
     lds_u8* const kA = (lds_u8*)kA_;
     lds_u8* const kB = (lds_u8*)kB_;
     lds_u8* const vA = (lds_u8*)vA_;
     lds_u8* const vB = (lds_u8*)vB_;
-    __shared__ uint32_t kept[MAX_NB / 32];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 31, lh = lane >> 5;
@@ -715,7 +757,6 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(Geo geo, AttnArgs a) 
     const int h = g * G + hl;
 
     const int rp0 = a.row_ptr[r], nnz = a.row_ptr[r + 1] - rp0;
-    // first kept tile starts loading before anything else
     const int j0 = a.col_idx[rp0];
     TileOffs<KSTR, BLK> ko;
     TileOffs<VSTR, BLK> vo;
@@ -751,22 +792,54 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(Geo geo, AttnArgs a) 
 #pragma unroll
         for (int v = 0; v < 16; ++v) oacc[db][v] = 0.f;
     const float f = a.scale_log2;
-    __syncthreads();                                  // tile 0 landed (barrier waits for loads)
+    const float lnb2 = (BLK == 128) ? 7.f : 6.f;    // log2 |block| of a pruned pseudo-token
+    __syncthreads();                                  // tile 0 landed; kept bitmap complete
 
-    // ---------------- kept blocks: exact tokens, one tile in flight ahead ----------------
-    // The column of the next tile is read before its loads are issued, so no
-    // vector-memory wait inside a tile's compute drains the prefetch.
-    auto kept_tile = [&](int j, const lds_u8* kc, const lds_u8* vc) __attribute__((always_inline)) {
+    // Tile sequence: the kept blocks in column order (codes >= 0 are block
+    // indices), then the summary sub-tiles that hold at least one pruned
+    // column (code -1 - m for sub-tile m). The code of the next tile is known
+    // before its loads are issued, so no vector-memory wait inside a tile's
+    // compute drains the prefetch.
+    auto next_summary = [&](int m0) -> int {
+        for (int mm = m0; mm * SUMC <= i - 1; ++mm) {
+            const int c_lo = max(1, mm * SUMC), c_hi = min(i - 1, mm * SUMC + SUMC - 1);
+            uint32_t anyw = 0u;
+            for (int wd = c_lo >> 5; wd <= (c_hi >> 5); ++wd)
+                anyw |= ~kept[wd] & range_bits(wd * 32, c_lo, c_hi);
+            if (anyw) return -1 - mm;
+        }
+        return NONE;
+    };
+    // The next kept column comes from the LDS bitmap (no global-memory
+    // round trip between tiles).
+    auto next_code = [&](int code) -> int {
+        if (code >= 0) {
+            int wd = (code + 1) >> 5;
+            uint32_t w = code + 1 <= i ? kept[wd] & (~0u << ((code + 1) & 31)) : 0u;
+            while (w == 0u && wd < (i >> 5)) w = kept[++wd];
+            w = __builtin_amdgcn_readfirstlane(w);
+            wd = __builtin_amdgcn_readfirstlane(wd);
+            if (w != 0u) return wd * 32 + __builtin_ctz(w);
+            return next_summary(0);
+        }
+        return next_summary(-code);
+    };
+    auto issue = [&](int code, lds_u8* kb, lds_u8* vb) __attribute__((always_inline)) {
+        if (code >= 0) issue_kv<BLK, PAGED>(a, b, s.L, g, code, kb, vb, wave, lane, ko, vo);
+        else issue_summary<BLK>(a, s, g, -1 - code, kb, vb, wave, lane);
+    };
+    // Exact tokens of kept block `code`, 64 keys at a time (32 S registers live).
+    auto compute_kept = [&](int code, const lds_u8* kc, const lds_u8* vc) __attribute__((always_inline)) {
 #pragma unroll
-        for (int hf = 0; hf < NKB / 2; ++hf) {        // 64 keys at a time: 32 S registers live
+        for (int hf = 0; hf < NKB / 2; ++hf) {
             f32x16 sh[2];
             qk_pad<2>(kc, qf, n, lh, 2 * hf, sh, false);
-            if (j == i) {
+            if (code == i) {
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
-                        const int sk = j * BLK + (2 * hf + kb) * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
+                        const int sk = code * BLK + (2 * hf + kb) * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
                         sh[kb][v] = sk > t ? NEG_INF : sh[kb][v];
                     }
             }
@@ -774,75 +847,64 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(Geo geo, AttnArgs a) 
             pv_tr<2>(sh, vc, lane, 2 * hf, oacc);
         }
     };
-    int jc = j0;
-    for (int e = 0; e < nnz; e += 2) {
-        const int jn = e + 1 < nnz ? a.col_idx[rp0 + e + 1] : 0;
-        if (e + 1 < nnz) issue_kv<BLK, PAGED>(a, b, s.L, g, jn, kB, vB, wave, lane, ko, vo);
-        kept_tile(jc, kA, vA);
-        __syncthreads();                              // tile e+1 landed; A is free
-        if (e + 1 >= nnz) break;
-        const int jn2 = e + 2 < nnz ? a.col_idx[rp0 + e + 2] : 0;
-        if (e + 2 < nnz) issue_kv<BLK, PAGED>(a, b, s.L, g, jn2, kA, vA, wave, lane, ko, vo);
-        kept_tile(jn, kB, vB);
-        __syncthreads();
-        jc = jn2;
-    }
+    // Pooled pseudo-tokens of summary sub-tile -1 - code: hi and lo halves of
+    // QK^T accumulate into one logit per pooled column; pseudo-tokens of kept
+    // or non-causal columns are masked from the LDS bitmap.
+    auto compute_summary = [&](int code, const lds_u8* kc, const lds_u8* vc) __attribute__((always_inline)) {
+        const int mm = -1 - code;
+        f32x16 sh[SB];
+        qk_pad<SB>(kc, qf, n, lh, 0, sh, false);       // hi rows
+        qk_pad<SB>(kc, qf, n, lh, SB, sh, true);       // lo rows, same columns
+#pragma unroll
+        for (int kb = 0; kb < SB; ++kb) {
+            const int c0 = mm * SUMC + kb * 32;
+            const uint32_t pw = ~kept[min(c0 >> 5, MAX_NB / 32 - 1)] & range_bits(c0, 1, i - 1);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int bit = 8 * (v >> 2) + 4 * lh + (v & 3);
+                sh[kb][v] = ((pw >> bit) & 1u) ? sh[kb][v] : NEG_INF;
+            }
+        }
+        online_update<SB, 8>(sh, f, lnb2, 0.f, m, lsum, oacc);
+        pv_tr<SB>(sh, vc, lane, 0, oacc);
+    };
 
-    // ---------------- pruned blocks: pooled pseudo-tokens ----------------
-    const float lnb2 = (BLK == 128) ? 7.f : 6.f;
-    for (int jt = 0; jt * BLK <= i - 1; ++jt) {
-        const int c_lo = max(1, jt * BLK), c_hi = min(i - 1, jt * BLK + BLK - 1);
-        uint32_t anyw = 0u;
-        for (int wd = c_lo >> 5; wd <= (c_hi >> 5); ++wd) anyw |= ~kept[wd] & range_bits(wd * 32, c_lo, c_hi);
-        if (anyw == 0u) continue;
-        // Kbar hi -> kbuf[0], Kbar lo -> kbuf[1], Vbar -> vbuf[0]; swizzled bf16 rows
-        for (int idx = tid; idx < BLK * 16; idx += 512) {
-            const int row = idx >> 4, c = idx & 15;
-            const int jp = jt * BLK + row;
-            float4 k0 = make_float4(0.f, 0.f, 0.f, 0.f), k1 = k0, v0 = k0, v1 = k0;
-            if (jp < s.nbk) {
-                const float* kp = a.kbar + kbar_row(s, a.Hkv, g, jp) * D + c * 8;
-                const float* vp = a.vbar + kbar_row(s, a.Hkv, g, jp) * D + c * 8;
-                k0 = *(const float4*)kp; k1 = *(const float4*)(kp + 4);
-                v0 = *(const float4*)vp; v1 = *(const float4*)(vp + 4);
-            }
-            const float kx[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
-            uint4 hi, lo;
-            uint32_t* hp = (uint32_t*)&hi;
-            uint32_t* lp = (uint32_t*)&lo;
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-                hp[e2] = pk_bf16(kx[2 * e2], kx[2 * e2 + 1]);
-                lp[e2] = pk_bf16(kx[2 * e2] - bf16_round(kx[2 * e2]), kx[2 * e2 + 1] - bf16_round(kx[2 * e2 + 1]));
-            }
-            const uint4 vv = make_uint4(pk_bf16(v0.x, v0.y), pk_bf16(v0.z, v0.w), pk_bf16(v1.x, v1.y),
-                                        pk_bf16(v1.z, v1.w));
-            typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-            typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
-            *(lds_u32x4*)(kA + row * KSTR + c * 16) = u32x4{hi.x, hi.y, hi.z, hi.w};
-            *(lds_u32x4*)(kB + row * KSTR + c * 16) = u32x4{lo.x, lo.y, lo.z, lo.w};
-            *(lds_u32x4*)(vA + row * VSTR + c * 16) = u32x4{vv.x, vv.y, vv.z, vv.w};
-        }
+    // Kept phase. Buffers alternate A, B; the loop ends once the code of the
+    // following tile is a summary code (already issued) or NONE (both < 0).
+    int nxt, ca = j0;
+    bool in_b;
+    while (true) {
+        const int cb = next_code(ca);
+        if (cb != NONE) issue(cb, kB, vB);
+        compute_kept(ca, kA, vA);
+        __syncthreads();                              // next tile landed; A is free
+        if (cb < 0) { nxt = cb; in_b = true; break; }
+        const int cn = next_code(cb);
+        if (cn != NONE) issue(cn, kA, vA);
+        compute_kept(cb, kB, vB);
         __syncthreads();
-#pragma unroll
-        for (int hf = 0; hf < NKB / 2; ++hf) {
-            f32x16 sh[2];
-            qk_pad<2>(kA, qf, n, lh, 2 * hf, sh, false);
-            qk_pad<2>(kB, qf, n, lh, 2 * hf, sh, true);
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const int c0 = jt * BLK + (2 * hf + kb) * 32;
-                const uint32_t pw = ~kept[min(c0 >> 5, MAX_NB / 32 - 1)] & range_bits(c0, 1, i - 1);
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int bit = 8 * (v >> 2) + 4 * lh + (v & 3);
-                    sh[kb][v] = ((pw >> bit) & 1u) ? sh[kb][v] : NEG_INF;
-                }
-            }
-            online_update<2, 8>(sh, f, lnb2, 0.f, m, lsum, oacc);
-            pv_tr<2>(sh, vA, lane, 2 * hf, oacc);
-        }
+        if (cn < 0) { nxt = cn; in_b = false; break; }
+        ca = cn;
+    }
+    // Summary phase: realign so the loop below always starts on buffer A.
+    if (in_b && nxt != NONE) {
+        const int cn = next_summary(-nxt);
+        if (cn != NONE) issue_summary<BLK>(a, s, g, -1 - cn, kA, vA, wave, lane);
+        compute_summary(nxt, kB, vB);
         __syncthreads();
+        nxt = cn;
+    }
+    while (nxt != NONE) {
+        const int cb = next_summary(-nxt);
+        if (cb != NONE) issue_summary<BLK>(a, s, g, -1 - cb, kB, vB, wave, lane);
+        compute_summary(nxt, kA, vA);
+        __syncthreads();
+        if (cb == NONE) break;
+        const int cn = next_summary(-cb);
+        if (cn != NONE) issue_summary<BLK>(a, s, g, -1 - cn, kA, vA, wave, lane);
+        compute_summary(cb, kB, vB);
+        __syncthreads();
+        nxt = cn;
     }
 
     // ---------------- epilogue ----------------
@@ -860,6 +922,33 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(Geo geo, AttnArgs a) 
             *(uint2*)(op + db * 32 + q4 * 8 + lh * 4) = w;
         }
     if (a.lse && lh == 0) a.lse[a.la.off(b, s, t, h)] = (m + __log2f(ltot)) * LN2;
+}
+
+// bf16 operands of the summary tiles: Kbar = hi + lo (two bf16 terms), Vbar.
+__global__ __launch_bounds__(256) void summary_prep_kernel(const float* kbar, const float* vbar, __bf16* hi,
+                                                           __bf16* lo, __bf16* vb, long long n4) {
+    const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (e >= n4) return;
+    const float4 k = ((const float4*)kbar)[e];
+    const float4 v = ((const float4*)vbar)[e];
+    uint2 h, l, w;
+    h.x = pk_bf16(k.x, k.y);
+    h.y = pk_bf16(k.z, k.w);
+    l.x = pk_bf16(k.x - bf16_round(k.x), k.y - bf16_round(k.y));
+    l.y = pk_bf16(k.z - bf16_round(k.z), k.w - bf16_round(k.w));
+    w.x = pk_bf16(v.x, v.y);
+    w.y = pk_bf16(v.z, v.w);
+    ((uint2*)hi)[e] = h;
+    ((uint2*)lo)[e] = l;
+    ((uint2*)vb)[e] = w;
+}
+
+hipError_t launch_summary_prep(const float* kbar, const float* vbar, __bf16* hi, __bf16* lo, __bf16* vb,
+                               long long nfloats, hipStream_t st) {
+    const long long n4 = nfloats / 4;
+    if (n4 == 0) return hipSuccess;
+    summary_prep_kernel<<<(unsigned)((n4 + 255) / 256), 256, 0, st>>>(kbar, vbar, hi, lo, vb, n4);
+    return hipGetLastError();
 }
 
 template <int BLK, typename Geo>

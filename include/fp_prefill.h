@@ -42,6 +42,7 @@
  *   - head_dim must be 128; block must be 64 or 128; Hq % Hkv == 0 and
  *     Hq / Hkv <= 16; block count per sequence <= 16384.
  *   - Strides are in elements; the last (head_dim) dimension is contiguous.
+ *     Fixed shape: k and v token strides x block x element size < 2 GiB.
  *   - Inputs are post-RoPE and finite (non-finite inputs: undefined results).
  *   - Kept-block lists are CSR over rows ordered (sequence b, KV head g, query
  *     block i ascending); columns ascending, absolute key-block indices.
@@ -111,6 +112,7 @@ const char* fp_last_error(void);
 int64_t fp_num_rows(const fp_problem* p);       /* batch * Hkv * nb           */
 int64_t fp_max_nnz(const fp_problem* p);        /* batch * Hkv * nb(nb+1)/2   */
 int64_t fp_workspace_size(const fp_problem* p); /* bytes for fp_select_blocks */
+int64_t fp_prefill_workspace_size(const fp_problem* p); /* bytes for fp_sparse_prefill */
 
 /* E1-E2. Pools Q, K, V per block (float32 accumulation) and writes the block
  * scores. q, k, v (device, read-only): bf16, or E4M3FN codes with q_scale,
@@ -137,13 +139,16 @@ int fp_select_blocks(const fp_problem* p, const float* scores, float tau,
  * valid kept list whose rows contain the sink and diagonal blocks, e.g. the
  * one fp_select_blocks wrote -- plus the mean-correction pseudo-tokens of the
  * pruned blocks, taken from kbar and vbar (device, as fp_block_scores wrote
- * them). sched (device, NULL = row order) only orders the work. Outputs
- * (device): o bf16 (o_stride), lse fp32 [batch, Hq, seqlen] or NULL. */
+ * them). sched (device, NULL = row order) only orders the work. workspace
+ * (device, ws_bytes >= fp_prefill_workspace_size, 256-byte aligned) receives
+ * bf16 copies of kbar and vbar for the correction; its contents need not be
+ * preserved between calls. Outputs (device): o bf16 (o_stride), lse fp32
+ * [batch, Hq, seqlen] or NULL. */
 int fp_sparse_prefill(const fp_problem* p, const void* q, const void* k, const void* v,
                       const float* q_scale, const float* k_scale, const float* v_scale,
                       const float* kbar, const float* vbar,
                       const int32_t* row_ptr, const int32_t* col_idx, const int32_t* sched,
-                      void* o, float* lse, void* stream);
+                      void* o, float* lse, void* workspace, size_t ws_bytes, void* stream);
 
 /* Sizing of a paged varlen call (host only). cu_seqlens_q int32 [num_seqs+1]
  * and seqlens_k int32 [num_seqs] are HOST arrays. */

@@ -96,7 +96,13 @@ def test_null_pointers_and_fp8_scales():
                                fake, fake, fake, fake, None) == N.FP_ERR_INVALID
     assert b"scale" in lib.fp_last_error()
     assert lib.fp_sparse_prefill(ctypes.byref(p), fake, fake, fake, None, None, None, fake, fake,
-                                 None, fake, None, fake, None, None) == N.FP_ERR_INVALID
+                                 None, fake, None, fake, None, fake, 1 << 30, None) == N.FP_ERR_INVALID
+    # workspace below fp_prefill_workspace_size
+    need = lib.fp_prefill_workspace_size(ctypes.byref(p))
+    assert need == 3 * (1 * 2 * (1024 // 128)) * 128 * 2     # hi, lo, v copies, bf16
+    assert lib.fp_sparse_prefill(ctypes.byref(p), fake, fake, fake, None, None, None, fake, fake,
+                                 fake, fake, None, fake, None, fake, need - 1, None) == N.FP_ERR_CAPACITY
+    assert b"workspace" in lib.fp_last_error()
 
 
 def test_misaligned_strides_rejected():
