@@ -8,22 +8,26 @@
 // H20 design they name (PackGQA, warp specialisation, pingpong) is prior art;
 // this is a gfx950 design:
 //
-//  * Work unit = (kept-list row, 128-row slice). A row is (sequence, KV head
+//  * Work unit = (kept-list row, 256-row slice). A row is (sequence, KV head
 //    g, query block i); its G query heads share the row's list, so the slice
 //    packs token-major rows (token, head) of all G heads into one M tile
 //    (the PackGQA idea: one K/V tile load serves G heads).
-//  * 4 wavefronts x 32 packed query rows. S^T = K Q^T and O^T = V^T P^T on
-//    v_mfma_f32_32x32x16_bf16, so each lane owns one query row: row max and
-//    row sum are lane-local plus one exchange with lane^32, and the
-//    accumulator rescale is a per-lane scalar.
-//  * P never leaves registers: the PV contraction order over the 16 keys of
-//    each MFMA step is chosen to be exactly the order in which the QK^T
-//    accumulator already holds them, and V^T is written to LDS in that same
-//    key order (key bits 2 and 3 swapped) while it is transposed.
-//  * The kept-tile loop is followed by summary tiles: the pooled keys of the
-//    pruned blocks (fp32, split hi+lo into two bf16 MFMAs so the logit keeps
-//    ~16 mantissa bits) with bias ln|block|, pooled values in bf16. Kept,
-//    future and sink/diagonal pooled columns are masked out.
+//  * 8 wavefronts x 32 packed query rows. S^T = K Q^T and O^T = V^T P^T on
+//    MFMA (bf16: 32x32x16; fp8: the scaled 32x32x64 f8f6f4 form with unit
+//    scales), so each lane owns one query row: row max and row sum are
+//    lane-local plus one exchange with lane ^ 32, and the accumulator
+//    rescale is a per-lane scalar.
+//  * P never leaves registers: the PV contraction order over the keys of each
+//    MFMA step is the order in which the QK^T accumulator already holds them.
+//    V stays row-major in LDS and the V^T operand comes from transpose reads
+//    (ds_read_b64_tr_b16 / _tr_b8) whose lane layout was pinned with probes.
+//  * K/V tiles are filled one tile ahead by direct global->LDS loads into two
+//    named buffers per operand (no register staging).
+//  * After the kept tiles come summary tiles: the bf16 hi and lo parts of the
+//    pooled keys of 64 consecutive blocks share one 128-row K tile, so two
+//    MFMA passes give each pseudo-token logit about 16 mantissa bits; pooled
+//    values are bf16; bias ln|block|. Kept, future and sink/diagonal pooled
+//    columns are masked out.
 //  * Units run heavy-row-first (sched), each row's slices on one XCD (unit
 //    u goes to XCD u % 8) so they share that XCD's L2 copy of the K/V tiles.
 #include "fp_internal.h"
@@ -33,13 +37,20 @@ namespace fp {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(2))) int i32x2;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
-constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
+// swap bits 2 and 3 of a key index
 __device__ __forceinline__ int vt_slot(int key) {
-    // swap bits 2 and 3 of the key index: the order in which a lane's QK^T
-    // accumulator holds keys inside each 16-key MFMA step
     return (key & ~0xC) | ((key >> 1) & 4) | ((key << 1) & 8);
 }
 
@@ -55,14 +66,16 @@ __device__ __forceinline__ float bf16_round(float x) {
     return __uint_as_float(pk_bf16(x, 0.f) << 16);
 }
 
-// Online-softmax update for one tile held as S^T accumulators (log2 domain).
-// Element value s maps to logit s * f + bias; masked elements are -inf.
 // value of x held by lane l ^ 32 (permlane32 swap, no LDS traffic)
 __device__ __forceinline__ float other_half(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(__lane_id() < 32 ? r[1] : r[0]);
 }
 
+// Online-softmax update for one tile held as S^T accumulators (log2 domain).
+// Element value s maps to logit s * f + bias; masked elements are -inf. The
+// probabilities are left in sacc multiplied by 2^lw (the PV operand scale);
+// lsum accumulates them without it.
 template <int NKB, int LAZY = 0>
 __device__ __forceinline__ void online_update(f32x16 (&sacc)[NKB], float f, float bias, float lw,
                                               float& m, float& lsum, f32x16 (&oacc)[4]) {
@@ -102,66 +115,6 @@ __device__ __forceinline__ void online_update(f32x16 (&sacc)[NKB], float f, floa
     lsum += lw == 0.f ? ts : ts * __builtin_amdgcn_exp2f(-lw);
 }
 
-// O^T += V^T P^T with P taken straight from the S^T accumulators.
-template <int NKB, int VLD>
-__device__ __forceinline__ void pv_bf16(const f32x16 (&sacc)[NKB], const __bf16* Vt, int n, int lh,
-                                        f32x16 (&oacc)[4]) {
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-            bf16x8 bop;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) bop[e] = (__bf16)sacc[kb][8 * s2 + e];
-#pragma unroll
-            for (int db = 0; db < 4; ++db) {
-                const bf16x8 aop = *(const bf16x8*)&Vt[(db * 32 + n) * VLD + kb * 32 + 16 * s2 + 8 * lh];
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop, oacc[db], 0, 0, 0);
-            }
-        }
-}
-
-// DORD 0: step ks covers dims 16 ks + 8 lh .. +8 (bf16 fragment order);
-// DORD 1: dims 64 (ks / 4) + 32 lh + 8 (ks % 4) .. +8 (the fp8 fragment's order).
-template <int NKB, int KLD, int DORD>
-__device__ __forceinline__ void qk_bf16(const __bf16* Ks, const bf16x8 (&qf)[8], int n, int lh,
-                                        f32x16 (&sacc)[NKB], bool accumulate) {
-    if (!accumulate) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) sacc[kb][v] = 0.f;
-    }
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            const int d0 = DORD ? 64 * (ks >> 2) + 32 * lh + 8 * (ks & 3) : ks * 16 + lh * 8;
-            const bf16x8 aop = *(const bf16x8*)&Ks[(kb * 32 + n) * KLD + d0];
-            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, qf[ks], sacc[kb], 0, 0, 0);
-        }
-}
-
-// Transposed, key-permuted store of 4 consecutive keys x 8 dims (bf16 bit
-// patterns in w[r]) into V^T: row d, column slot(key0) .. +3.
-template <int VLD>
-__device__ __forceinline__ void store_vt4x8(__bf16* Vt, int d0, int slot0, const uint4 (&w)[4]) {
-    const uint32_t* w0 = (const uint32_t*)&w[0];
-    const uint32_t* w1 = (const uint32_t*)&w[1];
-    const uint32_t* w2 = (const uint32_t*)&w[2];
-    const uint32_t* w3 = (const uint32_t*)&w[3];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        uint2 lo, hi;
-        lo.x = (w0[e] & 0xFFFFu) | (w1[e] << 16);
-        lo.y = (w2[e] & 0xFFFFu) | (w3[e] << 16);
-        hi.x = (w0[e] >> 16) | (w1[e] & 0xFFFF0000u);
-        hi.y = (w2[e] >> 16) | (w3[e] & 0xFFFF0000u);
-        *(uint2*)&Vt[(d0 + 2 * e) * VLD + slot0] = lo;
-        *(uint2*)&Vt[(d0 + 2 * e + 1) * VLD + slot0] = hi;
-    }
-}
-
 // Bits b of a 32-column word starting at column c0 with lo <= c0 + b <= hi.
 __device__ __forceinline__ uint32_t range_bits(int c0, int lo, int hi) {
     const int a = max(lo - c0, 0), z = min(hi - c0, 31);
@@ -169,388 +122,48 @@ __device__ __forceinline__ uint32_t range_bits(int c0, int lo, int hi) {
     return (0xFFFFFFFFu >> (31 - z)) & (0xFFFFFFFFu << a);
 }
 
-// fp8 P -> E4M3 codes, 4 per dword (round to nearest even)
+// P -> E4M3 codes, 4 per dword (round to nearest even)
 __device__ __forceinline__ uint32_t pk_fp8x4(float a, float b, float c, float d) {
     uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0u, false);
     return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
-// fp8 V^T slot of a key inside its 64-key MFMA step: the lane holding query n
-// (half lh) owns keys kb*32 + 8q + 4lh + r of kb in {2s, 2s+1}, in the order
-// (kb parity, q, r); store them contiguously per (s, lh).
-__device__ __forceinline__ int vt8_slot(int key) {
-    const int lh = (key >> 2) & 1, c = (key >> 5) & 1, q = (key >> 3) & 3, r = key & 3;
-    return (key & ~0x3F) | (lh << 5) | (c << 4) | (q << 2) | r;
-}
-
-// 4 keys x 16 dims of e4m3 codes (w[r] = 16 bytes of key r) -> V^T rows d0..d0+15,
-// 4 consecutive slots starting at slot0.
-template <int VLD8>
-__device__ __forceinline__ void store_vt8_4x16(uint8_t* Vt, int d0, int slot0, const uint4 (&w)[4]) {
-    const uint32_t* w0 = (const uint32_t*)&w[0];
-    const uint32_t* w1 = (const uint32_t*)&w[1];
-    const uint32_t* w2 = (const uint32_t*)&w[2];
-    const uint32_t* w3 = (const uint32_t*)&w[3];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-#pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
-            const int sh = 8 * bb;
-            const uint32_t x = ((w0[e] >> sh) & 0xFFu) | (((w1[e] >> sh) & 0xFFu) << 8) |
-                               (((w2[e] >> sh) & 0xFFu) << 16) | (((w3[e] >> sh) & 0xFFu) << 24);
-            *(uint32_t*)&Vt[(d0 + 4 * e + bb) * VLD8 + slot0] = x;
-        }
-}
-
+// OCP E4M3FN code -> float (exact)
 __device__ __forceinline__ float e4m3_val(uint32_t c) {
     const uint32_t sgn = (c & 0x80u) << 24, e = (c >> 3) & 0xFu, mm = c & 0x7u;
     const float mag = e ? __uint_as_float(((e + 120u) << 23) | (mm << 20)) : (float)mm * 0.001953125f;
     return __uint_as_float(__float_as_uint(mag) | sgn);
 }
 
-template <int BLK, bool FP8, bool PAGED, typename Geo>
-__global__ __launch_bounds__(256, 2) void attn_kernel(Geo geo, AttnArgs a) {
-    constexpr int NKB = BLK / 32;
-    constexpr int KLD = D + 8;         // bf16 K tile row, +16 B against bank conflicts
-    constexpr int VLD = BLK + 8;       // bf16 V^T tile row
-    constexpr int KLD8 = D + 16;       // fp8 K tile row (bytes)
-    constexpr int VLD8 = BLK + 16;     // fp8 V^T tile row (bytes)
-    constexpr int KS_BYTES = BLK * KLD * 2;
-    constexpr int VT_BYTES = D * VLD * 2;
-    __shared__ __align__(16) uint8_t smem[KS_BYTES + VT_BYTES];
-    __shared__ uint32_t kept[MAX_NB / 32];
-    __shared__ float svmax_sh;
-    __bf16* Ks = (__bf16*)smem;
-    __bf16* Vt = (__bf16*)(smem + KS_BYTES);
-    uint8_t* Ks8 = smem;
-    uint8_t* Vt8 = smem + KS_BYTES;
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int n = lane & 31, lh = lane >> 5;
-    const float NEG_INF = -__builtin_inff();
-
-    // unit -> (row position, slice); a row's slices share one XCD
-    const int u = blockIdx.x;
-    const int xcd = u & 7, k8 = u >> 3;
-    const int pidx = 8 * (k8 / a.slices) + xcd;
-    const int slice = k8 % a.slices;
-    if (pidx >= a.rows) return;
-    const int r = a.sched ? a.sched[pidx] : pidx;
-    const int b = geo.seq_of_row(r);
-    const SeqDesc s = geo.seq(b);
-    const int rl = r - s.row0;
-    const int g = rl / s.nq, il = rl % s.nq;
-    const int i = s.i0 + il;
-    const int t_lo = max(i * BLK, s.P), t_hi = min((i + 1) * BLK, s.L);
-    const int G = a.G;
-    const int npk = G * (t_hi - t_lo);               // packed rows of this row
-    if (slice * 128 >= npk) return;                  // uniform over the workgroup
-
-    const int prow = slice * 128 + wave * 32 + n;
-    const bool valid = prow < npk;
-    const int tl = prow / G, hl = prow - tl * G;
-    const int t = t_lo + tl;
-    const int h = g * G + hl;
-
-    // query fragment. bf16: lane (n, lh) holds q[t, h, 16 ks + 8 lh .. + 8];
-    // fp8: q[t, h, 64 ks + 32 lh .. + 32] (codes).
-    bf16x8 qf[8];
-    i32x8 qf8[2];
-    float f_row = a.scale_log2;
-    if (FP8) {
-        const uint8_t* qp = (const uint8_t*)a.q + (valid ? a.qa.off(b, s, t, h) : 0);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const uint4 w0 = valid ? *(const uint4*)(qp + ks * 64 + lh * 32) : make_uint4(0u, 0u, 0u, 0u);
-            const uint4 w1 = valid ? *(const uint4*)(qp + ks * 64 + lh * 32 + 16) : make_uint4(0u, 0u, 0u, 0u);
-            qf8[ks][0] = w0.x; qf8[ks][1] = w0.y; qf8[ks][2] = w0.z; qf8[ks][3] = w0.w;
-            qf8[ks][4] = w1.x; qf8[ks][5] = w1.y; qf8[ks][6] = w1.z; qf8[ks][7] = w1.w;
-        }
-        if (valid) f_row *= a.qs.at(b, h, t);
-    } else {
-        const __bf16* qp = (const __bf16*)a.q + (valid ? a.qa.off(b, s, t, h) : 0);
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            if (valid) qf[ks] = *(const bf16x8*)(qp + ks * 16 + lh * 8);
-            else
-#pragma unroll
-                for (int e = 0; e < 8; ++e) qf[ks][e] = (__bf16)0.f;
-        }
-    }
-
-    // kept bitmap of this row (pooled columns that must not be corrected)
-    const int rp0 = a.row_ptr[r], nnz = a.row_ptr[r + 1] - rp0;
-    const int nw = (i >> 5) + 1;
-    for (int w = tid; w < nw; w += 256) kept[w] = 0u;
-    if (tid == 0) svmax_sh = 0.f;
-    __syncthreads();
-    float svm = 0.f;
-    for (int e = tid; e < nnz; e += 256) {
-        const int j = a.col_idx[rp0 + e];
-        atomicOr(&kept[j >> 5], 1u << (j & 31));
-        if (FP8) svm = fmaxf(svm, a.vs.at(b, g, j * BLK));
-    }
-    if (FP8) {
-        svm = fmaxf(svm, __shfl_xor(svm, 32, 64));
-        svm = fmaxf(svm, __shfl_xor(svm, 16, 64));
-        svm = fmaxf(svm, __shfl_xor(svm, 8, 64));
-        svm = fmaxf(svm, __shfl_xor(svm, 4, 64));
-        svm = fmaxf(svm, __shfl_xor(svm, 2, 64));
-        svm = fmaxf(svm, __shfl_xor(svm, 1, 64));
-        if (lane == 0) atomicMax((int*)&svmax_sh, __float_as_int(svm));   // positive floats
-    }
-    __syncthreads();
-    // fp8 PV accumulates P * 2^8 * sv_j / svmax times value codes; undone at the end
-    const float svmax = FP8 ? svmax_sh : 1.f;
-    const float lsvmax = FP8 ? __log2f(svmax) : 0.f;
-
-    float m = NEG_INF, lsum = 0.f;
-    f32x16 oacc[4];
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) oacc[db][v] = 0.f;
-    f32x16 sacc[NKB];
-
-    // ---------------- kept blocks: exact tokens ----------------
-    for (int e = 0; e < nnz; ++e) {
-        const int j = a.col_idx[rp0 + e];
-        __syncthreads();
-        if (FP8) {
-            const uint8_t* kbase = (const uint8_t*)a.k;
-            const uint8_t* vbase = (const uint8_t*)a.v;
-            for (int c = tid; c < BLK * 8; c += 256) {
-                const int key = c >> 3, ch = c & 7;
-                const int sk = j * BLK + key;
-                uint4 w = make_uint4(0u, 0u, 0u, 0u);
-                if (sk < s.L) w = *(const uint4*)(kbase + a.ka.template off<PAGED>(b, sk, g) + ch * 16);
-                *(uint4*)&Ks8[key * KLD8 + ch * 16] = w;
-            }
-            for (int c = tid; c < (BLK / 4) * 8; c += 256) {
-                const int kq = c >> 3, ch = c & 7;
-                uint4 w[4];
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const int sk = j * BLK + 4 * kq + rr;
-                    w[rr] = make_uint4(0u, 0u, 0u, 0u);
-                    if (sk < s.L) w[rr] = *(const uint4*)(vbase + a.va.template off<PAGED>(b, sk, g) + ch * 16);
-                }
-                store_vt8_4x16<VLD8>(Vt8, ch * 16, vt8_slot(4 * kq), w);
-            }
-        } else {
-            const __bf16* kbase = (const __bf16*)a.k;
-            const __bf16* vbase = (const __bf16*)a.v;
-            for (int c = tid; c < BLK * 16; c += 256) {
-                const int key = c >> 4, ch = c & 15;
-                const int sk = j * BLK + key;
-                uint4 w = make_uint4(0u, 0u, 0u, 0u);
-                if (sk < s.L) w = *(const uint4*)(kbase + a.ka.template off<PAGED>(b, sk, g) + ch * 8);
-                *(uint4*)&Ks[key * KLD + ch * 8] = w;
-            }
-            for (int c = tid; c < (BLK / 4) * 16; c += 256) {
-                const int kq = c >> 4, ch = c & 15;
-                uint4 w[4];
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const int sk = j * BLK + 4 * kq + rr;
-                    w[rr] = make_uint4(0u, 0u, 0u, 0u);
-                    if (sk < s.L) w[rr] = *(const uint4*)(vbase + a.va.template off<PAGED>(b, sk, g) + ch * 8);
-                }
-                store_vt4x8<VLD>(Vt, ch * 8, vt_slot(4 * kq), w);
-            }
-        }
-        __syncthreads();
-        float f = f_row, lw = 0.f;
-        if (FP8) {
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) sacc[kb][v] = 0.f;
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb) {
-                    const uint8_t* ap = &Ks8[(kb * 32 + n) * KLD8 + ks * 64 + lh * 32];
-                    const uint4 w0 = *(const uint4*)ap, w1 = *(const uint4*)(ap + 16);
-                    i32x8 aop;
-                    aop[0] = w0.x; aop[1] = w0.y; aop[2] = w0.z; aop[3] = w0.w;
-                    aop[4] = w1.x; aop[5] = w1.y; aop[6] = w1.z; aop[7] = w1.w;
-                    sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, qf8[ks], sacc[kb],
-                                                                              0, 0, 0, 127, 0, 127);
-                }
-            const float sk = a.ks.at(b, g, j * BLK);
-            f *= sk;
-            lw = 8.f + __log2f(a.vs.at(b, g, j * BLK)) - lsvmax;   // P scale 2^8 sv_j / svmax
-        } else {
-            qk_bf16<NKB, KLD, 0>(Ks, qf, n, lh, sacc, false);
-        }
-        if (j == i) {                                  // causal mask inside the diagonal block
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int sk = j * BLK + kb * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
-                    sacc[kb][v] = sk > t ? NEG_INF : sacc[kb][v];
-                }
-        }
-        online_update<NKB>(sacc, f, 0.f, lw, m, lsum, oacc);
-        if (FP8) {
-#pragma unroll
-            for (int s2 = 0; s2 < NKB / 2; ++s2) {
-                i32x8 bop;
-#pragma unroll
-                for (int c = 0; c < 2; ++c)
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        const f32x16& sv = sacc[2 * s2 + c];
-                        bop[4 * c + q4] = (int)pk_fp8x4(sv[4 * q4], sv[4 * q4 + 1], sv[4 * q4 + 2], sv[4 * q4 + 3]);
-                    }
-#pragma unroll
-                for (int db = 0; db < 4; ++db) {
-                    const uint8_t* ap = &Vt8[(db * 32 + n) * VLD8 + s2 * 64 + lh * 32];
-                    const uint4 w0 = *(const uint4*)ap, w1 = *(const uint4*)(ap + 16);
-                    i32x8 aop;
-                    aop[0] = w0.x; aop[1] = w0.y; aop[2] = w0.z; aop[3] = w0.w;
-                    aop[4] = w1.x; aop[5] = w1.y; aop[6] = w1.z; aop[7] = w1.w;
-                    oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, bop, oacc[db],
-                                                                              0, 0, 0, 127, 0, 127);
-                }
-            }
-        } else {
-            pv_bf16<NKB, VLD>(sacc, Vt, n, lh, oacc);
-        }
-    }
-
-    // ---------------- pruned blocks: pooled pseudo-tokens ----------------
-    const float lnb2 = (BLK == 128) ? 7.f : 6.f;       // log2 |block|
-    // fp8: the pseudo-token weights join the accumulator in its 2^8 / svmax units
-    const float lw_sum = FP8 ? 8.f - lsvmax : 0.f;
-    bool have_qbf = false;
-    for (int jt = 0; jt * BLK <= i - 1; ++jt) {
-        // any pruned column in [max(1, jt*BLK), min(i-1, jt*BLK + BLK - 1)] ?
-        const int c_lo = max(1, jt * BLK), c_hi = min(i - 1, jt * BLK + BLK - 1);
-        uint32_t anyw = 0u;
-        for (int wd = c_lo >> 5; wd <= (c_hi >> 5); ++wd) anyw |= ~kept[wd] & range_bits(wd * 32, c_lo, c_hi);
-        const bool any = anyw != 0u;
-        if (!any) continue;
-        if (FP8 && !have_qbf) {
-            // widen the query codes to bf16 (exact) in the fp8 fragment's d order
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int byte = (ks & 3) * 8 + e;              // within the 32-byte half
-                    const uint32_t w = (uint32_t)qf8[ks >> 2][byte >> 2];
-                    qf[ks][e] = (__bf16)e4m3_val((w >> ((byte & 3) * 8)) & 0xFFu);
-                }
-            have_qbf = true;
-        }
-        __syncthreads();
-        for (int c = tid; c < BLK * 32; c += 256) {     // Kbar hi
-            const int key = c >> 5, c4 = c & 31;
-            const int jp = jt * BLK + key;
-            float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (jp < s.nbk) x = *(const float4*)(a.kbar + kbar_row(s, a.Hkv, g, jp) * D + c4 * 4);
-            uint2 hv;
-            hv.x = pk_bf16(x.x, x.y);
-            hv.y = pk_bf16(x.z, x.w);
-            *(uint2*)&Ks[key * KLD + c4 * 4] = hv;
-        }
-        for (int c = tid; c < (BLK / 4) * 16; c += 256) {   // Vbar, transposed
-            const int kq = c >> 4, ch = c & 15;
-            uint4 w[4];
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int jp = jt * BLK + 4 * kq + rr;
-                float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
-                if (jp < s.nbk) {
-                    const float* vp = a.vbar + kbar_row(s, a.Hkv, g, jp) * D + ch * 8;
-                    x0 = *(const float4*)vp;
-                    x1 = *(const float4*)(vp + 4);
-                }
-                w[rr] = make_uint4(pk_bf16(x0.x, x0.y), pk_bf16(x0.z, x0.w),
-                                   pk_bf16(x1.x, x1.y), pk_bf16(x1.z, x1.w));
-            }
-            store_vt4x8<VLD>(Vt, ch * 8, vt_slot(4 * kq), w);
-        }
-        __syncthreads();
-        qk_bf16<NKB, KLD, FP8 ? 1 : 0>(Ks, qf, n, lh, sacc, false);
-        __syncthreads();
-        for (int c = tid; c < BLK * 32; c += 256) {     // Kbar lo = bf16(x - hi)
-            const int key = c >> 5, c4 = c & 31;
-            const int jp = jt * BLK + key;
-            float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (jp < s.nbk) x = *(const float4*)(a.kbar + kbar_row(s, a.Hkv, g, jp) * D + c4 * 4);
-            uint2 lv;
-            lv.x = pk_bf16(x.x - bf16_round(x.x), x.y - bf16_round(x.y));
-            lv.y = pk_bf16(x.z - bf16_round(x.z), x.w - bf16_round(x.w));
-            *(uint2*)&Ks[key * KLD + c4 * 4] = lv;
-        }
-        __syncthreads();
-        qk_bf16<NKB, KLD, FP8 ? 1 : 0>(Ks, qf, n, lh, sacc, true);
-        // Branch-free mask: each 32-column group of the tile is one bitmap word;
-        // a column stays iff it lies in [1, i-1] and is not kept.
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            const int c0 = jt * BLK + kb * 32;
-            const uint32_t pw = ~kept[min(c0 >> 5, MAX_NB / 32 - 1)] & range_bits(c0, 1, i - 1);
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int bit = 8 * (v >> 2) + 4 * lh + (v & 3);
-                sacc[kb][v] = ((pw >> bit) & 1u) ? sacc[kb][v] : NEG_INF;
-            }
-        }
-        online_update<NKB>(sacc, f_row, lnb2, lw_sum, m, lsum, oacc);
-        pv_bf16<NKB, VLD>(sacc, Vt, n, lh, oacc);
-    }
-
-    // ---------------- epilogue ----------------
-    const float ltot = lsum + other_half(lsum);
-    if (!valid) return;
-    const float inv = (FP8 ? svmax * 0.00390625f : 1.f) / ltot;
-    __bf16* op = (__bf16*)a.o + a.oa.off(b, s, t, h);
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            uint2 w;
-            w.x = pk_bf16(oacc[db][4 * q4] * inv, oacc[db][4 * q4 + 1] * inv);
-            w.y = pk_bf16(oacc[db][4 * q4 + 2] * inv, oacc[db][4 * q4 + 3] * inv);
-            *(uint2*)(op + db * 32 + q4 * 8 + lh * 4) = w;
-        }
-    if (a.lse && lh == 0) a.lse[a.la.off(b, s, t, h)] = (m + __log2f(ltot)) * LN2;
-}
-
-// ===========================================================================
-// bf16 kernel: 8 wavefronts x 32 packed query rows (M = 256 per workgroup).
-// K and V tiles live row-major in LDS (256-byte rows, 16-byte chunks XOR-
-// swizzled by row) and are filled one tile ahead by direct global->LDS loads
-// (no VGPR staging); the V^T operand of PV comes from ds_read_b64_tr_b16.
-// ===========================================================================
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
-typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-// Tile layouts in LDS (bf16, 128 dims = 256 bytes of data per row):
-//   K rows every 272 bytes: the QK^T operand read (32 rows at one 16-byte
-//     chunk per lane half) hits row * 4 + chunk * 4 dwords mod 64, i.e. 16
-//     distinct bank groups per 16 lanes;
-//   V rows every 320 bytes: a transpose read covers 8 rows x 64 bytes, served
-//     32 lanes (4 rows) at a time; a row stride of 64 bytes mod 256 puts those
-//     4 rows on disjoint banks (measured: no bank conflicts, half the LDS
-//     cycles of a 288-byte stride).
-// Padding (not an XOR swizzle) keeps every operand address lane_base +
-// immediate, so no per-lane address table has to stay live in registers.
+// ---------------------------------------------------------------------------
+// Tile layouts in LDS (128 dims per row; rows padded, not XOR-swizzled, so
+// every operand address is lane_base + immediate and no per-lane address
+// table has to stay live in registers):
+//   bf16 K rows every 272 bytes: the QK^T operand read (16 lanes = 16 rows
+//     at one 16-byte chunk) lands on 16 distinct 4-bank groups;
+//   bf16 V rows every 320 bytes: a transpose read covers 8 rows x 64 bytes,
+//     served 32 lanes (4 rows) at a time; a stride of 64 bytes mod 256 puts
+//     those rows on disjoint banks (measured: no conflicts, half the LDS
+//     cycles of a 288-byte stride);
+//   fp8 K rows every 144 bytes (16 mod 256, same argument as bf16 K);
+//   fp8 V rows every 160 bytes, keys permuted inside each 64-key step (bits 2
+//     and 3 swapped) so that each 32-lane half of a transpose read covers 8
+//     consecutive rows x 32 bytes, which a stride of 40 dwords puts on 8
+//     disjoint 8-bank groups.
+// The summary tiles always use the bf16 layouts.
+// ---------------------------------------------------------------------------
 constexpr int KSTR = 272;
 constexpr int VSTR = 320;
+constexpr int KSTR8 = 144;
+constexpr int VSTR8 = 160;
 
-// Direct global->LDS loads of one K tile and one V tile: each wavefront
-// instruction fills 1 KiB of LDS (lane l -> bytes 16 l .. 16 l + 15), so a
-// lane works out which (row, chunk) its 16 bytes belong to; lanes that land on
-// row padding stay inactive. Rows past the sequence repeat its last key.
-template <int STR, int BLK, bool PAGED>
-__device__ __forceinline__ void issue_tile(const __bf16* base, const KVAddr& ka, int b, int L, int g,
+// Direct global->LDS loads of one tile: each wavefront instruction fills
+// 1 KiB of LDS (lane l -> bytes 16 l .. 16 l + 15), so a lane works out which
+// (row, chunk) its 16 bytes belong to; lanes that land on row padding stay
+// inactive. LDS row r holds key r (PERM: key vt_slot(r)); rows past the
+// sequence repeat its last key. ESZ = bytes per element.
+template <int STR, int BLK, int ESZ, bool PERM, bool PAGED>
+__device__ __forceinline__ void issue_tile(const uint8_t* base, const KVAddr& ka, int b, int L, int g,
                                            int j, lds_u8* buf, int wave, int lane) {
     constexpr int PIECES = BLK * STR / 1024;
     asm volatile("" : "+v"(lane));   // recompute addresses per call, keep none live
@@ -562,9 +175,10 @@ __device__ __forceinline__ void issue_tile(const __bf16* base, const KVAddr& ka,
             const int pb = t * 1024 + lane * 16;
             const int row = pb / STR;
             const int ch = (pb - row * STR) >> 4;
-            const int sk = j * BLK + min(row, rmax);
-            const __bf16* src = base + ka.template off<PAGED>(b, sk, g) + ch * 8;
-            if (ch < 16)
+            const int key = PERM ? vt_slot(row) : row;
+            const int sk = j * BLK + min(key, rmax);
+            const uint8_t* src = base + ka.template off<PAGED>(b, sk, g) * ESZ + ch * 16;
+            if (ch < 8 * ESZ)
                 __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(buf + t * 1024), 16, 0, 0);
         }
     }
@@ -574,7 +188,7 @@ __device__ __forceinline__ void issue_tile(const __bf16* base, const KVAddr& ka,
 // this lane loads, for contiguous K/V; computed once per workgroup. Unsigned
 // 32-bit offsets from a uniform base let each load use the scalar-base
 // addressing form, so only one register per piece stays live.
-template <int STR, int BLK>
+template <int STR, int BLK, int ESZ, bool PERM>
 struct TileOffs {
     static constexpr int PIECES = BLK * STR / 1024;
     static constexpr int NP = (PIECES + 7) / 8;
@@ -586,38 +200,51 @@ struct TileOffs {
             const int pb = (k * 8 + wave) * 1024 + lane * 16;
             const int row = pb / STR;
             const int ch = (pb - row * STR) >> 4;
-            off[k] = ch < 16 ? (uint32_t)(row * tok_stride + ch * 8) * 2u : PAD;
+            const int key = PERM ? vt_slot(row) : row;
+            off[k] = ch < 8 * ESZ ? (uint32_t)(key * tok_stride * ESZ + ch * 16) : PAD;
         }
     }
     // full tile (every row inside the sequence): one uniform base per tile
-    __device__ __forceinline__ void issue(const __bf16* tile_base, lds_u8* buf, int wave) const {
+    __device__ __forceinline__ void issue(const uint8_t* tile_base, lds_u8* buf, int wave) const {
 #pragma unroll
         for (int k = 0; k < NP; ++k) {
             const int t = k * 8 + wave;
             if (t < PIECES && off[k] != PAD)
-                __builtin_amdgcn_global_load_lds((const void*)((const char*)tile_base + off[k]),
+                __builtin_amdgcn_global_load_lds((const void*)(tile_base + off[k]),
                                                  (lds_void*)(buf + t * 1024), 16, 0, 0);
         }
     }
 };
 
-template <int BLK, bool PAGED>
+template <int BLK, bool FP8>
+struct KVOffs {
+    static constexpr int ESZ = FP8 ? 1 : 2;
+    TileOffs<FP8 ? KSTR8 : KSTR, BLK, ESZ, false> k;
+    TileOffs<FP8 ? VSTR8 : VSTR, BLK, ESZ, FP8> v;
+};
+
+template <int BLK, bool FP8, bool PAGED>
 __device__ __forceinline__ void issue_kv(const AttnArgs& a, int b, int L, int g, int j,
                                          lds_u8* kbuf, lds_u8* vbuf, int wave, int lane,
-                                         const TileOffs<KSTR, BLK>& ko, const TileOffs<VSTR, BLK>& vo) {
+                                         const KVOffs<BLK, FP8>& o) {
+    constexpr int ESZ = FP8 ? 1 : 2;
     if (!PAGED && (j + 1) * BLK <= L) {
-        const long long k0 = a.ka.template off<false>(b, j * BLK, g);
-        const long long v0 = a.va.template off<false>(b, j * BLK, g);
-        ko.issue((const __bf16*)a.k + k0, kbuf, wave);
-        vo.issue((const __bf16*)a.v + v0, vbuf, wave);
+        const long long k0 = a.ka.template off<false>(b, j * BLK, g) * ESZ;
+        const long long v0 = a.va.template off<false>(b, j * BLK, g) * ESZ;
+        o.k.issue((const uint8_t*)a.k + k0, kbuf, wave);
+        o.v.issue((const uint8_t*)a.v + v0, vbuf, wave);
         return;
     }
-    issue_tile<KSTR, BLK, PAGED>((const __bf16*)a.k, a.ka, b, L, g, j, kbuf, wave, lane);
-    issue_tile<VSTR, BLK, PAGED>((const __bf16*)a.v, a.va, b, L, g, j, vbuf, wave, lane);
+    issue_tile<FP8 ? KSTR8 : KSTR, BLK, ESZ, false, PAGED>((const uint8_t*)a.k, a.ka, b, L, g, j, kbuf, wave,
+                                                           lane);
+    issue_tile<FP8 ? VSTR8 : VSTR, BLK, ESZ, FP8, PAGED>((const uint8_t*)a.v, a.va, b, L, g, j, vbuf, wave,
+                                                         lane);
 }
 
-// S^T for key blocks kb0 .. kb0 + NB - 1 (32 keys each) of the tile.
-template <int NB>
+// bf16 S^T for key blocks kb0 .. kb0 + NB - 1 (32 keys each) of the tile.
+// DORD 0: step ks covers dims 16 ks + 8 lh .. +8; DORD 1: dims 64 (ks / 4) +
+// 32 lh + 8 (ks % 4) .. +8 (the fp8 query fragment's order).
+template <int NB, int DORD>
 __device__ __forceinline__ void qk_pad(const lds_u8* kt, const bf16x8 (&qf)[8], int n, int lh, int kb0,
                                        f32x16 (&sacc)[NB], bool accumulate) {
     if (!accumulate) {
@@ -630,14 +257,15 @@ __device__ __forceinline__ void qk_pad(const lds_u8* kt, const bf16x8 (&qf)[8], 
     for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
         for (int kb = 0; kb < NB; ++kb) {
-            const bf16x8 aop = *(const lds_bf16x8*)(kt + ((kb0 + kb) * 32 + n) * KSTR + (2 * ks + lh) * 16);
+            const int d0 = DORD ? 64 * (ks >> 2) + 32 * lh + 8 * (ks & 3) : 16 * ks + 8 * lh;
+            const bf16x8 aop = *(const lds_bf16x8*)(kt + ((kb0 + kb) * 32 + n) * KSTR + d0 * 2);
             sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, qf[ks], sacc[kb], 0, 0, 0);
         }
 }
 
-// O^T += V^T P^T: A operand = V^T fragment gathered by two transpose reads
-// (16-lane group: lane 4e + r addresses V[k0 + e][d0 + 4r .. +4], lane i
-// receives V[k0 + e][d0 + i] for e = 0..3); B operand = P from registers.
+// bf16 O^T += V^T P^T: A operand = V^T fragment gathered by two transpose
+// reads (16-lane group: lane 4e + r addresses V[k0 + e][d0 + 4r .. +4], lane
+// i receives V[k0 + e][d0 + i] for e = 0..3); B operand = P from registers.
 template <int NB>
 __device__ __forceinline__ void pv_tr(const f32x16 (&sacc)[NB], const lds_u8* vt, int lane, int kb0,
                                       f32x16 (&oacc)[4]) {
@@ -658,9 +286,7 @@ __device__ __forceinline__ void pv_tr(const f32x16 (&sacc)[NB], const lds_u8* vt
                 for (int aa = 0; aa < 2; ++aa) {
                     const int row = (kb0 + kb) * 32 + 16 * s2 + 8 * aa + rsub;
                     const int d = 32 * db + dsub;
-                    const lds_u8* ptr = vt + row * VSTR + d * 2;
-                    h[aa] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) s16x4*)(ptr));
+                    h[aa] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + row * VSTR + d * 2));
                 }
                 const s16x4 h0 = h[0], h1 = h[1];
                 typedef short s16x8 __attribute__((ext_vector_type(8)));
@@ -669,6 +295,59 @@ __device__ __forceinline__ void pv_tr(const f32x16 (&sacc)[NB], const lds_u8* vt
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop, oacc[db], 0, 0, 0);
             }
         }
+}
+
+// fp8 S^T for key blocks kb0 .. kb0 + NB - 1: A = K rows (32 bytes per lane
+// per 64-dim step, dims 64 ks + 32 lh ..), B = the query codes.
+template <int NB>
+__device__ __forceinline__ void qk_f8(const lds_u8* kt, const i32x8 (&qf8)[2], int n, int lh, int kb0,
+                                      f32x16 (&sacc)[NB]) {
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sacc[kb][v] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb) {
+            const lds_u8* ap = kt + ((kb0 + kb) * 32 + n) * KSTR8 + ks * 64 + lh * 32;
+            const u32x4 w0 = *(const lds_u32x4*)ap, w1 = *(const lds_u32x4*)(ap + 16);
+            i32x8 aop;
+            aop[0] = w0[0]; aop[1] = w0[1]; aop[2] = w0[2]; aop[3] = w0[3];
+            aop[4] = w1[0]; aop[5] = w1[1]; aop[6] = w1[2]; aop[7] = w1[3];
+            sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, qf8[ks], sacc[kb], 0, 0, 0, 127, 0,
+                                                                      127);
+        }
+}
+
+// fp8 O^T += V^T P^T over the 64-key step s2 (accumulators sacc[0], sacc[1]).
+// B-lane (n, lh) byte e = 16 kbit + v holds P of key 32 kbit + 8 (v / 4) +
+// 4 lh + v % 4. Transpose read c (16-lane group: lane i receives byte i % 8
+// of the 8 bytes addressed by lane 2 e' + i / 8, e' = 0..7) gives A bytes
+// 8c .. 8c + 7; with the keys stored at LDS row vt_slot(key), the 8 rows a
+// lane half needs are the consecutive rows 16 c + 8 lh + e'.
+__device__ __forceinline__ void pv_f8(const f32x16 (&sacc)[2], const lds_u8* vt, int lane, int s2,
+                                      f32x16 (&oacc)[4]) {
+    i32x8 bop;
+#pragma unroll
+    for (int kbit = 0; kbit < 2; ++kbit)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+            bop[4 * kbit + q4] = (int)pk_fp8x4(sacc[kbit][4 * q4], sacc[kbit][4 * q4 + 1], sacc[kbit][4 * q4 + 2],
+                                               sacc[kbit][4 * q4 + 3]);
+    const int a = lane & 15, half = (lane >> 4) & 1, lh = lane >> 5;
+    const lds_u8* base = vt + (s2 * 64 + 8 * lh + (a >> 1)) * VSTR8 + 16 * half + 8 * (a & 1);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+        i32x8 aop;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const i32x2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(base + 16 * c * VSTR8 + db * 32));
+            aop[2 * c] = r[0];
+            aop[2 * c + 1] = r[1];
+        }
+        oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, bop, oacc[db], 0, 0, 0, 127, 0, 127);
+    }
 }
 
 // Summary sub-tile m covers pooled columns [SUMC m, SUMC m + SUMC) (SUMC =
@@ -684,7 +363,7 @@ __device__ __forceinline__ void issue_summary(const AttnArgs& a, const SeqDesc& 
     asm volatile("" : "+v"(lane));
 #pragma unroll
     for (int w = 0; w < 2; ++w) {
-        constexpr int KP = BLK * KSTR / 1024, VP = BLK * VSTR / 1024;
+        constexpr int KP = BLK * KSTR / 1024, VP = SUMC * VSTR / 1024;
         const int STR = w == 0 ? KSTR : VSTR;
         const int PIECES = w == 0 ? KP : VP;
         lds_u8* buf = w == 0 ? kbuf : vbuf;
@@ -695,8 +374,8 @@ __device__ __forceinline__ void issue_summary(const AttnArgs& a, const SeqDesc& 
                 const int pb = t * 1024 + lane * 16;
                 const int row = pb / STR;
                 const int ch = (pb - row * STR) >> 4;
-                const int part = row >= SUMC;                       // 0 hi / 1 lo (K); V: upper rows unused
-                if (ch >= 16 || (w == 1 && part)) continue;
+                const int part = row >= SUMC;                       // 0 hi / 1 lo (K rows)
+                if (ch >= 16) continue;
                 const int jp = min(SUMC * m + row - part * SUMC, s.nbk - 1);
                 const long long pr = kbar_row(s, a.Hkv, g, jp) * D + ch * 8;
                 const __bf16* src = w == 0 ? (part ? a.kbar_lo : a.kbar_hi) + pr : a.vbar_bf + pr;
@@ -706,13 +385,21 @@ __device__ __forceinline__ void issue_summary(const AttnArgs& a, const SeqDesc& 
     }
 }
 
-template <int BLK, bool PAGED, typename Geo>
-__global__ __launch_bounds__(512, 1) void attn_bf16_kernel(Geo geo, AttnArgs a) {
+// fp8 tile scales (one per 128 keys) as vector loads: the value is consumed a
+// tile later, after the barrier's vector-memory wait, so it never stalls
+__device__ __forceinline__ float load_scale(const float* p, long long idx) {
+    int z = 0;
+    asm volatile("" : "+v"(z));
+    return p[idx + z];
+}
+
+template <int BLK, bool FP8, bool PAGED, typename Geo>
+__global__ __launch_bounds__(512, 1) void attn_tile_kernel(Geo geo, AttnArgs a) {
     constexpr int NKB = BLK / 32;
     constexpr int SB = NKB / 2;                     // 32-column blocks per summary sub-tile
     constexpr int SUMC = BLK / 2;
-    constexpr int KTILE = BLK * KSTR;
-    constexpr int VTILE = BLK * VSTR;
+    constexpr int KTILE = BLK * KSTR;               // fits an fp8 K tile and a summary K tile
+    constexpr int VTILE = FP8 ? (BLK * VSTR8 > SUMC * VSTR ? BLK * VSTR8 : SUMC * VSTR) : BLK * VSTR;
     constexpr int NONE = -0x7fffffff;
     // two distinct buffers per operand (not one indexed array), so the
     // compiler can tell the tile being read from the tile being loaded
@@ -721,6 +408,7 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(Geo geo, AttnArgs a) 
     __shared__ __align__(1024) uint8_t vA_[VTILE];
     __shared__ __align__(1024) uint8_t vB_[VTILE];
     __shared__ uint32_t kept[MAX_NB / 32];
+    __shared__ int svmax_sh;
     lds_u8* const kA = (lds_u8*)kA_;
     lds_u8* const kB = (lds_u8*)kB_;
     lds_u8* const vA = (lds_u8*)vA_;
@@ -759,16 +447,30 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(Geo geo, AttnArgs a) 
 
     const int rp0 = a.row_ptr[r], nnz = a.row_ptr[r + 1] - rp0;
     const int j0 = a.col_idx[rp0];
-    TileOffs<KSTR, BLK> ko;
-    TileOffs<VSTR, BLK> vo;
+    KVOffs<BLK, FP8> kvo;
     if (!PAGED) {
-        ko.init(a.ka.st, wave, lane);
-        vo.init(a.va.st, wave, lane);
+        kvo.k.init(a.ka.st, wave, lane);
+        kvo.v.init(a.va.st, wave, lane);
     }
-    issue_kv<BLK, PAGED>(a, b, s.L, g, j0, kA, vA, wave, lane, ko, vo);
+    issue_kv<BLK, FP8, PAGED>(a, b, s.L, g, j0, kA, vA, wave, lane, kvo);
 
+    // Query fragment. bf16: lane (n, lh) holds q[t, h, 16 ks + 8 lh .. + 8];
+    // fp8: the codes q[t, h, 64 ks + 32 lh .. + 32], widened to bf16 (exact)
+    // in that order only when the summary tiles start.
     bf16x8 qf[8];
-    {
+    i32x8 qf8[2];
+    float f_row = a.scale_log2;
+    if constexpr (FP8) {
+        const uint8_t* qp = (const uint8_t*)a.q + (valid ? a.qa.off(b, s, t, h) : 0);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const uint4 w0 = valid ? *(const uint4*)(qp + ks * 64 + lh * 32) : make_uint4(0u, 0u, 0u, 0u);
+            const uint4 w1 = valid ? *(const uint4*)(qp + ks * 64 + lh * 32 + 16) : make_uint4(0u, 0u, 0u, 0u);
+            qf8[ks][0] = w0.x; qf8[ks][1] = w0.y; qf8[ks][2] = w0.z; qf8[ks][3] = w0.w;
+            qf8[ks][4] = w1.x; qf8[ks][5] = w1.y; qf8[ks][6] = w1.z; qf8[ks][7] = w1.w;
+        }
+        if (valid) f_row *= a.qs.at(b, h, t);
+    } else {
         const __bf16* qp = (const __bf16*)a.q + (valid ? a.qa.off(b, s, t, h) : 0);
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
@@ -778,12 +480,29 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(Geo geo, AttnArgs a) 
                 for (int e = 0; e < 8; ++e) qf[ks][e] = (__bf16)0.f;
         }
     }
+    // fp8 tile scales of this row's (sequence, KV head): one per 128 keys
+    const float* ksp = FP8 ? a.ks.p + (long long)b * a.ks.sb + (long long)g * a.ks.sh : nullptr;
+    const float* vsp = FP8 ? a.vs.p + (long long)b * a.vs.sb + (long long)g * a.vs.sh : nullptr;
+    float ksA = 1.f, vsA = 1.f, ksB = 1.f, vsB = 1.f;
+    if constexpr (FP8) {
+        ksA = load_scale(ksp, (j0 * BLK) >> 7);
+        vsA = load_scale(vsp, (j0 * BLK) >> 7);
+    }
+
     const int nw = (i >> 5) + 1;
     for (int w = tid; w < nw; w += 512) kept[w] = 0u;
+    if (FP8 && tid == 0) svmax_sh = 0;
     __syncthreads();
+    float svm = 0.f;
     for (int e = tid; e < nnz; e += 512) {
         const int j = a.col_idx[rp0 + e];
         atomicOr(&kept[j >> 5], 1u << (j & 31));
+        if (FP8) svm = fmaxf(svm, vsp[(j * BLK) >> 7]);
+    }
+    if constexpr (FP8) {
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) svm = fmaxf(svm, __shfl_xor(svm, off, 64));
+        if (lane == 0) atomicMax(&svmax_sh, __float_as_int(svm));   // non-negative floats order as ints
     }
 
     float m = NEG_INF, lsum = 0.f;
@@ -792,9 +511,12 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(Geo geo, AttnArgs a) 
     for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int v = 0; v < 16; ++v) oacc[db][v] = 0.f;
-    const float f = a.scale_log2;
     const float lnb2 = (BLK == 128) ? 7.f : 6.f;    // log2 |block| of a pruned pseudo-token
     __syncthreads();                                  // tile 0 landed; kept bitmap complete
+    // fp8: PV accumulates P 2^8 sv_j / svmax times the value codes (P <= 1:
+    // no lazy rescale there), undone in the epilogue
+    const float svmax = FP8 ? fmaxf(__int_as_float(svmax_sh), 1e-30f) : 1.f;
+    const float lsvmax = FP8 ? __log2f(svmax) : 0.f;
 
     // Tile sequence: the kept blocks in column order (codes >= 0 are block
     // indices), then the summary sub-tiles that hold at least one pruned
@@ -825,37 +547,61 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(Geo geo, AttnArgs a) 
         }
         return next_summary(-code);
     };
-    auto issue = [&](int code, lds_u8* kb, lds_u8* vb) __attribute__((always_inline)) {
-        if (code >= 0) issue_kv<BLK, PAGED>(a, b, s.L, g, code, kb, vb, wave, lane, ko, vo);
-        else issue_summary<BLK>(a, s, g, -1 - code, kb, vb, wave, lane);
-    };
-    // Exact tokens of kept block `code`, 64 keys at a time (32 S registers live).
-    auto compute_kept = [&](int code, const lds_u8* kc, const lds_u8* vc) __attribute__((always_inline)) {
-#pragma unroll
-        for (int hf = 0; hf < NKB / 2; ++hf) {
-            f32x16 sh[2];
-            qk_pad<2>(kc, qf, n, lh, 2 * hf, sh, false);
-            if (code == i) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int sk = code * BLK + (2 * hf + kb) * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
-                        sh[kb][v] = sk > t ? NEG_INF : sh[kb][v];
-                    }
+    auto issue = [&](int code, lds_u8* kb, lds_u8* vb, float& ksn, float& vsn) __attribute__((always_inline)) {
+        if (code >= 0) {
+            issue_kv<BLK, FP8, PAGED>(a, b, s.L, g, code, kb, vb, wave, lane, kvo);
+            if constexpr (FP8) {
+                ksn = load_scale(ksp, (code * BLK) >> 7);
+                vsn = load_scale(vsp, (code * BLK) >> 7);
             }
-            online_update<2, 8>(sh, f, 0.f, 0.f, m, lsum, oacc);
-            pv_tr<2>(sh, vc, lane, 2 * hf, oacc);
+        } else {
+            issue_summary<BLK>(a, s, g, -1 - code, kb, vb, wave, lane);
         }
     };
+    auto mask_diag = [&](f32x16 (&sh)[2], int code, int hf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int sk = code * BLK + (2 * hf + kb) * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
+                sh[kb][v] = sk > t ? NEG_INF : sh[kb][v];
+            }
+    };
+    // Exact tokens of kept block `code`, 64 keys at a time (32 S registers live).
+    auto compute_kept = [&](int code, const lds_u8* kc, const lds_u8* vc, float ksj, float vsj)
+                            __attribute__((always_inline)) {
+        if constexpr (FP8) {
+            const float f = f_row * ksj;
+            const float lw = 8.f + __log2f(fmaxf(vsj, 1e-30f)) - lsvmax;
+#pragma unroll
+            for (int hf = 0; hf < NKB / 2; ++hf) {
+                f32x16 sh[2];
+                qk_f8<2>(kc, qf8, n, lh, 2 * hf, sh);
+                if (code == i) mask_diag(sh, code, hf);
+                online_update<2, 0>(sh, f, 0.f, lw, m, lsum, oacc);
+                pv_f8(sh, vc, lane, hf, oacc);
+            }
+        } else {
+#pragma unroll
+            for (int hf = 0; hf < NKB / 2; ++hf) {
+                f32x16 sh[2];
+                qk_pad<2, 0>(kc, qf, n, lh, 2 * hf, sh, false);
+                if (code == i) mask_diag(sh, code, hf);
+                online_update<2, 8>(sh, f_row, 0.f, 0.f, m, lsum, oacc);
+                pv_tr<2>(sh, vc, lane, 2 * hf, oacc);
+            }
+        }
+    };
+    // fp8: the pseudo-token weights join the accumulator in its 2^8 / svmax units
+    const float lw_sum = FP8 ? 8.f - lsvmax : 0.f;
     // Pooled pseudo-tokens of summary sub-tile -1 - code: hi and lo halves of
     // QK^T accumulate into one logit per pooled column; pseudo-tokens of kept
     // or non-causal columns are masked from the LDS bitmap.
     auto compute_summary = [&](int code, const lds_u8* kc, const lds_u8* vc) __attribute__((always_inline)) {
         const int mm = -1 - code;
         f32x16 sh[SB];
-        qk_pad<SB>(kc, qf, n, lh, 0, sh, false);       // hi rows
-        qk_pad<SB>(kc, qf, n, lh, SB, sh, true);       // lo rows, same columns
+        qk_pad<SB, FP8 ? 1 : 0>(kc, qf, n, lh, 0, sh, false);    // hi rows
+        qk_pad<SB, FP8 ? 1 : 0>(kc, qf, n, lh, SB, sh, true);    // lo rows, same columns
 #pragma unroll
         for (int kb = 0; kb < SB; ++kb) {
             const int c0 = mm * SUMC + kb * 32;
@@ -866,7 +612,7 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(Geo geo, AttnArgs a) 
                 sh[kb][v] = ((pw >> bit) & 1u) ? sh[kb][v] : NEG_INF;
             }
         }
-        online_update<SB, 8>(sh, f, lnb2, 0.f, m, lsum, oacc);
+        online_update<SB, 8>(sh, f_row, lnb2, lw_sum, m, lsum, oacc);
         pv_tr<SB>(sh, vc, lane, 0, oacc);
     };
 
@@ -876,16 +622,29 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(Geo geo, AttnArgs a) 
     bool in_b;
     while (true) {
         const int cb = next_code(ca);
-        if (cb != NONE) issue(cb, kB, vB);
-        compute_kept(ca, kA, vA);
+        if (cb != NONE) issue(cb, kB, vB, ksB, vsB);
+        compute_kept(ca, kA, vA, ksA, vsA);
         __syncthreads();                              // next tile landed; A is free
         if (cb < 0) { nxt = cb; in_b = true; break; }
         const int cn = next_code(cb);
-        if (cn != NONE) issue(cn, kA, vA);
-        compute_kept(cb, kB, vB);
+        if (cn != NONE) issue(cn, kA, vA, ksA, vsA);
+        compute_kept(cb, kB, vB, ksB, vsB);
         __syncthreads();
         if (cn < 0) { nxt = cn; in_b = false; break; }
         ca = cn;
+    }
+    if constexpr (FP8) {
+        // widen the query codes to bf16 (exact) in the fp8 fragment's dim order
+        if (nxt != NONE) {
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int byte = (ks & 3) * 8 + e;              // within the 32-byte half
+                    const uint32_t w = (uint32_t)qf8[ks >> 2][byte >> 2];
+                    qf[ks][e] = (__bf16)e4m3_val((w >> ((byte & 3) * 8)) & 0xFFu);
+                }
+        }
     }
     // Summary phase: realign so the loop below always starts on buffer A.
     if (in_b && nxt != NONE) {
@@ -911,7 +670,7 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(Geo geo, AttnArgs a) 
     // ---------------- epilogue ----------------
     const float ltot = lsum + other_half(lsum);
     if (!valid) return;
-    const float inv = 1.f / ltot;
+    const float inv = (FP8 ? svmax * 0.00390625f : 1.f) / ltot;
     __bf16* op = (__bf16*)a.o + a.oa.off(b, s, t, h);
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -954,17 +713,12 @@ hipError_t launch_summary_prep(const float* kbar, const float* vbar, __bf16* hi,
 
 template <int BLK, typename Geo>
 static void attn_launch(const Geo& geo, const AttnArgs& a, int fp8, int paged, hipStream_t st) {
-    if (fp8) {
-        const int units = cdiv(a.rows, 8) * 8 * a.slices;
-        if (paged) attn_kernel<BLK, true, true, Geo><<<units, 256, 0, st>>>(geo, a);
-        else attn_kernel<BLK, true, false, Geo><<<units, 256, 0, st>>>(geo, a);
-    } else {
-        AttnArgs b2 = a;
-        b2.slices = cdiv(a.G * BLK, 256);
-        const int units = cdiv(a.rows, 8) * 8 * b2.slices;
-        if (paged) attn_bf16_kernel<BLK, true, Geo><<<units, 512, 0, st>>>(geo, b2);
-        else attn_bf16_kernel<BLK, false, Geo><<<units, 512, 0, st>>>(geo, b2);
-    }
+    AttnArgs b2 = a;
+    b2.slices = cdiv(a.G * BLK, 256);
+    const int units = cdiv(a.rows, 8) * 8 * b2.slices;
+    if (fp8) attn_tile_kernel<BLK, true, false, Geo><<<units, 512, 0, st>>>(geo, b2);
+    else if (paged) attn_tile_kernel<BLK, false, true, Geo><<<units, 512, 0, st>>>(geo, b2);
+    else attn_tile_kernel<BLK, false, false, Geo><<<units, 512, 0, st>>>(geo, b2);
 }
 
 template <typename Geo>
