@@ -186,7 +186,7 @@ def cpu_baseline(inp, tau, rows_sample=768):
                 measured_s=t_est + t_att, projected_layer_s=t_layer)
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_S131072_tau4_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_S131072_tau4_traffic.md")
 KERNEL_SOURCE = os.path.join(ROOT, "block_sparse_long_estimate_amd", "csrc", "k_attn.hip")
 
 
@@ -194,18 +194,23 @@ def measured_traffic(S, tau):
     """HBM bytes per attention launch from the committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE readings (scaled by a plain copy kernel's readings), or None
     when they were taken on another workload or another version of the
-    kernel source."""
+    kernel source. The record is the `key: value` block of the summary."""
     import hashlib
     try:
         with open(TRAFFIC_FILE) as f:
-            rec = json.load(f)
+            rec = {}
+            for line in f:
+                key, sep, val = line.strip().partition(": ")
+                if sep and key in ("kernel_source_sha256", "seq_len", "tau", "hbm_bytes_per_launch"):
+                    rec[key] = val.strip()
         with open(KERNEL_SOURCE, "rb") as f:
             digest = hashlib.sha256(f.read()).hexdigest()
-    except OSError:
+        if (rec.get("kernel_source_sha256") != digest or int(rec["seq_len"]) != S
+                or float(rec["tau"]) != tau):
+            return None
+        return int(rec["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
         return None
-    if rec.get("kernel_source_sha256") != digest or rec.get("seq_len") != S or rec.get("tau") != tau:
-        return None
-    return rec["hbm_bytes_per_launch"]
 
 
 def main():
@@ -277,7 +282,7 @@ def main():
         "mfma_util_kept": round(bf["attn_kept_tflops"] / att_peak, 4),
         "mfma_util_executed": round(bf["attn_executed_tflops"] / att_peak, 4),
         "estimator_gbs": round(bf["estimate_gbs"], 1), "select_gbs": round(bf["select_gbs"], 1),
-        "roofline": {"bound": "mfma", "kernel": "attn_bf16_kernel (fp_sparse_prefill)",
+        "roofline": {"bound": "mfma", "kernel": "attn_tile_kernel<128, bf16> (fp_sparse_prefill)",
                      "achieved": round(bf["attn_kept_tflops"], 2), "peak": att_peak,
                      "unit": "TFLOP/s", "frac": round(bf["attn_kept_tflops"] / att_peak, 4),
                      "traffic": measured_traffic(cfg.S, args.tau)},
