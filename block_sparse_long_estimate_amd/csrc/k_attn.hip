@@ -414,7 +414,8 @@ __global__ __launch_bounds__(512, 1) void attn_tile_kernel(Geo geo, AttnArgs a) 
     lds_u8* const vA = (lds_u8*)vA_;
     lds_u8* const vB = (lds_u8*)vB_;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar LDS bases
     const int n = lane & 31, lh = lane >> 5;
     const float NEG_INF = -__builtin_inff();
 
