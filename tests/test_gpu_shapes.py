@@ -1,0 +1,91 @@
+"""GPU parity on shapes the headline workloads do not reach: other GQA
+ratios (including ones whose packed rows leave part of a slice empty), tiny
+and ragged sequence lengths, strided views of a fused qkv tensor, and a
+non-default softmax scale. Same comparison rules as test_gpu_parity."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from fp_testutil import LSE_TOL, check_csr_wellformed, compare_masks, compare_outputs, csr_to_keep
+from test_gpu_parity import check_fixed, fp, say, widen  # noqa: F401  (fp is a fixture)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (6, 2), (16, 2), (16, 1)])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_gqa_ratios(fp, Hq, Hkv, dtype):
+    """G = 1, 3, 8, 16. G = 3 packs 384 rows per query block: the second
+    256-row slice is half empty."""
+    cfg = synth.config(2, S=1536 + 45, Hq=Hq, Hkv=Hkv, seed=40 + Hq + Hkv, dtype=dtype)
+    say(f"GQA {Hq}/{Hkv} {dtype} S={cfg.S}")
+    inp = synth.gen_fixed(cfg)
+    check_fixed(fp, inp, 3.0, 128, kind=dtype)
+
+
+@pytest.mark.parametrize("S,block", [(1, 128), (5, 128), (127, 128), (128, 128), (129, 128),
+                                     (1, 64), (63, 64), (65, 64), (300, 64)])
+def test_tiny_and_ragged_lengths(fp, S, block):
+    cfg = synth.config(1, S=S, block=block, seed=70 + S)
+    say(f"S={S} block={block}")
+    inp = synth.gen_fixed(cfg)
+    check_fixed(fp, inp, 2.0, block)
+
+
+@pytest.mark.parametrize("S", [1, 129, 700])
+def test_fp8_tiny_and_ragged(fp, S):
+    cfg = synth.config(2, S=S, Hq=8, Hkv=2, seed=90 + S, dtype="fp8")
+    say(f"fp8 S={S}")
+    inp = synth.gen_fixed(cfg)
+    check_fixed(fp, inp, 2.0, 128, kind="fp8")
+
+
+def test_fused_qkv_strides(fp):
+    """q, k, v as views of one [batch, S, Hq + 2 Hkv, 128] tensor: the same
+    results, bit for bit, as contiguous copies."""
+    cfg = synth.config(2, S=2048 + 17, Hq=8, Hkv=2, seed=123, batch=2)
+    inp = synth.gen_fixed(cfg)
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in (inp.q, inp.k, inp.v))
+    fused = torch.cat([q, k, v], dim=2)                   # [B, S, 12, 128]
+    qv, kv, vv = fused[:, :, :8], fused[:, :, 8:10], fused[:, :, 10:12]
+    assert not qv.is_contiguous() and not kv.is_contiguous()
+    a = fp.sparse_prefill(q, k, v, 128, 3.0)
+    b = fp.sparse_prefill(qv, kv, vv, 128, 3.0)
+    torch.cuda.synchronize()
+    assert torch.equal(a["row_ptr"], b["row_ptr"])
+    n = int(a["row_ptr"][-1])
+    assert torch.equal(a["col_idx"][:n], b["col_idx"][:n])
+    assert torch.equal(a["o"], b["o"])
+    assert torch.equal(a["lse"], b["lse"])
+    check_fixed(fp, inp, 3.0, 128)
+
+
+def test_softmax_scale(fp):
+    """softmax_scale given explicitly (not 1/sqrt(d))."""
+    cscale = 0.05
+    cfg = synth.config(2, S=2048 + 99, Hq=8, Hkv=2, seed=321)
+    inp = synth.gen_fixed(cfg)
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in (inp.q, inp.k, inp.v))
+    tau = 2.0
+    out = fp.sparse_prefill(q, k, v, 128, tau, softmax_scale=cscale)
+    torch.cuda.synchronize()
+    S, Hkv = cfg.S, cfg.Hkv
+    nb = -(-S // 128)
+    rp, ci = out["row_ptr"].cpu().numpy(), out["col_idx"].cpu().numpy()
+    check_csr_wellformed(rp, ci, lambda r: r % nb)
+    qd, kd, vd = widen(inp, 0)
+    ref = oracle.prefill(qd, kd, vd, 128, tau, cscale, with_output=False)
+    assert np.abs(out["scores"][0].cpu().numpy()[np.isfinite(ref["S"])] - ref["S"][np.isfinite(ref["S"])]).max() \
+        <= 2e-4 * max(1.0, np.abs(ref["S"][np.isfinite(ref["S"])]).max())
+    keep = csr_to_keep(rp, ci, 0, Hkv, nb, nb)
+    compare_masks(keep, ref["keep"], ref["R"], tau)
+    o_ref, lse_ref = oracle.attend(qd, kd, vd, keep, ref["kbar"], ref["vbar"], cscale, 128, 0)
+    compare_outputs(out["o"][0].float().cpu().numpy(), o_ref, "bf16")
+    lg = out["lse"][0].cpu().numpy()
+    assert np.abs(lg - lse_ref).max() <= LSE_TOL
