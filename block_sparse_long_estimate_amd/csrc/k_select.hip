@@ -118,10 +118,10 @@ __global__ __launch_bounds__(256) void expand_rows_kernel(Geo geo, SelectArgs a)
 // Stable counting sort, keys = counts in [1, max_nbk], descending. One
 // workgroup of 1024 threads; bins in dynamic LDS.
 __global__ __launch_bounds__(1024) void sort_rows_kernel(SelectArgs a) {
-    extern __shared__ int sm[];
+    extern __shared__ __align__(16) int sm[];
     const int nbin = a.max_nbk + 1;
     int* cur = sm;                 // [nbin] bin cursor
-    int* keys = sm + nbin;         // [1024] keys of the current chunk
+    int* keys = sm + ((nbin + 3) & ~3);   // [1024] keys of the current chunk (16-byte aligned)
     __shared__ int part[1024];
     const int tid = threadIdx.x;
     for (int k = tid; k < nbin; k += 1024) cur[k] = 0;
@@ -153,8 +153,17 @@ __global__ __launch_bounds__(1024) void sort_rows_kernel(SelectArgs a) {
         const int key = r < a.rows ? a.counts[r] : -1;
         keys[tid] = key;
         __syncthreads();
+        // stable rank among equal keys of the chunk; 16-byte reads, unrolled,
+        // so several LDS reads are in flight (the loop is latency-bound)
         int rank = 0;
-        for (int t = 0; t < tid; ++t) rank += keys[t] == key;
+        const int4* k4 = (const int4*)keys;
+        const int n4 = tid >> 2;
+#pragma unroll 8
+        for (int t4 = 0; t4 < n4; ++t4) {
+            const int4 w = k4[t4];
+            rank += (w.x == key) + (w.y == key) + (w.z == key) + (w.w == key);
+        }
+        for (int t = n4 * 4; t < tid; ++t) rank += keys[t] == key;
         const int pos = key >= 0 ? cur[key] + rank : 0;
         __syncthreads();
         if (key >= 0) {
@@ -172,7 +181,7 @@ static hipError_t select_dispatch(const Geo& geo, const SelectArgs& a, hipStream
     scan_rows_kernel<<<1, 1024, 0, st>>>(a);
     expand_rows_kernel<Geo><<<wg, 256, 0, st>>>(geo, a);
     if (a.sched) {
-        const size_t shm = (size_t)(a.max_nbk + 1 + 1024) * sizeof(int);
+        const size_t shm = (size_t)(((a.max_nbk + 1 + 3) & ~3) + 1024) * sizeof(int);
         if (shm > 65536) {
             hipError_t e = hipFuncSetAttribute((const void*)sort_rows_kernel,
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
