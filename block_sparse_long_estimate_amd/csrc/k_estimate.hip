@@ -105,8 +105,8 @@ __global__ __launch_bounds__(256) void pool_kernel(Geo geo, PoolArgs a) {
 
 // ---------------------------------------------------------------------------
 // E2: 64 x 64 tiles of (query block, key block) per workgroup, one query head
-// per blockIdx.y. Tiles entirely above the diagonal only write -inf. fp32
-// FMA on 4 x 4 register blocks from LDS; the pooled rows stay L2-resident.
+// per blockIdx.y. Tiles entirely above the diagonal only write -inf. The
+// products run on fp32 MFMA from LDS; the pooled rows stay L2-resident.
 // ---------------------------------------------------------------------------
 template <typename Geo>
 __global__ __launch_bounds__(256) void scores_kernel(Geo geo, ScoreArgs a) {
@@ -149,39 +149,33 @@ __global__ __launch_bounds__(256) void scores_kernel(Geo geo, ScoreArgs a) {
     }
     __syncthreads();
 
-    float acc[4][4];
+    // Each wavefront computes one 32x32 quadrant on v_mfma_f32_32x32x2_f32
+    // (fp32 operands and accumulation). MFMA step kk takes dim kk from lanes
+    // 0-31 and dim 64 + kk from lanes 32-63 (any pairing works as long as both
+    // operands use it), so a lane reads 4 consecutive dims per LDS read.
+    typedef __attribute__((ext_vector_type(16))) float f32x16;
+    const int wave = tid >> 6, lane = tid & 63, n = lane & 31, lh = lane >> 5;
+    const int wr = wave >> 1, wc = wave & 1;
+    f32x16 acc;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+    for (int v = 0; v < 16; ++v) acc[v] = 0.f;
 #pragma unroll 4
-    for (int dd = 0; dd < D; dd += 4) {
-        float4 qv[4], kv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) qv[i] = *(const float4*)&Qs[ty + 16 * i][dd];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) kv[j] = *(const float4*)&Ks[tx + 16 * j][dd];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                acc[i][j] = fmaf(qv[i].x, kv[j].x, acc[i][j]);
-                acc[i][j] = fmaf(qv[i].y, kv[j].y, acc[i][j]);
-                acc[i][j] = fmaf(qv[i].z, kv[j].z, acc[i][j]);
-                acc[i][j] = fmaf(qv[i].w, kv[j].w, acc[i][j]);
-            }
+    for (int t = 0; t < 16; ++t) {
+        const float4 qv = *(const float4*)&Qs[32 * wr + n][64 * lh + 4 * t];
+        const float4 kv = *(const float4*)&Ks[32 * wc + n][64 * lh + 4 * t];
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qv.x, kv.x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qv.y, kv.y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qv.z, kv.z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qv.w, kv.w, acc, 0, 0, 0);
     }
+    // accumulator: lane holds column n, rows 8 (v / 4) + 4 lh + v % 4
+    const int jj = j0 + 32 * wc + n;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int il = il0 + ty + 16 * i;
-        if (il >= s.nq) continue;
+    for (int v = 0; v < 16; ++v) {
+        const int il = il0 + 32 * wr + 8 * (v >> 2) + 4 * lh + (v & 3);
+        if (il >= s.nq || jj >= s.nbk) continue;
         const int iabs = s.i0 + il;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int jj = j0 + tx + 16 * j;
-            if (jj >= s.nbk) continue;
-            a.scores[score_off(s, h, il, jj)] = jj <= iabs ? acc[i][j] * a.scale : NEG_INF;
-        }
+        a.scores[score_off(s, h, il, jj)] = jj <= iabs ? acc[v] * a.scale : NEG_INF;
     }
 }
 
