@@ -13,16 +13,6 @@
 
 namespace fp {
 
-// OCP E4M3FN decode by bit assembly (sign, 4-bit exponent with bias 7, 3-bit
-// mantissa; exponent 0 is subnormal m * 2^-9). Codes are finite by contract.
-__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
-    uint32_t s = (c & 0x80u) << 24;
-    uint32_t e = (c >> 3) & 0xFu;
-    uint32_t m = c & 0x7u;
-    float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
-    return __uint_as_float(__float_as_uint(mag) | s);
-}
-
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
@@ -78,10 +68,17 @@ __global__ __launch_bounds__(256) void pool_kernel(Geo geo, PoolArgs a) {
         const uint4 w = *(const uint4*)(base + (off + (long long)ch * EPC) * ESZ);
         const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
         if (FP8) {
-            const float sc = sa.at(b, head, t);
+            // codes widened by the hardware converter (exact for E4M3FN); the
+            // block's single scale is applied once at the end
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
-                acc[e] += e4m3_to_f32((ws[e >> 2] >> ((e & 3) * 8)) & 0xFFu) * sc;
+            for (int e = 0; e < 4; ++e) {
+                const auto lo2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[e], false);
+                const auto hi2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[e], true);
+                acc[4 * e] += lo2[0];
+                acc[4 * e + 1] += lo2[1];
+                acc[4 * e + 2] += hi2[0];
+                acc[4 * e + 3] += hi2[1];
+            }
         } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -97,7 +94,9 @@ __global__ __launch_bounds__(256) void pool_kernel(Geo geo, PoolArgs a) {
         float sum = 0.f;
 #pragma unroll 8
         for (int r = 0; r < TL; ++r) sum += red[r][tid];
-        const float mean = sum / (float)(hi - lo);
+        // fp8: one scale per 128 tokens, and a block (64 or 128 tokens, aligned)
+        // never spans two
+        const float mean = (FP8 ? sum * sa.at(b, head, lo) : sum) / (float)(hi - lo);
         if (isq) a.qbar[qbar_row(s, a.Hq, head, blk) * D + tid] = mean;
         else (isv ? a.vbar : a.kbar)[kbar_row(s, a.Hkv, head, blk) * D + tid] = mean;
     }
