@@ -12,7 +12,10 @@ version of the same tensors.
 Prints one JSON line: dense-equivalent TFLOP/s of the bf16 step as `value`,
 ms per layer, kept-block fraction, the attention kernel's MFMA roofline
 fraction over the FLOPs of the kept blocks, and the single-threaded CPU
-oracle's throughput on a bounded sample as `cpu_baseline`.
+oracle's throughput on a bounded sample as `cpu_baseline`. Context legs on
+the same tensors (skipped with --no-sweep): bf16 at tau 2, 6, 8, and tau=inf,
+where every block is kept and the path is this library's own dense causal
+attention.
 """
 from __future__ import annotations
 
@@ -222,6 +225,8 @@ def main():
     ap.add_argument("--seqlen", type=int, default=131072)
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the context legs (bf16 at tau 2/6/8, and tau=inf: every block kept)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (3 times): the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
@@ -257,6 +262,16 @@ def main():
     if not args.no_fp8:
         f8, _ = time_path(fp, N, inputs["fp8"], args.tau, args.steps, args.warmup, "fp8")
         log(f"fp8: {json.dumps(f8)}")
+    sweep, dense = {}, None
+    if not args.no_sweep:
+        for tau in (2.0, 6.0, 8.0):
+            r, _ = time_path(fp, N, inputs["bf16"], tau, 5, 1, f"bf16 tau={tau}")
+            sweep[str(tau)] = {"ms_per_layer": round(r["ms_per_step"], 4), "ms_attention": round(r["ms_attention"], 4),
+                               "kept_fraction": round(r["kept_fraction"], 5),
+                               "attn_kept_tflops": round(r["attn_kept_tflops"], 2)}
+            log(f"sweep tau={tau}: {json.dumps(sweep[str(tau)])}")
+        dense, _ = time_path(fp, N, inputs["bf16"], float("inf"), 2, 1, "bf16 dense")
+        log(f"dense (tau=inf): {json.dumps(dense)}")
     cpu = None
     if not args.no_cpu_baseline:
         t0 = time.time()
@@ -295,6 +310,15 @@ def main():
                        "attn_kept_tflops": round(f8["attn_kept_tflops"], 2),
                        "mfma_util_kept": round(f8["attn_kept_tflops"] / PEAK_TFLOPS["fp8"], 4),
                        "estimator_gbs": round(f8["estimate_gbs"], 1)}
+    if sweep:
+        line["tau_sweep_bf16"] = sweep
+    if dense is not None:
+        # the same path with every block kept: this library's own dense causal attention
+        line["dense_path_bf16"] = {"ms_per_layer": round(dense["ms_per_step"], 4),
+                                   "ms_attention": round(dense["ms_attention"], 4),
+                                   "attn_tflops": round(dense["attn_kept_tflops"], 2),
+                                   "mfma_util": round(dense["attn_kept_tflops"] / att_peak, 4),
+                                   "sparse_speedup": round(dense["ms_per_step"] / bf["ms_per_step"], 2)}
     if cpu is not None:
         line["cpu_baseline"] = {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")}
         line["cpu_baseline"]["value"] = round(cpu["value"], 6)
