@@ -58,11 +58,14 @@ class Problem:
 
 
 def make_problem(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block: int,
-                 softmax_scale: float = 0.0, o: Optional[torch.Tensor] = None) -> Problem:
+                 softmax_scale: float = 0.0, o: Optional[torch.Tensor] = None,
+                 out_fp32: bool = False) -> Problem:
     """Descriptor of a fixed-shape batch: q [batch, S, Hq, 128], k/v [batch, S, Hkv, 128]
-    (bf16, or uint8 E4M3FN codes), last dim contiguous."""
+    (bf16, or uint8 E4M3FN codes), last dim contiguous. out_fp32: fp_sparse_prefill
+    writes o in float32 (diagnostic) instead of bfloat16."""
     fp8 = q.dtype == torch.uint8
     c = FpProblem()
+    c.out_dtype = N.FP_OUT_FP32 if out_fp32 else N.FP_OUT_BF16
     c.batch, c.seqlen, c.num_q_heads, c.head_dim = q.shape[0], q.shape[1], q.shape[2], q.shape[3]
     c.num_kv_heads = k.shape[2]
     c.block = block
@@ -121,10 +124,11 @@ def fp_select_blocks(p: Problem, scores: torch.Tensor, tau: float, with_sched: b
 def fp_sparse_prefill(p: Problem, q, k, v, kbar, vbar, row_ptr, col_idx, sched=None,
                       q_scale=None, k_scale=None, v_scale=None, with_lse: bool = True,
                       o: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
-    """E6 -> (o bf16 like q, lse fp32 [batch, Hq, S] or None)."""
+    """E6 -> (o like q in bf16, or fp32 for an out_fp32 problem; lse fp32 [batch, Hq, S] or None)."""
     c = p.c
     if o is None:
-        o = torch.empty((c.batch, c.seqlen, c.num_q_heads, 128), dtype=torch.bfloat16, device=q.device)
+        odt = torch.float32 if c.out_dtype == N.FP_OUT_FP32 else torch.bfloat16
+        o = torch.empty((c.batch, c.seqlen, c.num_q_heads, 128), dtype=odt, device=q.device)
     lse = torch.empty((c.batch, c.num_q_heads, c.seqlen), dtype=torch.float32,
                       device=q.device) if with_lse else None
     lib = N.load()
@@ -139,9 +143,10 @@ def fp_sparse_prefill(p: Problem, q, k, v, kbar, vbar, row_ptr, col_idx, sched=N
 
 
 def sparse_prefill(q, k, v, block: int, tau: float, softmax_scale: float = 0.0,
-                   q_scale=None, k_scale=None, v_scale=None, with_lse: bool = True):
+                   q_scale=None, k_scale=None, v_scale=None, with_lse: bool = True,
+                   out_fp32: bool = False):
     """All three stages on the current stream. Returns a dict of device tensors."""
-    p = make_problem(q, k, v, block, softmax_scale)
+    p = make_problem(q, k, v, block, softmax_scale, out_fp32=out_fp32)
     qbar, kbar, vbar, scores = fp_block_scores(p, q, k, v, q_scale, k_scale, v_scale)
     row_ptr, col_idx, sched = fp_select_blocks(p, scores, tau)
     o, lse = fp_sparse_prefill(p, q, k, v, kbar, vbar, row_ptr, col_idx, sched,

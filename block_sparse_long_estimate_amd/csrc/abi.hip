@@ -70,8 +70,12 @@ int check_fixed(const fp_problem* p) {
     for (int t = 0; t < 3; ++t)
         for (int e = 0; e < 3; ++e)
             if ((st[t][e] * esz) % 16) return fail(FP_ERR_INVALID, "strides must be multiples of 16 bytes");
+    if (p->out_dtype != FP_OUT_BF16 && p->out_dtype != FP_OUT_FP32)
+        return fail(FP_ERR_UNSUPPORTED, "out_dtype %d unsupported", p->out_dtype);
+    const int osz = p->out_dtype == FP_OUT_FP32 ? 4 : 2;
     for (int e = 0; e < 3; ++e)
-        if ((p->o_stride[e] * 2) % 8) return fail(FP_ERR_INVALID, "o strides must be multiples of 8 bytes");
+        if ((p->o_stride[e] * osz) % (osz == 4 ? 16 : 8))
+            return fail(FP_ERR_INVALID, "o strides must be multiples of %d bytes", osz == 4 ? 16 : 8);
     // a K/V tile's per-lane load offsets are 32-bit byte offsets
     if (p->k_stride[1] * esz * p->block >= (1LL << 31) || p->v_stride[1] * esz * p->block >= (1LL << 31))
         return fail(FP_ERR_UNSUPPORTED, "k/v token stride x block must stay below 2 GiB");
@@ -261,10 +265,11 @@ int fp_sparse_prefill(const fp_problem* p, const void* q, const void* k, const v
     GeoFixed geo = geo_fixed(p);
     const int nsb = cdiv(p->seqlen, SCALE_TOK);
     const int G = p->num_q_heads / p->num_kv_heads;
-    AttnArgs a;
+    AttnArgs a{};
     a.q = q; a.k = k; a.v = v;
     a.qa = RowAddr{p->q_stride[0], p->q_stride[1], p->q_stride[2]};
     a.oa = RowAddr{p->o_stride[0], p->o_stride[1], p->o_stride[2]};
+    a.o_f32 = p->out_dtype == FP_OUT_FP32;
     a.ka = KVAddr{p->k_stride[0], p->k_stride[1], p->k_stride[2], 0, nullptr, 0, 0};
     a.va = KVAddr{p->v_stride[0], p->v_stride[1], p->v_stride[2], 0, nullptr, 0, 0};
     a.qs = ScaleAddr{q_scale, (long long)p->num_q_heads * nsb, nsb};
@@ -479,7 +484,7 @@ int fp_sparse_prefill_paged(const fp_varlen_problem* p, const void* q, const int
     if (e != hipSuccess) return fail(FP_ERR_HIP, "select launch: %s", hipGetErrorString(e));
 
     const int G = p->num_q_heads / p->num_kv_heads;
-    AttnArgs a;
+    AttnArgs a{};
     a.q = q; a.k = k_cache; a.v = v_cache;
     a.qa = RowAddr{0, p->q_stride[0], p->q_stride[1]};
     a.oa = RowAddr{0, p->o_stride[0], p->o_stride[1]};

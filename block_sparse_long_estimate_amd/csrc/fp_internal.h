@@ -160,6 +160,7 @@ struct AttnArgs {
     void* o; float* lse; RowAddr la;   // lse offset: b*sb + (q0+t-P)*st + h*sh
     int Hq, Hkv, G, rows, slices;
     float scale_log2;                  // c * log2(e)
+    int o_f32;                         // o in fp32 (diagnostic) instead of bf16
 };
 
 hipError_t launch_pool(const GeoFixed* gf, const GeoTable* gt, const PoolArgs& a, hipStream_t st);

@@ -672,16 +672,27 @@ __global__ __launch_bounds__(512, 1) void attn_tile_kernel(Geo geo, AttnArgs a) 
     const float ltot = lsum + other_half(lsum);
     if (!valid) return;
     const float inv = (FP8 ? svmax * 0.00390625f : 1.f) / ltot;
-    __bf16* op = (__bf16*)a.o + a.oa.off(b, s, t, h);
+    if (a.o_f32) {
+        float* op = (float*)a.o + a.oa.off(b, s, t, h);
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            uint2 w;
-            w.x = pk_bf16(oacc[db][4 * q4] * inv, oacc[db][4 * q4 + 1] * inv);
-            w.y = pk_bf16(oacc[db][4 * q4 + 2] * inv, oacc[db][4 * q4 + 3] * inv);
-            *(uint2*)(op + db * 32 + q4 * 8 + lh * 4) = w;
-        }
+            for (int q4 = 0; q4 < 4; ++q4)
+                *(float4*)(op + db * 32 + q4 * 8 + lh * 4) =
+                    make_float4(oacc[db][4 * q4] * inv, oacc[db][4 * q4 + 1] * inv, oacc[db][4 * q4 + 2] * inv,
+                                oacc[db][4 * q4 + 3] * inv);
+    } else {
+        __bf16* op = (__bf16*)a.o + a.oa.off(b, s, t, h);
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                uint2 w;
+                w.x = pk_bf16(oacc[db][4 * q4] * inv, oacc[db][4 * q4 + 1] * inv);
+                w.y = pk_bf16(oacc[db][4 * q4 + 2] * inv, oacc[db][4 * q4 + 3] * inv);
+                *(uint2*)(op + db * 32 + q4 * 8 + lh * 4) = w;
+            }
+    }
     if (a.lse && lh == 0) a.lse[a.la.off(b, s, t, h)] = (m + __log2f(ltot)) * LN2;
 }
 

@@ -65,10 +65,13 @@ extern "C" {
 
 #define FP_DTYPE_BF16 0          /* bfloat16 Q/K/V                               */
 #define FP_DTYPE_FP8_E4M3 1      /* OCP E4M3FN codes (uint8) + fp32 scales       */
+#define FP_OUT_BF16 0            /* fp_sparse_prefill output o in bfloat16        */
+#define FP_OUT_FP32 2            /* ... in float32 (diagnostic: no output rounding) */
 
 /* Fixed-shape batch: `batch` sequences of `seqlen` tokens each, one-shot
  * prefill (no cached prefix). q [batch, seqlen, Hq, 128], k and v
- * [batch, seqlen, Hkv, 128], o like q; strides given per tensor. */
+ * [batch, seqlen, Hkv, 128], o like q; strides given per tensor (o strides
+ * in elements of out_dtype; fp32 o rows 16-byte aligned). */
 typedef struct fp_problem {
     int32_t batch;
     int32_t seqlen;
@@ -82,6 +85,8 @@ typedef struct fp_problem {
     int64_t k_stride[3];
     int64_t v_stride[3];
     int64_t o_stride[3];
+    int32_t out_dtype;       /* FP_OUT_BF16 (0, default) or FP_OUT_FP32: diagnostic fp32 o */
+    int32_t pad_;
 } fp_problem;
 
 /* Paged varlen batch (continuous batching with cached prefixes). Sequence b
@@ -142,7 +147,8 @@ int fp_select_blocks(const fp_problem* p, const float* scores, float tau,
  * them). sched (device, NULL = row order) only orders the work. workspace
  * (device, ws_bytes >= fp_prefill_workspace_size, 256-byte aligned) receives
  * bf16 copies of kbar and vbar for the correction; its contents need not be
- * preserved between calls. Outputs (device): o bf16 (o_stride), lse fp32
+ * preserved between calls. Outputs (device): o (o_stride; bf16, or fp32 when
+ * out_dtype is FP_OUT_FP32), lse fp32
  * [batch, Hq, seqlen] or NULL. */
 int fp_sparse_prefill(const fp_problem* p, const void* q, const void* k, const void* v,
                       const float* q_scale, const float* k_scale, const float* v_scale,

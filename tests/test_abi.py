@@ -200,3 +200,15 @@ def test_paged_rejects_nan_tau_capacity_workspace():
     assert call(float("nan"), nnz, ws) == N.FP_ERR_INVALID
     assert call(4.0, nnz - 1, ws) == N.FP_ERR_CAPACITY
     assert call(4.0, nnz, ws - 1) == N.FP_ERR_CAPACITY
+
+
+def test_out_dtype_validation():
+    lib = N.load()
+    assert ctypes.sizeof(N.FpProblem) == 136
+    p = problem(out_dtype=1)
+    assert lib.fp_num_rows(ctypes.byref(p)) == N.FP_ERR_UNSUPPORTED
+    p = problem(out_dtype=N.FP_OUT_FP32)
+    assert lib.fp_num_rows(ctypes.byref(p)) > 0          # 128-element rows: 512-byte aligned
+    p.o_stride[1] = 8 * 128 + 2                           # 8-byte aligned fp32 rows only
+    assert lib.fp_num_rows(ctypes.byref(p)) == N.FP_ERR_INVALID
+
