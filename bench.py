@@ -58,9 +58,12 @@ def kept_flops_from_csr(row_ptr, col_idx, nb, S, B, G, d, Hkv, batch):
     return kept, corr
 
 
-def time_path(fp, N, inp, tau, steps, warmup, label):
+def time_path(fp, N, inp, tau, steps, warmup, label, flush_bytes=0, keep_outputs=False):
     """Run the path `warmup` + `steps` times; HIP events per stage on the
-    current stream (the library launches on it)."""
+    current stream (the library launches on it). flush_bytes > 0: before each
+    timed step a buffer of that size is overwritten (outside the events), so
+    L2 and the memory-side cache start cold. keep_outputs: also return the
+    outputs of KV head 0's query heads (host, fp32) and lse."""
     import torch
     dev = torch.device("cuda:0")
     q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
@@ -98,6 +101,7 @@ def time_path(fp, N, inp, tau, steps, warmup, label):
                                       ws2.numel(), sh))
 
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    flush = torch.empty(flush_bytes, dtype=torch.uint8, device=dev) if flush_bytes else None
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -109,6 +113,8 @@ def time_path(fp, N, inp, tau, steps, warmup, label):
     for _ in range(steps):
         e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
         ev = e
+        if flush is not None:
+            flush.fill_(1)
         e[0].record(stream)
         step()
         e[3].record(stream)
@@ -116,10 +122,12 @@ def time_path(fp, N, inp, tau, steps, warmup, label):
     all1.record(stream)
     torch.cuda.synchronize()
     total_ms = all0.elapsed_time(all1)
+    t_all = []
     for e in per:
         t_est.append(e[0].elapsed_time(e[1]))
         t_sel.append(e[1].elapsed_time(e[2]))
         t_att.append(e[2].elapsed_time(e[3]))
+        t_all.append(e[0].elapsed_time(e[3]))
     rp = row_ptr.cpu().numpy()
     ci = col_idx[:int(rp[-1])].cpu().numpy()
     G = c.num_q_heads // c.num_kv_heads
@@ -128,9 +136,11 @@ def time_path(fp, N, inp, tau, steps, warmup, label):
     nblk = c.batch * c.num_kv_heads * p.nb * (p.nb + 1) / 2.0
     res = dict(
         label=label,
-        ms_per_step=total_ms / steps,
+        # with flushes in between, the bracket would time them too: use the per-step events
+        ms_per_step=total_ms / steps if flush is None else float(np.mean(t_all)),
+        ms_step_median=float(np.median(t_all)),
         ms_estimate=float(np.mean(t_est)), ms_select=float(np.mean(t_sel)),
-        ms_attention=float(np.mean(t_att)),
+        ms_attention=float(np.mean(t_att)), ms_attention_median=float(np.median(t_att)),
         kept_fraction=float(len(ci) / nblk),
         kept_tflop=kept / 1e12, correction_tflop=corr / 1e12, dense_tflop=dense / 1e12,
     )
@@ -144,16 +154,21 @@ def time_path(fp, N, inp, tau, steps, warmup, label):
     res["estimate_gbs"] = est_bytes / (res["ms_estimate"] * 1e-3) / 1e9
     sel_bytes = scores.numel() * 4 // 2 + (len(ci) + 3 * p.rows) * 4
     res["select_gbs"] = sel_bytes / (res["ms_select"] * 1e-3) / 1e9
-    del q, k, v, qbar, kbar, vbar, scores, o, lse, ws, ws2
+    outs = None
+    if keep_outputs:
+        outs = (o[0, :, :G].float().cpu().numpy(), lse[0, :G].cpu().numpy())
+    del q, k, v, qbar, kbar, vbar, scores, o, lse, ws, ws2, flush
     torch.cuda.empty_cache()
-    return res, (rp, ci)
+    return res, (rp, ci, outs)
 
 
-def cpu_baseline(inp, tau, rows_sample=768):
+def cpu_baseline(inp, tau, rows_sample=768, gpu=None):
     """The fp64 oracle, as it stands, single-threaded, on a bounded sample of
     the same workload: E1-E5 for one KV head group (all query blocks) and E6
     for `rows_sample` (KV head, query block) rows spread over the sequence;
-    projected to the whole layer in dense-equivalent TFLOP/s."""
+    projected to the whole layer in dense-equivalent TFLOP/s. With the GPU's
+    CSR and KV head 0 outputs given, the same oracle results also give parity
+    statistics for that sample (outside the timed parts)."""
     from threadpoolctl import threadpool_limits
     import oracle
     from oracle.core import pool_queries, pool_keys, block_scores, select, attend
@@ -171,12 +186,13 @@ def cpu_baseline(inp, tau, rows_sample=768):
         qb = pool_queries(q, B, 0, S)
         kb, vb = pool_keys(k, B), pool_keys(v, B)
         Sc = block_scores(qb, kb, c, 0)
-        keep, _ = select(Sc, G, tau, 0)
+        keep, R_or = select(Sc, G, tau, 0)
         t_est = time.perf_counter() - t0
         il_list = np.linspace(0, nb - 1, rows_sample).round().astype(int)
         t0 = time.perf_counter()
-        attend(q, k, v, keep, kb, vb, c, B, 0, rows=[(0, int(il)) for il in il_list])
+        o_or, lse_or = attend(q, k, v, keep, kb, vb, c, B, 0, rows=[(0, int(il)) for il in il_list])
         t_att = time.perf_counter() - t0
+    parity = None if gpu is None else sample_parity(gpu, keep, R_or, o_or, lse_or, il_list, nb, B, tau)
     # projection: estimator time per group x Hkv; E6 time per row (evenly spaced
     # rows average the linear growth of row cost in i) x all rows
     t_layer = t_est * Hkv + t_att / rows_sample * (Hkv * nb)
@@ -186,7 +202,39 @@ def cpu_baseline(inp, tau, rows_sample=768):
                 sample=(f"E1-E5 for KV head 0 (4 query heads, all {nb} query blocks): {t_est:.2f} s; "
                         f"E6 for {rows_sample} evenly spaced query blocks of KV head 0: {t_att:.2f} s; "
                         f"projected layer time {t_layer:.0f} s (x{Hkv} heads, x{nb} rows)"),
-                measured_s=t_est + t_att, projected_layer_s=t_layer)
+                measured_s=t_est + t_att, projected_layer_s=t_layer, parity=parity)
+
+
+MASK_BAND = 1e-3          # a block may differ from the oracle's only where |R + tau| <= this
+O_TOL_MAX, O_TOL_MEAN = 2e-2, 2e-3
+
+
+def sample_parity(gpu, keep, R, o_or, lse_or, il_list, nb, B, tau):
+    """GPU vs oracle on the cpu_baseline sample (KV head 0): kept lists of all
+    query blocks, and o / lse of the sampled query blocks whose list equals
+    the oracle's (rows whose lists differ inside the band are valid results
+    of another mask and are counted, not compared)."""
+    rp, ci, (o_gpu, lse_gpu) = gpu
+    keep_gpu = np.zeros((nb, nb), dtype=bool)
+    for il in range(nb):                           # rows (b=0, g=0, il) come first
+        keep_gpu[il, ci[rp[il]:rp[il + 1]]] = True
+    diff = keep_gpu != keep[0]
+    band = np.abs(R[0] + tau) <= MASK_BAND
+    out_of_band = int((diff & ~band).sum())
+    same = [int(il) for il in np.unique(il_list) if not diff[il].any()]
+    err, lerr = [], []
+    for il in same:
+        lo, hi = il * B, min((il + 1) * B, o_gpu.shape[0])
+        err.append(np.abs(o_gpu[lo:hi] - o_or[lo:hi]).ravel())
+        lerr.append(np.abs(lse_gpu[:, lo:hi] - lse_or[:, lo:hi]).ravel())
+    err = np.concatenate(err) if err else np.zeros(1)
+    lerr = np.concatenate(lerr) if lerr else np.zeros(1)
+    return {"kv_head": 0, "mask_blocks": int(nb * (nb + 1) // 2), "mask_differs_in_band": int(diff.sum()) - out_of_band,
+            "mask_differs_out_of_band": out_of_band,
+            "rows_compared": len(same), "rows_skipped_mask_differs": len(np.unique(il_list)) - len(same),
+            "o_max_abs": float(err.max()), "o_mean_abs": float(err.mean()), "lse_max_abs": float(lerr.max()),
+            "tolerance": {"o_max_abs": O_TOL_MAX, "o_mean_abs": O_TOL_MEAN, "mask_band": MASK_BAND},
+            "ok": bool(out_of_band == 0 and err.max() <= O_TOL_MAX and err.mean() <= O_TOL_MEAN)}
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_S131072_tau4_traffic.md")
@@ -256,8 +304,12 @@ def main():
     t0 = time.time()
     inputs = synth.gen_fixed_multi(cfg, ("bf16",) if args.no_fp8 else ("bf16", "fp8"))
     log(f"generated S={cfg.S} inputs in {time.time() - t0:.1f} s")
-    bf, _ = time_path(fp, N, inputs["bf16"], args.tau, args.steps, args.warmup, "bf16")
+    bf, bf_csr = time_path(fp, N, inputs["bf16"], args.tau, args.steps, args.warmup, "bf16",
+                           keep_outputs=not args.no_cpu_baseline)
     log(f"bf16: {json.dumps(bf)}")
+    # cold caches: a 1 GiB write before each step evicts L2 and the memory-side cache
+    cold, _ = time_path(fp, N, inputs["bf16"], args.tau, 5, 1, "bf16 cold", flush_bytes=1 << 30)
+    log(f"bf16 cold: {json.dumps(cold)}")
     f8 = None
     if not args.no_fp8:
         f8, _ = time_path(fp, N, inputs["fp8"], args.tau, args.steps, args.warmup, "fp8")
@@ -275,7 +327,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         t0 = time.time()
-        cpu = cpu_baseline(inputs["bf16"], args.tau)
+        cpu = cpu_baseline(inputs["bf16"], args.tau, gpu=bf_csr)
         log(f"cpu baseline ({time.time() - t0:.1f} s): {json.dumps(cpu)}")
 
     att_peak = PEAK_TFLOPS["bf16"]
@@ -294,6 +346,11 @@ def main():
         "kept_fraction": round(bf["kept_fraction"], 5),
         "ms_per_layer": {"total": round(bf["ms_per_step"], 4), "estimate": round(bf["ms_estimate"], 4),
                          "select": round(bf["ms_select"], 4), "attention": round(bf["ms_attention"], 4)},
+        "ms_per_layer_median": {"total": round(bf["ms_step_median"], 4),
+                                "attention": round(bf["ms_attention_median"], 4)},
+        "cold_cache": {"runs": 5, "flush": "1 GiB written before each step",
+                       "ms_per_layer_median": round(cold["ms_step_median"], 4),
+                       "ms_attention_median": round(cold["ms_attention_median"], 4)},
         "mfma_util_kept": round(bf["attn_kept_tflops"] / att_peak, 4),
         "mfma_util_executed": round(bf["attn_executed_tflops"] / att_peak, 4),
         "estimator_gbs": round(bf["estimate_gbs"], 1), "select_gbs": round(bf["select_gbs"], 1),
@@ -322,6 +379,7 @@ def main():
     if cpu is not None:
         line["cpu_baseline"] = {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")}
         line["cpu_baseline"]["value"] = round(cpu["value"], 6)
+        line["parity_sample"] = cpu["parity"]
     print(json.dumps(line), flush=True)
 
 
