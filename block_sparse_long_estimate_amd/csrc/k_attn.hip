@@ -90,7 +90,9 @@ __device__ __forceinline__ void online_update(f32x16 (&sacc)[NKB], float f, floa
     // Lazy rescale: keep the running reference m while the tile maximum stays
     // within 2^LAZY of it (probabilities then reach at most 2^LAZY, harmless
     // in fp32 sums and bf16 P); rescale only when some lane of the wave needs to.
-    const bool need = LAZY == 0 ? true : (mcand > m + (float)LAZY);
+    // LAZY = 0 rescales whenever the maximum grows; when it does not, the
+    // factor would be exactly 1, so skipping it changes no bit.
+    const bool need = mcand > m + (float)LAZY;
     if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
         const float mnew = need ? mcand : m;
         const float alpha = __builtin_amdgcn_exp2f(m - (mnew == NEG_INF ? 0.f : mnew));
