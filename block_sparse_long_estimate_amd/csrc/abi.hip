@@ -97,7 +97,7 @@ GeoFixed geo_fixed(const fp_problem* p) {
 bool misaligned(const void* ptr, size_t a) { return ((uintptr_t)ptr) % a != 0; }
 
 struct SelectWs {
-    size_t counts, bits, total;
+    size_t counts, bits, hist, total;
     int nbw;
 };
 
@@ -106,7 +106,8 @@ SelectWs select_ws(long long rows, int max_nbk) {
     w.nbw = cdiv(max_nbk, 32) + 1;
     w.counts = 0;
     w.bits = align_up((size_t)rows * 4);
-    w.total = w.bits + align_up((size_t)rows * w.nbw * 4);
+    w.hist = w.bits + align_up((size_t)rows * w.nbw * 4);
+    w.total = w.hist + align_up((size_t)((rows + SORT_CHUNK - 1) / SORT_CHUNK) * (max_nbk + 1) * 4);
     return w;
 }
 
@@ -232,6 +233,7 @@ int fp_select_blocks(const fp_problem* p, const float* scores, float tau, int32_
     a.scores = scores;
     a.counts = (int32_t*)((char*)workspace + w.counts);
     a.bits = (uint32_t*)((char*)workspace + w.bits);
+    a.hist = (int32_t*)((char*)workspace + w.hist);
     a.nbw = w.nbw;
     a.row_ptr = row_ptr; a.col_idx = col_idx; a.sched = sched;
     a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads;
@@ -475,6 +477,7 @@ int fp_sparse_prefill_paged(const fp_varlen_problem* p, const void* q, const int
     se.scores = scores;
     se.counts = (int32_t*)(selws + plan.sel.counts);
     se.bits = (uint32_t*)(selws + plan.sel.bits);
+    se.hist = (int32_t*)(selws + plan.sel.hist);
     se.nbw = plan.sel.nbw;
     se.row_ptr = row_ptr; se.col_idx = col_idx; se.sched = sched;
     se.Hq = p->num_q_heads; se.Hkv = p->num_kv_heads;

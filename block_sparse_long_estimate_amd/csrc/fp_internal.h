@@ -142,9 +142,12 @@ struct ScoreArgs {
     float scale;
 };
 
+constexpr int SORT_CHUNK = 256;    // rows per chunk of the schedule sort
+
 struct SelectArgs {
     const float* scores;
     int32_t* counts; uint32_t* bits; int nbw;   // bitmask row stride (u32 words)
+    int32_t* hist;                              // [chunks][max_nbk + 1] sort histograms / offsets
     int32_t* row_ptr; int32_t* col_idx; int32_t* sched;
     int Hq, Hkv, rows, max_nbk;
     float neg_tau;

@@ -14,8 +14,8 @@
 // scan_rows:   single workgroup exclusive scan of the counts -> row_ptr.
 // expand_rows: one wavefront per row, ballot + lane-prefix popcount writes the
 //   ascending column list at row_ptr.
-// sort_rows:   single workgroup stable counting sort of the rows by count
-//   (descending), ties by row id -> sched.
+// sort_*:      stable counting sort of the rows by count (descending), ties
+//   by row id -> sched, over chunks of rows (histograms, offsets, scatter).
 #include "fp_internal.h"
 
 namespace fp {
@@ -115,24 +115,33 @@ __global__ __launch_bounds__(256) void expand_rows_kernel(Geo geo, SelectArgs a)
     }
 }
 
-// Stable counting sort, keys = counts in [1, max_nbk], descending. One
-// workgroup of 1024 threads; bins in dynamic LDS.
-__global__ __launch_bounds__(1024) void sort_rows_kernel(SelectArgs a) {
-    extern __shared__ __align__(16) int sm[];
-    const int nbin = a.max_nbk + 1;
-    int* cur = sm;                 // [nbin] bin cursor
-    int* keys = sm + ((nbin + 3) & ~3);   // [1024] keys of the current chunk (16-byte aligned)
+// Stable counting sort of the rows by kept count, descending, ties by row id
+// ascending, in three passes over chunks of SORT_CHUNK consecutive rows:
+//   sort_hist:    per chunk, a histogram of the counts (LDS atomics) -> hist[c][k];
+//   sort_offsets: per count k (descending) and chunk c (ascending), the first
+//                 position of chunk c's rows with count k, written over hist;
+//   sort_scatter: per chunk, each row's rank among the equal counts before it
+//                 in the chunk, added to that position -> sched.
+__global__ __launch_bounds__(SORT_CHUNK) void sort_hist_kernel(SelectArgs a) {
+    extern __shared__ __align__(16) int hsh[];   // [nbin]
+    const int nbin = a.max_nbk + 1, c = blockIdx.x, tid = threadIdx.x;
+    for (int k = tid; k < nbin; k += SORT_CHUNK) hsh[k] = 0;
+    __syncthreads();
+    const int r = c * SORT_CHUNK + tid;
+    if (r < a.rows) atomicAdd(&hsh[a.counts[r]], 1);
+    __syncthreads();
+    int* out = a.hist + (long long)c * nbin;
+    for (int k = tid; k < nbin; k += SORT_CHUNK) out[k] = hsh[k];
+}
+
+__global__ __launch_bounds__(1024) void sort_offsets_kernel(SelectArgs a) {
     __shared__ int part[1024];
-    const int tid = threadIdx.x;
-    for (int k = tid; k < nbin; k += 1024) cur[k] = 0;
-    __syncthreads();
-    for (int r = tid; r < a.rows; r += 1024) atomicAdd(&cur[a.counts[r]], 1);
-    __syncthreads();
-    // cursor[k] = number of rows with a larger count (descending order)
+    const int nbin = a.max_nbk + 1, nch = cdiv(a.rows, SORT_CHUNK), tid = threadIdx.x;
     const int per = cdiv(nbin, 1024);
     const int lo = min(tid * per, nbin), hi = min(lo + per, nbin);
-    int sum = 0;
-    for (int k = lo; k < hi; ++k) sum += cur[k];
+    int sum = 0;                                   // rows with a count in [lo, hi)
+    for (int k = lo; k < hi; ++k)
+        for (int c = 0; c < nch; ++c) sum += a.hist[(long long)c * nbin + k];
     part[tid] = sum;
     __syncthreads();
     for (int o = 1; o < 1024; o <<= 1) {           // inclusive suffix scan over threads
@@ -141,37 +150,34 @@ __global__ __launch_bounds__(1024) void sort_rows_kernel(SelectArgs a) {
         part[tid] += v;
         __syncthreads();
     }
-    int run = part[tid] - sum;                      // rows in bins above this chunk
-    for (int k = hi - 1; k >= lo; --k) {
-        const int c = cur[k];
-        cur[k] = run;
-        run += c;
-    }
+    int run = part[tid] - sum;                     // rows with a larger count than hi - 1
+    for (int k = hi - 1; k >= lo; --k)
+        for (int c = 0; c < nch; ++c) {
+            int* h = a.hist + (long long)c * nbin + k;
+            const int n = *h;
+            *h = run;
+            run += n;
+        }
+}
+
+__global__ __launch_bounds__(SORT_CHUNK) void sort_scatter_kernel(SelectArgs a) {
+    __shared__ __align__(16) int keys[SORT_CHUNK];
+    const int nbin = a.max_nbk + 1, c = blockIdx.x, tid = threadIdx.x;
+    const int r = c * SORT_CHUNK + tid;
+    const int key = r < a.rows ? a.counts[r] : -1;
+    keys[tid] = key;
     __syncthreads();
-    for (int base = 0; base < a.rows; base += 1024) {
-        const int r = base + tid;
-        const int key = r < a.rows ? a.counts[r] : -1;
-        keys[tid] = key;
-        __syncthreads();
-        // stable rank among equal keys of the chunk; 16-byte reads, unrolled,
-        // so several LDS reads are in flight (the loop is latency-bound)
-        int rank = 0;
-        const int4* k4 = (const int4*)keys;
-        const int n4 = tid >> 2;
+    if (key < 0) return;
+    int rank = 0;                                  // equal counts earlier in the chunk
+    const int4* k4 = (const int4*)keys;
+    const int n4 = tid >> 2;
 #pragma unroll 8
-        for (int t4 = 0; t4 < n4; ++t4) {
-            const int4 w = k4[t4];
-            rank += (w.x == key) + (w.y == key) + (w.z == key) + (w.w == key);
-        }
-        for (int t = n4 * 4; t < tid; ++t) rank += keys[t] == key;
-        const int pos = key >= 0 ? cur[key] + rank : 0;
-        __syncthreads();
-        if (key >= 0) {
-            a.sched[pos] = r;
-            atomicAdd(&cur[key], 1);
-        }
-        __syncthreads();
+    for (int t4 = 0; t4 < n4; ++t4) {
+        const int4 w = k4[t4];
+        rank += (w.x == key) + (w.y == key) + (w.z == key) + (w.w == key);
     }
+    for (int t = n4 * 4; t < tid; ++t) rank += keys[t] == key;
+    a.sched[a.hist[(long long)c * nbin + key] + rank] = r;
 }
 
 template <typename Geo>
@@ -181,13 +187,16 @@ static hipError_t select_dispatch(const Geo& geo, const SelectArgs& a, hipStream
     scan_rows_kernel<<<1, 1024, 0, st>>>(a);
     expand_rows_kernel<Geo><<<wg, 256, 0, st>>>(geo, a);
     if (a.sched) {
-        const size_t shm = (size_t)(((a.max_nbk + 1 + 3) & ~3) + 1024) * sizeof(int);
+        const int nch = cdiv(a.rows, SORT_CHUNK);
+        const size_t shm = (size_t)(a.max_nbk + 1) * sizeof(int);
         if (shm > 65536) {
-            hipError_t e = hipFuncSetAttribute((const void*)sort_rows_kernel,
+            hipError_t e = hipFuncSetAttribute((const void*)sort_hist_kernel,
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
             if (e != hipSuccess) return e;
         }
-        sort_rows_kernel<<<1, 1024, shm, st>>>(a);
+        sort_hist_kernel<<<nch, SORT_CHUNK, shm, st>>>(a);
+        sort_offsets_kernel<<<1, 1024, 0, st>>>(a);
+        sort_scatter_kernel<<<nch, SORT_CHUNK, 0, st>>>(a);
     }
     return hipGetLastError();
 }
