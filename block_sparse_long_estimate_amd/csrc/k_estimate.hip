@@ -110,7 +110,9 @@ __global__ __launch_bounds__(256) void pool_kernel(Geo geo, PoolArgs a) {
 template <typename Geo>
 __global__ __launch_bounds__(256) void scores_kernel(Geo geo, ScoreArgs a) {
     constexpr int T = SC_TILE;
-    constexpr int LD = D + 4;
+    constexpr int NPASS = 4;
+    constexpr int DH = D / NPASS;             // dims staged per pass (a quarter of the LDS: more workgroups per CU)
+    constexpr int LD = DH + 4;
     __shared__ __align__(16) float Qs[T][LD];
     __shared__ __align__(16) float Ks[T][LD];
 
@@ -137,35 +139,39 @@ __global__ __launch_bounds__(256) void scores_kernel(Geo geo, ScoreArgs a) {
         }
         return;
     }
-    // stage pooled rows (zero outside the sequence)
-    for (int e = tid; e < T * (D / 4); e += 256) {
-        const int r = e / (D / 4), c4 = e % (D / 4);
-        float4 qv = make_float4(0.f, 0.f, 0.f, 0.f), kv = qv;
-        if (il0 + r < s.nq) qv = *(const float4*)(a.qbar + qbar_row(s, a.Hq, h, il0 + r) * D + c4 * 4);
-        if (j0 + r < s.nbk) kv = *(const float4*)(a.kbar + kbar_row(s, a.Hkv, g, j0 + r) * D + c4 * 4);
-        *(float4*)&Qs[r][c4 * 4] = qv;
-        *(float4*)&Ks[r][c4 * 4] = kv;
-    }
-    __syncthreads();
-
     // Each wavefront computes one 32x32 quadrant on v_mfma_f32_32x32x2_f32
-    // (fp32 operands and accumulation). MFMA step kk takes dim kk from lanes
-    // 0-31 and dim 64 + kk from lanes 32-63 (any pairing works as long as both
-    // operands use it), so a lane reads 4 consecutive dims per LDS read.
+    // (fp32 operands and accumulation), over NPASS passes of DH staged dims.
+    // MFMA step kk of a pass takes dim kk from lanes 0-31 and dim DH/2 + kk
+    // from lanes 32-63 (any pairing works as long as both operands use it), so
+    // a lane reads 4 consecutive dims per LDS read.
     typedef __attribute__((ext_vector_type(16))) float f32x16;
     const int wave = tid >> 6, lane = tid & 63, n = lane & 31, lh = lane >> 5;
     const int wr = wave >> 1, wc = wave & 1;
     f32x16 acc;
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[v] = 0.f;
-#pragma unroll 4
-    for (int t = 0; t < 16; ++t) {
-        const float4 qv = *(const float4*)&Qs[32 * wr + n][64 * lh + 4 * t];
-        const float4 kv = *(const float4*)&Ks[32 * wc + n][64 * lh + 4 * t];
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qv.x, kv.x, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qv.y, kv.y, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qv.z, kv.z, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qv.w, kv.w, acc, 0, 0, 0);
+    for (int pass = 0; pass < NPASS; ++pass) {
+        if (pass) __syncthreads();                // the first pass's operands are consumed
+        // stage dims [64 pass, 64 pass + 64) of the pooled rows (zero outside the sequence)
+        for (int e = tid; e < T * (DH / 4); e += 256) {
+            const int r = e / (DH / 4), c4 = e % (DH / 4);
+            float4 qv = make_float4(0.f, 0.f, 0.f, 0.f), kv = qv;
+            const int d0 = pass * DH + c4 * 4;
+            if (il0 + r < s.nq) qv = *(const float4*)(a.qbar + qbar_row(s, a.Hq, h, il0 + r) * D + d0);
+            if (j0 + r < s.nbk) kv = *(const float4*)(a.kbar + kbar_row(s, a.Hkv, g, j0 + r) * D + d0);
+            *(float4*)&Qs[r][c4 * 4] = qv;
+            *(float4*)&Ks[r][c4 * 4] = kv;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < DH / 8; ++t) {
+            const float4 qv = *(const float4*)&Qs[32 * wr + n][(DH / 2) * lh + 4 * t];
+            const float4 kv = *(const float4*)&Ks[32 * wc + n][(DH / 2) * lh + 4 * t];
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qv.x, kv.x, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qv.y, kv.y, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qv.z, kv.z, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qv.w, kv.w, acc, 0, 0, 0);
+        }
     }
     // accumulator: lane holds column n, rows 8 (v / 4) + 4 lh + v % 4
     const int jj = j0 + 32 * wc + n;
