@@ -15,7 +15,8 @@ fraction over the FLOPs of the kept blocks, and the single-threaded CPU
 oracle's throughput on a bounded sample as `cpu_baseline`. Context legs on
 the same tensors (skipped with --no-sweep): bf16 at tau 2, 6, 8, and tau=inf,
 where every block is kept and the path is this library's own dense causal
-attention.
+attention. The paged varlen entry point is timed on its own 8-sequence
+batch (skipped with --no-paged).
 """
 from __future__ import annotations
 
@@ -56,6 +57,76 @@ def kept_flops_from_csr(row_ptr, col_idx, nb, S, B, G, d, Hkv, batch):
     npr = (i_all + 1) - counts
     corr = 4.0 * d * G * float((n_all * npr).sum())
     return kept, corr
+
+
+def varlen_flops(rp, ci, L, P, B, G, d, Hkv):
+    """Kept, correction and dense-equivalent FLOPs of a varlen batch whose CSR
+    rows are (b, g, il), il over the query blocks of [P_b, L_b) on the
+    absolute block grid; causal (t, s) pairs counted exactly."""
+    kept = corr = dense = 0.0
+    row = 0
+    for Lb, Pb in zip(L, P):
+        Lb, Pb = int(Lb), int(Pb)
+        i0, i1 = Pb // B, (Lb - 1) // B
+        dense += 4.0 * d * G * Hkv * sum(t + 1 for t in range(Pb, Lb))
+        for g in range(Hkv):
+            for i in range(i0, i1 + 1):
+                lo, hi = max(i * B, Pb), min((i + 1) * B, Lb)
+                cols = ci[rp[row]:rp[row + 1]]
+                row += 1
+                for j in cols:
+                    j = int(j)
+                    if j < i:
+                        kept += (hi - lo) * (min((j + 1) * B, Lb) - j * B)
+                    else:                      # diagonal: s in [iB, t]
+                        kept += sum(t - i * B + 1 for t in range(lo, hi))
+                corr += (hi - lo) * ((i + 1) - len(cols))
+    assert row == len(rp) - 1
+    return 4.0 * d * G * kept, 4.0 * d * G * corr, dense
+
+
+def time_paged(fp, N, steps, warmup):
+    """The paged varlen entry point (all stages in one call) on the 8-sequence
+    batch of 4K-64K tokens with cached prefixes and 64-token pages."""
+    import torch
+    import synth
+    cfg = synth.config(5)
+    inp = synth.gen_paged(cfg)
+    dev = torch.device("cuda:0")
+    q, kc, vc, bt = inp.q.to(dev), inp.k_cache.to(dev), inp.v_cache.to(dev), inp.block_table.to(dev)
+    vp = fp.make_varlen_problem(q, inp.cu_seqlens_q, inp.seqlens_k, kc, bt, cfg.block)
+    ws = torch.empty(vp.ws_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        out = fp.fp_sparse_prefill_paged(vp, q, kc, vc, bt, cfg.tau, workspace=ws)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        out = fp.fp_sparse_prefill_paged(vp, q, kc, vc, bt, cfg.tau, workspace=ws)
+        e1.record(stream)
+        ts.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ts]
+    rp, ci = out[2].cpu().numpy(), out[3].cpu().numpy()
+    G = cfg.Hq // cfg.Hkv
+    kept, corr, dense = varlen_flops(rp, ci, inp.seqlens_k, inp.prefix, cfg.block, G, 128, cfg.Hkv)
+    nblk = sum(cfg.Hkv * sum(i + 1 for i in range(int(P) // cfg.block, (int(L) - 1) // cfg.block + 1))
+               for L, P in zip(inp.seqlens_k, inp.prefix))
+    t = float(np.median(ms))
+    res = {"workload": f"{len(inp.seqlens_k)} sequences, L={inp.seqlens_k.tolist()}, "
+                       f"cached prefix P={inp.prefix.tolist()}, {cfg.page_size}-token pages, "
+                       f"32/8 heads, 128x128 blocks, tau={cfg.tau}",
+           "ms_per_layer_median": round(t, 4), "steps": steps,
+           "dense_equiv_tflops": round(dense / (t * 1e-3) / 1e12, 2),
+           "kept_fraction": round(len(ci[:rp[-1]]) / nblk, 5),
+           "kept_tflops_whole_call": round(kept / (t * 1e-3) / 1e12, 2),
+           "mfma_util_kept_whole_call": round(kept / (t * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4),
+           "correction_tflop": round(corr / 1e12, 3)}
+    del q, kc, vc, bt, ws, out
+    torch.cuda.empty_cache()
+    return res
 
 
 def time_path(fp, N, inp, tau, steps, warmup, label, flush_bytes=0, keep_outputs=False):
@@ -273,6 +344,7 @@ def main():
     ap.add_argument("--seqlen", type=int, default=131072)
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-paged", action="store_true", help="skip the paged varlen batch leg")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the context legs (bf16 at tau 2/6/8, and tau=inf: every block kept)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -314,6 +386,10 @@ def main():
     if not args.no_fp8:
         f8, _ = time_path(fp, N, inputs["fp8"], args.tau, args.steps, args.warmup, "fp8")
         log(f"fp8: {json.dumps(f8)}")
+    paged = None
+    if not args.no_paged:
+        paged = time_paged(fp, N, 5, 1)
+        log(f"paged varlen: {json.dumps(paged)}")
     sweep, dense = {}, None
     if not args.no_sweep:
         for tau in (2.0, 6.0, 8.0):
@@ -367,6 +443,8 @@ def main():
                        "attn_kept_tflops": round(f8["attn_kept_tflops"], 2),
                        "mfma_util_kept": round(f8["attn_kept_tflops"] / PEAK_TFLOPS["fp8"], 4),
                        "estimator_gbs": round(f8["estimate_gbs"], 1)}
+    if paged is not None:
+        line["paged_varlen_bf16"] = paged
     if sweep:
         line["tau_sweep_bf16"] = sweep
     if dense is not None:

@@ -492,6 +492,8 @@ int fp_sparse_prefill_paged(const fp_varlen_problem* p, const void* q, const int
     a.qa = RowAddr{0, p->q_stride[0], p->q_stride[1]};
     a.oa = RowAddr{0, p->o_stride[0], p->o_stride[1]};
     a.ka = kva; a.va = kva;
+    // per-lane in-page offsets of a tile are kept in 24 bits (bf16: 2 bytes)
+    a.paged_fast = (long long)std::min(p->page_size, p->block) * p->kv_stride[1] * 2 < (1LL << 24);
     a.qs = a.ks = a.vs = ScaleAddr{nullptr, 0, 0};
     a.kbar = kbar; a.vbar = vbar;
     {

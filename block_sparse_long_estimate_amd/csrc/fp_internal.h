@@ -101,6 +101,10 @@ struct KVAddr {
         }
         return (long long)b * sb + (long long)s * st + (long long)g * sh;
     }
+    // paged offset with the page id already looked up
+    __device__ __forceinline__ long long off_page(int pg, int s, int g) const {
+        return (long long)pg * spage + (long long)(s & ((1 << page_shift) - 1)) * st + (long long)g * sh;
+    }
 };
 
 // Pooled tensors: Qbar [qb0*Hq + h*nq + il], Kbar/Vbar [kb0*Hkv + g*nbk + j], rows of D floats.
@@ -164,6 +168,7 @@ struct AttnArgs {
     int Hq, Hkv, G, rows, slices;
     float scale_log2;                  // c * log2(e)
     int o_f32;                         // o in fp32 (diagnostic) instead of bf16
+    int paged_fast;                    // paged: in-page offsets of a tile fit 24 bits (precomputed per lane)
 };
 
 hipError_t launch_pool(const GeoFixed* gf, const GeoTable* gt, const PoolArgs& a, hipStream_t st);

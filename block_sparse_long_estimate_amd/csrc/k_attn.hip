@@ -46,6 +46,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) int lds_int;
 
 constexpr float LN2 = 0.6931471805599453f;
 
@@ -166,7 +167,7 @@ constexpr int VSTR8 = 160;
 // sequence repeat its last key. ESZ = bytes per element.
 template <int STR, int BLK, int ESZ, bool PERM, bool PAGED>
 __device__ __forceinline__ void issue_tile(const uint8_t* base, const KVAddr& ka, int b, int L, int g,
-                                           int j, lds_u8* buf, int wave, int lane) {
+                                           int j, lds_u8* buf, int wave, int lane, const lds_int* pages) {
     constexpr int PIECES = BLK * STR / 1024;
     asm volatile("" : "+v"(lane));   // recompute addresses per call, keep none live
     const int rmax = L - 1 - j * BLK;
@@ -179,7 +180,10 @@ __device__ __forceinline__ void issue_tile(const uint8_t* base, const KVAddr& ka
             const int ch = (pb - row * STR) >> 4;
             const int key = PERM ? vt_slot(row) : row;
             const int sk = j * BLK + min(key, rmax);
-            const uint8_t* src = base + ka.template off<PAGED>(b, sk, g) * ESZ + ch * 16;
+            // paged: the sequence's page ids staged in LDS when they fit, else the block table
+            const long long off = PAGED && pages ? ka.off_page(pages[sk >> ka.page_shift], sk, g)
+                                                 : ka.template off<PAGED>(b, sk, g);
+            const uint8_t* src = base + off * ESZ + ch * 16;
             if (ch < 8 * ESZ)
                 __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(buf + t * 1024), 16, 0, 0);
         }
@@ -216,6 +220,35 @@ struct TileOffs {
                                                  (lds_void*)(buf + t * 1024), 16, 0, 0);
         }
     }
+    // Paged K/V: a tile's key `key` lies in page slot key >> lshift of the
+    // tile (lshift = log2 min(page, BLK)) at in-page row key & (2^lshift - 1).
+    // off packs that in-page byte offset (low 24 bits) with the slot.
+    __device__ __forceinline__ void init_paged(long long tok_stride, int lshift, int wave, int lane) {
+#pragma unroll
+        for (int k = 0; k < NP; ++k) {
+            const int pb = (k * 8 + wave) * 1024 + lane * 16;
+            const int row = pb / STR;
+            const int ch = (pb - row * STR) >> 4;
+            const int key = PERM ? vt_slot(row) : row;
+            const uint32_t inpage = (uint32_t)((key & ((1 << lshift) - 1)) * tok_stride * ESZ + ch * 16);
+            off[k] = ch < 8 * ESZ ? (inpage | ((uint32_t)(key >> lshift) << 24)) : PAD;
+        }
+    }
+    // full paged tile: pages = the tile's first page slot in the staged page
+    // list, base = the uniform part (head, in-page start of the tile)
+    __device__ __forceinline__ void issue_paged(const uint8_t* base, const lds_int* pages,
+                                                unsigned long long page_bytes, lds_u8* buf, int wave) const {
+#pragma unroll
+        for (int k = 0; k < NP; ++k) {
+            const int t = k * 8 + wave;
+            if (t < PIECES && off[k] != PAD) {
+                const int pg = pages[off[k] >> 24];
+                __builtin_amdgcn_global_load_lds(
+                    (const void*)(base + (unsigned long long)pg * page_bytes + (off[k] & 0xFFFFFFu)),
+                    (lds_void*)(buf + t * 1024), 16, 0, 0);
+            }
+        }
+    }
 };
 
 template <int BLK, bool FP8>
@@ -228,8 +261,16 @@ struct KVOffs {
 template <int BLK, bool FP8, bool PAGED>
 __device__ __forceinline__ void issue_kv(const AttnArgs& a, int b, int L, int g, int j,
                                          lds_u8* kbuf, lds_u8* vbuf, int wave, int lane,
-                                         const KVOffs<BLK, FP8>& o) {
+                                         const KVOffs<BLK, FP8>& o, const lds_int* pages) {
     constexpr int ESZ = FP8 ? 1 : 2;
+    if (PAGED && pages && a.paged_fast && (j + 1) * BLK <= L) {
+        const int sh = a.ka.page_shift;
+        const long long ub = (long long)((j * BLK) & ((1 << sh) - 1)) * a.ka.st + (long long)g * a.ka.sh;
+        const lds_int* pt = pages + ((j * BLK) >> sh);
+        o.k.issue_paged((const uint8_t*)a.k + ub * ESZ, pt, (unsigned long long)a.ka.spage * ESZ, kbuf, wave);
+        o.v.issue_paged((const uint8_t*)a.v + ub * ESZ, pt, (unsigned long long)a.va.spage * ESZ, vbuf, wave);
+        return;
+    }
     if (!PAGED && (j + 1) * BLK <= L) {
         const long long k0 = a.ka.template off<false>(b, j * BLK, g) * ESZ;
         const long long v0 = a.va.template off<false>(b, j * BLK, g) * ESZ;
@@ -238,9 +279,9 @@ __device__ __forceinline__ void issue_kv(const AttnArgs& a, int b, int L, int g,
         return;
     }
     issue_tile<FP8 ? KSTR8 : KSTR, BLK, ESZ, false, PAGED>((const uint8_t*)a.k, a.ka, b, L, g, j, kbuf, wave,
-                                                           lane);
+                                                           lane, pages);
     issue_tile<FP8 ? VSTR8 : VSTR, BLK, ESZ, FP8, PAGED>((const uint8_t*)a.v, a.va, b, L, g, j, vbuf, wave,
-                                                         lane);
+                                                         lane, pages);
 }
 
 // bf16 S^T for key blocks kb0 .. kb0 + NB - 1 (32 keys each) of the tile.
@@ -411,6 +452,9 @@ __global__ __launch_bounds__(512, 1) void attn_tile_kernel(Geo geo, AttnArgs a) 
     __shared__ __align__(1024) uint8_t vB_[VTILE];
     __shared__ uint32_t kept[MAX_NB / 32];
     __shared__ int svmax_sh;
+    // paged K/V: the sequence's page ids (K and V share the block table)
+    constexpr int PAGE_CAP = 2048;
+    __shared__ int pages_sh[PAGED ? PAGE_CAP : 1];
     lds_u8* const kA = (lds_u8*)kA_;
     lds_u8* const kB = (lds_u8*)kB_;
     lds_u8* const vA = (lds_u8*)vA_;
@@ -454,8 +498,24 @@ __global__ __launch_bounds__(512, 1) void attn_tile_kernel(Geo geo, AttnArgs a) 
     if (!PAGED) {
         kvo.k.init(a.ka.st, wave, lane);
         kvo.v.init(a.va.st, wave, lane);
+    } else if (a.paged_fast) {
+        constexpr int LB = BLK == 128 ? 7 : 6;
+        const int lshift = min(a.ka.page_shift, LB);
+        kvo.k.init_paged(a.ka.st, lshift, wave, lane);
+        kvo.v.init_paged(a.va.st, lshift, wave, lane);
     }
-    issue_kv<BLK, FP8, PAGED>(a, b, s.L, g, j0, kA, vA, wave, lane, kvo);
+    issue_kv<BLK, FP8, PAGED>(a, b, s.L, g, j0, kA, vA, wave, lane, kvo, nullptr);
+    // paged: stage the page ids for the later tiles (visible after the
+    // barrier that follows the kept-bitmap build)
+    const lds_int* pages = nullptr;
+    if constexpr (PAGED) {
+        const int npg = (s.L + (1 << a.ka.page_shift) - 1) >> a.ka.page_shift;
+        if (npg <= PAGE_CAP) {
+            const int* row = a.ka.table + (long long)b * a.ka.maxp;
+            for (int p = tid; p < npg; p += 512) pages_sh[p] = row[p];
+            pages = (const lds_int*)pages_sh;
+        }
+    }
 
     // Query fragment. bf16: lane (n, lh) holds q[t, h, 16 ks + 8 lh .. + 8];
     // fp8: the codes q[t, h, 64 ks + 32 lh .. + 32], widened to bf16 (exact)
@@ -552,7 +612,7 @@ __global__ __launch_bounds__(512, 1) void attn_tile_kernel(Geo geo, AttnArgs a) 
     };
     auto issue = [&](int code, lds_u8* kb, lds_u8* vb, float& ksn, float& vsn) __attribute__((always_inline)) {
         if (code >= 0) {
-            issue_kv<BLK, FP8, PAGED>(a, b, s.L, g, code, kb, vb, wave, lane, kvo);
+            issue_kv<BLK, FP8, PAGED>(a, b, s.L, g, code, kb, vb, wave, lane, kvo, pages);
             if constexpr (FP8) {
                 ksn = load_scale(ksp, (code * BLK) >> 7);
                 vsn = load_scale(vsp, (code * BLK) >> 7);

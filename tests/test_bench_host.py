@@ -103,3 +103,29 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_varlen_flops_match_oracle_counts():
+    """Two sequences with cached prefixes that start mid-block."""
+    B, Hkv, G, d = 64, 2, 2, 128
+    L, P = [300, 200], [70, 0]
+    rng = np.random.default_rng(11)
+    rps, cis, keeps = [0], [], []
+    for Lb, Pb in zip(L, P):
+        i0, nq = oc.query_blocks(Pb, Lb, B)
+        nb = oc.nblocks(Lb, B)
+        keep = np.zeros((Hkv, nq, nb), dtype=bool)
+        for g in range(Hkv):
+            for il in range(nq):
+                i = i0 + il
+                keep[g, il, :i + 1] = rng.random(i + 1) < 0.5
+                keep[g, il, 0] = keep[g, il, i] = True
+                cols = np.nonzero(keep[g, il])[0]
+                cis.extend(cols.tolist())
+                rps.append(len(cis))
+        keeps.append(keep)
+    rp, ci = np.array(rps), np.array(cis)
+    kept, corr, dense = bench.varlen_flops(rp, ci, L, P, B, G, d, Hkv)
+    assert kept == sum(oc.kept_flops(k, Pb, Lb, B, d, G) for k, Lb, Pb in zip(keeps, L, P))
+    assert corr == sum(oc.correction_flops(k, Pb, Lb, B, d, G) for k, Lb, Pb in zip(keeps, L, P))
+    assert dense == sum(oc.dense_flops(Pb, Lb, d, G * Hkv) for Lb, Pb in zip(L, P))
