@@ -345,6 +345,7 @@ def main():
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-paged", action="store_true", help="skip the paged varlen batch leg")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache leg")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the context legs (bf16 at tau 2/6/8, and tau=inf: every block kept)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -380,8 +381,10 @@ def main():
                            keep_outputs=not args.no_cpu_baseline)
     log(f"bf16: {json.dumps(bf)}")
     # cold caches: a 1 GiB write before each step evicts L2 and the memory-side cache
-    cold, _ = time_path(fp, N, inputs["bf16"], args.tau, 5, 1, "bf16 cold", flush_bytes=1 << 30)
-    log(f"bf16 cold: {json.dumps(cold)}")
+    cold = None
+    if not args.no_cold:
+        cold, _ = time_path(fp, N, inputs["bf16"], args.tau, 5, 1, "bf16 cold", flush_bytes=1 << 30)
+        log(f"bf16 cold: {json.dumps(cold)}")
     f8 = None
     if not args.no_fp8:
         f8, _ = time_path(fp, N, inputs["fp8"], args.tau, args.steps, args.warmup, "fp8")
@@ -424,9 +427,6 @@ def main():
                          "select": round(bf["ms_select"], 4), "attention": round(bf["ms_attention"], 4)},
         "ms_per_layer_median": {"total": round(bf["ms_step_median"], 4),
                                 "attention": round(bf["ms_attention_median"], 4)},
-        "cold_cache": {"runs": 5, "flush": "1 GiB written before each step",
-                       "ms_per_layer_median": round(cold["ms_step_median"], 4),
-                       "ms_attention_median": round(cold["ms_attention_median"], 4)},
         "mfma_util_kept": round(bf["attn_kept_tflops"] / att_peak, 4),
         "mfma_util_executed": round(bf["attn_executed_tflops"] / att_peak, 4),
         "estimator_gbs": round(bf["estimate_gbs"], 1), "select_gbs": round(bf["select_gbs"], 1),
@@ -443,6 +443,10 @@ def main():
                        "attn_kept_tflops": round(f8["attn_kept_tflops"], 2),
                        "mfma_util_kept": round(f8["attn_kept_tflops"] / PEAK_TFLOPS["fp8"], 4),
                        "estimator_gbs": round(f8["estimate_gbs"], 1)}
+    if cold is not None:
+        line["cold_cache"] = {"runs": 5, "flush": "1 GiB written before each step",
+                              "ms_per_layer_median": round(cold["ms_step_median"], 4),
+                              "ms_attention_median": round(cold["ms_attention_median"], 4)}
     if paged is not None:
         line["paged_varlen_bf16"] = paged
     if sweep:
