@@ -244,7 +244,7 @@ def check_paged(fp, inp, tau, sample_rows=None):
     assert row0 == len(rp) - 1
 
 
-@pytest.mark.parametrize("page", [64, 16])
+@pytest.mark.parametrize("page", [64, 16, 256])
 def test_paged_varlen_small(fp, page):
     cfg = synth.config(5, Hq=8, Hkv=2, n_seqs=4, len_range=(300, 3500), page_size=page, tau=2.0)
     L, P = synth.paged_lengths(cfg)
@@ -253,10 +253,15 @@ def test_paged_varlen_small(fp, page):
     check_paged(fp, synth.gen_paged(cfg, (L, P)), cfg.tau)
 
 
-def test_paged_equals_contiguous(fp):
-    """A shuffled block table gives bit-identical results to contiguous storage."""
-    cfg = synth.config(5, Hq=8, Hkv=2, n_seqs=1, tau=2.0)
-    inp = synth.gen_paged(cfg, (np.array([3000]), np.array([0])))
+@pytest.mark.parametrize("L,page", [(3000, 64), (3000, 256), (33000, 16)])
+def test_paged_equals_contiguous(fp, L, page):
+    """A shuffled block table gives bit-identical results to contiguous storage.
+    Pages of 256 tokens hold two 128-key tiles each (a tile starts mid-page);
+    33000 tokens in 16-token pages need 2063 page ids, more than the kernel
+    stages in LDS, so its tiles take the block-table path."""
+    cfg = synth.config(5, Hq=8, Hkv=2, n_seqs=1, tau=2.0, page_size=page)
+    say(f"paged == contiguous: L={L} page={page}")
+    inp = synth.gen_paged(cfg, (np.array([L]), np.array([0])))
     o, lse, rp, ci = run_paged(fp, inp, cfg.tau)
     k, v = synth.unpage(inp, 0)
     fixed = synth.FixedInputs(cfg, inp.q[None], k[None], v[None])
