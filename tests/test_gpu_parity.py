@@ -244,12 +244,14 @@ def check_paged(fp, inp, tau, sample_rows=None):
     assert row0 == len(rp) - 1
 
 
-@pytest.mark.parametrize("page", [64, 16, 256])
-def test_paged_varlen_small(fp, page):
-    cfg = synth.config(5, Hq=8, Hkv=2, n_seqs=4, len_range=(300, 3500), page_size=page, tau=2.0)
+@pytest.mark.parametrize("page,block", [(64, 128), (16, 128), (256, 128), (32, 64), (128, 64)])
+def test_paged_varlen_small(fp, page, block):
+    """Pages smaller than, equal to and larger than the block (a tile then
+    starts mid-page), for both block sizes."""
+    cfg = synth.config(5, Hq=8, Hkv=2, n_seqs=4, len_range=(300, 3500), page_size=page, block=block, tau=2.0)
     L, P = synth.paged_lengths(cfg)
     P[0] = 0                                    # one sequence without a cached prefix
-    say(f"paged varlen page={page}: L={L.tolist()} P={P.tolist()}")
+    say(f"paged varlen page={page} block={block}: L={L.tolist()} P={P.tolist()}")
     check_paged(fp, synth.gen_paged(cfg, (L, P)), cfg.tau)
 
 
