@@ -59,13 +59,15 @@ class Problem:
 
 def make_problem(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block: int,
                  softmax_scale: float = 0.0, o: Optional[torch.Tensor] = None,
-                 out_fp32: bool = False) -> Problem:
+                 out_fp32: bool = False, correction: bool = True) -> Problem:
     """Descriptor of a fixed-shape batch: q [batch, S, Hq, 128], k/v [batch, S, Hkv, 128]
     (bf16, or uint8 E4M3FN codes), last dim contiguous. out_fp32: fp_sparse_prefill
-    writes o in float32 (diagnostic) instead of bfloat16."""
+    writes o in float32 (diagnostic) instead of bfloat16. correction=False: the
+    ablation without the mean correction (pruned blocks dropped)."""
     fp8 = q.dtype == torch.uint8
     c = FpProblem()
     c.out_dtype = N.FP_OUT_FP32 if out_fp32 else N.FP_OUT_BF16
+    c.variant = N.FP_VARIANT_MEAN_CORRECTION if correction else N.FP_VARIANT_NO_CORRECTION
     c.batch, c.seqlen, c.num_q_heads, c.head_dim = q.shape[0], q.shape[1], q.shape[2], q.shape[3]
     c.num_kv_heads = k.shape[2]
     c.block = block
@@ -144,9 +146,9 @@ def fp_sparse_prefill(p: Problem, q, k, v, kbar, vbar, row_ptr, col_idx, sched=N
 
 def sparse_prefill(q, k, v, block: int, tau: float, softmax_scale: float = 0.0,
                    q_scale=None, k_scale=None, v_scale=None, with_lse: bool = True,
-                   out_fp32: bool = False):
+                   out_fp32: bool = False, correction: bool = True):
     """All three stages on the current stream. Returns a dict of device tensors."""
-    p = make_problem(q, k, v, block, softmax_scale, out_fp32=out_fp32)
+    p = make_problem(q, k, v, block, softmax_scale, out_fp32=out_fp32, correction=correction)
     qbar, kbar, vbar, scores = fp_block_scores(p, q, k, v, q_scale, k_scale, v_scale)
     row_ptr, col_idx, sched = fp_select_blocks(p, scores, tau)
     o, lse = fp_sparse_prefill(p, q, k, v, kbar, vbar, row_ptr, col_idx, sched,

@@ -18,6 +18,8 @@ FP_DTYPE_BF16 = 0
 FP_DTYPE_FP8_E4M3 = 1
 FP_OUT_BF16 = 0
 FP_OUT_FP32 = 2
+FP_VARIANT_MEAN_CORRECTION = 0
+FP_VARIANT_NO_CORRECTION = 1
 
 EXPORTS = (
     "fp_version", "fp_last_error", "fp_num_rows", "fp_max_nnz", "fp_workspace_size",
@@ -36,7 +38,7 @@ class FpProblem(ctypes.Structure):
         ("softmax_scale", ctypes.c_float),
         ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3),
         ("v_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3),
-        ("out_dtype", ctypes.c_int32), ("pad_", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32), ("variant", ctypes.c_int32),
     ]
 
 

@@ -72,6 +72,8 @@ int check_fixed(const fp_problem* p) {
             if ((st[t][e] * esz) % 16) return fail(FP_ERR_INVALID, "strides must be multiples of 16 bytes");
     if (p->out_dtype != FP_OUT_BF16 && p->out_dtype != FP_OUT_FP32)
         return fail(FP_ERR_UNSUPPORTED, "out_dtype %d unsupported", p->out_dtype);
+    if (p->variant != FP_VARIANT_MEAN_CORRECTION && p->variant != FP_VARIANT_NO_CORRECTION)
+        return fail(FP_ERR_UNSUPPORTED, "variant %d unsupported", p->variant);
     const int osz = p->out_dtype == FP_OUT_FP32 ? 4 : 2;
     for (int e = 0; e < 3; ++e)
         if ((p->o_stride[e] * osz) % (osz == 4 ? 16 : 8))
@@ -272,6 +274,7 @@ int fp_sparse_prefill(const fp_problem* p, const void* q, const void* k, const v
     a.qa = RowAddr{p->q_stride[0], p->q_stride[1], p->q_stride[2]};
     a.oa = RowAddr{p->o_stride[0], p->o_stride[1], p->o_stride[2]};
     a.o_f32 = p->out_dtype == FP_OUT_FP32;
+    a.no_correction = p->variant == FP_VARIANT_NO_CORRECTION;
     a.ka = KVAddr{p->k_stride[0], p->k_stride[1], p->k_stride[2], 0, nullptr, 0, 0};
     a.va = KVAddr{p->v_stride[0], p->v_stride[1], p->v_stride[2], 0, nullptr, 0, 0};
     a.qs = ScaleAddr{q_scale, (long long)p->num_q_heads * nsb, nsb};

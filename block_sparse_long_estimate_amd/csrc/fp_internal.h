@@ -169,6 +169,7 @@ struct AttnArgs {
     float scale_log2;                  // c * log2(e)
     int o_f32;                         // o in fp32 (diagnostic) instead of bf16
     int paged_fast;                    // paged: in-page offsets of a tile fit 24 bits (precomputed per lane)
+    int no_correction;                 // ablation: pruned blocks dropped (no summary tiles)
 };
 
 hipError_t launch_pool(const GeoFixed* gf, const GeoTable* gt, const PoolArgs& a, hipStream_t st);

@@ -587,6 +587,7 @@ __global__ __launch_bounds__(512, 1) void attn_tile_kernel(Geo geo, AttnArgs a) 
     // before its loads are issued, so no vector-memory wait inside a tile's
     // compute drains the prefetch.
     auto next_summary = [&](int m0) -> int {
+        if (a.no_correction) return NONE;             // ablation: no pseudo-tokens
         for (int mm = m0; mm * SUMC <= i - 1; ++mm) {
             const int c_lo = max(1, mm * SUMC), c_hi = min(i - 1, mm * SUMC + SUMC - 1);
             uint32_t anyw = 0u;

@@ -67,6 +67,8 @@ extern "C" {
 #define FP_DTYPE_FP8_E4M3 1      /* OCP E4M3FN codes (uint8) + fp32 scales       */
 #define FP_OUT_BF16 0            /* fp_sparse_prefill output o in bfloat16        */
 #define FP_OUT_FP32 2            /* ... in float32 (diagnostic: no output rounding) */
+#define FP_VARIANT_MEAN_CORRECTION 0   /* E6 as specified: pruned blocks as pooled pseudo-tokens */
+#define FP_VARIANT_NO_CORRECTION 1     /* ablation: pruned blocks simply dropped        */
 
 /* Fixed-shape batch: `batch` sequences of `seqlen` tokens each, one-shot
  * prefill (no cached prefix). q [batch, seqlen, Hq, 128], k and v
@@ -86,7 +88,8 @@ typedef struct fp_problem {
     int64_t v_stride[3];
     int64_t o_stride[3];
     int32_t out_dtype;       /* FP_OUT_BF16 (0, default) or FP_OUT_FP32: diagnostic fp32 o */
-    int32_t pad_;
+    int32_t variant;         /* FP_VARIANT_MEAN_CORRECTION (0, default) or FP_VARIANT_NO_CORRECTION:
+                                an ablation of the mean correction (fp_sparse_prefill only) */
 } fp_problem;
 
 /* Paged varlen batch (continuous batching with cached prefixes). Sequence b

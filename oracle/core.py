@@ -95,7 +95,8 @@ def select(S: np.ndarray, G: int, tau: float, i0: int) -> Tuple[np.ndarray, np.n
 
 def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, keep: np.ndarray,
            kbar: np.ndarray, vbar: np.ndarray, c: float, B: int, P: int,
-           rows: Optional[Sequence[Tuple[int, int]]] = None) -> Tuple[np.ndarray, np.ndarray]:
+           rows: Optional[Sequence[Tuple[int, int]]] = None,
+           correction: bool = True) -> Tuple[np.ndarray, np.ndarray]:
     """E6: sparse attention over kept blocks plus the mean-correction pseudo-tokens.
 
     Sparse operator over kept blocks: lode.cx page, "How It Works" and the
@@ -104,6 +105,8 @@ def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, keep: np.ndarray,
 
     q [L-P, Hq, d] (rows P..L-1), k/v [L, Hkv, d], keep [Hkv, nq, nb].
     rows: optional list of (g, il) to evaluate; other outputs stay NaN.
+    correction=False is the ablation without the correction: the pruned blocks
+    are dropped (no pseudo-tokens).
     Returns o [L-P, Hq, d] and lse [Hq, L-P]."""
     L, Hkv, d = k.shape
     Hq = q.shape[1]
@@ -116,7 +119,7 @@ def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, keep: np.ndarray,
         i = i0 + il
         lo, hi = max(i * B, P), min((i + 1) * B, L)
         kept_j = [j for j in range(i + 1) if keep[g, il, j]]
-        pruned_j = [j for j in range(i + 1) if not keep[g, il, j]]
+        pruned_j = [j for j in range(i + 1) if not keep[g, il, j]] if correction else []
         tok = np.concatenate([np.arange(j * B, min((j + 1) * B, L)) for j in kept_j])
         Kx = k[tok, g, :]
         Vx = v[tok, g, :]
@@ -143,9 +146,10 @@ def prefill(q: np.ndarray, k: np.ndarray, v: np.ndarray, B: int, tau: float,
             c: Optional[float] = None, P: int = 0,
             keep: Optional[np.ndarray] = None,
             rows: Optional[Sequence[Tuple[int, int]]] = None,
-            with_output: bool = True) -> Dict[str, np.ndarray]:
+            with_output: bool = True, correction: bool = True) -> Dict[str, np.ndarray]:
     """E1-E6 for one sequence.  keep overrides the oracle's own mask (used to
-    evaluate E6 under another, validated mask)."""
+    evaluate E6 under another, validated mask); correction=False evaluates the
+    ablation without the mean correction."""
     L, Hkv, d = k.shape
     Hq = q.shape[1]
     assert q.shape[0] == L - P and Hq % Hkv == 0 and v.shape == k.shape
@@ -161,7 +165,7 @@ def prefill(q: np.ndarray, k: np.ndarray, v: np.ndarray, B: int, tau: float,
     out = dict(qbar=qbar, kbar=kbar, vbar=vbar, S=S, R=R, keep=own_keep, i0=i0, nq=nq)
     if with_output:
         use = own_keep if keep is None else keep
-        out["o"], out["lse"] = attend(q, k, v, use, kbar, vbar, c, B, P, rows=rows)
+        out["o"], out["lse"] = attend(q, k, v, use, kbar, vbar, c, B, P, rows=rows, correction=correction)
     return out
 
 

@@ -202,6 +202,14 @@ def test_paged_rejects_nan_tau_capacity_workspace():
     assert call(4.0, nnz, ws - 1) == N.FP_ERR_CAPACITY
 
 
+def test_variant_validation():
+    """variant (the ablation of the mean correction) sits where the padding was."""
+    lib = N.load()
+    assert ctypes.sizeof(N.FpProblem) == 136
+    assert lib.fp_num_rows(ctypes.byref(problem(variant=N.FP_VARIANT_NO_CORRECTION))) > 0
+    assert lib.fp_num_rows(ctypes.byref(problem(variant=7))) == N.FP_ERR_UNSUPPORTED
+
+
 def test_out_dtype_validation():
     lib = N.load()
     assert ctypes.sizeof(N.FpProblem) == 136

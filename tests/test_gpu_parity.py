@@ -255,6 +255,33 @@ def test_paged_varlen_small(fp, page, block):
     check_paged(fp, synth.gen_paged(cfg, (L, P)), cfg.tau)
 
 
+@pytest.mark.parametrize("tau", [1.0, 3.0])
+def test_no_correction_variant(fp, tau):
+    """The ablation without the mean correction, against the oracle's variant
+    under the GPU's kept lists; the kept lists are those of the default run."""
+    cfg = synth.config(2, S=4096 + 77, Hq=8, Hkv=2, seed=61, tau=tau)
+    inp = synth.gen_fixed(cfg)
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in (inp.q, inp.k, inp.v))
+    a = fp.sparse_prefill(q, k, v, 128, tau)
+    b = fp.sparse_prefill(q, k, v, 128, tau, correction=False)
+    torch.cuda.synchronize()
+    assert torch.equal(a["row_ptr"], b["row_ptr"])
+    S, Hkv = cfg.S, cfg.Hkv
+    nb = -(-S // 128)
+    rp, ci = b["row_ptr"].cpu().numpy(), b["col_idx"].cpu().numpy()
+    keep = csr_to_keep(rp, ci, 0, Hkv, nb, nb)
+    assert (~keep[np.tril(np.ones((nb, nb), dtype=bool))[None].repeat(Hkv, 0)]).any()   # real pruning
+    qd, kd, vd = widen(inp, 0)
+    c = 1 / math.sqrt(128)
+    ref = oracle.prefill(qd, kd, vd, 128, tau, c, with_output=False)
+    o_ref, lse_ref = oracle.attend(qd, kd, vd, keep, ref["kbar"], ref["vbar"], c, 128, 0, correction=False)
+    say(f"no-correction tau={tau}")
+    compare_outputs(b["o"][0].float().cpu().numpy(), o_ref, "bf16")
+    assert np.abs(b["lse"][0].cpu().numpy() - lse_ref).max() <= LSE_TOL
+    assert not torch.equal(a["o"], b["o"])          # the correction changes the result
+
+
 @pytest.mark.parametrize("L,page", [(3000, 64), (3000, 256), (33000, 16)])
 def test_paged_equals_contiguous(fp, L, page):
     """A shuffled block table gives bit-identical results to contiguous storage.

@@ -246,6 +246,33 @@ def test_attend_matches_augmented_loops(P, tau):
     assert np.abs(out["lse"] - lse).max() < 1e-12
 
 
+@pytest.mark.parametrize("P,tau", [(0, 0.3), (7, 1.0), (0, -1.0)])
+def test_no_correction_is_masked_dense(P, tau):
+    """The ablation without the mean correction is causal softmax attention over
+    the tokens of the kept blocks alone, written out here token by token."""
+    L, B, Hq, Hkv, d = 34, 4, 4, 2, 4
+    q = rnd((L - P, Hq, d), 26) + 0.8
+    k = rnd((L, Hkv, d), 27) + np.cumsum(rnd((L, Hkv, d), 28, 0.6), axis=0)
+    v = rnd((L, Hkv, d), 29)
+    out = prefill(q, k, v, B, tau, 0.5, P=P, correction=False)
+    keep, i0 = out["keep"], out["i0"]
+    assert (~keep).any()
+    G = Hq // Hkv
+    for h in range(Hq):
+        g = h // G
+        for t in range(P, L):
+            il = t // B - i0
+            s_ok = [s for s in range(t + 1) if keep[g, il, s // B]]
+            z = np.array([0.5 * float(q[t - P, h] @ k[s, g]) for s in s_ok])
+            w = np.exp(z - z.max())
+            o = sum(wi * v[s, g] for wi, s in zip(w, s_ok)) / w.sum()
+            assert np.abs(out["o"][t - P, h] - o).max() < 1e-12
+            assert abs(out["lse"][h, t - P] - (z.max() + math.log(w.sum()))) < 1e-12
+    # with every block kept the two variants coincide
+    both = [prefill(q, k, v, B, np.inf, 0.5, P=P, correction=cr)["o"] for cr in (True, False)]
+    assert np.abs(both[0] - both[1]).max() == 0.0
+
+
 # --------------------------------------------------------------------------
 # P7: causality with the mask held fixed;  P8: key-offset invariance
 # --------------------------------------------------------------------------
