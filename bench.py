@@ -16,7 +16,9 @@ oracle's throughput on a bounded sample as `cpu_baseline`. Context legs on
 the same tensors (skipped with --no-sweep): bf16 at tau 2, 6, 8, and tau=inf,
 where every block is kept and the path is this library's own dense causal
 attention. The paged varlen entry point is timed on its own 8-sequence
-batch (skipped with --no-paged).
+batch (skipped with --no-paged). The error of the sparse outputs against
+that dense attention, with and without the mean correction, is reported at
+tau 2, 4, 8 (skipped with --no-ablation).
 """
 from __future__ import annotations
 
@@ -125,6 +127,42 @@ def time_paged(fp, N, steps, warmup):
            "mfma_util_kept_whole_call": round(kept / (t * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4),
            "correction_tflop": round(corr / 1e12, 3)}
     del q, kc, vc, bt, ws, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def ablation_vs_dense(fp, inp, taus=(2.0, 4.0, 8.0), chunk=8192):
+    """Error of the sparse path against this library's dense causal attention
+    (tau = inf: every block kept) on the same tensors, with and without the
+    mean correction: max and mean |o - o_dense| (V is in units of max|V|) and
+    the relative Frobenius norm. A synthetic stand-in for the pages' accuracy
+    claim, which needs trained weights to check."""
+    import torch
+    dev = torch.device("cuda:0")
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    B = inp.cfg.block
+    dense = fp.sparse_prefill(q, k, v, B, float("inf"), with_lse=False)["o"]
+    ref_sq = 0.0
+    for t0 in range(0, dense.shape[1], chunk):
+        ref_sq += float(dense[:, t0:t0 + chunk].float().pow(2).sum())
+    res = {}
+    for tau in taus:
+        row = {}
+        for name, corr in (("with_correction", True), ("without_correction", False)):
+            out = fp.sparse_prefill(q, k, v, B, tau, with_lse=False, correction=corr)
+            o = out["o"]
+            mx, sm, sq, n = 0.0, 0.0, 0.0, 0
+            for t0 in range(0, o.shape[1], chunk):
+                d = (o[:, t0:t0 + chunk].float() - dense[:, t0:t0 + chunk].float()).abs_()
+                mx = max(mx, float(d.max()))
+                sm += float(d.sum())
+                sq += float(d.pow_(2).sum())
+                n += d.numel()
+            row[name] = {"max_abs": round(mx, 5), "mean_abs": round(sm / n, 6),
+                         "rel_fro": round(math.sqrt(sq / ref_sq), 6)}
+            del out, o
+        res[str(tau)] = row
+    del q, k, v, dense
     torch.cuda.empty_cache()
     return res
 
@@ -346,6 +384,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-paged", action="store_true", help="skip the paged varlen batch leg")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache leg")
+    ap.add_argument("--no-ablation", action="store_true",
+                    help="skip the error-vs-dense comparison with and without the mean correction")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the context legs (bf16 at tau 2/6/8, and tau=inf: every block kept)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -403,6 +443,10 @@ def main():
             log(f"sweep tau={tau}: {json.dumps(sweep[str(tau)])}")
         dense, _ = time_path(fp, N, inputs["bf16"], float("inf"), 2, 1, "bf16 dense")
         log(f"dense (tau=inf): {json.dumps(dense)}")
+    ablation = None
+    if not args.no_ablation:
+        ablation = ablation_vs_dense(fp, inputs["bf16"])
+        log(f"ablation vs dense: {json.dumps(ablation)}")
     cpu = None
     if not args.no_cpu_baseline:
         t0 = time.time()
@@ -458,6 +502,8 @@ def main():
                                    "attn_tflops": round(dense["attn_kept_tflops"], 2),
                                    "mfma_util": round(dense["attn_kept_tflops"] / att_peak, 4),
                                    "sparse_speedup": round(dense["ms_per_step"] / bf["ms_per_step"], 2)}
+    if ablation is not None:
+        line["error_vs_dense_bf16"] = ablation
     if cpu is not None:
         line["cpu_baseline"] = {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")}
         line["cpu_baseline"]["value"] = round(cpu["value"], 6)
