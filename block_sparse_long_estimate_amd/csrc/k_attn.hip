@@ -165,30 +165,6 @@ constexpr int VSTR8 = 160;
 // (row, chunk) its 16 bytes belong to; lanes that land on row padding stay
 // inactive. LDS row r holds key r (PERM: key vt_slot(r)); rows past the
 // sequence repeat its last key. ESZ = bytes per element.
-template <int STR, int BLK, int ESZ, bool PERM, bool PAGED>
-__device__ __forceinline__ void issue_tile(const uint8_t* base, const KVAddr& ka, int b, int L, int g,
-                                           int j, lds_u8* buf, int wave, int lane, const lds_int* pages) {
-    constexpr int PIECES = BLK * STR / 1024;
-    asm volatile("" : "+v"(lane));   // recompute addresses per call, keep none live
-    const int rmax = L - 1 - j * BLK;
-#pragma unroll
-    for (int t0 = 0; t0 < PIECES; t0 += 8) {
-        const int t = t0 + wave;
-        if (t < PIECES) {
-            const int pb = t * 1024 + lane * 16;
-            const int row = pb / STR;
-            const int ch = (pb - row * STR) >> 4;
-            const int key = PERM ? vt_slot(row) : row;
-            const int sk = j * BLK + min(key, rmax);
-            // paged: the sequence's page ids staged in LDS when they fit, else the block table
-            const long long off = PAGED && pages ? ka.off_page(pages[sk >> ka.page_shift], sk, g)
-                                                 : ka.template off<PAGED>(b, sk, g);
-            const uint8_t* src = base + off * ESZ + ch * 16;
-            if (ch < 8 * ESZ)
-                __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(buf + t * 1024), 16, 0, 0);
-        }
-    }
-}
 
 // Lane byte offsets (relative to the tile's first key row) of the pieces
 // this lane loads, for contiguous K/V; computed once per workgroup. Unsigned
@@ -234,19 +210,67 @@ struct TileOffs {
             off[k] = ch < 8 * ESZ ? (inpage | ((uint32_t)(key >> lshift) << 24)) : PAD;
         }
     }
-    // full paged tile: pages = the tile's first page slot in the staged page
-    // list, base = the uniform part (head, in-page start of the tile)
-    __device__ __forceinline__ void issue_paged(const uint8_t* base, const lds_int* pages,
+    // Full paged tile, in two phases: read_pages looks up every piece's page
+    // id first (pages = the tile's first slot in the staged list), then
+    // issue_paged issues the loads (base = the uniform part: head and the
+    // tile's in-page start). Reading LDS after some of the tile's loads are
+    // in flight would make the compiler drain them (it cannot tell the page
+    // list from the buffers being filled), so no LDS read may follow a load.
+    __device__ __forceinline__ void read_pages(const lds_int* pages, int wave, int (&pg)[NP]) const {
+#pragma unroll
+        for (int k = 0; k < NP; ++k) {
+            const int t = k * 8 + wave;
+            pg[k] = (t < PIECES && off[k] != PAD) ? pages[off[k] >> 24] : 0;
+        }
+    }
+    __device__ __forceinline__ void issue_paged(const uint8_t* base, const int (&pg)[NP],
                                                 unsigned long long page_bytes, lds_u8* buf, int wave) const {
 #pragma unroll
         for (int k = 0; k < NP; ++k) {
             const int t = k * 8 + wave;
-            if (t < PIECES && off[k] != PAD) {
-                const int pg = pages[off[k] >> 24];
+            if (t < PIECES && off[k] != PAD)
                 __builtin_amdgcn_global_load_lds(
-                    (const void*)(base + (unsigned long long)pg * page_bytes + (off[k] & 0xFFFFFFu)),
+                    (const void*)(base + (unsigned long long)pg[k] * page_bytes + (off[k] & 0xFFFFFFu)),
                     (lds_void*)(buf + t * 1024), 16, 0, 0);
+        }
+    }
+};
+
+// Generic tile addresses (ragged tiles, or paged tiles whose page list is not
+// staged): every piece's source is computed before any load is issued, for
+// the same reason as above (a paged lookup is a memory read).
+template <int STR, int BLK, int ESZ, bool PERM, bool PAGED>
+struct TileSrcs {
+    static constexpr int PIECES = BLK * STR / 1024;
+    static constexpr int NP = (PIECES + 7) / 8;
+    const uint8_t* src[NP];
+    __device__ __forceinline__ void compute(const uint8_t* base, const KVAddr& ka, int b, int L, int g, int j,
+                                            int wave, int lane, const lds_int* pages) {
+        asm volatile("" : "+v"(lane));   // recompute addresses per call, keep none live
+        const int rmax = L - 1 - j * BLK;
+#pragma unroll
+        for (int k = 0; k < NP; ++k) {
+            const int t = k * 8 + wave;
+            const int pb = t * 1024 + lane * 16;
+            const int row = pb / STR;
+            const int ch = (pb - row * STR) >> 4;
+            const int key = PERM ? vt_slot(row) : row;
+            const int sk = j * BLK + min(key, rmax);
+            src[k] = nullptr;
+            if (t < PIECES && ch < 8 * ESZ) {
+                // paged: the sequence's page ids staged in LDS when they fit, else the block table
+                const long long off = PAGED && pages ? ka.off_page(pages[sk >> ka.page_shift], sk, g)
+                                                     : ka.template off<PAGED>(b, sk, g);
+                src[k] = base + off * ESZ + ch * 16;
             }
+        }
+    }
+    __device__ __forceinline__ void issue(lds_u8* buf, int wave) const {
+#pragma unroll
+        for (int k = 0; k < NP; ++k) {
+            const int t = k * 8 + wave;
+            if (t < PIECES && src[k] != nullptr)
+                __builtin_amdgcn_global_load_lds((const void*)src[k], (lds_void*)(buf + t * 1024), 16, 0, 0);
         }
     }
 };
@@ -256,6 +280,7 @@ struct KVOffs {
     static constexpr int ESZ = FP8 ? 1 : 2;
     TileOffs<FP8 ? KSTR8 : KSTR, BLK, ESZ, false> k;
     TileOffs<FP8 ? VSTR8 : VSTR, BLK, ESZ, FP8> v;
+    static constexpr int NPK = decltype(k)::NP, NPV = decltype(v)::NP;
 };
 
 template <int BLK, bool FP8, bool PAGED>
@@ -267,8 +292,12 @@ __device__ __forceinline__ void issue_kv(const AttnArgs& a, int b, int L, int g,
         const int sh = a.ka.page_shift;
         const long long ub = (long long)((j * BLK) & ((1 << sh) - 1)) * a.ka.st + (long long)g * a.ka.sh;
         const lds_int* pt = pages + ((j * BLK) >> sh);
-        o.k.issue_paged((const uint8_t*)a.k + ub * ESZ, pt, (unsigned long long)a.ka.spage * ESZ, kbuf, wave);
-        o.v.issue_paged((const uint8_t*)a.v + ub * ESZ, pt, (unsigned long long)a.va.spage * ESZ, vbuf, wave);
+        int pgk[KVOffs<BLK, FP8>::NPK], pgv[KVOffs<BLK, FP8>::NPV];
+        o.k.read_pages(pt, wave, pgk);
+        o.v.read_pages(pt, wave, pgv);
+        __builtin_amdgcn_sched_barrier(0);
+        o.k.issue_paged((const uint8_t*)a.k + ub * ESZ, pgk, (unsigned long long)a.ka.spage * ESZ, kbuf, wave);
+        o.v.issue_paged((const uint8_t*)a.v + ub * ESZ, pgv, (unsigned long long)a.va.spage * ESZ, vbuf, wave);
         return;
     }
     if (!PAGED && (j + 1) * BLK <= L) {
@@ -278,10 +307,13 @@ __device__ __forceinline__ void issue_kv(const AttnArgs& a, int b, int L, int g,
         o.v.issue((const uint8_t*)a.v + v0, vbuf, wave);
         return;
     }
-    issue_tile<FP8 ? KSTR8 : KSTR, BLK, ESZ, false, PAGED>((const uint8_t*)a.k, a.ka, b, L, g, j, kbuf, wave,
-                                                           lane, pages);
-    issue_tile<FP8 ? VSTR8 : VSTR, BLK, ESZ, FP8, PAGED>((const uint8_t*)a.v, a.va, b, L, g, j, vbuf, wave,
-                                                         lane, pages);
+    TileSrcs<FP8 ? KSTR8 : KSTR, BLK, ESZ, false, PAGED> ks;
+    TileSrcs<FP8 ? VSTR8 : VSTR, BLK, ESZ, FP8, PAGED> vs;
+    ks.compute((const uint8_t*)a.k, a.ka, b, L, g, j, wave, lane, pages);
+    vs.compute((const uint8_t*)a.v, a.va, b, L, g, j, wave, lane, pages);
+    __builtin_amdgcn_sched_barrier(0);
+    ks.issue(kbuf, wave);
+    vs.issue(vbuf, wave);
 }
 
 // bf16 S^T for key blocks kb0 .. kb0 + NB - 1 (32 keys each) of the tile.
