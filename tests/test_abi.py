@@ -52,6 +52,16 @@ def test_sizes():
     assert lib.fp_num_rows(ctypes.byref(p)) == 2 * 16
 
 
+def test_largest_supported_sequence():
+    """16384 blocks of 128 tokens is the longest sequence; one more token is refused."""
+    lib = N.load()
+    p = problem(seqlen=16384 * 128, num_q_heads=1, num_kv_heads=1)
+    for arr in (p.q_stride, p.k_stride, p.v_stride, p.o_stride):
+        arr[0], arr[1], arr[2] = 16384 * 128 * 128, 128, 128
+    assert lib.fp_num_rows(ctypes.byref(p)) == 16384
+    assert lib.fp_max_nnz(ctypes.byref(p)) == 16384 * 16385 // 2
+
+
 @pytest.mark.parametrize("field,value,code", [
     ("num_q_heads", 7, N.FP_ERR_INVALID),          # Hq % Hkv != 0
     ("head_dim", 64, N.FP_ERR_UNSUPPORTED),
@@ -60,6 +70,8 @@ def test_sizes():
     ("dtype", 7, N.FP_ERR_UNSUPPORTED),
     ("batch", 0, N.FP_ERR_INVALID),
     ("seqlen", -5, N.FP_ERR_INVALID),
+    ("seqlen", 0, N.FP_ERR_INVALID),                 # empty sequence
+    ("seqlen", 16384 * 128 + 1, N.FP_ERR_UNSUPPORTED),   # one block past the 16384-block limit
     ("softmax_scale", float("nan"), N.FP_ERR_INVALID),
     ("num_kv_heads", 0, N.FP_ERR_INVALID),
 ])

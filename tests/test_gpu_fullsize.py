@@ -135,3 +135,13 @@ def test_config5_paged_full(fp):
         say(f"  seq {b}: L={L} P={P} mask diffs {ndiff} (band {nband}) max|err| {mx:.2e} mean {mean:.2e}")
         row0 += Hkv * nq
     assert row0 == len(rp) - 1
+
+
+def test_largest_sequence_single_head(fp):
+    """The longest supported sequence: 16384 blocks of 128 tokens (2,097,152
+    tokens), one query and one KV head, tau = 1 (about 0.04% kept, so nearly
+    every row runs through the correction's summary tiles). This size also
+    takes the schedule sort's histogram past 64 KiB of LDS."""
+    cfg = synth.config(2, S=16384 * 128, Hq=1, Hkv=1, tau=1.0, seed=77)
+    say("largest sequence: S=2097152, 1/1 heads")
+    run_and_check(fp, synth.gen_fixed(cfg), cfg.tau, "bf16", 6)
