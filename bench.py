@@ -474,6 +474,8 @@ def main():
         "mfma_util_kept": round(bf["attn_kept_tflops"] / att_peak, 4),
         "mfma_util_executed": round(bf["attn_executed_tflops"] / att_peak, 4),
         "estimator_gbs": round(bf["estimate_gbs"], 1), "select_gbs": round(bf["select_gbs"], 1),
+        "estimator_hbm_frac": round(bf["estimate_gbs"] / HBM_GBS, 4),
+        "select_hbm_frac": round(bf["select_gbs"] / HBM_GBS, 4),
         "roofline": {"bound": "mfma", "kernel": "attn_tile_kernel<128, bf16> (fp_sparse_prefill)",
                      "achieved": round(bf["attn_kept_tflops"], 2), "peak": att_peak,
                      "unit": "TFLOP/s", "frac": round(bf["attn_kept_tflops"] / att_peak, 4),
