@@ -16,7 +16,8 @@ oracle's throughput on a bounded sample as `cpu_baseline`. Context legs on
 the same tensors (skipped with --no-sweep): bf16 at tau 2, 6, 8, and tau=inf,
 where every block is kept and the path is this library's own dense causal
 attention. The paged varlen entry point is timed on its own 8-sequence
-batch (skipped with --no-paged). The error of the sparse outputs against
+batch (skipped with --no-paged), and the S=2048 and S=32768 configurations
+on their own (skipped with --no-configs). The error of the sparse outputs against
 that dense attention, with and without the mean correction, is reported at
 tau 2, 4, 8 (skipped with --no-ablation).
 """
@@ -129,6 +130,37 @@ def time_paged(fp, N, steps, warmup):
     del q, kc, vc, bt, ws, out
     torch.cuda.empty_cache()
     return res
+
+
+def graph_replay_ms(fp, inp, tau, replays=20):
+    """The whole path captured once in a HIP graph and replayed: median ms per
+    replay (for small prefills, where launch overhead dominates)."""
+    import torch
+    dev = torch.device("cuda:0")
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fp.sparse_prefill(q, k, v, inp.cfg.block, tau)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fp.sparse_prefill(q, k, v, inp.cfg.block, tau)
+    g.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(replays):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        ts.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in ts]))
+    del g, q, k, v
+    torch.cuda.empty_cache()
+    return ms
 
 
 def ablation_vs_dense(fp, inp, taus=(2.0, 4.0, 8.0), chunk=8192):
@@ -384,6 +416,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-paged", action="store_true", help="skip the paged varlen batch leg")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache leg")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the smaller fixed-shape configurations (S=2048 and S=32768)")
     ap.add_argument("--no-ablation", action="store_true",
                     help="skip the error-vs-dense comparison with and without the mean correction")
     ap.add_argument("--no-sweep", action="store_true",
@@ -429,6 +463,20 @@ def main():
     if not args.no_fp8:
         f8, _ = time_path(fp, N, inputs["fp8"], args.tau, args.steps, args.warmup, "fp8")
         log(f"fp8: {json.dumps(f8)}")
+    configs = {}
+    if not args.no_configs:
+        for cid in (1, 2):
+            c = synth.config(cid)
+            ci_inp = synth.gen_fixed(c)
+            r, _ = time_path(fp, N, ci_inp, c.tau, 10, 3, f"config {cid}")
+            configs[c.name] = {"seq_len": c.S, "heads": f"{c.Hq}/{c.Hkv}", "block": c.block, "tau": c.tau,
+                               "ms_per_layer_median": round(r["ms_step_median"], 4),
+                               "ms_attention_median": round(r["ms_attention_median"], 4),
+                               "dense_equiv_tflops": round(r["dense_equiv_tflops"], 2),
+                               "kept_fraction": round(r["kept_fraction"], 5),
+                               "mfma_util_kept": round(r["attn_kept_tflops"] / PEAK_TFLOPS["bf16"], 4),
+                               "ms_per_layer_graph_replay": round(graph_replay_ms(fp, ci_inp, c.tau), 4)}
+            log(f"config {cid}: {json.dumps(configs[c.name])}")
     paged = None
     if not args.no_paged:
         paged = time_paged(fp, N, 5, 1)
@@ -493,6 +541,8 @@ def main():
         line["cold_cache"] = {"runs": 5, "flush": "1 GiB written before each step",
                               "ms_per_layer_median": round(cold["ms_step_median"], 4),
                               "ms_attention_median": round(cold["ms_attention_median"], 4)}
+    if configs:
+        line["other_configs_bf16"] = configs
     if paged is not None:
         line["paged_varlen_bf16"] = paged
     if sweep:
