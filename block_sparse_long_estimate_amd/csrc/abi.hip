@@ -98,19 +98,54 @@ GeoFixed geo_fixed(const fp_problem* p) {
 
 bool misaligned(const void* ptr, size_t a) { return ((uintptr_t)ptr) % a != 0; }
 
+// Schedule groups: consecutive (sequence, KV head) pairs whose K/V together
+// fit SCHED_GROUP_BYTES run one group after another (heavy rows first within
+// a group), so the K/V that the running rows read stays within the
+// memory-side cache (256 MiB on this part) instead of spanning every head of
+// the batch. Measured at S = 131072, 32/8 heads: 3% less attention time than
+// one heavy-first order over all heads; groups of 4 heads (256 MiB) were 10%
+// slower. The histogram of the schedule sort holds ngrp * (max_nbk + 1) bins
+// and is kept within SORT_MAX_BINS by widening the groups.
+constexpr long long SCHED_GROUP_BYTES = 128LL << 20;
+constexpr int SORT_MAX_BINS = 32768;
+
+struct SortPlan {
+    int ngrp;
+    long long grp_units;   // key blocks x KV heads per group
+};
+
+SortPlan sort_plan(long long total_units, int max_nbk, int blk, int esz) {
+    const long long unit_bytes = (long long)blk * D * esz * 2;          // one key block of K and V, one head
+    long long units = std::max(SCHED_GROUP_BYTES / unit_bytes, 1LL);
+    long long ng = std::max((total_units + units - 1) / units, 1LL);
+    const long long nmax = std::max(SORT_MAX_BINS / (max_nbk + 1), 1);
+    if (ng > nmax) {
+        units = (total_units + nmax - 1) / nmax;
+        ng = std::max((total_units + units - 1) / units, 1LL);
+    }
+    return SortPlan{(int)ng, units};
+}
+
 struct SelectWs {
-    size_t counts, bits, hist, total;
+    size_t counts, bits, keys, hist, total;
     int nbw;
 };
 
-SelectWs select_ws(long long rows, int max_nbk) {
+SelectWs select_ws(long long rows, int max_nbk, int ngrp) {
     SelectWs w;
     w.nbw = cdiv(max_nbk, 32) + 1;
     w.counts = 0;
     w.bits = align_up((size_t)rows * 4);
-    w.hist = w.bits + align_up((size_t)rows * w.nbw * 4);
-    w.total = w.hist + align_up((size_t)((rows + SORT_CHUNK - 1) / SORT_CHUNK) * (max_nbk + 1) * 4);
+    w.keys = w.bits + align_up((size_t)rows * w.nbw * 4);
+    w.hist = w.keys + align_up((size_t)rows * 4);
+    w.total = w.hist + align_up((size_t)((rows + SORT_CHUNK - 1) / SORT_CHUNK) * ngrp * (max_nbk + 1) * 4);
     return w;
+}
+
+SortPlan fixed_sort_plan(const fp_problem* p) {
+    const int nb = cdiv(p->seqlen, p->block);
+    return sort_plan((long long)p->batch * p->num_kv_heads * nb, nb, p->block,
+                     p->dtype == FP_DTYPE_FP8_E4M3 ? 1 : 2);
 }
 
 // bf16 copies of the pooled keys (hi, lo) and values used by the summary tiles
@@ -170,7 +205,7 @@ int64_t fp_workspace_size(const fp_problem* p) {
     int rc = check_fixed(p);
     if (rc) return rc;
     const int nb = cdiv(p->seqlen, p->block);
-    return (int64_t)select_ws((long long)p->batch * p->num_kv_heads * nb, nb).total;
+    return (int64_t)select_ws((long long)p->batch * p->num_kv_heads * nb, nb, fixed_sort_plan(p).ngrp).total;
 }
 
 int fp_block_scores(const fp_problem* p, const void* q, const void* k, const void* v,
@@ -226,7 +261,8 @@ int fp_select_blocks(const fp_problem* p, const float* scores, float tau, int32_
     const long long need = rows * (nb + 1) / 2;
     if (capacity < need)
         return fail(FP_ERR_CAPACITY, "fp_select_blocks: capacity %lld < max nnz %lld", (long long)capacity, need);
-    const SelectWs w = select_ws(rows, nb);
+    const SortPlan sp = fixed_sort_plan(p);
+    const SelectWs w = select_ws(rows, nb, sp.ngrp);
     if (ws_bytes < w.total)
         return fail(FP_ERR_CAPACITY, "fp_select_blocks: workspace %zu < %zu bytes", ws_bytes, w.total);
     if (misaligned(workspace, ALIGN)) return fail(FP_ERR_INVALID, "workspace must be 256-byte aligned");
@@ -235,11 +271,13 @@ int fp_select_blocks(const fp_problem* p, const float* scores, float tau, int32_
     a.scores = scores;
     a.counts = (int32_t*)((char*)workspace + w.counts);
     a.bits = (uint32_t*)((char*)workspace + w.bits);
+    a.keys = (int32_t*)((char*)workspace + w.keys);
     a.hist = (int32_t*)((char*)workspace + w.hist);
     a.nbw = w.nbw;
     a.row_ptr = row_ptr; a.col_idx = col_idx; a.sched = sched;
     a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads;
     a.rows = (int)rows; a.max_nbk = nb;
+    a.ngrp = sp.ngrp; a.grp_units = sp.grp_units;
     a.neg_tau = -tau;
     hipError_t e = launch_select(&geo, nullptr, a, (hipStream_t)stream);
     if (e != hipSuccess) return fail(FP_ERR_HIP, "select launch: %s", hipGetErrorString(e));
@@ -316,6 +354,7 @@ struct VarPlan {
     size_t o_table = 0, o_qbar = 0, o_kbar = 0, o_vbar = 0, o_scores = 0, o_sched = 0, o_sel = 0, o_sum = 0,
            total = 0;
     SelectWs sel;
+    SortPlan sort;
 };
 
 int check_varlen(const fp_varlen_problem* p, const int32_t* cu, const int32_t* lk, VarPlan& plan) {
@@ -384,7 +423,8 @@ int check_varlen(const fp_varlen_problem* p, const int32_t* cu, const int32_t* l
     plan.o_vbar = off; off = align_up(off + (size_t)kb * p->num_kv_heads * D * 4);
     plan.o_scores = off; off = align_up(off + (size_t)sc * 4);
     plan.o_sched = off; off = align_up(off + (size_t)plan.rows * 4);
-    plan.sel = select_ws(plan.rows, std::max(plan.max_nbk, 1));
+    plan.sort = sort_plan(kb * p->num_kv_heads, std::max(plan.max_nbk, 1), B, 2);
+    plan.sel = select_ws(plan.rows, std::max(plan.max_nbk, 1), plan.sort.ngrp);
     plan.o_sel = off; off = align_up(off + plan.sel.total);
     plan.o_sum = off; off += summary_ws_bytes(kb * p->num_kv_heads);
     plan.total = off;
@@ -480,11 +520,13 @@ int fp_sparse_prefill_paged(const fp_varlen_problem* p, const void* q, const int
     se.scores = scores;
     se.counts = (int32_t*)(selws + plan.sel.counts);
     se.bits = (uint32_t*)(selws + plan.sel.bits);
+    se.keys = (int32_t*)(selws + plan.sel.keys);
     se.hist = (int32_t*)(selws + plan.sel.hist);
     se.nbw = plan.sel.nbw;
     se.row_ptr = row_ptr; se.col_idx = col_idx; se.sched = sched;
     se.Hq = p->num_q_heads; se.Hkv = p->num_kv_heads;
     se.rows = (int)plan.rows; se.max_nbk = std::max(plan.max_nbk, 1);
+    se.ngrp = plan.sort.ngrp; se.grp_units = plan.sort.grp_units;
     se.neg_tau = -tau;
     e = launch_select(nullptr, &geo, se, st);
     if (e != hipSuccess) return fail(FP_ERR_HIP, "select launch: %s", hipGetErrorString(e));

@@ -151,11 +151,23 @@ constexpr int SORT_CHUNK = 256;    // rows per chunk of the schedule sort
 struct SelectArgs {
     const float* scores;
     int32_t* counts; uint32_t* bits; int nbw;   // bitmask row stride (u32 words)
-    int32_t* hist;                              // [chunks][max_nbk + 1] sort histograms / offsets
+    int32_t* keys;                              // [rows] schedule sort key (group, count)
+    int32_t* hist;                              // [chunks][ngrp * (max_nbk + 1)] sort histograms / offsets
     int32_t* row_ptr; int32_t* col_idx; int32_t* sched;
     int Hq, Hkv, rows, max_nbk;
+    int ngrp;                                   // schedule groups (rows sharing a K/V working set)
+    long long grp_units;                        // group size in (key block x KV head) units
     float neg_tau;
 };
+
+// Schedule group of the rows of (sequence s, KV head g): the (sequence, KV
+// head) pairs in row order are cut into groups of grp_units key blocks' worth
+// of K/V, by where the pair's K/V starts.
+__host__ __device__ inline int row_group(const SeqDesc& s, int g, int Hkv, long long grp_units, int ngrp) {
+    const long long start = (long long)Hkv * s.kb0 + (long long)g * s.nbk;
+    const long long grp = start / grp_units;
+    return (int)(grp < ngrp - 1 ? grp : ngrp - 1);
+}
 
 struct AttnArgs {
     const void* q; const void* k; const void* v;

@@ -14,8 +14,11 @@
 // scan_rows:   single workgroup exclusive scan of the counts -> row_ptr.
 // expand_rows: one wavefront per row, ballot + lane-prefix popcount writes the
 //   ascending column list at row_ptr.
-// sort_*:      stable counting sort of the rows by count (descending), ties
-//   by row id -> sched, over chunks of rows (histograms, offsets, scatter).
+// sort_*:      stable counting sort of the rows -> sched, over chunks of rows
+//   (histograms, offsets, scatter). The order is heavy-row-first inside
+//   groups of consecutive (sequence, KV head) pairs whose K/V together stay
+//   within a budget sized for the memory-side cache, groups in row order:
+//   key = (group ascending, count descending), ties by row id.
 #include "fp_internal.h"
 
 namespace fp {
@@ -67,7 +70,10 @@ __global__ __launch_bounds__(256) void select_rows_kernel(Geo geo, SelectArgs a)
         if (lane == 0) bits[jc >> 5] = (uint32_t)bal;
         if (lane == 1 && (jc >> 5) + 1 < a.nbw) bits[(jc >> 5) + 1] = (uint32_t)(bal >> 32);
     }
-    if (lane == 0) a.counts[r] = count;
+    if (lane == 0) {
+        a.counts[r] = count;
+        a.keys[r] = (a.ngrp - 1 - row_group(s, g, a.Hkv, a.grp_units, a.ngrp)) * (a.max_nbk + 1) + count;
+    }
 }
 
 // Exclusive scan of counts into row_ptr[0..rows]; one workgroup of 1024.
@@ -115,20 +121,21 @@ __global__ __launch_bounds__(256) void expand_rows_kernel(Geo geo, SelectArgs a)
     }
 }
 
-// Stable counting sort of the rows by kept count, descending, ties by row id
-// ascending, in three passes over chunks of SORT_CHUNK consecutive rows:
-//   sort_hist:    per chunk, a histogram of the counts (LDS atomics) -> hist[c][k];
-//   sort_offsets: per count k (descending) and chunk c (ascending), the first
-//                 position of chunk c's rows with count k, written over hist;
-//   sort_scatter: per chunk, each row's rank among the equal counts before it
+// Stable counting sort of the rows by key (group-major, then kept count),
+// descending, ties by row id ascending, in three passes over chunks of
+// SORT_CHUNK consecutive rows:
+//   sort_hist:    per chunk, a histogram of the keys (LDS atomics) -> hist[c][k];
+//   sort_offsets: per key k (descending) and chunk c (ascending), the first
+//                 position of chunk c's rows with key k, written over hist;
+//   sort_scatter: per chunk, each row's rank among the equal keys before it
 //                 in the chunk, added to that position -> sched.
 __global__ __launch_bounds__(SORT_CHUNK) void sort_hist_kernel(SelectArgs a) {
     extern __shared__ __align__(16) int hsh[];   // [nbin]
-    const int nbin = a.max_nbk + 1, c = blockIdx.x, tid = threadIdx.x;
+    const int nbin = a.ngrp * (a.max_nbk + 1), c = blockIdx.x, tid = threadIdx.x;
     for (int k = tid; k < nbin; k += SORT_CHUNK) hsh[k] = 0;
     __syncthreads();
     const int r = c * SORT_CHUNK + tid;
-    if (r < a.rows) atomicAdd(&hsh[a.counts[r]], 1);
+    if (r < a.rows) atomicAdd(&hsh[a.keys[r]], 1);
     __syncthreads();
     int* out = a.hist + (long long)c * nbin;
     for (int k = tid; k < nbin; k += SORT_CHUNK) out[k] = hsh[k];
@@ -136,10 +143,10 @@ __global__ __launch_bounds__(SORT_CHUNK) void sort_hist_kernel(SelectArgs a) {
 
 __global__ __launch_bounds__(1024) void sort_offsets_kernel(SelectArgs a) {
     __shared__ int part[1024];
-    const int nbin = a.max_nbk + 1, nch = cdiv(a.rows, SORT_CHUNK), tid = threadIdx.x;
+    const int nbin = a.ngrp * (a.max_nbk + 1), nch = cdiv(a.rows, SORT_CHUNK), tid = threadIdx.x;
     const int per = cdiv(nbin, 1024);
     const int lo = min(tid * per, nbin), hi = min(lo + per, nbin);
-    int sum = 0;                                   // rows with a count in [lo, hi)
+    int sum = 0;                                   // rows with a key in [lo, hi)
     for (int k = lo; k < hi; ++k)
         for (int c = 0; c < nch; ++c) sum += a.hist[(long long)c * nbin + k];
     part[tid] = sum;
@@ -150,7 +157,7 @@ __global__ __launch_bounds__(1024) void sort_offsets_kernel(SelectArgs a) {
         part[tid] += v;
         __syncthreads();
     }
-    int run = part[tid] - sum;                     // rows with a larger count than hi - 1
+    int run = part[tid] - sum;                     // rows with a larger key than hi - 1
     for (int k = hi - 1; k >= lo; --k)
         for (int c = 0; c < nch; ++c) {
             int* h = a.hist + (long long)c * nbin + k;
@@ -162,13 +169,13 @@ __global__ __launch_bounds__(1024) void sort_offsets_kernel(SelectArgs a) {
 
 __global__ __launch_bounds__(SORT_CHUNK) void sort_scatter_kernel(SelectArgs a) {
     __shared__ __align__(16) int keys[SORT_CHUNK];
-    const int nbin = a.max_nbk + 1, c = blockIdx.x, tid = threadIdx.x;
+    const int nbin = a.ngrp * (a.max_nbk + 1), c = blockIdx.x, tid = threadIdx.x;
     const int r = c * SORT_CHUNK + tid;
-    const int key = r < a.rows ? a.counts[r] : -1;
+    const int key = r < a.rows ? a.keys[r] : -1;
     keys[tid] = key;
     __syncthreads();
     if (key < 0) return;
-    int rank = 0;                                  // equal counts earlier in the chunk
+    int rank = 0;                                  // equal keys earlier in the chunk
     const int4* k4 = (const int4*)keys;
     const int n4 = tid >> 2;
 #pragma unroll 8
@@ -188,7 +195,7 @@ static hipError_t select_dispatch(const Geo& geo, const SelectArgs& a, hipStream
     expand_rows_kernel<Geo><<<wg, 256, 0, st>>>(geo, a);
     if (a.sched) {
         const int nch = cdiv(a.rows, SORT_CHUNK);
-        const size_t shm = (size_t)(a.max_nbk + 1) * sizeof(int);
+        const size_t shm = (size_t)a.ngrp * (a.max_nbk + 1) * sizeof(int);
         if (shm > 65536) {
             hipError_t e = hipFuncSetAttribute((const void*)sort_hist_kernel,
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);

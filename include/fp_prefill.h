@@ -136,8 +136,11 @@ int fp_block_scores(const fp_problem* p, const void* q, const void* k, const voi
  * tau: +inf keeps everything, tau < 0 keeps only the sink and diagonal
  * blocks, NaN is an error. Outputs (device): row_ptr int32 [rows + 1],
  * col_idx int32 [capacity] (capacity >= fp_max_nnz checked on the host),
- * sched int32 [rows] or NULL: the rows ordered by kept count descending,
- * ties by row id ascending (heavy-row-first order for fp_sparse_prefill).
+ * sched int32 [rows] or NULL: the work order for fp_sparse_prefill. The
+ * (sequence, KV head) pairs, in row order, form groups by where each pair's
+ * K/V starts, in units of 128 MiB of K and V (widened so that groups x
+ * (key blocks + 1) stays within 32768); groups come in order, rows inside a
+ * group by kept count descending (heavy-row-first), ties by row id ascending.
  * workspace (device) of ws_bytes >= fp_workspace_size(p). */
 int fp_select_blocks(const fp_problem* p, const float* scores, float tau,
                      int32_t* row_ptr, int32_t* col_idx, int64_t capacity,

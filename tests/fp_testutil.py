@@ -52,7 +52,37 @@ def compare_outputs(o_gpu: np.ndarray, o_ref: np.ndarray, kind: str):
     return mx, mean
 
 
-def check_sched(sched: np.ndarray, counts: np.ndarray) -> None:
+# Schedule groups (the library's documented rule): the (sequence, KV head)
+# pairs, in row order, are cut by where each pair's K/V starts, in units of
+# 128 MiB of K and V; the groups are widened when ngroups * (max_nbk + 1)
+# would pass 32768 histogram bins.
+SCHED_GROUP_BYTES = 128 << 20
+SORT_MAX_BINS = 32768
+
+
+def sched_groups(seg_nbk, seg_rows, block, esz, max_nbk):
+    """Group id of every row; seg_nbk / seg_rows: key blocks and rows of each
+    (sequence, KV head) pair in row order."""
+    units = max(SCHED_GROUP_BYTES // (block * 128 * esz * 2), 1)
+    total = int(sum(seg_nbk))
+    ng = max(-(-total // units), 1)
+    nmax = max(SORT_MAX_BINS // (max_nbk + 1), 1)
+    if ng > nmax:
+        units = -(-total // nmax)
+        ng = max(-(-total // units), 1)
+    groups, start = [], 0
+    for nbk, nr in zip(seg_nbk, seg_rows):
+        groups += [min(start // units, ng - 1)] * nr
+        start += nbk
+    return np.array(groups, dtype=np.int64)
+
+
+def fixed_sched_groups(batch, Hkv, nb, block, esz):
+    return sched_groups([nb] * (batch * Hkv), [nb] * (batch * Hkv), block, esz, nb)
+
+
+def check_sched(sched: np.ndarray, counts: np.ndarray, groups: np.ndarray) -> None:
+    """Heavy-row-first within each group, groups in order, ties by row id."""
     assert sorted(sched.tolist()) == list(range(len(counts)))
-    order = sorted(range(len(counts)), key=lambda r: (-counts[r], r))
+    order = sorted(range(len(counts)), key=lambda r: (groups[r], -counts[r], r))
     assert sched.tolist() == order

@@ -129,3 +129,16 @@ def test_varlen_flops_match_oracle_counts():
     assert kept == sum(oc.kept_flops(k, Pb, Lb, B, d, G) for k, Lb, Pb in zip(keeps, L, P))
     assert corr == sum(oc.correction_flops(k, Pb, Lb, B, d, G) for k, Lb, Pb in zip(keeps, L, P))
     assert dense == sum(oc.dense_flops(Pb, Lb, d, G * Hkv) for Lb, Pb in zip(L, P))
+
+
+def test_schedule_groups_rule():
+    """The schedule-group rule on the benchmark shapes: S = 131072 with 8 KV
+    heads pairs the heads in bf16 (64 MiB of K and V each) and takes four in
+    fp8; S = 32768 and the longest single-head sequence form one group."""
+    from fp_testutil import fixed_sched_groups
+    g = fixed_sched_groups(1, 8, 1024, 128, 2)
+    assert g.reshape(8, 1024)[:, 0].tolist() == [0, 0, 1, 1, 2, 2, 3, 3]
+    g = fixed_sched_groups(1, 8, 1024, 128, 1)
+    assert g.reshape(8, 1024)[:, 0].tolist() == [0, 0, 0, 0, 1, 1, 1, 1]
+    assert fixed_sched_groups(1, 8, 256, 128, 2).max() == 0
+    assert fixed_sched_groups(1, 1, 16384, 128, 2).max() == 0

@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import synth
-from fp_testutil import LSE_TOL, check_sched, compare_masks, compare_outputs, csr_to_keep
+from fp_testutil import LSE_TOL, check_sched, compare_masks, compare_outputs, csr_to_keep, fixed_sched_groups
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -53,7 +53,9 @@ def run_and_check(fp, inp, tau, kind, rows_k, scores_tol=None):
     assert np.isfinite(o).all() and np.isfinite(lse).all()
     rp = out["row_ptr"].cpu().numpy()
     ci = out["col_idx"].cpu().numpy()
-    check_sched(out["sched"].cpu().numpy(), np.diff(rp))
+    nb = -(-cfg.S // cfg.block)
+    groups = fixed_sched_groups(1, inp.k.shape[2], nb, cfg.block, 2 if kind == "bf16" else 1)
+    check_sched(out["sched"].cpu().numpy(), np.diff(rp), groups)
     del q, k, v, out
     torch.cuda.empty_cache()
     if kind == "bf16":

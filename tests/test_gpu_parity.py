@@ -14,7 +14,7 @@ import torch
 import oracle
 import synth
 from fp_testutil import (TOL, LSE_TOL, check_csr_wellformed, check_sched, compare_masks, compare_outputs,
-                         csr_to_keep)
+                         csr_to_keep, fixed_sched_groups)
 
 pytestmark = pytest.mark.gpu
 
@@ -63,7 +63,8 @@ def check_fixed(fp, inp, tau, block, rows=None, kind="bf16", check_pooled=True):
     rp, ci = out["row_ptr"].numpy(), out["col_idx"].numpy()
     check_csr_wellformed(rp, ci, lambda r: r % nb)
     counts = np.diff(rp)
-    check_sched(out["sched"].numpy(), counts)
+    esz = 2 if inp.q.dtype == torch.bfloat16 else 1
+    check_sched(out["sched"].numpy(), counts, fixed_sched_groups(B, Hkv, nb, block, esz))
     stats = []
     for b in range(B):
         q, k, v = widen(inp, b)
