@@ -379,14 +379,16 @@ def sample_parity(gpu, keep, R, o_or, lse_or, il_list, nb, B, tau):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_S131072_tau4_traffic.md")
-KERNEL_SOURCE = os.path.join(ROOT, "block_sparse_long_estimate_amd", "csrc", "k_attn.hip")
+# the attention kernel and the selection stage that orders its work (both shape its traffic)
+KERNEL_SOURCES = [os.path.join(ROOT, "block_sparse_long_estimate_amd", "csrc", f) for f in ("k_attn.hip", "k_select.hip")]
 
 
 def measured_traffic(S, tau):
     """HBM bytes per attention launch from the committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE readings (scaled by a plain copy kernel's readings), or None
     when they were taken on another workload or another version of the
-    kernel source. The record is the `key: value` block of the summary."""
+    kernel or selection source. The record is the `key: value` block of the
+    summary."""
     import hashlib
     try:
         with open(TRAFFIC_FILE) as f:
@@ -395,8 +397,11 @@ def measured_traffic(S, tau):
                 key, sep, val = line.strip().partition(": ")
                 if sep and key in ("kernel_source_sha256", "seq_len", "tau", "hbm_bytes_per_launch"):
                     rec[key] = val.strip()
-        with open(KERNEL_SOURCE, "rb") as f:
-            digest = hashlib.sha256(f.read()).hexdigest()
+        h = hashlib.sha256()
+        for path in KERNEL_SOURCES:
+            with open(path, "rb") as f:
+                h.update(f.read())
+        digest = h.hexdigest()
         if (rec.get("kernel_source_sha256") != digest or int(rec["seq_len"]) != S
                 or float(rec["tau"]) != tau):
             return None

@@ -127,7 +127,7 @@ SortPlan sort_plan(long long total_units, int max_nbk, int blk, int esz) {
 }
 
 struct SelectWs {
-    size_t counts, bits, keys, hist, total;
+    size_t counts, bits, keys, maxc, hist, total;
     int nbw;
 };
 
@@ -137,7 +137,8 @@ SelectWs select_ws(long long rows, int max_nbk, int ngrp) {
     w.counts = 0;
     w.bits = align_up((size_t)rows * 4);
     w.keys = w.bits + align_up((size_t)rows * w.nbw * 4);
-    w.hist = w.keys + align_up((size_t)rows * 4);
+    w.maxc = w.keys + align_up((size_t)rows * 4);
+    w.hist = w.maxc + align_up(4);
     w.total = w.hist + align_up((size_t)((rows + SORT_CHUNK - 1) / SORT_CHUNK) * ngrp * (max_nbk + 1) * 4);
     return w;
 }
@@ -272,6 +273,7 @@ int fp_select_blocks(const fp_problem* p, const float* scores, float tau, int32_
     a.counts = (int32_t*)((char*)workspace + w.counts);
     a.bits = (uint32_t*)((char*)workspace + w.bits);
     a.keys = (int32_t*)((char*)workspace + w.keys);
+    a.maxc = (int32_t*)((char*)workspace + w.maxc);
     a.hist = (int32_t*)((char*)workspace + w.hist);
     a.nbw = w.nbw;
     a.row_ptr = row_ptr; a.col_idx = col_idx; a.sched = sched;
@@ -521,6 +523,7 @@ int fp_sparse_prefill_paged(const fp_varlen_problem* p, const void* q, const int
     se.counts = (int32_t*)(selws + plan.sel.counts);
     se.bits = (uint32_t*)(selws + plan.sel.bits);
     se.keys = (int32_t*)(selws + plan.sel.keys);
+    se.maxc = (int32_t*)(selws + plan.sel.maxc);
     se.hist = (int32_t*)(selws + plan.sel.hist);
     se.nbw = plan.sel.nbw;
     se.row_ptr = row_ptr; se.col_idx = col_idx; se.sched = sched;

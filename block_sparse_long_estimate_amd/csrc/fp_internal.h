@@ -151,8 +151,9 @@ constexpr int SORT_CHUNK = 256;    // rows per chunk of the schedule sort
 struct SelectArgs {
     const float* scores;
     int32_t* counts; uint32_t* bits; int nbw;   // bitmask row stride (u32 words)
-    int32_t* keys;                              // [rows] schedule sort key (group, count)
-    int32_t* hist;                              // [chunks][ngrp * (max_nbk + 1)] sort histograms / offsets
+    int32_t* keys;                              // [rows] schedule group of the row
+    int32_t* maxc;                              // largest kept count (written by the scan)
+    int32_t* hist;                              // [chunks][ngrp * (largest count + 1)] sort histograms / offsets
     int32_t* row_ptr; int32_t* col_idx; int32_t* sched;
     int Hq, Hkv, rows, max_nbk;
     int ngrp;                                   // schedule groups (rows sharing a K/V working set)

@@ -15,7 +15,8 @@
 // expand_rows: one wavefront per row, ballot + lane-prefix popcount writes the
 //   ascending column list at row_ptr.
 // sort_*:      stable counting sort of the rows -> sched, over chunks of rows
-//   (histograms, offsets, scatter). The order is heavy-row-first inside
+//   (histograms, offsets, scatter; the bins span the counts up to the largest
+//   one, which scan_rows records). The order is heavy-row-first inside
 //   groups of consecutive (sequence, KV head) pairs whose K/V together stay
 //   within a budget sized for the memory-side cache, groups in row order:
 //   key = (group ascending, count descending), ties by row id.
@@ -72,7 +73,7 @@ __global__ __launch_bounds__(256) void select_rows_kernel(Geo geo, SelectArgs a)
     }
     if (lane == 0) {
         a.counts[r] = count;
-        a.keys[r] = (a.ngrp - 1 - row_group(s, g, a.Hkv, a.grp_units, a.ngrp)) * (a.max_nbk + 1) + count;
+        a.keys[r] = row_group(s, g, a.Hkv, a.grp_units, a.ngrp);
     }
 }
 
@@ -82,10 +83,16 @@ __global__ __launch_bounds__(1024) void scan_rows_kernel(SelectArgs a) {
     const int tid = threadIdx.x;
     const int per = cdiv(a.rows, 1024);
     const int lo = min(tid * per, a.rows), hi = min(lo + per, a.rows);
-    int sum = 0;
-    for (int r = lo; r < hi; ++r) sum += a.counts[r];
+    __shared__ int cmax;
+    if (tid == 0) cmax = 0;
+    int sum = 0, mx = 0;
+    for (int r = lo; r < hi; ++r) {
+        sum += a.counts[r];
+        mx = max(mx, a.counts[r]);
+    }
     part[tid] = sum;
     __syncthreads();
+    atomicMax(&cmax, mx);
     for (int o = 1; o < 1024; o <<= 1) {           // Hillis-Steele inclusive scan
         const int v = tid >= o ? part[tid - o] : 0;
         __syncthreads();
@@ -93,7 +100,10 @@ __global__ __launch_bounds__(1024) void scan_rows_kernel(SelectArgs a) {
         __syncthreads();
     }
     int run = part[tid] - sum;                      // exclusive prefix of this chunk
-    if (tid == 0) a.row_ptr[0] = 0;
+    if (tid == 0) {
+        a.row_ptr[0] = 0;
+        *a.maxc = cmax;                             // read by the schedule sort
+    }
     for (int r = lo; r < hi; ++r) {
         run += a.counts[r];
         a.row_ptr[r + 1] = run;
@@ -129,13 +139,19 @@ __global__ __launch_bounds__(256) void expand_rows_kernel(Geo geo, SelectArgs a)
 //                 position of chunk c's rows with key k, written over hist;
 //   sort_scatter: per chunk, each row's rank among the equal keys before it
 //                 in the chunk, added to that position -> sched.
+// Sort key of row r: group-major (group 0 largest), then the kept count; the
+// histograms hold ngrp * (largest count + 1) bins.
+__device__ __forceinline__ int sort_key(const SelectArgs& a, int r, int nc) {
+    return (a.ngrp - 1 - a.keys[r]) * nc + a.counts[r];
+}
+
 __global__ __launch_bounds__(SORT_CHUNK) void sort_hist_kernel(SelectArgs a) {
     extern __shared__ __align__(16) int hsh[];   // [nbin]
-    const int nbin = a.ngrp * (a.max_nbk + 1), c = blockIdx.x, tid = threadIdx.x;
+    const int nc = *a.maxc + 1, nbin = a.ngrp * nc, c = blockIdx.x, tid = threadIdx.x;
     for (int k = tid; k < nbin; k += SORT_CHUNK) hsh[k] = 0;
     __syncthreads();
     const int r = c * SORT_CHUNK + tid;
-    if (r < a.rows) atomicAdd(&hsh[a.keys[r]], 1);
+    if (r < a.rows) atomicAdd(&hsh[sort_key(a, r, nc)], 1);
     __syncthreads();
     int* out = a.hist + (long long)c * nbin;
     for (int k = tid; k < nbin; k += SORT_CHUNK) out[k] = hsh[k];
@@ -143,7 +159,7 @@ __global__ __launch_bounds__(SORT_CHUNK) void sort_hist_kernel(SelectArgs a) {
 
 __global__ __launch_bounds__(1024) void sort_offsets_kernel(SelectArgs a) {
     __shared__ int part[1024];
-    const int nbin = a.ngrp * (a.max_nbk + 1), nch = cdiv(a.rows, SORT_CHUNK), tid = threadIdx.x;
+    const int nbin = a.ngrp * (*a.maxc + 1), nch = cdiv(a.rows, SORT_CHUNK), tid = threadIdx.x;
     const int per = cdiv(nbin, 1024);
     const int lo = min(tid * per, nbin), hi = min(lo + per, nbin);
     int sum = 0;                                   // rows with a key in [lo, hi)
@@ -169,9 +185,9 @@ __global__ __launch_bounds__(1024) void sort_offsets_kernel(SelectArgs a) {
 
 __global__ __launch_bounds__(SORT_CHUNK) void sort_scatter_kernel(SelectArgs a) {
     __shared__ __align__(16) int keys[SORT_CHUNK];
-    const int nbin = a.ngrp * (a.max_nbk + 1), c = blockIdx.x, tid = threadIdx.x;
+    const int nc = *a.maxc + 1, nbin = a.ngrp * nc, c = blockIdx.x, tid = threadIdx.x;
     const int r = c * SORT_CHUNK + tid;
-    const int key = r < a.rows ? a.keys[r] : -1;
+    const int key = r < a.rows ? sort_key(a, r, nc) : -1;
     keys[tid] = key;
     __syncthreads();
     if (key < 0) return;
