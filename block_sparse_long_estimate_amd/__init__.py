@@ -188,7 +188,7 @@ def make_varlen_problem(q: torch.Tensor, cu_seqlens_q, seqlens_k, k_cache: torch
     c.num_kv_heads = k_cache.shape[2]
     c.block = block
     c.page_size = k_cache.shape[1]
-    c.dtype = N.FP_DTYPE_BF16
+    c.dtype = N.FP_DTYPE_FP8_E4M3 if q.dtype == torch.uint8 else N.FP_DTYPE_BF16
     c.softmax_scale = softmax_scale
     c.max_pages_per_seq = block_table.shape[1]
     c.q_stride[0], c.q_stride[1] = q.stride(0), q.stride(1)
@@ -204,8 +204,11 @@ def make_varlen_problem(q: torch.Tensor, cu_seqlens_q, seqlens_k, k_cache: torch
 
 
 def fp_sparse_prefill_paged(vp: VarlenProblem, q, k_cache, v_cache, block_table, tau: float,
-                            with_lse: bool = True, workspace: Optional[torch.Tensor] = None):
-    """E1-E6 on a paged varlen batch -> (o, lse, row_ptr, col_idx)."""
+                            with_lse: bool = True, workspace: Optional[torch.Tensor] = None,
+                            q_scale=None, k_scale=None, v_scale=None):
+    """E1-E6 on a paged varlen batch -> (o, lse, row_ptr, col_idx). fp8
+    (uint8 E4M3FN codes) takes fp32 scales [num_seqs, H, nsb], one per 128
+    positions of each sequence."""
     dev = q.device
     i32 = dict(dtype=torch.int32, device=dev)
     row_ptr = torch.empty(vp.rows + 1, **i32)
@@ -216,7 +219,8 @@ def fp_sparse_prefill_paged(vp: VarlenProblem, q, k_cache, v_cache, block_table,
         workspace = torch.empty(vp.ws_bytes, dtype=torch.uint8, device=dev)
     cup, lkp = vp.host_ptrs()
     N.check(N.load().fp_sparse_prefill_paged(vp.ref, _ptr(q), cup, lkp, _ptr(k_cache), _ptr(v_cache),
-                                             _ptr(block_table), float(tau), _ptr(row_ptr),
+                                             _ptr(block_table), _ptr(q_scale), _ptr(k_scale),
+                                             _ptr(v_scale), float(tau), _ptr(row_ptr),
                                              _ptr(col_idx), vp.max_nnz, _ptr(o), _ptr(lse),
                                              _ptr(workspace), workspace.numel(), _stream()))
     return o, lse, row_ptr, col_idx

@@ -86,8 +86,8 @@ def load() -> ctypes.CDLL:
     lib.fp_sparse_prefill.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                       ctypes.c_size_t, vp]
     lib.fp_sparse_prefill_paged.restype = ctypes.c_int
-    lib.fp_sparse_prefill_paged.argtypes = [VP, vp, i32p, i32p, vp, vp, vp, ctypes.c_float, vp,
-                                            vp, ctypes.c_int64, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.fp_sparse_prefill_paged.argtypes = [VP, vp, i32p, i32p, vp, vp, vp, vp, vp, vp, ctypes.c_float,
+                                            vp, vp, ctypes.c_int64, vp, vp, vp, ctypes.c_size_t, vp]
     _lib = lib
     return lib
 

@@ -364,7 +364,9 @@ int check_varlen(const fp_varlen_problem* p, const int32_t* cu, const int32_t* l
     int rc = check_heads(p->num_q_heads, p->num_kv_heads, p->head_dim, p->block);
     if (rc) return rc;
     if (p->num_seqs <= 0 || p->num_seqs > 4096) return fail(FP_ERR_INVALID, "num_seqs must be in [1, 4096]");
-    if (p->dtype != FP_DTYPE_BF16) return fail(FP_ERR_UNSUPPORTED, "paged path supports bf16 only");
+    if (p->dtype != FP_DTYPE_BF16 && p->dtype != FP_DTYPE_FP8_E4M3)
+        return fail(FP_ERR_UNSUPPORTED, "dtype %d unsupported", p->dtype);
+    const int esz = p->dtype == FP_DTYPE_FP8_E4M3 ? 1 : 2;
     if (p->page_size < 16 || p->page_size > 256 || (p->page_size & (p->page_size - 1)))
         return fail(FP_ERR_UNSUPPORTED, "page_size %d unsupported (power of two in [16, 256])", p->page_size);
     if (p->max_pages_per_seq <= 0) return fail(FP_ERR_INVALID, "max_pages_per_seq must be positive");
@@ -375,8 +377,9 @@ int check_varlen(const fp_varlen_problem* p, const int32_t* cu, const int32_t* l
     for (int e = 0; e < 2; ++e)
         if (p->q_stride[e] < 0 || p->o_stride[e] < 0) return fail(FP_ERR_INVALID, "negative stride");
     for (int e = 0; e < 3; ++e)
-        if (p->kv_stride[e] < 0 || (p->kv_stride[e] * 2) % 16) return fail(FP_ERR_INVALID, "bad kv stride");
-    if ((p->q_stride[0] * 2) % 16 || (p->q_stride[1] * 2) % 16 || (p->o_stride[0] * 2) % 8 || (p->o_stride[1] * 2) % 8)
+        if (p->kv_stride[e] < 0 || (p->kv_stride[e] * esz) % 16) return fail(FP_ERR_INVALID, "bad kv stride");
+    if ((p->q_stride[0] * esz) % 16 || (p->q_stride[1] * esz) % 16 || (p->o_stride[0] * 2) % 8 ||
+        (p->o_stride[1] * 2) % 8)
         return fail(FP_ERR_INVALID, "q/o strides must be multiples of 16/8 bytes");
     const int B = p->block;
     plan.table.assign(p->num_seqs + 1, SeqDesc{});
@@ -425,7 +428,7 @@ int check_varlen(const fp_varlen_problem* p, const int32_t* cu, const int32_t* l
     plan.o_vbar = off; off = align_up(off + (size_t)kb * p->num_kv_heads * D * 4);
     plan.o_scores = off; off = align_up(off + (size_t)sc * 4);
     plan.o_sched = off; off = align_up(off + (size_t)plan.rows * 4);
-    plan.sort = sort_plan(kb * p->num_kv_heads, std::max(plan.max_nbk, 1), B, 2);
+    plan.sort = sort_plan(kb * p->num_kv_heads, std::max(plan.max_nbk, 1), B, esz);
     plan.sel = select_ws(plan.rows, std::max(plan.max_nbk, 1), plan.sort.ngrp);
     plan.o_sel = off; off = align_up(off + plan.sel.total);
     plan.o_sum = off; off += summary_ws_bytes(kb * p->num_kv_heads);
@@ -455,14 +458,20 @@ int64_t fp_varlen_workspace_size(const fp_varlen_problem* p, const int32_t* cu, 
 
 int fp_sparse_prefill_paged(const fp_varlen_problem* p, const void* q, const int32_t* cu,
                             const int32_t* lk, const void* k_cache, const void* v_cache,
-                            const int32_t* block_table, float tau, int32_t* row_ptr,
-                            int32_t* col_idx, int64_t capacity, void* o, float* lse,
-                            void* workspace, size_t ws_bytes, void* stream) {
+                            const int32_t* block_table, const float* q_scale, const float* k_scale,
+                            const float* v_scale, float tau, int32_t* row_ptr, int32_t* col_idx,
+                            int64_t capacity, void* o, float* lse, void* workspace, size_t ws_bytes,
+                            void* stream) {
     VarPlan plan;
     int rc = check_varlen(p, cu, lk, plan);
     if (rc) return rc;
     if (!q || !k_cache || !v_cache || !block_table || !row_ptr || !col_idx || !o || !workspace)
         return fail(FP_ERR_INVALID, "fp_sparse_prefill_paged: NULL pointer");
+    const bool fp8 = p->dtype == FP_DTYPE_FP8_E4M3;
+    if (fp8 && (!q_scale || !k_scale || !v_scale))
+        return fail(FP_ERR_INVALID, "fp_sparse_prefill_paged: fp8 needs q_scale, k_scale and v_scale");
+    // fp8 scales: [num_seqs, H, nsb], one per 128 positions of each sequence
+    const long long nsb = ((long long)p->max_pages_per_seq * p->page_size + SCALE_TOK - 1) / SCALE_TOK;
     if (isnan(tau)) return fail(FP_ERR_INVALID, "fp_sparse_prefill_paged: tau is NaN");
     if (capacity < plan.max_nnz)
         return fail(FP_ERR_CAPACITY, "fp_sparse_prefill_paged: capacity %lld < max nnz %lld",
@@ -502,10 +511,12 @@ int fp_sparse_prefill_paged(const fp_varlen_problem* p, const void* q, const int
     pa.q = q; pa.k = k_cache; pa.v = v_cache;
     pa.qa = RowAddr{0, p->q_stride[0], p->q_stride[1]};
     pa.ka = kva; pa.va = kva;
-    pa.qs = pa.ks = pa.vs = ScaleAddr{nullptr, 0, 0};
+    pa.qs = ScaleAddr{q_scale, p->num_q_heads * nsb, nsb};
+    pa.ks = ScaleAddr{k_scale, p->num_kv_heads * nsb, nsb};
+    pa.vs = ScaleAddr{v_scale, p->num_kv_heads * nsb, nsb};
     pa.qbar = qbar; pa.kbar = kbar; pa.vbar = vbar;
     pa.Hq = p->num_q_heads; pa.Hkv = p->num_kv_heads; pa.blk = p->block;
-    pa.fp8 = 0; pa.paged = 1;
+    pa.fp8 = fp8; pa.paged = 1;
     pa.total_qblocks = plan.total_qblocks; pa.total_kblocks = plan.total_kblocks;
     e = launch_pool(nullptr, &geo, pa, st);
     if (e != hipSuccess) return fail(FP_ERR_HIP, "pool launch: %s", hipGetErrorString(e));
@@ -540,9 +551,9 @@ int fp_sparse_prefill_paged(const fp_varlen_problem* p, const void* q, const int
     a.qa = RowAddr{0, p->q_stride[0], p->q_stride[1]};
     a.oa = RowAddr{0, p->o_stride[0], p->o_stride[1]};
     a.ka = kva; a.va = kva;
-    // per-lane in-page offsets of a tile are kept in 24 bits (bf16: 2 bytes)
-    a.paged_fast = (long long)std::min(p->page_size, p->block) * p->kv_stride[1] * 2 < (1LL << 24);
-    a.qs = a.ks = a.vs = ScaleAddr{nullptr, 0, 0};
+    // per-lane in-page offsets of a tile are kept in 24 bits
+    a.paged_fast = (long long)std::min(p->page_size, p->block) * p->kv_stride[1] * (fp8 ? 1 : 2) < (1LL << 24);
+    a.qs = pa.qs; a.ks = pa.ks; a.vs = pa.vs;
     a.kbar = kbar; a.vbar = vbar;
     {
         const size_t part = align_up((size_t)plan.total_kblocks * p->num_kv_heads * D * 2);
@@ -560,7 +571,7 @@ int fp_sparse_prefill_paged(const fp_varlen_problem* p, const void* q, const int
     e = launch_summary_prep(kbar, vbar, (__bf16*)a.kbar_hi, (__bf16*)a.kbar_lo, (__bf16*)a.vbar_bf,
                             (long long)plan.total_kblocks * p->num_kv_heads * D, st);
     if (e != hipSuccess) return fail(FP_ERR_HIP, "summary prep launch: %s", hipGetErrorString(e));
-    e = launch_attn(nullptr, &geo, a, p->block, 0, 1, st);
+    e = launch_attn(nullptr, &geo, a, p->block, fp8, 1, st);
     if (e != hipSuccess) return fail(FP_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
     return ok();
 }

@@ -41,6 +41,7 @@ __host__ __device__ inline int score_tiles(int nq, int nbk) {
 // Fixed shape: every sequence has S tokens and no prefix. Everything is
 // arithmetic; no table in memory.
 struct GeoFixed {
+    static constexpr bool PAGED_KV = false;   // contiguous K/V
     int nseq, S, Hq, Hkv, blk, nb, ntile;
     __device__ __forceinline__ SeqDesc seq(int b) const {
         SeqDesc s;
@@ -58,6 +59,7 @@ struct GeoFixed {
 // Varlen: a table of nseq descriptors in device memory, entry nseq holding
 // the running totals (qb0, kb0, row0, tile0, sc0) past the last sequence.
 struct GeoTable {
+    static constexpr bool PAGED_KV = true;    // K/V in the paged cache
     const SeqDesc* t;
     int nseq, Hq, Hkv, blk;
     __device__ __forceinline__ SeqDesc seq(int b) const { return t[b]; }

@@ -823,9 +823,15 @@ static void attn_launch(const Geo& geo, const AttnArgs& a, int fp8, int paged, h
     AttnArgs b2 = a;
     b2.slices = cdiv(a.G * BLK, 256);
     const int units = cdiv(a.rows, 8) * 8 * b2.slices;
-    if (fp8) attn_tile_kernel<BLK, true, false, Geo><<<units, 512, 0, st>>>(geo, b2);
-    else if (paged) attn_tile_kernel<BLK, false, true, Geo><<<units, 512, 0, st>>>(geo, b2);
-    else attn_tile_kernel<BLK, false, false, Geo><<<units, 512, 0, st>>>(geo, b2);
+    // contiguous K/V come with the fixed geometry, the paged cache with the
+    // sequence table (the entry points pair them so)
+    if constexpr (Geo::PAGED_KV) {
+        if (fp8) attn_tile_kernel<BLK, true, true, Geo><<<units, 512, 0, st>>>(geo, b2);
+        else attn_tile_kernel<BLK, false, true, Geo><<<units, 512, 0, st>>>(geo, b2);
+    } else {
+        if (fp8) attn_tile_kernel<BLK, true, false, Geo><<<units, 512, 0, st>>>(geo, b2);
+        else attn_tile_kernel<BLK, false, false, Geo><<<units, 512, 0, st>>>(geo, b2);
+    }
 }
 
 template <typename Geo>

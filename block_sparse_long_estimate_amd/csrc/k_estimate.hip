@@ -188,14 +188,10 @@ __global__ __launch_bounds__(256) void scores_kernel(Geo geo, ScoreArgs a) {
 template <typename Geo>
 static hipError_t pool_dispatch(const Geo& geo, const PoolArgs& a, hipStream_t st) {
     dim3 grid(max(a.total_qblocks, a.total_kblocks), a.Hq + 2 * a.Hkv);
-    if (a.fp8) {
-        if (a.paged) return hipErrorInvalidValue;
-        pool_kernel<true, false, Geo><<<grid, 256, 0, st>>>(geo, a);
-    } else if (a.paged) {
-        pool_kernel<false, true, Geo><<<grid, 256, 0, st>>>(geo, a);
-    } else {
-        pool_kernel<false, false, Geo><<<grid, 256, 0, st>>>(geo, a);
-    }
+    // contiguous K/V come with the fixed geometry, the paged cache with the sequence table
+    if (a.paged != Geo::PAGED_KV) return hipErrorInvalidValue;
+    if (a.fp8) pool_kernel<true, Geo::PAGED_KV, Geo><<<grid, 256, 0, st>>>(geo, a);
+    else pool_kernel<false, Geo::PAGED_KV, Geo><<<grid, 256, 0, st>>>(geo, a);
     return hipGetLastError();
 }
 

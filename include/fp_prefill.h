@@ -101,9 +101,9 @@ typedef struct fp_varlen_problem {
     int32_t num_q_heads;
     int32_t num_kv_heads;
     int32_t head_dim;        /* 128 */
-    int32_t block;           /* 128 */
-    int32_t page_size;       /* 64 or 128; block must be a multiple */
-    int32_t dtype;           /* FP_DTYPE_BF16 */
+    int32_t block;           /* 64 or 128 */
+    int32_t page_size;       /* power of two in [16, 256] */
+    int32_t dtype;           /* FP_DTYPE_BF16 or FP_DTYPE_FP8_E4M3 */
     float softmax_scale;     /* 0 means 1/sqrt(head_dim) */
     int32_t max_pages_per_seq;  /* row length of block_table */
     int32_t pad_;
@@ -171,20 +171,28 @@ int64_t fp_varlen_max_nnz(const fp_varlen_problem* p, const int32_t* cu_seqlens_
 int64_t fp_varlen_workspace_size(const fp_varlen_problem* p, const int32_t* cu_seqlens_q,
                                  const int32_t* seqlens_k);
 
-/* E1-E6 for a paged varlen batch in one call. q (device) packed
- * [sum q_len, Hq, 128] bf16; k_cache, v_cache (device) [pages, page_size,
- * Hkv, 128] bf16; block_table (device) int32 [num_seqs, max_pages_per_seq]
+/* E1-E6 for a paged varlen batch in one call (the pages' paged KV cache and
+ * continuous batching: aimodeling.com page, "Framework integration" bullet).
+ * q (device) packed [sum q_len, Hq, 128]; k_cache, v_cache (device)
+ * [pages, page_size, Hkv, 128]; bf16, or E4M3FN codes when dtype is
+ * FP_DTYPE_FP8_E4M3. block_table (device) int32 [num_seqs, max_pages_per_seq]
  * (token s of sequence b lives in page block_table[b][s / page_size], slot
  * s % page_size; the new chunk's keys must already be in the cache).
+ * q_scale, k_scale, v_scale (device, fp8 only, else NULL): fp32
+ * [num_seqs, H, nsb] with nsb = ceil(max_pages_per_seq * page_size / 128),
+ * one scale per 128 positions of each sequence (the query row at position t
+ * of sequence b uses q_scale[b][h][t / 128]; keys and values likewise).
  * cu_seqlens_q, seqlens_k: HOST arrays, read during the call only.
  * Outputs (device): row_ptr [rows+1] and col_idx [capacity] (the kept lists,
- * capacity >= fp_varlen_max_nnz), o packed like q, lse fp32 [Hq, sum q_len]
- * or NULL. workspace (device) >= fp_varlen_workspace_size bytes. */
+ * capacity >= fp_varlen_max_nnz), o packed like q in bf16, lse fp32
+ * [Hq, sum q_len] or NULL. workspace (device) >= fp_varlen_workspace_size
+ * bytes. */
 int fp_sparse_prefill_paged(const fp_varlen_problem* p, const void* q,
                             const int32_t* cu_seqlens_q, const int32_t* seqlens_k,
                             const void* k_cache, const void* v_cache,
-                            const int32_t* block_table, float tau,
-                            int32_t* row_ptr, int32_t* col_idx, int64_t capacity,
+                            const int32_t* block_table,
+                            const float* q_scale, const float* k_scale, const float* v_scale,
+                            float tau, int32_t* row_ptr, int32_t* col_idx, int64_t capacity,
                             void* o, float* lse, void* workspace, size_t ws_bytes,
                             void* stream);
 

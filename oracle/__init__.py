@@ -51,11 +51,11 @@ from .core import (
     dense_flops, kept_flops, correction_flops,
 )
 from .fp8 import decode_e4m3, widen_fp8
-from .batch import prefill_fixed, prefill_varlen, widen_bf16
+from .batch import prefill_fixed, prefill_varlen, varlen_sequence, widen_bf16
 
 __all__ = [
     "nblocks", "query_blocks", "pool_queries", "pool_keys", "block_scores", "select",
     "attend", "prefill", "kept_fraction", "threshold_margin", "causal_block_pairs",
     "dense_flops", "kept_flops", "correction_flops", "decode_e4m3", "widen_fp8",
-    "prefill_fixed", "prefill_varlen", "widen_bf16",
+    "prefill_fixed", "prefill_varlen", "varlen_sequence", "widen_bf16",
 ]

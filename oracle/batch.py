@@ -57,25 +57,39 @@ def gather_pages(cache: torch.Tensor, table_row: np.ndarray, L: int) -> torch.Te
     return torch.cat(toks, dim=0)
 
 
+def varlen_sequence(q: torch.Tensor, cu_seqlens_q: np.ndarray, seqlens_k: np.ndarray,
+                    k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: np.ndarray, b: int,
+                    q_scale=None, k_scale=None, v_scale=None) -> Tuple[np.ndarray, np.ndarray, np.ndarray, int]:
+    """(q, k, v) of sequence b widened to float64 -- present query rows
+    [P, L), keys and values [0, L) gathered from the pages -- and P. fp8 codes
+    take the sequence's scales, one per 128 positions ([H, nsb] per sequence)."""
+    L = int(seqlens_k[b])
+    lo, hi = int(cu_seqlens_q[b]), int(cu_seqlens_q[b + 1])
+    P = L - (hi - lo)
+    row = np.asarray(block_table)[b]
+    kb, vb, qb = gather_pages(k_cache, row, L), gather_pages(v_cache, row, L), q[lo:hi]
+    if q.dtype == torch.bfloat16:
+        return widen_bf16(qb), widen_bf16(kb), widen_bf16(vb), P
+    return (widen_fp8(qb.numpy(), q_scale[b].numpy(), pos0=P), widen_fp8(kb.numpy(), k_scale[b].numpy()),
+            widen_fp8(vb.numpy(), v_scale[b].numpy()), P)
+
+
 def prefill_varlen(q: torch.Tensor, cu_seqlens_q: np.ndarray, seqlens_k: np.ndarray,
                    k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: np.ndarray,
                    B: int, tau: float, c: Optional[float] = None,
                    keep: Optional[Sequence[np.ndarray]] = None,
                    rows: Optional[Sequence[Sequence[Tuple[int, int]]]] = None,
-                   with_output: bool = True) -> List[Dict[str, np.ndarray]]:
+                   with_output: bool = True,
+                   q_scale=None, k_scale=None, v_scale=None) -> List[Dict[str, np.ndarray]]:
     """E1-E6 per sequence of a paged varlen batch.  Sequence b has L_b =
     seqlens_k[b] keys (cache, new chunk included) and q_len_b = cu[b+1] - cu[b]
-    present rows [L_b - q_len_b, L_b) packed in q."""
+    present rows [L_b - q_len_b, L_b) packed in q (bf16, or fp8 codes with
+    per-sequence scales)."""
     out = []
-    bt = np.asarray(block_table)
     for b in range(len(seqlens_k)):
-        L = int(seqlens_k[b])
-        ql = int(cu_seqlens_q[b + 1] - cu_seqlens_q[b])
-        P = L - ql
-        kb = gather_pages(k_cache, bt[b], L)
-        vb = gather_pages(v_cache, bt[b], L)
-        qb = q[int(cu_seqlens_q[b]):int(cu_seqlens_q[b + 1])]
-        out.append(prefill(widen_bf16(qb), widen_bf16(kb), widen_bf16(vb), B, tau, c, P=P,
+        qw, kw, vw, P = varlen_sequence(q, cu_seqlens_q, seqlens_k, k_cache, v_cache, block_table, b,
+                                        q_scale, k_scale, v_scale)
+        out.append(prefill(qw, kw, vw, B, tau, c, P=P,
                            keep=None if keep is None else keep[b],
                            rows=None if rows is None else rows[b], with_output=with_output))
     return out

@@ -30,11 +30,14 @@ def decode_e4m3(codes: np.ndarray) -> np.ndarray:
     return _TABLE[np.asarray(codes, dtype=np.uint8)]
 
 
-def widen_fp8(codes: np.ndarray, scales: np.ndarray, block: int = 128) -> np.ndarray:
-    """codes [T, H, d] uint8 and scales [H, ceil(T/block)] float32 -> float64
-    values code * scale (scale of the token's 128-token block)."""
+def widen_fp8(codes: np.ndarray, scales: np.ndarray, block: int = 128, pos0: int = 0) -> np.ndarray:
+    """codes [T, H, d] uint8 for positions pos0 .. pos0 + T - 1 and scales
+    [H, nsb] float32 (one per 128 positions, nsb >= ceil((pos0 + T)/block))
+    -> float64 values code * scale (the scale of the token's 128-position
+    block)."""
     T = codes.shape[0]
     x = decode_e4m3(codes)
     sc = np.asarray(scales, dtype=np.float64)             # [H, nsb]
-    per_tok = np.repeat(sc, block, axis=1)[:, :T]         # [H, T]
+    per_tok = np.repeat(sc, block, axis=1)[:, pos0:pos0 + T]   # [H, T]
+    assert per_tok.shape[1] == T
     return x * per_tok.T[:, :, None]

@@ -328,14 +328,19 @@ class _alloc_fixed:
 @dataclass
 class PagedInputs:
     cfg: Config
-    q: torch.Tensor              # [sum_q, Hq, d] bf16, rows [P_b, L_b) of each sequence
-    k_cache: torch.Tensor        # [n_pages, page, Hkv, d] bf16
+    q: torch.Tensor              # [sum_q, Hq, d] bf16 (fp8: uint8 codes), rows [P_b, L_b) of each sequence
+    k_cache: torch.Tensor        # [n_pages, page, Hkv, d] bf16 (fp8: uint8 codes)
     v_cache: torch.Tensor
     block_table: torch.Tensor    # int32 [n_seqs, max_pages]; unused entries 0
     cu_seqlens_q: np.ndarray     # int32 [n_seqs + 1]
     seqlens_k: np.ndarray        # int32 [n_seqs]  (L_b)
     prefix: np.ndarray           # int32 [n_seqs]  (P_b = L_b - q_len_b)
     meta: List[SeqMeta] = field(default_factory=list)
+    # fp8 only: float32 [n_seqs, H, ceil(max_pages * page / 128)], one scale per
+    # 128 positions of each sequence (the queries' from their present rows only)
+    q_scale: Optional[torch.Tensor] = None
+    k_scale: Optional[torch.Tensor] = None
+    v_scale: Optional[torch.Tensor] = None
 
 
 def paged_lengths(cfg: Config) -> Tuple[np.ndarray, np.ndarray]:
@@ -348,11 +353,14 @@ def paged_lengths(cfg: Config) -> Tuple[np.ndarray, np.ndarray]:
 
 
 def gen_paged(cfg: Config, lengths: Optional[Tuple[np.ndarray, np.ndarray]] = None) -> PagedInputs:
-    """Inputs for a paged varlen configuration (bf16 only).
+    """Inputs for a paged varlen configuration, bf16 or fp8 (cfg.dtype).
 
     Each sequence b is drawn by the fixed-shape generator at length L_b with
-    its own child seed; its keys/values go to 64-token pages whose physical ids
-    are one random permutation; the queries of rows [P_b, L_b) are packed."""
+    its own child seed; its keys/values go to pages whose physical ids are one
+    random permutation; the queries of rows [P_b, L_b) are packed. fp8 codes
+    use one scale per 128 positions of the sequence (quantize_fp8 over the
+    sequence's rows; for the queries, over the present rows with the cached
+    prefix rows zeroed)."""
     L, P = lengths if lengths is not None else paged_lengths(cfg)
     L = np.asarray(L, dtype=np.int64)
     P = np.asarray(P, dtype=np.int64)
@@ -372,26 +380,41 @@ def gen_paged(cfg: Config, lengths: Optional[Tuple[np.ndarray, np.ndarray]] = No
     cu = np.zeros(n + 1, dtype=np.int32)
     cu[1:] = np.cumsum(qlen)
     d = cfg.d
-    q = torch.empty((int(cu[-1]), cfg.Hq, d), dtype=torch.bfloat16)
-    kc = torch.zeros((n_pages, ps, cfg.Hkv, d), dtype=torch.bfloat16)
-    vc = torch.zeros((n_pages, ps, cfg.Hkv, d), dtype=torch.bfloat16)
+    fp8 = cfg.dtype == "fp8"
+    tdt = torch.uint8 if fp8 else torch.bfloat16
+    q = torch.empty((int(cu[-1]), cfg.Hq, d), dtype=tdt)
+    kc = torch.zeros((n_pages, ps, cfg.Hkv, d), dtype=tdt)
+    vc = torch.zeros((n_pages, ps, cfg.Hkv, d), dtype=tdt)
+    nsb = (max_pages * ps + SCALE_BLOCK - 1) // SCALE_BLOCK
+    scales = {}
+    if fp8:
+        scales = {n_: torch.ones((n, H, nsb), dtype=torch.float32)
+                  for n_, H in (("q", cfg.Hq), ("k", cfg.Hkv), ("v", cfg.Hkv))}
     metas = []
     for b, ss in enumerate(np.random.SeedSequence(cfg.seed).spawn(n)):
         Lb, Pb = int(L[b]), int(P[b])
         pages = torch.from_numpy(table[b, :pages_per[b]].astype(np.int64))
 
         def store(kind, h, x, Lb=Lb, Pb=Pb, b=b, pages=pages):
+            if fp8:
+                if kind == "q":
+                    x = x.copy()
+                    x[:Pb] = 0.0                # scales from the present rows only
+                xt, sc = quantize_fp8(x)
+                scales[kind][b, h, :len(sc)] = torch.from_numpy(sc)
+            else:
+                xt = _to_bf16(x)
             if kind == "q":
-                q[cu[b]:cu[b + 1], h, :] = _to_bf16(x[Pb:])
+                q[cu[b]:cu[b + 1], h, :] = xt[Pb:]
             else:
                 cache = kc if kind == "k" else vc
-                xb = _to_bf16(x)
-                full = torch.zeros((len(pages) * ps, d), dtype=torch.bfloat16)
-                full[:Lb] = xb
+                full = torch.zeros((len(pages) * ps, d), dtype=tdt)
+                full[:Lb] = xt
                 cache[pages, :, h, :] = full.view(len(pages), ps, d)
         metas.append(_gen_sequence(cfg, Lb, ss, store, False))
     return PagedInputs(cfg, q, kc, vc, torch.from_numpy(table), cu,
-                       L.astype(np.int32), P.astype(np.int32), metas)
+                       L.astype(np.int32), P.astype(np.int32), metas,
+                       scales.get("q"), scales.get("k"), scales.get("v"))
 
 
 def unpage(inp: PagedInputs, b: int) -> Tuple[torch.Tensor, torch.Tensor]:

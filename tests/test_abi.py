@@ -184,7 +184,7 @@ def test_varlen_sizes_match_a_direct_count():
     ([0, 300, 400, 1000], [200, 200, 1000], {}, N.FP_ERR_INVALID),     # L < q_len
     ([1, 300, 400, 1000], [500, 200, 1000], {}, N.FP_ERR_INVALID),     # cu[0] != 0
     ([0, 300, 400, 1000], [500, 200, 1000], {"page_size": 48}, N.FP_ERR_UNSUPPORTED),
-    ([0, 300, 400, 1000], [500, 200, 1000], {"dtype": 1}, N.FP_ERR_UNSUPPORTED),
+    ([0, 300, 400, 1000], [500, 200, 1000], {"dtype": 7}, N.FP_ERR_UNSUPPORTED),
     ([0, 300, 400, 1000], [500, 200, 1000], {"max_pages_per_seq": 8}, N.FP_ERR_INVALID),
     ([0, 300, 400, 1000], [500, 200, 1000], {"num_seqs": 0}, N.FP_ERR_INVALID),
 ])
@@ -195,8 +195,8 @@ def test_varlen_invalid(cu, lk, kw, code):
     _, lkp = arr(lk)
     assert lib.fp_varlen_num_rows(ctypes.byref(p), cup, lkp) == code
     fake = ctypes.c_void_p(1 << 20)
-    assert lib.fp_sparse_prefill_paged(ctypes.byref(p), fake, cup, lkp, fake, fake, fake, 4.0,
-                                       fake, fake, 1 << 30, fake, None, fake, 1 << 40, None) == code
+    assert lib.fp_sparse_prefill_paged(ctypes.byref(p), fake, cup, lkp, fake, fake, fake, None, None, None,
+                                       4.0, fake, fake, 1 << 30, fake, None, fake, 1 << 40, None) == code
 
 
 def test_paged_rejects_nan_tau_capacity_workspace():
@@ -208,10 +208,29 @@ def test_paged_rejects_nan_tau_capacity_workspace():
     nnz = lib.fp_varlen_max_nnz(ctypes.byref(p), cup, lkp)
     ws = lib.fp_varlen_workspace_size(ctypes.byref(p), cup, lkp)
     call = lambda tau, cap, wsb: lib.fp_sparse_prefill_paged(
-        ctypes.byref(p), fake, cup, lkp, fake, fake, fake, tau, fake, fake, cap, fake, None, fake, wsb, None)
+        ctypes.byref(p), fake, cup, lkp, fake, fake, fake, None, None, None, tau, fake, fake, cap, fake, None,
+        fake, wsb, None)
     assert call(float("nan"), nnz, ws) == N.FP_ERR_INVALID
     assert call(4.0, nnz - 1, ws) == N.FP_ERR_CAPACITY
     assert call(4.0, nnz, ws - 1) == N.FP_ERR_CAPACITY
+
+
+def test_paged_fp8_needs_scales():
+    """fp8 codes in the paged cache take q/k/v scales; a missing one is refused
+    before any HIP call. fp8 also halves the byte strides the checks see."""
+    lib = N.load()
+    p = vproblem(dtype=N.FP_DTYPE_FP8_E4M3)
+    _, cup = arr([0, 300, 400, 1000])
+    _, lkp = arr([500, 200, 1000])
+    nnz = lib.fp_varlen_max_nnz(ctypes.byref(p), cup, lkp)
+    ws = lib.fp_varlen_workspace_size(ctypes.byref(p), cup, lkp)
+    assert nnz > 0 and ws > 0
+    fake = ctypes.c_void_p(1 << 20)
+    for scales in ((None, fake, fake), (fake, None, fake), (fake, fake, None)):
+        assert lib.fp_sparse_prefill_paged(ctypes.byref(p), fake, cup, lkp, fake, fake, fake, *scales, 4.0,
+                                           fake, fake, nnz, fake, None, fake, ws, None) == N.FP_ERR_INVALID
+    p.q_stride[1] = 8 + 128                       # 136 bytes per head row: not a multiple of 16
+    assert lib.fp_varlen_num_rows(ctypes.byref(p), cup, lkp) == N.FP_ERR_INVALID
 
 
 def test_variant_validation():

@@ -208,8 +208,10 @@ def test_fp8_block64_iid(fp):
 def run_paged(fp, inp, tau):
     dev = torch.device("cuda:0")
     q, kc, vc, bt = inp.q.to(dev), inp.k_cache.to(dev), inp.v_cache.to(dev), inp.block_table.to(dev)
+    sc = [None if t is None else t.to(dev) for t in (inp.q_scale, inp.k_scale, inp.v_scale)]
     vp = fp.make_varlen_problem(q, inp.cu_seqlens_q, inp.seqlens_k, kc, bt, inp.cfg.block)
-    o, lse, rp, ci = fp.fp_sparse_prefill_paged(vp, q, kc, vc, bt, tau)
+    o, lse, rp, ci = fp.fp_sparse_prefill_paged(vp, q, kc, vc, bt, tau, q_scale=sc[0], k_scale=sc[1],
+                                                v_scale=sc[2])
     torch.cuda.synchronize()
     return o.cpu(), lse.cpu(), rp.cpu().numpy(), ci.cpu().numpy()
 
@@ -218,8 +220,10 @@ def check_paged(fp, inp, tau, sample_rows=None):
     o, lse, rp, ci = run_paged(fp, inp, tau)
     cfg = inp.cfg
     c = 1 / math.sqrt(128)
+    kind = "fp8" if inp.q.dtype == torch.uint8 else "bf16"
+    scales = dict(q_scale=inp.q_scale, k_scale=inp.k_scale, v_scale=inp.v_scale)
     refs = oracle.prefill_varlen(inp.q, inp.cu_seqlens_q, inp.seqlens_k, inp.k_cache, inp.v_cache,
-                                 inp.block_table.numpy(), cfg.block, tau, with_output=False)
+                                 inp.block_table.numpy(), cfg.block, tau, with_output=False, **scales)
     row0 = 0
     for b, ref in enumerate(refs):
         L, P = int(inp.seqlens_k[b]), int(inp.prefix[b])
@@ -230,13 +234,11 @@ def check_paged(fp, inp, tau, sample_rows=None):
             assert cols[0] == 0 and cols[-1] == ref["i0"] + r % nq and np.all(np.diff(cols) > 0)
         ndiff, nband = compare_masks(keep, ref["keep"], ref["R"], tau)
         lo, hi = int(inp.cu_seqlens_q[b]), int(inp.cu_seqlens_q[b + 1])
-        kb = oracle.batch.gather_pages(inp.k_cache, inp.block_table[b].numpy(), L)
-        vb = oracle.batch.gather_pages(inp.v_cache, inp.block_table[b].numpy(), L)
+        qw, kw, vw, _ = oracle.varlen_sequence(inp.q, inp.cu_seqlens_q, inp.seqlens_k, inp.k_cache,
+                                               inp.v_cache, inp.block_table.numpy(), b, **scales)
         rows = None if sample_rows is None else sample_rows(Hkv, nq)
-        o_ref, lse_ref = oracle.attend(oracle.widen_bf16(inp.q[lo:hi]), oracle.widen_bf16(kb),
-                                       oracle.widen_bf16(vb), keep, ref["kbar"], ref["vbar"], c,
-                                       cfg.block, P, rows=rows)
-        mx, mean = compare_outputs(o[lo:hi].float().numpy(), o_ref, "bf16")
+        o_ref, lse_ref = oracle.attend(qw, kw, vw, keep, ref["kbar"], ref["vbar"], c, cfg.block, P, rows=rows)
+        mx, mean = compare_outputs(o[lo:hi].float().numpy(), o_ref, kind)
         okl = ~np.isnan(lse_ref)
         assert np.abs(lse[:, lo:hi].numpy()[okl] - lse_ref[okl]).max() <= LSE_TOL
         say(f"  seq {b}: L={L} P={P} kept {keep.sum() / max(1, (np.tril(np.ones((nq, nb)), ref['i0']).sum()) * Hkv):.2%} "
@@ -253,6 +255,18 @@ def test_paged_varlen_small(fp, page, block):
     L, P = synth.paged_lengths(cfg)
     P[0] = 0                                    # one sequence without a cached prefix
     say(f"paged varlen page={page} block={block}: L={L.tolist()} P={P.tolist()}")
+    check_paged(fp, synth.gen_paged(cfg, (L, P)), cfg.tau)
+
+
+@pytest.mark.parametrize("page,block", [(64, 128), (32, 64), (256, 128)])
+def test_paged_varlen_small_fp8(fp, page, block):
+    """fp8-e4m3 codes in the paged cache and packed queries, one scale per 128
+    positions of each sequence (cached prefixes start mid-block)."""
+    cfg = synth.config(5, Hq=8, Hkv=2, n_seqs=4, len_range=(300, 3500), page_size=page, block=block, tau=2.0,
+                       dtype="fp8", seed=15)
+    L, P = synth.paged_lengths(cfg)
+    P[1] = 0
+    say(f"paged varlen fp8 page={page} block={block}: L={L.tolist()} P={P.tolist()}")
     check_paged(fp, synth.gen_paged(cfg, (L, P)), cfg.tau)
 
 
@@ -295,6 +309,24 @@ def test_paged_equals_contiguous(fp, L, page):
     o, lse, rp, ci = run_paged(fp, inp, cfg.tau)
     k, v = synth.unpage(inp, 0)
     fixed = synth.FixedInputs(cfg, inp.q[None], k[None], v[None])
+    out = run_fixed(fp, fixed, cfg.tau, cfg.block)
+    assert np.array_equal(rp, out["row_ptr"].numpy())
+    assert torch.equal(o, out["o"][0])
+    assert torch.equal(lse, out["lse"][0])
+
+
+def test_paged_fp8_equals_contiguous_fp8(fp):
+    """The same fp8 codes and scales through the paged entry point (shuffled
+    64-token pages) and the fixed-shape one: bit-identical results."""
+    L = 5000 + 37
+    cfg = synth.config(5, Hq=8, Hkv=2, n_seqs=1, tau=2.0, dtype="fp8")
+    say(f"paged fp8 == contiguous fp8: L={L}")
+    inp = synth.gen_paged(cfg, (np.array([L]), np.array([0])))
+    o, lse, rp, ci = run_paged(fp, inp, cfg.tau)
+    k, v = synth.unpage(inp, 0)
+    nsb = -(-L // 128)
+    fixed = synth.FixedInputs(cfg, inp.q[None], k[None], v[None], inp.q_scale[:, :, :nsb].contiguous(),
+                              inp.k_scale[:, :, :nsb].contiguous(), inp.v_scale[:, :, :nsb].contiguous())
     out = run_fixed(fp, fixed, cfg.tau, cfg.block)
     assert np.array_equal(rp, out["row_ptr"].numpy())
     assert torch.equal(o, out["o"][0])

@@ -399,3 +399,19 @@ def test_flop_counts(P, L, B):
         keep[:, il, :i0 + il + 1] = True
     assert oracle.kept_flops(keep, P, L, B, d, Hq // Hkv) == dense
     assert oracle.correction_flops(keep, P, L, B, d, Hq // Hkv) == 0
+
+
+def test_widen_fp8_position_offset():
+    """Rows that start at position pos0 take the scales of their own
+    128-position blocks: widening rows [P, T) with pos0 = P equals rows
+    [P, T) of the widening from position 0, and each value is code * scale."""
+    rng = np.random.default_rng(5)
+    T, H, d, P = 300, 2, 4, 77
+    codes = rng.integers(0, 256, size=(T, H, d), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0                      # no NaN codes
+    scales = rng.uniform(0.5, 2.0, size=(H, 3)).astype(np.float32)
+    full = oracle.widen_fp8(codes, scales)
+    part = oracle.widen_fp8(codes[P:], scales, pos0=P)
+    assert np.array_equal(part, full[P:])
+    t, h, e = 200, 1, 3                                    # position 200 lies in block 1
+    assert full[t, h, e] == oracle.decode_e4m3(codes[t:t + 1, h:h + 1, e:e + 1])[0, 0, 0] * np.float64(scales[h, 1])
