@@ -88,26 +88,29 @@ def varlen_flops(rp, ci, L, P, B, G, d, Hkv):
     return 4.0 * d * G * kept, 4.0 * d * G * corr, dense
 
 
-def time_paged(fp, N, steps, warmup):
+def time_paged(fp, N, steps, warmup, dtype="bf16"):
     """The paged varlen entry point (all stages in one call) on the 8-sequence
-    batch of 4K-64K tokens with cached prefixes and 64-token pages."""
+    batch of 4K-64K tokens with cached prefixes and 64-token pages; fp8: the
+    same batch as E4M3FN codes with one scale per 128 positions."""
     import torch
     import synth
-    cfg = synth.config(5)
+    cfg = synth.config(5, dtype=dtype)
     inp = synth.gen_paged(cfg)
     dev = torch.device("cuda:0")
     q, kc, vc, bt = inp.q.to(dev), inp.k_cache.to(dev), inp.v_cache.to(dev), inp.block_table.to(dev)
+    sc = {n: None if t is None else t.to(dev)
+          for n, t in (("q_scale", inp.q_scale), ("k_scale", inp.k_scale), ("v_scale", inp.v_scale))}
     vp = fp.make_varlen_problem(q, inp.cu_seqlens_q, inp.seqlens_k, kc, bt, cfg.block)
     ws = torch.empty(vp.ws_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
-        out = fp.fp_sparse_prefill_paged(vp, q, kc, vc, bt, cfg.tau, workspace=ws)
+        out = fp.fp_sparse_prefill_paged(vp, q, kc, vc, bt, cfg.tau, workspace=ws, **sc)
     torch.cuda.synchronize()
     ts = []
     for _ in range(steps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        out = fp.fp_sparse_prefill_paged(vp, q, kc, vc, bt, cfg.tau, workspace=ws)
+        out = fp.fp_sparse_prefill_paged(vp, q, kc, vc, bt, cfg.tau, workspace=ws, **sc)
         e1.record(stream)
         ts.append((e0, e1))
     torch.cuda.synchronize()
@@ -125,9 +128,9 @@ def time_paged(fp, N, steps, warmup):
            "dense_equiv_tflops": round(dense / (t * 1e-3) / 1e12, 2),
            "kept_fraction": round(len(ci[:rp[-1]]) / nblk, 5),
            "kept_tflops_whole_call": round(kept / (t * 1e-3) / 1e12, 2),
-           "mfma_util_kept_whole_call": round(kept / (t * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4),
+           "mfma_util_kept_whole_call": round(kept / (t * 1e-3) / 1e12 / PEAK_TFLOPS[dtype], 4),
            "correction_tflop": round(corr / 1e12, 3)}
-    del q, kc, vc, bt, ws, out
+    del q, kc, vc, bt, ws, out, sc
     torch.cuda.empty_cache()
     return res
 
@@ -482,10 +485,13 @@ def main():
                                "mfma_util_kept": round(r["attn_kept_tflops"] / PEAK_TFLOPS["bf16"], 4),
                                "ms_per_layer_graph_replay": round(graph_replay_ms(fp, ci_inp, c.tau), 4)}
             log(f"config {cid}: {json.dumps(configs[c.name])}")
-    paged = None
+    paged = paged8 = None
     if not args.no_paged:
         paged = time_paged(fp, N, 5, 1)
         log(f"paged varlen: {json.dumps(paged)}")
+        if not args.no_fp8:
+            paged8 = time_paged(fp, N, 5, 1, "fp8")
+            log(f"paged varlen fp8: {json.dumps(paged8)}")
     sweep, dense = {}, None
     if not args.no_sweep:
         for tau in (2.0, 6.0, 8.0):
@@ -550,6 +556,8 @@ def main():
         line["other_configs_bf16"] = configs
     if paged is not None:
         line["paged_varlen_bf16"] = paged
+    if paged8:
+        line["paged_varlen_fp8"] = paged8
     if sweep:
         line["tau_sweep_bf16"] = sweep
     if dense is not None:

@@ -104,20 +104,26 @@ def test_config4_fp8_full(fp, cfg3_inputs):
     run_and_check(fp, cfg3_inputs["fp8"], 4.0, "fp8", 10)
 
 
-def test_config5_paged_full(fp):
-    cfg = synth.config(5)
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_config5_paged_full(fp, dtype):
+    """Config 5 in bf16, and the same batch as fp8-e4m3 codes with per-sequence
+    scales (one per 128 positions)."""
+    cfg = synth.config(5, dtype=dtype)
     inp = synth.gen_paged(cfg)
-    say(f"config 5: L={inp.seqlens_k.tolist()} P={inp.prefix.tolist()}")
+    say(f"config 5 {dtype}: L={inp.seqlens_k.tolist()} P={inp.prefix.tolist()}")
     dev = torch.device("cuda:0")
     q, kc, vc, bt = inp.q.to(dev), inp.k_cache.to(dev), inp.v_cache.to(dev), inp.block_table.to(dev)
+    sc = [None if t is None else t.to(dev) for t in (inp.q_scale, inp.k_scale, inp.v_scale)]
     vp = fp.make_varlen_problem(q, inp.cu_seqlens_q, inp.seqlens_k, kc, bt, cfg.block)
-    o, lse, rp, ci = fp.fp_sparse_prefill_paged(vp, q, kc, vc, bt, cfg.tau)
+    o, lse, rp, ci = fp.fp_sparse_prefill_paged(vp, q, kc, vc, bt, cfg.tau, q_scale=sc[0], k_scale=sc[1],
+                                                v_scale=sc[2])
     torch.cuda.synchronize()
     o, lse, rp, ci = o.float().cpu().numpy(), lse.cpu().numpy(), rp.cpu().numpy(), ci.cpu().numpy()
     assert np.isfinite(o).all() and np.isfinite(lse).all()
     c = 1 / math.sqrt(128)
+    scales = dict(q_scale=inp.q_scale, k_scale=inp.k_scale, v_scale=inp.v_scale)
     refs = oracle.prefill_varlen(inp.q, inp.cu_seqlens_q, inp.seqlens_k, inp.k_cache, inp.v_cache,
-                                 inp.block_table.numpy(), cfg.block, cfg.tau, with_output=False)
+                                 inp.block_table.numpy(), cfg.block, cfg.tau, with_output=False, **scales)
     row0 = 0
     for b, ref in enumerate(refs):
         L, P = int(inp.seqlens_k[b]), int(inp.prefix[b])
@@ -125,13 +131,11 @@ def test_config5_paged_full(fp):
         keep = csr_to_keep(rp, ci, row0, Hkv, nq, nb)
         ndiff, nband = compare_masks(keep, ref["keep"], ref["R"], cfg.tau)
         lo, hi = int(inp.cu_seqlens_q[b]), int(inp.cu_seqlens_q[b + 1])
-        kb = oracle.batch.gather_pages(inp.k_cache, inp.block_table[b].numpy(), L)
-        vb = oracle.batch.gather_pages(inp.v_cache, inp.block_table[b].numpy(), L)
+        qw, kw, vw, _ = oracle.varlen_sequence(inp.q, inp.cu_seqlens_q, inp.seqlens_k, inp.k_cache,
+                                               inp.v_cache, inp.block_table.numpy(), b, **scales)
         rows = sample_rows(Hkv, nq, 4)
-        o_ref, lse_ref = oracle.attend(oracle.widen_bf16(inp.q[lo:hi]), oracle.widen_bf16(kb),
-                                       oracle.widen_bf16(vb), keep, ref["kbar"], ref["vbar"], c,
-                                       cfg.block, P, rows=rows)
-        mx, mean = compare_outputs(o[lo:hi], o_ref, "bf16")
+        o_ref, lse_ref = oracle.attend(qw, kw, vw, keep, ref["kbar"], ref["vbar"], c, cfg.block, P, rows=rows)
+        mx, mean = compare_outputs(o[lo:hi], o_ref, dtype)
         okl = ~np.isnan(lse_ref)
         assert np.abs(lse[:, lo:hi][okl] - lse_ref[okl]).max() <= LSE_TOL
         say(f"  seq {b}: L={L} P={P} mask diffs {ndiff} (band {nband}) max|err| {mx:.2e} mean {mean:.2e}")
