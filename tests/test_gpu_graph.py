@@ -67,27 +67,30 @@ def test_fixed_path_graph_replays(fp):
     say("fixed path: 4 graph replays bit-identical to eager runs")
 
 
-def test_paged_path_graph_replays(fp):
-    cfg = synth.config(5, Hq=8, Hkv=2, n_seqs=3, len_range=(300, 3000), tau=2.0)
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_paged_path_graph_replays(fp, dtype):
+    cfg = synth.config(5, Hq=8, Hkv=2, n_seqs=3, len_range=(300, 3000), tau=2.0, dtype=dtype)
     L, P = synth.paged_lengths(cfg)
     inp = synth.gen_paged(cfg, (L, P))
     dev = torch.device("cuda:0")
     q, kc, vc, bt = inp.q.to(dev), inp.k_cache.to(dev), inp.v_cache.to(dev), inp.block_table.to(dev)
+    sc = {n: None if t is None else t.to(dev)
+          for n, t in (("q_scale", inp.q_scale), ("k_scale", inp.k_scale), ("v_scale", inp.v_scale))}
     vp = fp.make_varlen_problem(q, inp.cu_seqlens_q, inp.seqlens_k, kc, bt, cfg.block)
     ws = torch.empty(vp.ws_bytes, dtype=torch.uint8, device=dev)
-    o0, lse0, rp0, ci0 = fp.fp_sparse_prefill_paged(vp, q, kc, vc, bt, cfg.tau, workspace=ws)
+    o0, lse0, rp0, ci0 = fp.fp_sparse_prefill_paged(vp, q, kc, vc, bt, cfg.tau, workspace=ws, **sc)
     torch.cuda.synchronize()
     n = int(rp0[-1])
     ref = [t.clone() for t in (o0, lse0, rp0, ci0[:n])]
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        fp.fp_sparse_prefill_paged(vp, q, kc, vc, bt, cfg.tau, workspace=ws)
+        fp.fp_sparse_prefill_paged(vp, q, kc, vc, bt, cfg.tau, workspace=ws, **sc)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        o, lse, rp, ci = fp.fp_sparse_prefill_paged(vp, q, kc, vc, bt, cfg.tau, workspace=ws)
+        o, lse, rp, ci = fp.fp_sparse_prefill_paged(vp, q, kc, vc, bt, cfg.tau, workspace=ws, **sc)
     for r in range(3):
         o.zero_()
         lse.fill_(float("nan"))
@@ -96,4 +99,4 @@ def test_paged_path_graph_replays(fp):
         torch.cuda.synchronize()
         for got, want in zip((o, lse, rp, ci[:n]), ref):
             assert torch.equal(got, want), f"paged replay {r} differs"
-    say("paged path: 3 graph replays bit-identical to the eager run")
+    say(f"paged path ({dtype}): 3 graph replays bit-identical to the eager run")
