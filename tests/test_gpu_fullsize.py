@@ -151,3 +151,39 @@ def test_largest_sequence_single_head(fp):
     cfg = synth.config(2, S=16384 * 128, Hq=1, Hkv=1, tau=1.0, seed=77)
     say("largest sequence: S=2097152, 1/1 heads")
     run_and_check(fp, synth.gen_fixed(cfg), cfg.tau, "bf16", 6)
+
+
+def test_batch_of_two_schedule_groups(fp):
+    """Two 65536-token sequences, 32/8 heads: 512 MiB of K/V, so the schedule
+    has four groups of four (sequence, KV head) pairs and the groups cross the
+    sequence boundary. The schedule, the kept lists of every row and sampled
+    outputs of both sequences are checked."""
+    cfg = synth.config(3, S=65536, batch=2, tau=4.0, seed=21)
+    inp = synth.gen_fixed(cfg)
+    say("batch 2 x S=65536, 32/8 heads")
+    dev = torch.device("cuda:0")
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    out = fp.sparse_prefill(q, k, v, cfg.block, cfg.tau)
+    torch.cuda.synchronize()
+    o = out["o"].float().cpu().numpy()
+    lse = out["lse"].cpu().numpy()
+    rp, ci = out["row_ptr"].cpu().numpy(), out["col_idx"].cpu().numpy()
+    sched = out["sched"].cpu().numpy()
+    del q, k, v, out
+    torch.cuda.empty_cache()
+    nb, Hkv = cfg.S // cfg.block, cfg.Hkv
+    groups = fixed_sched_groups(2, Hkv, nb, cfg.block, 2)
+    assert groups.max() == 3 and groups[Hkv * nb - 1] == 1 and groups[Hkv * nb] == 2
+    check_sched(sched, np.diff(rp), groups)
+    c = 1 / math.sqrt(128)
+    for b in range(2):
+        qn, kn, vn = (oracle.widen_bf16(t[b]) for t in (inp.q, inp.k, inp.v))
+        ref = oracle.prefill(qn, kn, vn, cfg.block, cfg.tau, c, with_output=False)
+        keep = csr_to_keep(rp, ci, b * Hkv * nb, Hkv, nb, nb)
+        ndiff, nband = compare_masks(keep, ref["keep"], ref["R"], cfg.tau)
+        o_ref, lse_ref = oracle.attend(qn, kn, vn, keep, ref["kbar"], ref["vbar"], c, cfg.block, 0,
+                                       rows=sample_rows(Hkv, nb, 4))
+        mx, mean = compare_outputs(o[b], o_ref, "bf16")
+        okl = ~np.isnan(lse_ref)
+        assert np.abs(lse[b][okl] - lse_ref[okl]).max() <= LSE_TOL
+        say(f"  seq {b}: mask diffs {ndiff} (band {nband}) max|err| {mx:.2e} mean {mean:.2e}")
