@@ -21,8 +21,11 @@ def nblocks(L: int, B: int) -> int:
 
 
 def query_blocks(P: int, L: int, B: int) -> Tuple[int, int]:
-    """(first, count) of the query blocks holding present rows [P, L)."""
+    """(first, count) of the query blocks holding present rows [P, L); none
+    when there are no present rows (P = L: the whole sequence is cached)."""
     i0 = P // B
+    if P >= L:
+        return i0, 0
     i1 = (L - 1) // B
     return i0, i1 - i0 + 1
 

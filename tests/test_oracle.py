@@ -415,3 +415,16 @@ def test_widen_fp8_position_offset():
     assert np.array_equal(part, full[P:])
     t, h, e = 200, 1, 3                                    # position 200 lies in block 1
     assert full[t, h, e] == oracle.decode_e4m3(codes[t:t + 1, h:h + 1, e:e + 1])[0, 0, 0] * np.float64(scales[h, 1])
+
+
+def test_query_blocks_without_present_rows():
+    """Query blocks are the blocks holding present rows: a prefix that ends
+    mid-block starts in that block, and a fully cached sequence has none (its
+    prefill has no rows, no kept lists and no outputs)."""
+    assert oracle.query_blocks(300, 1000, 128) == (2, 6)
+    assert oracle.query_blocks(256, 257, 128) == (2, 1)
+    assert oracle.query_blocks(700, 700, 128)[1] == 0
+    rng = np.random.default_rng(1)
+    k = rng.standard_normal((700, 1, 8))
+    ref = prefill(np.zeros((0, 2, 8)), k, k, 128, 1.0, P=700)
+    assert ref["keep"].shape == (1, 0, 6) and ref["o"].shape[0] == 0
