@@ -228,6 +228,9 @@ def check_paged(fp, inp, tau, sample_rows=None):
     for b, ref in enumerate(refs):
         L, P = int(inp.seqlens_k[b]), int(inp.prefix[b])
         Hkv, nq, nb = ref["keep"].shape
+        if nq == 0:                             # no new rows: no kept-list rows, no outputs
+            assert L == P
+            continue
         keep = csr_to_keep(rp, ci, row0, Hkv, nq, nb)
         for r in range(Hkv * nq):
             cols = ci[rp[row0 + r]:rp[row0 + r + 1]]
@@ -255,6 +258,18 @@ def test_paged_varlen_small(fp, page, block):
     L, P = synth.paged_lengths(cfg)
     P[0] = 0                                    # one sequence without a cached prefix
     say(f"paged varlen page={page} block={block}: L={L.tolist()} P={P.tolist()}")
+    check_paged(fp, synth.gen_paged(cfg, (L, P)), cfg.tau)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_paged_edge_sequences(fp, dtype):
+    """A batch holding a sequence with no new rows (all cached), a one-token
+    sequence, a cached prefix that ends on a block boundary, one that leaves a
+    single new row, and a sequence one token past a block boundary."""
+    cfg = synth.config(5, Hq=8, Hkv=2, n_seqs=5, tau=2.0, dtype=dtype, page_size=64)
+    L = np.array([700, 1, 1024 + 300, 900, 2049])
+    P = np.array([700, 0, 1024, 899, 0])
+    say(f"paged edge sequences {dtype}: L={L.tolist()} P={P.tolist()}")
     check_paged(fp, synth.gen_paged(cfg, (L, P)), cfg.tau)
 
 
