@@ -103,6 +103,124 @@ __global__ __launch_bounds__(256) void pool_kernel(Geo geo, PoolArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// E1 for fp8 codes: one workgroup per (block, group of HG = 32 heads).
+// blockIdx.y enumerates the head groups of Q, then of K, then of V. Thread pi
+// of a token lane owns 16-byte chunk pi % 8 of head pi / 8 of the group, so
+// each step reads the group's rows of one token: one contiguous stretch in
+// the usual [token, head, dim] layout. Groups with fewer chunks than threads
+// split the tokens over TL lanes and sum them through LDS at the end. NLD
+// tokens per lane are loaded before any is added. Measured: 14% faster than
+// the per-head kernel above for fp8 codes (16-byte chunks hold 16 codes, so a
+// per-head workgroup reads only 128 bytes per token); slower for bf16.
+// ---------------------------------------------------------------------------
+template <bool PAGED, typename Geo>
+__global__ __launch_bounds__(256) void pool_rows_fp8_kernel(Geo geo, PoolArgs a) {
+    constexpr bool FP8 = true;
+    constexpr int EPC = FP8 ? 16 : 8;        // elements per 16-byte chunk
+    constexpr int CHR = D / EPC;             // chunks per head row
+    constexpr int HG = 256 / CHR;            // heads per group
+    constexpr int NLD = 8;                   // tokens in flight per lane
+    __shared__ float red[256 * EPC];
+
+    const int gq = cdiv(a.Hq, HG), gk = cdiv(a.Hkv, HG);
+    const int y = blockIdx.y;
+    const bool isq = y < gq;
+    const bool isv = !isq && y >= gq + gk;
+    const int H = isq ? a.Hq : a.Hkv;
+    const int h0 = (isq ? y : (isv ? y - gq - gk : y - gq)) * HG;
+    const int pairs = min(HG, H - h0) * CHR;
+    int tpt = CHR;                           // threads per token lane: a power of two >= pairs
+    while (tpt < pairs) tpt <<= 1;
+    const int TL = 256 / tpt;
+    const int tid = threadIdx.x;
+    const int tl = tid / tpt, pi = tid % tpt;
+    const bool act = pi < pairs;
+    const int head = h0 + (act ? pi / CHR : 0), ch = pi % CHR;
+
+    const int u = blockIdx.x;
+    if (isq ? (u >= a.total_qblocks) : (u >= a.total_kblocks)) return;
+    const int b = isq ? geo.seq_of_qblock(u) : geo.seq_of_kblock(u);
+    const SeqDesc s = geo.seq(b);
+    const int B = a.blk;
+    int lo, hi, blk;
+    if (isq) {
+        blk = u - s.qb0;                      // local query block
+        const int i = s.i0 + blk;
+        lo = max(i * B, s.P);
+        hi = min((i + 1) * B, s.L);
+    } else {
+        blk = u - s.kb0;
+        lo = blk * B;
+        hi = min((blk + 1) * B, s.L);
+    }
+
+    float acc[EPC];
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
+
+    const char* base = (const char*)(isq ? a.q : (isv ? a.v : a.k));
+    const ScaleAddr& sa = isq ? a.qs : (isv ? a.vs : a.ks);
+    const KVAddr& kva = isv ? a.va : a.ka;
+    constexpr int ESZ = FP8 ? 1 : 2;
+
+    for (int t0 = lo + tl; t0 < hi; t0 += NLD * TL) {
+        uint4 wv[NLD];
+#pragma unroll
+        for (int k = 0; k < NLD; ++k) {
+            const int t = min(t0 + k * TL, hi - 1);
+            const long long off = isq ? a.qa.off(b, s, t, head) : kva.template off<PAGED>(b, t, head);
+            wv[k] = act ? *(const uint4*)(base + (off + (long long)ch * EPC) * ESZ) : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int k = 0; k < NLD; ++k) {
+            if (t0 + k * TL >= hi) break;
+            const uint32_t ws[4] = {wv[k].x, wv[k].y, wv[k].z, wv[k].w};
+            if (FP8) {
+                // codes widened by the hardware converter (exact for E4M3FN);
+                // the block's single scale is applied once at the end
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const auto lo2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[e], false);
+                    const auto hi2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[e], true);
+                    acc[4 * e] += lo2[0];
+                    acc[4 * e + 1] += lo2[1];
+                    acc[4 * e + 2] += hi2[0];
+                    acc[4 * e + 3] += hi2[1];
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    acc[2 * e] += bf16_lo(ws[e]);
+                    acc[2 * e + 1] += bf16_hi(ws[e]);
+                }
+            }
+        }
+    }
+    if (TL > 1) {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) red[tid * EPC + e] = acc[e];
+        __syncthreads();
+        if (tl == 0) {
+            for (int l = 1; l < TL; ++l)
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) acc[e] += red[(l * tpt + pi) * EPC + e];
+        }
+    }
+    if (tl != 0 || !act) return;
+    // fp8: one scale per 128 tokens, and a block (64 or 128 tokens, aligned)
+    // never spans two
+    const float sc = FP8 ? sa.at(b, head, lo) : 1.f;
+    const float n = (float)(hi - lo);
+    float* dst = isq ? a.qbar + qbar_row(s, a.Hq, head, blk) * D
+                     : (isv ? a.vbar : a.kbar) + kbar_row(s, a.Hkv, head, blk) * D;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[e] = (FP8 ? acc[e] * sc : acc[e]) / n;
+#pragma unroll
+    for (int e = 0; e < EPC; e += 4)
+        *(float4*)(dst + ch * EPC + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+}
+
+// ---------------------------------------------------------------------------
 // E2: 64 x 64 tiles of (query block, key block) per workgroup, one query head
 // per blockIdx.y. Tiles entirely above the diagonal only write -inf. The
 // products run on fp32 MFMA from LDS; the pooled rows stay L2-resident.
@@ -187,11 +305,17 @@ __global__ __launch_bounds__(256) void scores_kernel(Geo geo, ScoreArgs a) {
 // ---------------------------------------------------------------------------
 template <typename Geo>
 static hipError_t pool_dispatch(const Geo& geo, const PoolArgs& a, hipStream_t st) {
-    dim3 grid(max(a.total_qblocks, a.total_kblocks), a.Hq + 2 * a.Hkv);
     // contiguous K/V come with the fixed geometry, the paged cache with the sequence table
     if (a.paged != Geo::PAGED_KV) return hipErrorInvalidValue;
-    if (a.fp8) pool_kernel<true, Geo::PAGED_KV, Geo><<<grid, 256, 0, st>>>(geo, a);
-    else pool_kernel<false, Geo::PAGED_KV, Geo><<<grid, 256, 0, st>>>(geo, a);
+    const int nb = max(a.total_qblocks, a.total_kblocks);
+    if (a.fp8) {
+        constexpr int HG = 32;                  // heads per workgroup of pool_rows_fp8_kernel
+        const dim3 grid(nb, cdiv(a.Hq, HG) + 2 * cdiv(a.Hkv, HG));
+        pool_rows_fp8_kernel<Geo::PAGED_KV, Geo><<<grid, 256, 0, st>>>(geo, a);
+    } else {
+        const dim3 grid(nb, a.Hq + 2 * a.Hkv);
+        pool_kernel<false, Geo::PAGED_KV, Geo><<<grid, 256, 0, st>>>(geo, a);
+    }
     return hipGetLastError();
 }
 
