@@ -209,6 +209,11 @@ def fp_sparse_prefill_paged(vp: VarlenProblem, q, k_cache, v_cache, block_table,
     """E1-E6 on a paged varlen batch -> (o, lse, row_ptr, col_idx). fp8
     (uint8 E4M3FN codes) takes fp32 scales [num_seqs, H, nsb], one per 128
     positions of each sequence."""
+    if v_cache.stride() != k_cache.stride() or v_cache.dtype != k_cache.dtype or q.dtype != k_cache.dtype:
+        raise ValueError("k_cache and v_cache must share strides and dtype with each other and with q")
+    kv = (k_cache.stride(0), k_cache.stride(1), k_cache.stride(2))
+    if tuple(vp.c.kv_stride) != kv:
+        raise ValueError(f"cache strides {kv} differ from the problem's {tuple(vp.c.kv_stride)}")
     dev = q.device
     i32 = dict(dtype=torch.int32, device=dev)
     row_ptr = torch.empty(vp.rows + 1, **i32)

@@ -251,3 +251,23 @@ def test_out_dtype_validation():
     p.o_stride[1] = 8 * 128 + 2                           # 8-byte aligned fp32 rows only
     assert lib.fp_num_rows(ctypes.byref(p)) == N.FP_ERR_INVALID
 
+
+
+def test_binding_rejects_mismatched_cache_views():
+    """The Python binding checks that V shares K's strides and dtype and that
+    both match the strides the problem was sized with, before any device call."""
+    import torch
+    import block_sparse_long_estimate_amd as fp
+    Hkv, page, pages = 2, 16, 8
+    q = torch.zeros((40, 4, 128), dtype=torch.bfloat16)
+    cache = torch.zeros((pages, 2, page, Hkv, 128), dtype=torch.bfloat16)
+    kc, vc = cache[:, 0], cache[:, 1]
+    bt = torch.arange(pages, dtype=torch.int32).reshape(2, 4)
+    cu, lk = np.array([0, 20, 40], dtype=np.int32), np.array([30, 50], dtype=np.int32)
+    vp = fp.make_varlen_problem(q, cu, lk, kc, bt, 64)
+    with pytest.raises(ValueError, match="share strides"):
+        fp.fp_sparse_prefill_paged(vp, q, kc, vc.contiguous(), bt, 1.0)
+    with pytest.raises(ValueError, match="share strides"):
+        fp.fp_sparse_prefill_paged(vp, q, kc, vc.float(), bt, 1.0)
+    with pytest.raises(ValueError, match="differ from the problem"):
+        fp.fp_sparse_prefill_paged(vp, q, kc.contiguous(), vc.contiguous(), bt, 1.0)

@@ -330,6 +330,30 @@ def test_paged_equals_contiguous(fp, L, page):
     assert torch.equal(lse, out["lse"][0])
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_paged_interleaved_kv_cache(fp, dtype):
+    """K and V pages interleaved in one device tensor [pages, 2, page, Hkv, 128]
+    (k_cache = cache[:, 0], v_cache = cache[:, 1], page stride twice a page):
+    bit-identical to separate contiguous caches."""
+    cfg = synth.config(5, Hq=8, Hkv=2, n_seqs=3, len_range=(300, 3000), tau=2.0, dtype=dtype)
+    inp = synth.gen_paged(cfg)
+    o, lse, rp, ci = run_paged(fp, inp, cfg.tau)
+    dev = torch.device("cuda:0")
+    cache = torch.stack([inp.k_cache, inp.v_cache], dim=1).to(dev)
+    kc, vc = cache[:, 0], cache[:, 1]
+    assert kc.stride(0) == 2 * inp.k_cache.stride(0) and kc.data_ptr() != vc.data_ptr()
+    q, bt = inp.q.to(dev), inp.block_table.to(dev)
+    sc = {n: None if t is None else t.to(dev)
+          for n, t in (("q_scale", inp.q_scale), ("k_scale", inp.k_scale), ("v_scale", inp.v_scale))}
+    vp = fp.make_varlen_problem(q, inp.cu_seqlens_q, inp.seqlens_k, kc, bt, cfg.block)
+    o2, lse2, rp2, ci2 = fp.fp_sparse_prefill_paged(vp, q, kc, vc, bt, cfg.tau, **sc)
+    torch.cuda.synchronize()
+    rp2, ci2 = rp2.cpu().numpy(), ci2.cpu().numpy()
+    assert np.array_equal(rp, rp2) and np.array_equal(ci[:rp[-1]], ci2[:rp[-1]])
+    assert torch.equal(o, o2.cpu()) and torch.equal(lse, lse2.cpu())
+    say(f"paged ({dtype}): interleaved K/V cache views bit-identical to separate caches")
+
+
 def test_paged_fp8_equals_contiguous_fp8(fp):
     """The same fp8 codes and scales through the paged entry point (shuffled
     64-token pages) and the fixed-shape one: bit-identical results."""
