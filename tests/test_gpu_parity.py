@@ -273,6 +273,18 @@ def test_paged_edge_sequences(fp, dtype):
     check_paged(fp, synth.gen_paged(cfg, (L, P)), cfg.tau)
 
 
+@pytest.mark.parametrize("Hq,Hkv,block", [(8, 8, 128), (6, 2, 128), (16, 1, 64), (6, 2, 64)])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_paged_gqa_ratios(fp, Hq, Hkv, block, dtype):
+    """The paged path at G = 1, 3 and 16: with G = 3 a query block packs 384
+    (block 128) or 192 (block 64) rows, so a slice is left partly empty."""
+    cfg = synth.config(5, Hq=Hq, Hkv=Hkv, n_seqs=3, len_range=(200, 2500), page_size=32, block=block, tau=2.0,
+                       dtype=dtype, seed=17 + Hq + Hkv)
+    L, P = synth.paged_lengths(cfg)
+    say(f"paged GQA {Hq}/{Hkv} block={block} {dtype}: L={L.tolist()} P={P.tolist()}")
+    check_paged(fp, synth.gen_paged(cfg, (L, P)), cfg.tau)
+
+
 @pytest.mark.parametrize("page,block", [(64, 128), (32, 64), (256, 128)])
 def test_paged_varlen_small_fp8(fp, page, block):
     """fp8-e4m3 codes in the paged cache and packed queries, one scale per 128

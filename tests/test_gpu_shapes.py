@@ -27,6 +27,17 @@ def test_gqa_ratios(fp, Hq, Hkv, dtype):
     check_fixed(fp, inp, 3.0, 128, kind=dtype)
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(6, 2), (16, 1)])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_gqa_ratios_block64(fp, Hq, Hkv, dtype):
+    """64-token blocks at G = 3 (192 packed rows: one slice, a quarter empty)
+    and G = 16 (1024 packed rows: four slices)."""
+    cfg = synth.config(2, S=1536 + 45, Hq=Hq, Hkv=Hkv, block=64, seed=50 + Hq + Hkv, dtype=dtype)
+    say(f"GQA {Hq}/{Hkv} block 64 {dtype} S={cfg.S}")
+    inp = synth.gen_fixed(cfg)
+    check_fixed(fp, inp, 3.0, 64, kind=dtype)
+
+
 @pytest.mark.parametrize("S,block", [(1, 128), (5, 128), (127, 128), (128, 128), (129, 128),
                                      (1, 64), (63, 64), (65, 64), (300, 64)])
 def test_tiny_and_ragged_lengths(fp, S, block):
