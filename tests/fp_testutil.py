@@ -37,7 +37,8 @@ def check_csr_wellformed(row_ptr: np.ndarray, col_idx: np.ndarray, i_of_row) -> 
 
 def compare_masks(gpu_keep: np.ndarray, ref_keep: np.ndarray, R: np.ndarray, tau: float):
     diff = gpu_keep != ref_keep
-    band = np.abs(R + tau) <= BAND
+    with np.errstate(invalid="ignore"):         # R = -inf (future) with tau = +inf: NaN, not in the band
+        band = np.abs(R + tau) <= BAND
     out_band = int((diff & ~band).sum())
     assert out_band == 0, f"{out_band} kept-block mismatches outside the threshold band"
     return int(diff.sum()), int(band.sum())
