@@ -15,7 +15,8 @@ HEADER = os.path.join(ROOT, "include", "fp_prefill.h")
 
 
 def header_functions():
-    text = open(HEADER).read()
+    with open(HEADER) as fh:
+        text = fh.read()
     return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z0-9_]+\s*\*?\s*(fp_[a-z_]+)\s*\(", text, re.M)))
 
 
