@@ -272,3 +272,21 @@ def test_binding_rejects_mismatched_cache_views():
         fp.fp_sparse_prefill_paged(vp, q, kc, vc.float(), bt, 1.0)
     with pytest.raises(ValueError, match="differ from the problem"):
         fp.fp_sparse_prefill_paged(vp, q, kc.contiguous(), vc.contiguous(), bt, 1.0)
+
+
+def test_plain_c_program_uses_the_abi(tmp_path):
+    """tests/c/abi_host.c: the header compiled as C99 (-Wall -Wextra -Werror),
+    linked against the in-tree library, sizing and argument checks called from C."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    assert gcc, "gcc is required for the C ABI check"
+    libdir = os.path.dirname(N.LIB_PATH)
+    exe = str(tmp_path / "abi_host")
+    cmd = [gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"),
+           os.path.join(ROOT, "tests", "c", "abi_host.c"), "-L", libdir, "-lfp_prefill",
+           f"-Wl,-rpath,{libdir}", "-lm", "-o", exe]
+    b = subprocess.run(cmd, capture_output=True, text=True, timeout=120)
+    assert b.returncode == 0, b.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
