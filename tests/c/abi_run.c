@@ -3,10 +3,17 @@
  * fp_block_scores -> fp_select_blocks -> fp_sparse_prefill, results copied
  * back and written as raw files for comparison with the Python binding.
  *
- *   abi_run DIR     reads DIR/meta.txt ("S Hq Hkv block tau") and DIR/q.bin,
- *                   k.bin, v.bin (bf16, contiguous [S, H, 128]); writes
- *                   DIR/o.bin (bf16 [S, Hq, 128]), lse.bin (fp32 [Hq, S]),
- *                   row_ptr.bin, col_idx.bin (int32, nnz entries), sched.bin.
+ *   abi_run DIR         reads DIR/meta.txt ("S Hq Hkv block tau") and DIR/q.bin,
+ *                       k.bin, v.bin (bf16, contiguous [S, H, 128]); writes
+ *                       DIR/o.bin (bf16 [S, Hq, 128]), lse.bin (fp32 [Hq, S]),
+ *                       row_ptr.bin, col_idx.bin (int32, nnz entries), sched.bin.
+ *   abi_run paged DIR   fp_sparse_prefill_paged on a bf16 paged batch: reads
+ *                       DIR/meta.txt ("num_seqs Hq Hkv block page_size n_pages
+ *                       max_pages tau"), cu_seqlens_q.bin, seqlens_k.bin (int32),
+ *                       q.bin (bf16 [sum q, Hq, 128]), k_cache.bin, v_cache.bin
+ *                       (bf16 [n_pages, page_size, Hkv, 128]), block_table.bin
+ *                       (int32 [num_seqs, max_pages]); writes o.bin, lse.bin
+ *                       (fp32 [Hq, sum q]), row_ptr.bin, col_idx.bin.
  * Prints "ok" and exits 0 on success; any error is printed and exits 1. */
 #include <stdio.h>
 #include <stdlib.h>
@@ -70,8 +77,84 @@ static void* device(size_t bytes) {
     return d;
 }
 
+static int run_paged(const char* dir) {
+    int nseq, Hq, Hkv, block, page, npages, maxp;
+    float tau;
+    FILE* mf = fopen(path(dir, "meta.txt"), "r");
+    if (!mf || fscanf(mf, "%d %d %d %d %d %d %d %f", &nseq, &Hq, &Hkv, &block, &page, &npages, &maxp, &tau) != 8) {
+        printf("bad meta.txt\n");
+        return 1;
+    }
+    fclose(mf);
+    int32_t* cu = (int32_t*)read_file(dir, "cu_seqlens_q.bin", (size_t)(nseq + 1) * 4);
+    int32_t* lk = (int32_t*)read_file(dir, "seqlens_k.bin", (size_t)nseq * 4);
+    const int64_t nq = cu[nseq];
+
+    fp_varlen_problem p;
+    memset(&p, 0, sizeof(p));
+    p.num_seqs = nseq;
+    p.num_q_heads = Hq;
+    p.num_kv_heads = Hkv;
+    p.head_dim = 128;
+    p.block = block;
+    p.page_size = page;
+    p.dtype = FP_DTYPE_BF16;
+    p.max_pages_per_seq = maxp;
+    p.q_stride[0] = Hq * 128; p.q_stride[1] = 128;
+    p.kv_stride[0] = (int64_t)page * Hkv * 128; p.kv_stride[1] = Hkv * 128; p.kv_stride[2] = 128;
+    p.o_stride[0] = Hq * 128; p.o_stride[1] = 128;
+    const int64_t rows = fp_varlen_num_rows(&p, cu, lk), cap = fp_varlen_max_nnz(&p, cu, lk);
+    const int64_t wsb = fp_varlen_workspace_size(&p, cu, lk);
+    if (rows < 0 || cap < 0 || wsb < 0) { printf("sizing: %s\n", fp_last_error()); return 1; }
+
+    const size_t qb = (size_t)nq * Hq * 128 * 2, cb = (size_t)npages * page * Hkv * 128 * 2;
+    const size_t btb = (size_t)nseq * maxp * 4;
+    void* hq = read_file(dir, "q.bin", qb);
+    void* hk = read_file(dir, "k_cache.bin", cb);
+    void* hv = read_file(dir, "v_cache.bin", cb);
+    void* hbt = read_file(dir, "block_table.bin", btb);
+    void* dq = to_device(hq, qb);
+    void* dk = to_device(hk, cb);
+    void* dv = to_device(hv, cb);
+    void* dbt = to_device(hbt, btb);
+    int32_t* row_ptr = (int32_t*)device((size_t)(rows + 1) * 4);
+    int32_t* col_idx = (int32_t*)device((size_t)(cap > 0 ? cap : 1) * 4);
+    void* o = device(qb);
+    float* lse = (float*)device((size_t)Hq * nq * 4);
+    void* ws = device((size_t)wsb);
+
+    hipStream_t st;
+    HIP_OK(hipStreamCreate(&st));
+    FP_OK_(fp_sparse_prefill_paged(&p, dq, cu, lk, dk, dv, (const int32_t*)dbt, NULL, NULL, NULL, tau, row_ptr,
+                                   col_idx, cap, o, lse, ws, (size_t)wsb, st));
+    HIP_OK(hipStreamSynchronize(st));
+
+    int32_t* h_rp = (int32_t*)malloc((size_t)(rows + 1) * 4);
+    HIP_OK(hipMemcpy(h_rp, row_ptr, (size_t)(rows + 1) * 4, hipMemcpyDeviceToHost));
+    const int32_t nnz = h_rp[rows];
+    if (nnz < rows || nnz > cap) { printf("bad nnz %d\n", nnz); return 1; }
+    int32_t* h_ci = (int32_t*)malloc((size_t)(nnz > 0 ? nnz : 1) * 4);
+    void* h_o = malloc(qb ? qb : 1);
+    float* h_lse = (float*)malloc((size_t)Hq * nq * 4 + 4);
+    HIP_OK(hipMemcpy(h_ci, col_idx, (size_t)nnz * 4, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(h_o, o, qb, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(h_lse, lse, (size_t)Hq * nq * 4, hipMemcpyDeviceToHost));
+    write_file(dir, "row_ptr.bin", h_rp, (size_t)(rows + 1) * 4);
+    write_file(dir, "col_idx.bin", h_ci, (size_t)nnz * 4);
+    write_file(dir, "o.bin", h_o, qb);
+    write_file(dir, "lse.bin", h_lse, (size_t)Hq * nq * 4);
+
+    HIP_OK(hipStreamDestroy(st));
+    void* bufs[] = {dq, dk, dv, dbt, row_ptr, col_idx, o, lse, ws};
+    for (size_t i = 0; i < sizeof(bufs) / sizeof(bufs[0]); ++i) HIP_OK(hipFree(bufs[i]));
+    free(cu); free(lk); free(hq); free(hk); free(hv); free(hbt); free(h_rp); free(h_ci); free(h_o); free(h_lse);
+    printf("ok nnz=%d\n", nnz);
+    return 0;
+}
+
 int main(int argc, char** argv) {
-    if (argc != 2) { printf("usage: abi_run DIR\n"); return 1; }
+    if (argc == 3 && strcmp(argv[1], "paged") == 0) return run_paged(argv[2]);
+    if (argc != 2) { printf("usage: abi_run DIR | abi_run paged DIR\n"); return 1; }
     const char* dir = argv[1];
     int S, Hq, Hkv, block;
     float tau;
