@@ -177,7 +177,10 @@ int64_t fp_varlen_workspace_size(const fp_varlen_problem* p, const int32_t* cu_s
  * [pages, page_size, Hkv, 128]; bf16, or E4M3FN codes when dtype is
  * FP_DTYPE_FP8_E4M3. block_table (device) int32 [num_seqs, max_pages_per_seq]
  * (token s of sequence b lives in page block_table[b][s / page_size], slot
- * s % page_size; the new chunk's keys must already be in the cache).
+ * s % page_size; the new chunk's keys must already be in the cache). Every
+ * entry a sequence uses (its first ceil(seqlens_k[b] / page_size)) must name
+ * a page of the caches: the library does not know the pool's size and does
+ * not check them; unused entries are never read.
  * q_scale, k_scale, v_scale (device, fp8 only, else NULL): fp32
  * [num_seqs, H, nsb] with nsb = ceil(max_pages_per_seq * page_size / 128),
  * one scale per 128 positions of each sequence (the query row at position t
