@@ -366,6 +366,31 @@ def test_paged_interleaved_kv_cache(fp, dtype):
     say(f"paged ({dtype}): interleaved K/V cache views bit-identical to separate caches")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_paged_unused_table_entries_not_read(fp, dtype):
+    """Block-table entries past a sequence's last page point at an extra page
+    of NaNs (a valid page id): results stay bit-identical, so no unused entry
+    is followed."""
+    cfg = synth.config(5, Hq=8, Hkv=2, n_seqs=3, len_range=(300, 3000), page_size=64, tau=2.0, dtype=dtype,
+                       seed=29)
+    inp = synth.gen_paged(cfg)
+    o, lse, rp, ci = run_paged(fp, inp, cfg.tau)
+    n_pages, page = inp.k_cache.shape[0], inp.k_cache.shape[1]
+    nan_page = torch.full_like(inp.k_cache[:1], 0x7F) if dtype == "fp8" else torch.full_like(inp.k_cache[:1],
+                                                                                               float("nan"))
+    kc, vc = torch.cat([inp.k_cache, nan_page]), torch.cat([inp.v_cache, nan_page])
+    bt = inp.block_table.clone()
+    for b, L in enumerate(inp.seqlens_k):
+        bt[b, -(-int(L) // page):] = n_pages
+    assert (bt == n_pages).any()
+    poisoned = synth.PagedInputs(inp.cfg, inp.q, kc, vc, bt, inp.cu_seqlens_q, inp.seqlens_k, inp.prefix, inp.meta,
+                                 inp.q_scale, inp.k_scale, inp.v_scale)
+    o2, lse2, rp2, ci2 = run_paged(fp, poisoned, cfg.tau)
+    assert np.array_equal(rp, rp2) and np.array_equal(ci[:rp[-1]], ci2[:rp[-1]])
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    say(f"paged ({dtype}): unused block-table entries pointing at a NaN page change nothing")
+
+
 def test_paged_fp8_equals_contiguous_fp8(fp):
     """The same fp8 codes and scales through the paged entry point (shuffled
     64-token pages) and the fixed-shape one: bit-identical results."""
