@@ -391,6 +391,36 @@ def test_paged_unused_table_entries_not_read(fp, dtype):
     say(f"paged ({dtype}): unused block-table entries pointing at a NaN page change nothing")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_paged_slots_past_sequence_end_not_read(fp, dtype):
+    """The slots of each sequence's last page past its length hold NaN (fp8:
+    NaN codes): results stay bit-identical."""
+    cfg = synth.config(5, Hq=8, Hkv=2, n_seqs=3, len_range=(300, 3000), page_size=64, tau=2.0, dtype=dtype,
+                       seed=31)
+    inp = synth.gen_paged(cfg)
+    o, lse, rp, ci = run_paged(fp, inp, cfg.tau)
+    page = inp.k_cache.shape[1]
+    kc, vc = inp.k_cache.clone(), inp.v_cache.clone()
+    poisoned_slots = 0
+    for b, L in enumerate(inp.seqlens_k):
+        L = int(L)
+        if L % page:
+            last = int(inp.block_table[b, (L - 1) // page])
+            for c in (kc, vc):
+                if dtype == "fp8":
+                    c[last, L % page:] = 0x7F
+                else:
+                    c[last, L % page:] = float("nan")
+            poisoned_slots += page - L % page
+    assert poisoned_slots > 0
+    poisoned = synth.PagedInputs(inp.cfg, inp.q, kc, vc, inp.block_table, inp.cu_seqlens_q, inp.seqlens_k,
+                                 inp.prefix, inp.meta, inp.q_scale, inp.k_scale, inp.v_scale)
+    o2, lse2, rp2, ci2 = run_paged(fp, poisoned, cfg.tau)
+    assert np.array_equal(rp, rp2) and np.array_equal(ci[:rp[-1]], ci2[:rp[-1]])
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    say(f"paged ({dtype}): {poisoned_slots} NaN slots past the sequence ends change nothing")
+
+
 def test_paged_fp8_equals_contiguous_fp8(fp):
     """The same fp8 codes and scales through the paged entry point (shuffled
     64-token pages) and the fixed-shape one: bit-identical results."""

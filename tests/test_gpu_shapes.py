@@ -134,3 +134,38 @@ def test_fp32_output_derived_bound(fp, cid, S):
     bound = 2.0 ** -7 * vmax + 1e-5
     say(f"fp32 out: max|err| {err.max():.3e} (bound {bound:.3e}), mean {err.mean():.3e}")
     assert err.max() <= bound
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("S,block", [(1000 + 77, 128), (700 + 5, 64)])
+def test_no_reads_past_sequence_end(fp, dtype, S, block):
+    """q, k and v are views of tensors whose tokens past S are NaN (fp8: NaN
+    codes): every output, lse and kept list is bit-identical to the run on
+    exact-size tensors, so the ragged last block reads nothing past the end."""
+    cfg = synth.config(2, S=S, Hq=8, Hkv=2, block=block, seed=301 + block, dtype=dtype)
+    inp = synth.gen_fixed(cfg)
+    dev = torch.device("cuda:0")
+    mv = lambda t: None if t is None else t.to(dev)
+    qs, ks, vs = mv(inp.q_scale), mv(inp.k_scale), mv(inp.v_scale)
+
+    def padded(t):
+        big = torch.empty((t.shape[0], S + 300, t.shape[2], t.shape[3]), dtype=t.dtype, device=dev)
+        if dtype == "fp8":
+            big.fill_(0x7F)
+        else:
+            big.fill_(float("nan"))
+        big[:, :S] = t.to(dev)
+        return big[:, :S]
+
+    a = fp.sparse_prefill(mv(inp.q), mv(inp.k), mv(inp.v), block, 2.0, q_scale=qs, k_scale=ks, v_scale=vs)
+    b = fp.sparse_prefill(padded(inp.q), padded(inp.k), padded(inp.v), block, 2.0, q_scale=qs, k_scale=ks,
+                          v_scale=vs)
+    torch.cuda.synchronize()
+    n = int(a["row_ptr"][-1])
+    assert torch.equal(a["row_ptr"], b["row_ptr"]) and torch.equal(a["col_idx"][:n], b["col_idx"][:n])
+    for key in ("qbar", "kbar", "vbar", "o", "lse"):
+        assert torch.equal(a[key], b[key]), key
+    assert torch.equal(torch.isinf(a["scores"]), torch.isinf(b["scores"]))
+    fin = torch.isfinite(a["scores"])
+    assert torch.equal(a["scores"][fin], b["scores"][fin])
+    say(f"S={S} block={block} {dtype}: NaN tokens past the end change nothing")
