@@ -205,25 +205,26 @@ def test_fp8_block64_iid(fp):
 # ---------------------------------------------------------------------------
 # paged varlen
 # ---------------------------------------------------------------------------
-def run_paged(fp, inp, tau):
+def run_paged(fp, inp, tau, softmax_scale=0.0):
     dev = torch.device("cuda:0")
     q, kc, vc, bt = inp.q.to(dev), inp.k_cache.to(dev), inp.v_cache.to(dev), inp.block_table.to(dev)
     sc = [None if t is None else t.to(dev) for t in (inp.q_scale, inp.k_scale, inp.v_scale)]
-    vp = fp.make_varlen_problem(q, inp.cu_seqlens_q, inp.seqlens_k, kc, bt, inp.cfg.block)
+    vp = fp.make_varlen_problem(q, inp.cu_seqlens_q, inp.seqlens_k, kc, bt, inp.cfg.block,
+                                softmax_scale=softmax_scale)
     o, lse, rp, ci = fp.fp_sparse_prefill_paged(vp, q, kc, vc, bt, tau, q_scale=sc[0], k_scale=sc[1],
                                                 v_scale=sc[2])
     torch.cuda.synchronize()
     return o.cpu(), lse.cpu(), rp.cpu().numpy(), ci.cpu().numpy()
 
 
-def check_paged(fp, inp, tau, sample_rows=None):
-    o, lse, rp, ci = run_paged(fp, inp, tau)
+def check_paged(fp, inp, tau, sample_rows=None, softmax_scale=0.0):
+    o, lse, rp, ci = run_paged(fp, inp, tau, softmax_scale)
     cfg = inp.cfg
-    c = 1 / math.sqrt(128)
+    c = softmax_scale if softmax_scale > 0 else 1 / math.sqrt(128)
     kind = "fp8" if inp.q.dtype == torch.uint8 else "bf16"
     scales = dict(q_scale=inp.q_scale, k_scale=inp.k_scale, v_scale=inp.v_scale)
     refs = oracle.prefill_varlen(inp.q, inp.cu_seqlens_q, inp.seqlens_k, inp.k_cache, inp.v_cache,
-                                 inp.block_table.numpy(), cfg.block, tau, with_output=False, **scales)
+                                 inp.block_table.numpy(), cfg.block, tau, c, with_output=False, **scales)
     row0 = 0
     for b, ref in enumerate(refs):
         L, P = int(inp.seqlens_k[b]), int(inp.prefix[b])
@@ -419,6 +420,17 @@ def test_paged_slots_past_sequence_end_not_read(fp, dtype):
     assert np.array_equal(rp, rp2) and np.array_equal(ci[:rp[-1]], ci2[:rp[-1]])
     assert torch.equal(o, o2) and torch.equal(lse, lse2)
     say(f"paged ({dtype}): {poisoned_slots} NaN slots past the sequence ends change nothing")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_paged_softmax_scale(fp, dtype):
+    """softmax_scale given explicitly (0.05, not 1/sqrt(d)) on the paged path:
+    scores, kept lists and outputs against the oracle at the same scale."""
+    cfg = synth.config(5, Hq=8, Hkv=2, n_seqs=3, len_range=(300, 3000), page_size=64, tau=2.0, dtype=dtype,
+                       seed=37)
+    L, P = synth.paged_lengths(cfg)
+    say(f"paged softmax_scale 0.05 {dtype}: L={L.tolist()} P={P.tolist()}")
+    check_paged(fp, synth.gen_paged(cfg, (L, P)), cfg.tau, softmax_scale=0.05)
 
 
 def test_paged_fp8_equals_contiguous_fp8(fp):
