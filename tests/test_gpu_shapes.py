@@ -76,15 +76,18 @@ def test_fused_qkv_strides(fp):
     check_fixed(fp, inp, 3.0, 128)
 
 
-def test_softmax_scale(fp):
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_softmax_scale(fp, dtype):
     """softmax_scale given explicitly (not 1/sqrt(d))."""
     cscale = 0.05
-    cfg = synth.config(2, S=2048 + 99, Hq=8, Hkv=2, seed=321)
+    cfg = synth.config(2, S=2048 + 99, Hq=8, Hkv=2, seed=321, dtype=dtype)
     inp = synth.gen_fixed(cfg)
     dev = torch.device("cuda:0")
+    mv = lambda t: None if t is None else t.to(dev)
     q, k, v = (t.to(dev) for t in (inp.q, inp.k, inp.v))
     tau = 2.0
-    out = fp.sparse_prefill(q, k, v, 128, tau, softmax_scale=cscale)
+    out = fp.sparse_prefill(q, k, v, 128, tau, softmax_scale=cscale, q_scale=mv(inp.q_scale),
+                            k_scale=mv(inp.k_scale), v_scale=mv(inp.v_scale))
     torch.cuda.synchronize()
     S, Hkv = cfg.S, cfg.Hkv
     nb = -(-S // 128)
@@ -97,7 +100,7 @@ def test_softmax_scale(fp):
     keep = csr_to_keep(rp, ci, 0, Hkv, nb, nb)
     compare_masks(keep, ref["keep"], ref["R"], tau)
     o_ref, lse_ref = oracle.attend(qd, kd, vd, keep, ref["kbar"], ref["vbar"], cscale, 128, 0)
-    compare_outputs(out["o"][0].float().cpu().numpy(), o_ref, "bf16")
+    compare_outputs(out["o"][0].float().cpu().numpy(), o_ref, dtype)
     lg = out["lse"][0].cpu().numpy()
     assert np.abs(lg - lse_ref).max() <= LSE_TOL
 
