@@ -139,6 +139,43 @@ def test_fp32_output_derived_bound(fp, cid, S):
     assert err.max() <= bound
 
 
+@pytest.mark.parametrize("block", [128, 64])
+def test_fp32_output_fp8(fp, block):
+    """Diagnostic fp32 output on fp8 inputs: the bf16 result is its bf16
+    rounding, bit for bit, and against the fp64 oracle (same kept lists) the
+    error is bounded by the kernel's roundings: P to E4M3 (RNE, relative
+    <= 2^-4 per weight while normal; below the normal range an absolute
+    2^-10 of the scaled weight), P of the correction and the pooled V to bf16
+    (2^-8 each), so |o - o_ref| <= (2^-4 + 2^-7) max|v| plus the subnormal
+    term, taken here as 2^-8 max|v|."""
+    cfg = synth.config(2, S=3000 + 21, Hq=8, Hkv=2, block=block, seed=561 + block, dtype="fp8")
+    inp = synth.gen_fixed(cfg)
+    dev = torch.device("cuda:0")
+    mv = lambda t: None if t is None else t.to(dev)
+    q, k, v = (t.to(dev) for t in (inp.q, inp.k, inp.v))
+    sc = dict(q_scale=mv(inp.q_scale), k_scale=mv(inp.k_scale), v_scale=mv(inp.v_scale))
+    tau = 2.0
+    ob = fp.sparse_prefill(q, k, v, block, tau, **sc)
+    of = fp.sparse_prefill(q, k, v, block, tau, out_fp32=True, **sc)
+    torch.cuda.synchronize()
+    assert of["o"].dtype == torch.float32
+    assert torch.equal(ob["row_ptr"], of["row_ptr"])
+    assert torch.equal(of["o"].to(torch.bfloat16), ob["o"])
+    assert torch.equal(ob["lse"], of["lse"])
+    nb = -(-cfg.S // block)
+    rp, ci = of["row_ptr"].cpu().numpy(), of["col_idx"].cpu().numpy()
+    qd, kd, vd = widen(inp, 0)
+    c = 1 / math.sqrt(128)
+    ref = oracle.prefill(qd, kd, vd, block, tau, c, with_output=False)
+    keep = csr_to_keep(rp, ci, 0, cfg.Hkv, nb, nb)
+    o_ref, _ = oracle.attend(qd, kd, vd, keep, ref["kbar"], ref["vbar"], c, block, 0)
+    err = np.abs(of["o"][0].cpu().numpy() - o_ref)
+    vmax = np.abs(vd).max()
+    bound = (2.0 ** -4 + 2.0 ** -7 + 2.0 ** -8) * vmax
+    say(f"fp8 fp32 out block {block}: max|err| {err.max():.3e} (bound {bound:.3e}), mean {err.mean():.3e}")
+    assert err.max() <= bound
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 @pytest.mark.parametrize("S,block", [(1000 + 77, 128), (700 + 5, 64)])
 def test_no_reads_past_sequence_end(fp, dtype, S, block):
