@@ -299,15 +299,18 @@ def test_paged_varlen_small_fp8(fp, page, block):
 
 
 @pytest.mark.parametrize("tau", [1.0, 3.0])
-def test_no_correction_variant(fp, tau):
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_no_correction_variant(fp, tau, dtype):
     """The ablation without the mean correction, against the oracle's variant
     under the GPU's kept lists; the kept lists are those of the default run."""
-    cfg = synth.config(2, S=4096 + 77, Hq=8, Hkv=2, seed=61, tau=tau)
+    cfg = synth.config(2, S=4096 + 77, Hq=8, Hkv=2, seed=61, tau=tau, dtype=dtype)
     inp = synth.gen_fixed(cfg)
     dev = torch.device("cuda:0")
+    mv = lambda t: None if t is None else t.to(dev)
     q, k, v = (t.to(dev) for t in (inp.q, inp.k, inp.v))
-    a = fp.sparse_prefill(q, k, v, 128, tau)
-    b = fp.sparse_prefill(q, k, v, 128, tau, correction=False)
+    sc = dict(q_scale=mv(inp.q_scale), k_scale=mv(inp.k_scale), v_scale=mv(inp.v_scale))
+    a = fp.sparse_prefill(q, k, v, 128, tau, **sc)
+    b = fp.sparse_prefill(q, k, v, 128, tau, correction=False, **sc)
     torch.cuda.synchronize()
     assert torch.equal(a["row_ptr"], b["row_ptr"])
     S, Hkv = cfg.S, cfg.Hkv
@@ -319,8 +322,8 @@ def test_no_correction_variant(fp, tau):
     c = 1 / math.sqrt(128)
     ref = oracle.prefill(qd, kd, vd, 128, tau, c, with_output=False)
     o_ref, lse_ref = oracle.attend(qd, kd, vd, keep, ref["kbar"], ref["vbar"], c, 128, 0, correction=False)
-    say(f"no-correction tau={tau}")
-    compare_outputs(b["o"][0].float().cpu().numpy(), o_ref, "bf16")
+    say(f"no-correction tau={tau} {dtype}")
+    compare_outputs(b["o"][0].float().cpu().numpy(), o_ref, dtype)
     assert np.abs(b["lse"][0].cpu().numpy() - lse_ref).max() <= LSE_TOL
     assert not torch.equal(a["o"], b["o"])          # the correction changes the result
 
