@@ -37,7 +37,40 @@ def version() -> str:
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
-    return None if t is None else t.data_ptr()
+    """Device address of t; the kernels read and write through it, so t must
+    live on the current GPU (a host pointer would fault the device)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise FpError(N.FP_ERR_INVALID, "every tensor argument must be on the GPU (got a CPU tensor)")
+    if t.device.index != torch.cuda.current_device():
+        raise FpError(N.FP_ERR_INVALID,
+                      f"tensor on {t.device}, but the current device is cuda:{torch.cuda.current_device()}")
+    return t.data_ptr()
+
+
+def _check(t: Optional[torch.Tensor], name: str, dtype: torch.dtype, shape=None, required: bool = False):
+    """dtype, contiguity and (optionally) shape of an argument the C ABI reads
+    as a packed array."""
+    if t is None:
+        if required:
+            raise FpError(N.FP_ERR_INVALID, f"{name} is required")
+        return
+    if t.dtype != dtype:
+        raise FpError(N.FP_ERR_INVALID, f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise FpError(N.FP_ERR_INVALID, f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise FpError(N.FP_ERR_INVALID, f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _check_scales(fp8: bool, nseq: int, Hq: int, Hkv: int, nsb: int, q_scale, k_scale, v_scale):
+    if not fp8:
+        if any(t is not None for t in (q_scale, k_scale, v_scale)):
+            raise FpError(N.FP_ERR_INVALID, "scales are for fp8 inputs only")
+        return
+    for name, t, H in (("q_scale", q_scale, Hq), ("k_scale", k_scale, Hkv), ("v_scale", v_scale, Hkv)):
+        _check(t, name, torch.float32, (nseq, H, nsb), required=True)
 
 
 def _stream() -> int:
@@ -65,6 +98,12 @@ def make_problem(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block: int,
     writes o in float32 (diagnostic) instead of bfloat16. correction=False: the
     ablation without the mean correction (pruned blocks dropped)."""
     fp8 = q.dtype == torch.uint8
+    if q.dtype not in (torch.bfloat16, torch.uint8) or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise FpError(N.FP_ERR_INVALID, f"q, k, v must all be bfloat16 or all uint8 E4M3FN codes "
+                                        f"(got {q.dtype}, {k.dtype}, {v.dtype})")
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or q.shape[:2] != k.shape[:2]:
+        raise FpError(N.FP_ERR_INVALID, f"q [batch, S, Hq, d] and k, v [batch, S, Hkv, d] expected "
+                                        f"(got {tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)})")
     c = FpProblem()
     c.out_dtype = N.FP_OUT_FP32 if out_fp32 else N.FP_OUT_BF16
     c.variant = N.FP_VARIANT_MEAN_CORRECTION if correction else N.FP_VARIANT_NO_CORRECTION
@@ -92,6 +131,8 @@ def make_problem(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block: int,
 def fp_block_scores(p: Problem, q, k, v, q_scale=None, k_scale=None, v_scale=None):
     """E1-E2 -> (qbar, kbar, vbar, scores), fp32 device tensors."""
     c = p.c
+    _check_scales(p.fp8, c.batch, c.num_q_heads, c.num_kv_heads, (c.seqlen + 127) // 128, q_scale, k_scale,
+                  v_scale)
     dev = q.device
     f32 = dict(dtype=torch.float32, device=dev)
     qbar = torch.empty((c.batch, c.num_q_heads, p.nb, 128), **f32)
@@ -128,6 +169,11 @@ def fp_sparse_prefill(p: Problem, q, k, v, kbar, vbar, row_ptr, col_idx, sched=N
                       o: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
     """E6 -> (o like q in bf16, or fp32 for an out_fp32 problem; lse fp32 [batch, Hq, S] or None)."""
     c = p.c
+    _check_scales(p.fp8, c.batch, c.num_q_heads, c.num_kv_heads, (c.seqlen + 127) // 128, q_scale, k_scale,
+                  v_scale)
+    _check(row_ptr, "row_ptr", torch.int32, (p.rows + 1,), required=True)
+    _check(col_idx, "col_idx", torch.int32, required=True)
+    _check(sched, "sched", torch.int32, (p.rows,))
     if o is None:
         odt = torch.float32 if c.out_dtype == N.FP_OUT_FP32 else torch.bfloat16
         o = torch.empty((c.batch, c.seqlen, c.num_q_heads, 128), dtype=odt, device=q.device)
@@ -214,6 +260,14 @@ def fp_sparse_prefill_paged(vp: VarlenProblem, q, k_cache, v_cache, block_table,
     kv = (k_cache.stride(0), k_cache.stride(1), k_cache.stride(2))
     if tuple(vp.c.kv_stride) != kv:
         raise ValueError(f"cache strides {kv} differ from the problem's {tuple(vp.c.kv_stride)}")
+    c = vp.c
+    if q.dim() != 3 or q.shape[0] != int(vp.cu[-1]) or q.shape[1] != c.num_q_heads:
+        raise FpError(N.FP_ERR_INVALID, f"q must be packed [{int(vp.cu[-1])}, {c.num_q_heads}, 128] "
+                                        f"(got {tuple(q.shape)})")
+    _check(block_table, "block_table", torch.int32, (c.num_seqs, c.max_pages_per_seq), required=True)
+    nsb = (c.max_pages_per_seq * c.page_size + 127) // 128
+    _check_scales(c.dtype == N.FP_DTYPE_FP8_E4M3, c.num_seqs, c.num_q_heads, c.num_kv_heads, nsb,
+                  q_scale, k_scale, v_scale)
     dev = q.device
     i32 = dict(dtype=torch.int32, device=dev)
     row_ptr = torch.empty(vp.rows + 1, **i32)

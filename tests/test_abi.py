@@ -290,3 +290,48 @@ def test_plain_c_program_uses_the_abi(tmp_path):
     assert b.returncode == 0, b.stderr
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
+
+
+def test_binding_argument_checks():
+    """The binding refuses, before any device call, tensors that the kernels
+    would misread: mixed q/k/v dtypes, missing or misshapen fp8 scales,
+    scales on bf16 inputs, non-int32 kept lists or block tables, and host
+    (CPU) tensors, whose addresses would fault the GPU."""
+    import torch
+    import block_sparse_long_estimate_amd as fp
+    S, Hq, Hkv = 300, 4, 2
+    q = torch.zeros((1, S, Hq, 128), dtype=torch.bfloat16)
+    k = torch.zeros((1, S, Hkv, 128), dtype=torch.bfloat16)
+    with pytest.raises(fp.FpError, match="must all be bfloat16"):
+        fp.make_problem(q, k.to(torch.uint8), k, 128)
+    with pytest.raises(fp.FpError, match="expected"):
+        fp.make_problem(q, k[:, :200], k[:, :200], 128)
+    p = fp.make_problem(q, k, k, 128)
+    with pytest.raises(fp.FpError, match="fp8 inputs only"):
+        fp.fp_block_scores(p, q, k, k, q_scale=torch.ones(1, Hq, 3))
+    with pytest.raises(fp.FpError, match="on the GPU"):
+        fp.fp_block_scores(p, q, k, k)
+    q8, k8 = q.to(torch.uint8), k.to(torch.uint8)
+    p8 = fp.make_problem(q8, k8, k8, 128)
+    ks = torch.ones(1, Hkv, 3)
+    with pytest.raises(fp.FpError, match="q_scale is required"):
+        fp.fp_block_scores(p8, q8, k8, k8, None, ks, ks)
+    with pytest.raises(fp.FpError, match="shape"):
+        fp.fp_block_scores(p8, q8, k8, k8, torch.ones(1, Hq, 2), ks, ks)
+    with pytest.raises(fp.FpError, match="float32"):
+        fp.fp_block_scores(p8, q8, k8, k8, torch.ones(1, Hq, 3, dtype=torch.float64), ks, ks)
+    rp = torch.zeros(p.rows + 1, dtype=torch.int64)
+    with pytest.raises(fp.FpError, match="row_ptr must be torch.int32"):
+        fp.fp_sparse_prefill(p, q, k, k, None, None, rp, rp)
+    # paged: the block table must be int32 [num_seqs, max_pages]
+    cache = torch.zeros((8, 16, Hkv, 128), dtype=torch.bfloat16)
+    qp = torch.zeros((40, Hq, 128), dtype=torch.bfloat16)
+    bt = torch.arange(8, dtype=torch.int32).reshape(2, 4)
+    cu, lk = np.array([0, 20, 40], dtype=np.int32), np.array([30, 50], dtype=np.int32)
+    vp = fp.make_varlen_problem(qp, cu, lk, cache, bt, 64)
+    with pytest.raises(fp.FpError, match="block_table must be torch.int32"):
+        fp.fp_sparse_prefill_paged(vp, qp, cache, cache, bt.long(), 1.0)
+    with pytest.raises(fp.FpError, match="packed"):
+        fp.fp_sparse_prefill_paged(vp, qp[:30], cache, cache, bt, 1.0)
+    with pytest.raises(fp.FpError, match="on the GPU"):
+        fp.fp_sparse_prefill_paged(vp, qp, cache, cache, bt, 1.0)
