@@ -342,11 +342,23 @@ def cpu_baseline(inp, tau, rows_sample=768, gpu=None):
     t_layer = t_est * Hkv + t_att / rows_sample * (Hkv * nb)
     dense = 4.0 * 128 * Hq * S * (S + 1) / 2.0
     return dict(value=dense / t_layer / 1e12, unit="TFLOP/s (dense-equivalent)", cores=1,
-                kind="oracle",
+                kind="oracle", host_cores=os.cpu_count(), host_cpu=host_cpu_model(),
                 sample=(f"E1-E5 for KV head 0 (4 query heads, all {nb} query blocks): {t_est:.2f} s; "
                         f"E6 for {rows_sample} evenly spaced query blocks of KV head 0: {t_att:.2f} s; "
                         f"projected layer time {t_layer:.0f} s (x{Hkv} heads, x{nb} rows)"),
                 measured_s=t_est + t_att, projected_layer_s=t_layer, parity=parity)
+
+
+def host_cpu_model() -> str:
+    """The host CPU's model name (first "model name" line of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 MASK_BAND = 1e-3          # a block may differ from the oracle's only where |R + tau| <= this
@@ -570,7 +582,8 @@ def main():
     if ablation is not None:
         line["error_vs_dense_bf16"] = ablation
     if cpu is not None:
-        line["cpu_baseline"] = {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")}
+        line["cpu_baseline"] = {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample", "host_cores",
+                                                    "host_cpu")}
         line["cpu_baseline"]["value"] = round(cpu["value"], 6)
         line["parity_sample"] = cpu["parity"]
     print(json.dumps(line), flush=True)

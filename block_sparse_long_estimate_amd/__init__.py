@@ -64,6 +64,31 @@ def _check(t: Optional[torch.Tensor], name: str, dtype: torch.dtype, shape=None,
         raise FpError(N.FP_ERR_INVALID, f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
+def _check_view(t: Optional[torch.Tensor], name: str, dtype: torch.dtype, shape, strides=None):
+    """A strided tensor the kernels address through the problem's strides:
+    dtype, shape, a contiguous last dimension and (when given) the leading
+    strides the problem descriptor was built with must all match."""
+    if t is None:
+        raise FpError(N.FP_ERR_INVALID, f"{name} is required")
+    if t.dtype != dtype:
+        raise FpError(N.FP_ERR_INVALID, f"{name} must be {dtype} (got {t.dtype})")
+    if tuple(t.shape) != tuple(shape):
+        raise FpError(N.FP_ERR_INVALID, f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.stride(-1) != 1:
+        raise FpError(N.FP_ERR_INVALID, f"{name}: last dim must be contiguous")
+    if strides is not None and tuple(t.stride()[:len(strides)]) != tuple(strides):
+        raise FpError(N.FP_ERR_INVALID, f"{name} has strides {tuple(t.stride())}, but the problem was "
+                                        f"built with {tuple(strides)}")
+
+
+def _check_qkv(p: "Problem", q, k, v):
+    c = p.c
+    dt = torch.uint8 if p.fp8 else torch.bfloat16
+    _check_view(q, "q", dt, (c.batch, c.seqlen, c.num_q_heads, 128), tuple(c.q_stride))
+    _check_view(k, "k", dt, (c.batch, c.seqlen, c.num_kv_heads, 128), tuple(c.k_stride))
+    _check_view(v, "v", dt, (c.batch, c.seqlen, c.num_kv_heads, 128), tuple(c.v_stride))
+
+
 def _check_scales(fp8: bool, nseq: int, Hq: int, Hkv: int, nsb: int, q_scale, k_scale, v_scale):
     if not fp8:
         if any(t is not None for t in (q_scale, k_scale, v_scale)):
@@ -131,6 +156,7 @@ def make_problem(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block: int,
 def fp_block_scores(p: Problem, q, k, v, q_scale=None, k_scale=None, v_scale=None):
     """E1-E2 -> (qbar, kbar, vbar, scores), fp32 device tensors."""
     c = p.c
+    _check_qkv(p, q, k, v)
     _check_scales(p.fp8, c.batch, c.num_q_heads, c.num_kv_heads, (c.seqlen + 127) // 128, q_scale, k_scale,
                   v_scale)
     dev = q.device
@@ -149,6 +175,8 @@ def fp_select_blocks(p: Problem, scores: torch.Tensor, tau: float, with_sched: b
                      workspace: Optional[torch.Tensor] = None):
     """E3-E5 -> (row_ptr, col_idx, sched) int32 device tensors (col_idx has
     capacity max_nnz; its first row_ptr[-1] entries are valid)."""
+    c = p.c
+    _check(scores, "scores", torch.float32, (c.batch, c.num_q_heads, p.nb, p.nb), required=True)
     dev = scores.device
     i32 = dict(dtype=torch.int32, device=dev)
     row_ptr = torch.empty(p.rows + 1, **i32)
@@ -169,14 +197,23 @@ def fp_sparse_prefill(p: Problem, q, k, v, kbar, vbar, row_ptr, col_idx, sched=N
                       o: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
     """E6 -> (o like q in bf16, or fp32 for an out_fp32 problem; lse fp32 [batch, Hq, S] or None)."""
     c = p.c
+    _check_qkv(p, q, k, v)
     _check_scales(p.fp8, c.batch, c.num_q_heads, c.num_kv_heads, (c.seqlen + 127) // 128, q_scale, k_scale,
                   v_scale)
+    pooled = (c.batch, c.num_kv_heads, p.nb, 128)
+    _check(kbar, "kbar", torch.float32, pooled, required=True)
+    _check(vbar, "vbar", torch.float32, pooled, required=True)
     _check(row_ptr, "row_ptr", torch.int32, (p.rows + 1,), required=True)
     _check(col_idx, "col_idx", torch.int32, required=True)
     _check(sched, "sched", torch.int32, (p.rows,))
+    odt = torch.float32 if c.out_dtype == N.FP_OUT_FP32 else torch.bfloat16
+    oshape = (c.batch, c.seqlen, c.num_q_heads, 128)
     if o is None:
-        odt = torch.float32 if c.out_dtype == N.FP_OUT_FP32 else torch.bfloat16
-        o = torch.empty((c.batch, c.seqlen, c.num_q_heads, 128), dtype=odt, device=q.device)
+        if tuple(c.o_stride) != (c.seqlen * c.num_q_heads * 128, c.num_q_heads * 128, 128):
+            raise FpError(N.FP_ERR_INVALID, "the problem was built for a strided o: pass that o")
+        o = torch.empty(oshape, dtype=odt, device=q.device)
+    else:
+        _check_view(o, "o", odt, oshape, tuple(c.o_stride))
     lse = torch.empty((c.batch, c.num_q_heads, c.seqlen), dtype=torch.float32,
                       device=q.device) if with_lse else None
     lib = N.load()
@@ -255,15 +292,18 @@ def fp_sparse_prefill_paged(vp: VarlenProblem, q, k_cache, v_cache, block_table,
     """E1-E6 on a paged varlen batch -> (o, lse, row_ptr, col_idx). fp8
     (uint8 E4M3FN codes) takes fp32 scales [num_seqs, H, nsb], one per 128
     positions of each sequence."""
-    if v_cache.stride() != k_cache.stride() or v_cache.dtype != k_cache.dtype or q.dtype != k_cache.dtype:
-        raise ValueError("k_cache and v_cache must share strides and dtype with each other and with q")
-    kv = (k_cache.stride(0), k_cache.stride(1), k_cache.stride(2))
-    if tuple(vp.c.kv_stride) != kv:
-        raise ValueError(f"cache strides {kv} differ from the problem's {tuple(vp.c.kv_stride)}")
     c = vp.c
+    dt = torch.uint8 if c.dtype == N.FP_DTYPE_FP8_E4M3 else torch.bfloat16
     if q.dim() != 3 or q.shape[0] != int(vp.cu[-1]) or q.shape[1] != c.num_q_heads:
         raise FpError(N.FP_ERR_INVALID, f"q must be packed [{int(vp.cu[-1])}, {c.num_q_heads}, 128] "
                                         f"(got {tuple(q.shape)})")
+    _check_view(q, "q", dt, (int(vp.cu[-1]), c.num_q_heads, 128), tuple(c.q_stride))
+    if k_cache.dim() != 4 or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise FpError(N.FP_ERR_INVALID, f"k_cache and v_cache must share one shape [pages, page_size, Hkv, 128] "
+                                        f"(got {tuple(k_cache.shape)} and {tuple(v_cache.shape)})")
+    cshape = (k_cache.shape[0], c.page_size, c.num_kv_heads, 128)
+    _check_view(k_cache, "k_cache", dt, cshape, tuple(c.kv_stride))
+    _check_view(v_cache, "v_cache", dt, cshape, tuple(c.kv_stride))
     _check(block_table, "block_table", torch.int32, (c.num_seqs, c.max_pages_per_seq), required=True)
     nsb = (c.max_pages_per_seq * c.page_size + 127) // 128
     _check_scales(c.dtype == N.FP_DTYPE_FP8_E4M3, c.num_seqs, c.num_q_heads, c.num_kv_heads, nsb,

@@ -167,6 +167,13 @@ __global__ void table_copy_kernel(TableChunk c, int n, SeqDesc* dst) {
     const int t = threadIdx.x;
     if (t < n) dst[t] = c.e[t];
 }
+// row_ptr[0] = 0 for a batch without present rows (a kernel rather than a
+// memset node, so the call stays capturable in a graph)
+__global__ void zero_first_kernel(int32_t* p) { *p = 0; }
+hipError_t launch_zero_first(int32_t* p, hipStream_t st) {
+    zero_first_kernel<<<1, 1, 0, st>>>(p);
+    return hipGetLastError();
+}
 hipError_t launch_table_copy(const SeqDesc* host, int n, SeqDesc* dev, hipStream_t st) {
     for (int base = 0; base < n; base += TABLE_CHUNK) {
         TableChunk c;
@@ -303,8 +310,9 @@ int fp_sparse_prefill(const fp_problem* p, const void* q, const void* k, const v
     const bool fp8 = p->dtype == FP_DTYPE_FP8_E4M3;
     if (fp8 && (!q_scale || !k_scale || !v_scale))
         return fail(FP_ERR_INVALID, "fp_sparse_prefill: fp8 needs q_scale, k_scale and v_scale");
+    // fp32 o rows are written with 16-byte stores, bf16 rows with 8-byte stores
     if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(kbar, 16) ||
-        misaligned(vbar, 16) || misaligned(o, 8))
+        misaligned(vbar, 16) || misaligned(o, p->out_dtype == FP_OUT_FP32 ? 16 : 8))
         return fail(FP_ERR_INVALID, "fp_sparse_prefill: misaligned tensor");
     GeoFixed geo = geo_fixed(p);
     const int nsb = cdiv(p->seqlen, SCALE_TOK);
@@ -465,8 +473,10 @@ int fp_sparse_prefill_paged(const fp_varlen_problem* p, const void* q, const int
     VarPlan plan;
     int rc = check_varlen(p, cu, lk, plan);
     if (rc) return rc;
-    if (!q || !k_cache || !v_cache || !block_table || !row_ptr || !col_idx || !o || !workspace)
+    if (!k_cache || !v_cache || !block_table || !row_ptr || !col_idx || !workspace)
         return fail(FP_ERR_INVALID, "fp_sparse_prefill_paged: NULL pointer");
+    // q and o hold sum q_len rows: they may be empty (NULL) when every sequence is fully cached
+    if (plan.sum_q > 0 && (!q || !o)) return fail(FP_ERR_INVALID, "fp_sparse_prefill_paged: NULL q or o");
     const bool fp8 = p->dtype == FP_DTYPE_FP8_E4M3;
     if (fp8 && (!q_scale || !k_scale || !v_scale))
         return fail(FP_ERR_INVALID, "fp_sparse_prefill_paged: fp8 needs q_scale, k_scale and v_scale");
@@ -481,7 +491,12 @@ int fp_sparse_prefill_paged(const fp_varlen_problem* p, const void* q, const int
     if (misaligned(workspace, ALIGN)) return fail(FP_ERR_INVALID, "workspace must be 256-byte aligned");
     if (misaligned(q, 16) || misaligned(k_cache, 16) || misaligned(v_cache, 16) || misaligned(o, 8))
         return fail(FP_ERR_INVALID, "fp_sparse_prefill_paged: misaligned tensor");
-    if (plan.rows == 0) return ok();
+    if (plan.rows == 0) {
+        // nothing to attend: the kept lists are empty, row_ptr = {0}
+        hipError_t e = launch_zero_first(row_ptr, (hipStream_t)stream);
+        if (e != hipSuccess) return fail(FP_ERR_HIP, "row_ptr write: %s", hipGetErrorString(e));
+        return ok();
+    }
 
     char* ws = (char*)workspace;
     SeqDesc* dtable = (SeqDesc*)(ws + plan.o_table);

@@ -195,5 +195,6 @@ hipError_t launch_attn(const GeoFixed* gf, const GeoTable* gt, const AttnArgs& a
 hipError_t launch_summary_prep(const float* kbar, const float* vbar, __bf16* hi, __bf16* lo,
                                __bf16* vb, long long nfloats, hipStream_t st);
 hipError_t launch_table_copy(const SeqDesc* host, int n, SeqDesc* dev, hipStream_t st);
+hipError_t launch_zero_first(int32_t* p, hipStream_t st);
 
 }  // namespace fp

@@ -122,7 +122,10 @@ int64_t fp_max_nnz(const fp_problem* p);        /* batch * Hkv * nb(nb+1)/2   */
 int64_t fp_workspace_size(const fp_problem* p); /* bytes for fp_select_blocks */
 int64_t fp_prefill_workspace_size(const fp_problem* p); /* bytes for fp_sparse_prefill */
 
-/* E1-E2. Pools Q, K, V per block (float32 accumulation) and writes the block
+/* E1-E2: the block-level score estimate (aipulsen.com article body: scores
+ * estimated per block pair instead of per token; lode.cx page, "How It
+ * Works": a small sample of attention scores decides the kept blocks).
+ * Pools Q, K, V per block (float32 accumulation) and writes the block
  * scores. q, k, v (device, read-only): bf16, or E4M3FN codes with q_scale,
  * k_scale, v_scale (device, fp32 [batch, H, ceil(seqlen/128)], one scale per
  * 128-token block; NULL for bf16). Outputs (device, fp32, fully overwritten):
@@ -132,7 +135,10 @@ int fp_block_scores(const fp_problem* p, const void* q, const void* k, const voi
                     const float* q_scale, const float* k_scale, const float* v_scale,
                     float* qbar, float* kbar, float* vbar, float* scores, void* stream);
 
-/* E3-E5 plus compaction. scores (device) as written by fp_block_scores.
+/* E3-E5 plus compaction: the max-based dynamic threshold (lode.cx page, "How
+ * It Works"; aimodeling.com page, "From Prototype to Production") with the G
+ * query heads of a KV head sharing one list (lode.cx page, implementation
+ * bullet list: PackGQA). scores (device) as written by fp_block_scores.
  * tau: +inf keeps everything, tau < 0 keeps only the sink and diagonal
  * blocks, NaN is an error. Outputs (device): row_ptr int32 [rows + 1],
  * col_idx int32 [capacity] (capacity >= fp_max_nnz checked on the host),
@@ -146,15 +152,20 @@ int fp_select_blocks(const fp_problem* p, const float* scores, float tau,
                      int32_t* row_ptr, int32_t* col_idx, int64_t capacity,
                      int32_t* sched, void* workspace, size_t ws_bytes, void* stream);
 
-/* E6. Sparse attention over the kept blocks of (row_ptr, col_idx) -- any
+/* E6: the sparse flash-attention operator over the kept blocks (lode.cx
+ * page, implementation paragraph and bullet list; aimodeling.com page,
+ * "Operator alignment" bullet) plus the mean correction for the pruned
+ * blocks (lode.cx page, "How It Works"; aimodeling.com page, "Error
+ * correction" bullet). Sparse attention over the kept blocks of (row_ptr, col_idx) -- any
  * valid kept list whose rows contain the sink and diagonal blocks, e.g. the
  * one fp_select_blocks wrote -- plus the mean-correction pseudo-tokens of the
  * pruned blocks, taken from kbar and vbar (device, as fp_block_scores wrote
  * them). sched (device, NULL = row order) only orders the work. workspace
  * (device, ws_bytes >= fp_prefill_workspace_size, 256-byte aligned) receives
  * bf16 copies of kbar and vbar for the correction; its contents need not be
- * preserved between calls. Outputs (device): o (o_stride; bf16, or fp32 when
- * out_dtype is FP_OUT_FP32), lse fp32
+ * preserved between calls. Outputs (device): o (o_stride; bf16 with 8-byte
+ * aligned rows, or fp32 with 16-byte aligned rows when out_dtype is
+ * FP_OUT_FP32), lse fp32
  * [batch, Hq, seqlen] or NULL. */
 int fp_sparse_prefill(const fp_problem* p, const void* q, const void* k, const void* v,
                       const float* q_scale, const float* k_scale, const float* v_scale,
@@ -172,7 +183,10 @@ int64_t fp_varlen_workspace_size(const fp_varlen_problem* p, const int32_t* cu_s
                                  const int32_t* seqlens_k);
 
 /* E1-E6 for a paged varlen batch in one call (the pages' paged KV cache and
- * continuous batching: aimodeling.com page, "Framework integration" bullet).
+ * continuous batching: aimodeling.com page, "Framework integration" bullet;
+ * lode.cx page, implementation paragraph). When no sequence has present rows
+ * (every one fully cached) q and o may be NULL and only row_ptr[0] = 0 is
+ * written.
  * q (device) packed [sum q_len, Hq, 128]; k_cache, v_cache (device)
  * [pages, page_size, Hkv, 128]; bf16, or E4M3FN codes when dtype is
  * FP_DTYPE_FP8_E4M3. block_table (device) int32 [num_seqs, max_pages_per_seq]

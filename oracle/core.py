@@ -99,7 +99,8 @@ def select(S: np.ndarray, G: int, tau: float, i0: int) -> Tuple[np.ndarray, np.n
 def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, keep: np.ndarray,
            kbar: np.ndarray, vbar: np.ndarray, c: float, B: int, P: int,
            rows: Optional[Sequence[Tuple[int, int]]] = None,
-           correction: bool = True) -> Tuple[np.ndarray, np.ndarray]:
+           correction: bool = True,
+           out: Optional[Tuple[np.ndarray, np.ndarray]] = None) -> Tuple[np.ndarray, np.ndarray]:
     """E6: sparse attention over kept blocks plus the mean-correction pseudo-tokens.
 
     Sparse operator over kept blocks: lode.cx page, "How It Works" and the
@@ -110,13 +111,18 @@ def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, keep: np.ndarray,
     rows: optional list of (g, il) to evaluate; other outputs stay NaN.
     correction=False is the ablation without the correction: the pruned blocks
     are dropped (no pseudo-tokens).
+    out: optional preallocated (o, lse) to fill instead (only the rows
+    evaluated are written; callers may split the rows over threads).
     Returns o [L-P, Hq, d] and lse [Hq, L-P]."""
     L, Hkv, d = k.shape
     Hq = q.shape[1]
     G = Hq // Hkv
     i0, nq = query_blocks(P, L, B)
-    o = np.full((L - P, Hq, d), np.nan)
-    lse = np.full((Hq, L - P), np.nan)
+    if out is None:
+        o = np.full((L - P, Hq, d), np.nan)
+        lse = np.full((Hq, L - P), np.nan)
+    else:
+        o, lse = out
     todo = rows if rows is not None else [(g, il) for g in range(Hkv) for il in range(nq)]
     for (g, il) in todo:
         i = i0 + il

@@ -266,12 +266,21 @@ def test_binding_rejects_mismatched_cache_views():
     bt = torch.arange(pages, dtype=torch.int32).reshape(2, 4)
     cu, lk = np.array([0, 20, 40], dtype=np.int32), np.array([30, 50], dtype=np.int32)
     vp = fp.make_varlen_problem(q, cu, lk, kc, bt, 64)
-    with pytest.raises(ValueError, match="share strides"):
+    with pytest.raises(fp.FpError, match="v_cache has strides"):
         fp.fp_sparse_prefill_paged(vp, q, kc, vc.contiguous(), bt, 1.0)
-    with pytest.raises(ValueError, match="share strides"):
+    with pytest.raises(fp.FpError, match="v_cache must be torch.bfloat16"):
         fp.fp_sparse_prefill_paged(vp, q, kc, vc.float(), bt, 1.0)
-    with pytest.raises(ValueError, match="differ from the problem"):
+    with pytest.raises(fp.FpError, match="k_cache has strides"):
         fp.fp_sparse_prefill_paged(vp, q, kc.contiguous(), vc.contiguous(), bt, 1.0)
+    # a permuted cache (head dim not contiguous) and a v_cache with fewer pages
+    with pytest.raises(fp.FpError, match="last dim must be contiguous"):
+        fp.fp_sparse_prefill_paged(vp, q, kc.transpose(2, 3).contiguous().transpose(2, 3), vc, bt, 1.0)
+    with pytest.raises(fp.FpError, match="share one shape"):
+        fp.fp_sparse_prefill_paged(vp, q, kc, vc[:4], bt, 1.0)
+    with pytest.raises(fp.FpError, match="q: last dim must be contiguous"):
+        fp.fp_sparse_prefill_paged(vp, q.transpose(1, 2).contiguous().transpose(1, 2), kc, vc, bt, 1.0)
+    with pytest.raises(fp.FpError, match="q must be torch.bfloat16"):
+        fp.fp_sparse_prefill_paged(vp, q.to(torch.uint8), kc, vc, bt, 1.0)
 
 
 def test_plain_c_program_uses_the_abi(tmp_path):
@@ -320,9 +329,42 @@ def test_binding_argument_checks():
         fp.fp_block_scores(p8, q8, k8, k8, torch.ones(1, Hq, 2), ks, ks)
     with pytest.raises(fp.FpError, match="float32"):
         fp.fp_block_scores(p8, q8, k8, k8, torch.ones(1, Hq, 3, dtype=torch.float64), ks, ks)
+    # q/k/v must match the problem they were described with
+    with pytest.raises(fp.FpError, match="q has shape"):
+        fp.fp_block_scores(p, q[:, :200], k, k)
+    with pytest.raises(fp.FpError, match="k must be torch.bfloat16"):
+        fp.fp_block_scores(p, q, k.float(), k)
+    with pytest.raises(fp.FpError, match="v has strides"):
+        fp.fp_block_scores(p, q, k, torch.zeros((1, S, 2 * Hkv, 128), dtype=torch.bfloat16)[:, :, :Hkv])
+    # fp_select_blocks reads scores as fp32 [batch, Hq, nb, nb]
+    with pytest.raises(fp.FpError, match="scores has shape"):
+        fp.fp_select_blocks(p, torch.zeros(1, Hq, 3, 2), 1.0)
+    with pytest.raises(fp.FpError, match="scores must be torch.float32"):
+        fp.fp_select_blocks(p, torch.zeros(1, Hq, 3, 3, dtype=torch.float64), 1.0)
+    # fp_sparse_prefill: pooled rows fp32 [batch, Hkv, nb, 128], o per the problem's out dtype and strides
+    kb = torch.zeros(1, Hkv, 3, 128)
+    rp = torch.zeros(p.rows + 1, dtype=torch.int32)
+    ci = torch.zeros(p.max_nnz, dtype=torch.int32)
+    with pytest.raises(fp.FpError, match="kbar has shape"):
+        fp.fp_sparse_prefill(p, q, k, k, torch.zeros(1, Hkv, 2, 128), kb, rp, ci)
+    with pytest.raises(fp.FpError, match="vbar must be torch.float32"):
+        fp.fp_sparse_prefill(p, q, k, k, kb, kb.double(), rp, ci)
+    with pytest.raises(fp.FpError, match="o must be torch.bfloat16"):
+        fp.fp_sparse_prefill(p, q, k, k, kb, kb, rp, ci, o=torch.zeros(1, S, Hq, 128))
+    pf = fp.make_problem(q, k, k, 128, out_fp32=True)
+    with pytest.raises(fp.FpError, match="o must be torch.float32"):
+        fp.fp_sparse_prefill(pf, q, k, k, kb, kb, rp, ci, o=torch.zeros(1, S, Hq, 128, dtype=torch.bfloat16))
+    with pytest.raises(fp.FpError, match="o has shape"):
+        fp.fp_sparse_prefill(p, q, k, k, kb, kb, rp, ci, o=torch.zeros(1, S, Hq, 64, dtype=torch.bfloat16))
+    ostr = torch.zeros(1, S, Hq, 256, dtype=torch.bfloat16)[..., :128]
+    po = fp.make_problem(q, k, k, 128, o=ostr)
+    with pytest.raises(fp.FpError, match="strided o"):
+        fp.fp_sparse_prefill(po, q, k, k, kb, kb, rp, ci)
+    with pytest.raises(fp.FpError, match="o has strides"):
+        fp.fp_sparse_prefill(po, q, k, k, kb, kb, rp, ci, o=torch.zeros(1, S, Hq, 128, dtype=torch.bfloat16))
     rp = torch.zeros(p.rows + 1, dtype=torch.int64)
     with pytest.raises(fp.FpError, match="row_ptr must be torch.int32"):
-        fp.fp_sparse_prefill(p, q, k, k, None, None, rp, rp)
+        fp.fp_sparse_prefill(p, q, k, k, kb, kb, rp, rp)
     # paged: the block table must be int32 [num_seqs, max_pages]
     cache = torch.zeros((8, 16, Hkv, 128), dtype=torch.bfloat16)
     qp = torch.zeros((40, Hq, 128), dtype=torch.bfloat16)

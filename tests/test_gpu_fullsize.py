@@ -2,9 +2,13 @@
 times (all three entry points, heavy-row-first schedule).
 
 Kept lists are compared in full against the oracle (exact except inside the
-1e-3 threshold band). Outputs are compared on sampled (KV head, query block)
-rows that the oracle evaluates one by one -- under the GPU's validated kept
-lists -- plus a property that holds at any size (every output and lse finite)."""
+1e-3 threshold band). Outputs and lse are compared element by element on
+every (KV head, query block) row of the S=32768 and S=131072 (tau=4, bf16 and
+fp8) configurations and of the paged 8-sequence batch: the oracle's E6 runs
+under the GPU's validated kept lists on a thread pool. The context points
+(tau = 2, 6, 8 at S=131072) and the edge-size cases compare a fixed sample of
+rows: every 8th query block plus the last 8, all KV heads. lse is held to a
+per-element bound derived from the data (fp_testutil.lse_bound)."""
 import math
 import sys
 
@@ -14,7 +18,8 @@ import torch
 
 import oracle
 import synth
-from fp_testutil import LSE_TOL, check_sched, compare_masks, compare_outputs, csr_to_keep, fixed_sched_groups
+from fp_testutil import (attend_threaded, check_lse, check_sched, compare_masks, compare_outputs,
+                         csr_to_keep, fixed_sched_groups, lse_bound)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -32,14 +37,26 @@ def fp():
     return m
 
 
-def sample_rows(Hkv, nq, k):
-    """k (g, il) rows spread over heads and over the sequence, always including
-    the first, second and last query blocks."""
-    ils = sorted(set([0, 1, nq - 1] + list(np.linspace(2, nq - 2, max(k - 3, 1)).round().astype(int))))
-    return [(int(idx % Hkv), int(il)) for idx, il in enumerate(ils)]
+def sample_rows(Hkv, nq, every=8, last=8):
+    """Every `every`-th query block plus the last `last`, all KV heads."""
+    ils = sorted(set(range(0, nq, every)) | set(range(max(nq - last, 0), nq)))
+    return [(g, il) for il in ils for g in range(Hkv)]
 
 
-def run_and_check(fp, inp, tau, kind, rows_k, scores_tol=None):
+def check_rows(q, k, v, keep, ref, c, block, P, o_gpu, lse_gpu, kind, rows=None):
+    """Oracle E6 (under the GPU's kept lists) on every row, or on `rows`, and
+    the element-wise comparison of o and lse."""
+    o_ref, lse_ref = attend_threaded(q, k, v, keep, ref["kbar"], ref["vbar"], c, block, P, rows=rows)
+    if rows is None:
+        assert not np.isnan(o_ref).any() and not np.isnan(lse_ref).any()
+    mx, mean = compare_outputs(o_gpu, o_ref, kind)
+    bound = lse_bound(q, k, keep, ref["kbar"], lse_ref, c, block, P, rows=rows)
+    lerr, worst = check_lse(lse_gpu, lse_ref, bound)
+    n = int((~np.isnan(lse_ref)).sum())
+    return mx, mean, lerr, worst, n
+
+
+def run_and_check(fp, inp, tau, kind, full=True, every=8):
     cfg = inp.cfg
     dev = torch.device("cuda:0")
     mv = lambda t: None if t is None else t.to(dev)
@@ -69,22 +86,19 @@ def run_and_check(fp, inp, tau, kind, rows_k, scores_tol=None):
     Hkv, nq, nb = ref["keep"].shape
     keep = csr_to_keep(rp, ci, 0, Hkv, nq, nb)
     ndiff, nband = compare_masks(keep, ref["keep"], ref["R"], tau)
-    rows = sample_rows(Hkv, nq, rows_k)
+    rows = None if full else sample_rows(Hkv, nq, every)
     say(f"  kept {keep.sum() / (Hkv * nq * (nq + 1) / 2):.3%}, mask diffs {ndiff} (band {nband}); "
-        f"oracle E6 on {len(rows)} rows")
-    o_ref, lse_ref = oracle.attend(qn, kn, vn, keep, ref["kbar"], ref["vbar"], c, cfg.block, 0, rows=rows)
-    mx, mean = compare_outputs(o, o_ref, kind)
-    okl = ~np.isnan(lse_ref)
-    lerr = float(np.abs(lse[okl] - lse_ref[okl]).max())
-    say(f"  sampled rows: max|err| {mx:.2e} mean|err| {mean:.2e} lse max|err| {lerr:.2e}")
-    assert lerr <= LSE_TOL
+        f"oracle E6 on {'every row' if full else f'{len(rows)} rows'}")
+    mx, mean, lerr, worst, n = check_rows(qn, kn, vn, keep, ref, c, cfg.block, 0, o, lse, kind, rows)
+    say(f"  {n} (token, head) outputs: max|err| {mx:.2e} mean|err| {mean:.2e}; "
+        f"lse max|err| {lerr:.2e} ({worst:.2f} of its bound)")
     return keep
 
 
 def test_config2_full(fp):
     cfg = synth.config(2)
     say("config 2")
-    run_and_check(fp, synth.gen_fixed(cfg), cfg.tau, "bf16", 24)
+    run_and_check(fp, synth.gen_fixed(cfg), cfg.tau, "bf16")
 
 
 @pytest.fixture(scope="module")
@@ -96,12 +110,12 @@ def cfg3_inputs():
 @pytest.mark.parametrize("tau", [4.0, 2.0, 8.0, 6.0])
 def test_config3_full(fp, cfg3_inputs, tau):
     say(f"config 3, tau={tau}")
-    run_and_check(fp, cfg3_inputs["bf16"], tau, "bf16", 10 if tau == 4.0 else 5)
+    run_and_check(fp, cfg3_inputs["bf16"], tau, "bf16", full=tau == 4.0)
 
 
 def test_config4_fp8_full(fp, cfg3_inputs):
     say("config 4 (fp8)")
-    run_and_check(fp, cfg3_inputs["fp8"], 4.0, "fp8", 10)
+    run_and_check(fp, cfg3_inputs["fp8"], 4.0, "fp8")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
@@ -133,12 +147,10 @@ def test_config5_paged_full(fp, dtype):
         lo, hi = int(inp.cu_seqlens_q[b]), int(inp.cu_seqlens_q[b + 1])
         qw, kw, vw, _ = oracle.varlen_sequence(inp.q, inp.cu_seqlens_q, inp.seqlens_k, inp.k_cache,
                                                inp.v_cache, inp.block_table.numpy(), b, **scales)
-        rows = sample_rows(Hkv, nq, 4)
-        o_ref, lse_ref = oracle.attend(qw, kw, vw, keep, ref["kbar"], ref["vbar"], c, cfg.block, P, rows=rows)
-        mx, mean = compare_outputs(o[lo:hi], o_ref, dtype)
-        okl = ~np.isnan(lse_ref)
-        assert np.abs(lse[:, lo:hi][okl] - lse_ref[okl]).max() <= LSE_TOL
-        say(f"  seq {b}: L={L} P={P} mask diffs {ndiff} (band {nband}) max|err| {mx:.2e} mean {mean:.2e}")
+        mx, mean, lerr, worst, n = check_rows(qw, kw, vw, keep, ref, c, cfg.block, P, o[lo:hi],
+                                              lse[:, lo:hi], dtype)
+        say(f"  seq {b}: L={L} P={P} mask diffs {ndiff} (band {nband}); all {n} outputs: max|err| {mx:.2e} "
+            f"mean {mean:.2e}; lse {lerr:.2e} ({worst:.2f} of bound)")
         row0 += Hkv * nq
     assert row0 == len(rp) - 1
 
@@ -150,7 +162,7 @@ def test_largest_sequence_single_head(fp):
     takes the schedule sort's histogram past 64 KiB of LDS."""
     cfg = synth.config(2, S=16384 * 128, Hq=1, Hkv=1, tau=1.0, seed=77)
     say("largest sequence: S=2097152, 1/1 heads")
-    run_and_check(fp, synth.gen_fixed(cfg), cfg.tau, "bf16", 6)
+    run_and_check(fp, synth.gen_fixed(cfg), cfg.tau, "bf16", full=False, every=256)
 
 
 def test_batch_of_two_schedule_groups(fp):
@@ -181,9 +193,7 @@ def test_batch_of_two_schedule_groups(fp):
         ref = oracle.prefill(qn, kn, vn, cfg.block, cfg.tau, c, with_output=False)
         keep = csr_to_keep(rp, ci, b * Hkv * nb, Hkv, nb, nb)
         ndiff, nband = compare_masks(keep, ref["keep"], ref["R"], cfg.tau)
-        o_ref, lse_ref = oracle.attend(qn, kn, vn, keep, ref["kbar"], ref["vbar"], c, cfg.block, 0,
-                                       rows=sample_rows(Hkv, nb, 4))
-        mx, mean = compare_outputs(o[b], o_ref, "bf16")
-        okl = ~np.isnan(lse_ref)
-        assert np.abs(lse[b][okl] - lse_ref[okl]).max() <= LSE_TOL
-        say(f"  seq {b}: mask diffs {ndiff} (band {nband}) max|err| {mx:.2e} mean {mean:.2e}")
+        mx, mean, lerr, worst, n = check_rows(qn, kn, vn, keep, ref, c, cfg.block, 0, o[b], lse[b], "bf16",
+                                              rows=sample_rows(Hkv, nb, 32))
+        say(f"  seq {b}: mask diffs {ndiff} (band {nband}) {n} outputs: max|err| {mx:.2e} mean {mean:.2e}; "
+            f"lse {lerr:.2e} ({worst:.2f} of bound)")
