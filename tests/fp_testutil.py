@@ -45,13 +45,23 @@ def attend_threaded(q, k, v, keep, kbar, vbar, c, B, P, rows=None, correction=Tr
     return o, lse
 
 
-def lse_bound(q, k, keep, kbar, lse_ref, c, B, P, rows=None, correction=True):
+# Worst relative error of one 128-dim logit c<q,k> computed on the MFMA units,
+# as a fraction of c * sum_d |q_d| |k_d|: bf16 (32x32x16, fp32 accumulation)
+# is held to the fp32 summation bound of 128 terms, 2^-17 (a probe of random,
+# wide-range and cancelling bf16 operands against exact sums measured at most
+# 2^-21.2); the fp8 form (32x32x64 f8f6f4) adds its 64 products with far
+# fewer bits -- the same probe on random E4M3 codes measured up to 2^-12.4 --
+# so fp8 logits are held to 2^-11.
+KEPT_REL = {"bf16": 2.0 ** -17, "fp8": 2.0 ** -11}
+
+
+def lse_bound(q, k, keep, kbar, lse_ref, c, B, P, rows=None, correction=True, kind="bf16"):
     """Per-element bound on |lse_gpu - lse_oracle| [Hq, L-P], from the data.
 
     lse is 1-Lipschitz in every logit (max norm), so the bound is the largest
     error of any one logit of the row plus the rounding of lse itself:
-      kept token s:   c<q,k_s> from exact products summed in fp32 over 128
-                      dims: at most 2^-17 * c * sum_d |q_d| |k_sd|;
+      kept token s:   c<q,k_s> from exact products summed on the MFMA over
+                      128 dims: at most KEPT_REL[kind] * c * sum_d |q_d| |k_sd|;
       pseudo-token j: c<q,Kbar_j> with Kbar_j split into bf16 hi + lo
                       (residual at most 2^-16 |Kbar_j| per element) and 256
                       products summed in fp32 (2^-16 again): 2^-15 * c *
@@ -68,12 +78,13 @@ def lse_bound(q, k, keep, kbar, lse_ref, c, B, P, rows=None, correction=True):
     bound = np.full((Hq, L - P), np.nan)
     todo = list(rows) if rows is not None else [(g, il) for il in range(nq) for g in range(Hkv)]
     with ThreadPoolExecutor(workers()) as ex:
-        list(ex.map(lambda ch: _lse_bound_rows(q, k, keep, kbar, lse_ref, c, B, P, G, i0, ch, bound, correction),
+        list(ex.map(lambda ch: _lse_bound_rows(q, k, keep, kbar, lse_ref, c, B, P, G, i0, ch, bound, correction,
+                                               KEPT_REL[kind]),
                     _row_chunks(todo, workers())))
     return bound
 
 
-def _lse_bound_rows(q, k, keep, kbar, lse_ref, c, B, P, G, i0, todo, bound, correction):
+def _lse_bound_rows(q, k, keep, kbar, lse_ref, c, B, P, G, i0, todo, bound, correction, kept_rel):
     L = k.shape[0]
     for g, il in todo:
         i = i0 + il
@@ -85,7 +96,7 @@ def _lse_bound_rows(q, k, keep, kbar, lse_ref, c, B, P, G, i0, todo, bound, corr
         a_kept = c * (qa @ kmax)                                   # [rows, G]
         a_pr = (c * (qa @ np.abs(kbar[g, pj]).T)).max(axis=2) if len(pj) else 0.0
         lr = lse_ref[g * G:(g + 1) * G, lo - P:hi - P].T
-        bound[g * G:(g + 1) * G, lo - P:hi - P] = (2.0 ** -17 * a_kept + 2.0 ** -15 * a_pr
+        bound[g * G:(g + 1) * G, lo - P:hi - P] = (kept_rel * a_kept + 2.0 ** -15 * a_pr
                                                    + 2.0 ** -19 * (1 + np.abs(lr))).T
 
 

@@ -50,7 +50,7 @@ def check_rows(q, k, v, keep, ref, c, block, P, o_gpu, lse_gpu, kind, rows=None)
     if rows is None:
         assert not np.isnan(o_ref).any() and not np.isnan(lse_ref).any()
     mx, mean = compare_outputs(o_gpu, o_ref, kind)
-    bound = lse_bound(q, k, keep, ref["kbar"], lse_ref, c, block, P, rows=rows)
+    bound = lse_bound(q, k, keep, ref["kbar"], lse_ref, c, block, P, rows=rows, kind=kind)
     lerr, worst = check_lse(lse_gpu, lse_ref, bound)
     n = int((~np.isnan(lse_ref)).sum())
     return mx, mean, lerr, worst, n

@@ -85,7 +85,8 @@ def check_fixed(fp, inp, tau, block, rows=None, kind="bf16", check_pooled=True):
                                        rows=None if rows is None else rows[b])
         mx, mean = compare_outputs(out["o"][b].float().numpy(), o_ref, kind)
         check_lse(out["lse"][b].numpy(), lse_ref,
-                  lse_bound(q, k, keep, ref["kbar"], lse_ref, c, block, 0, rows=None if rows is None else rows[b]))
+                  lse_bound(q, k, keep, ref["kbar"], lse_ref, c, block, 0, rows=None if rows is None else rows[b],
+                            kind=kind))
         frac = keep.sum() / (Hkv * nb * (nb + 1) / 2)
         stats.append((frac, ndiff, nband, mx, mean))
         say(f"  seq {b}: kept {frac:.3%}, mask diffs {ndiff} (band {nband}), max|err| {mx:.2e}, mean {mean:.2e}")
@@ -267,7 +268,7 @@ def check_paged(fp, inp, tau, sample_rows=None, softmax_scale=0.0):
         o_ref, lse_ref = oracle.attend(qw, kw, vw, keep, ref["kbar"], ref["vbar"], c, cfg.block, P, rows=rows)
         mx, mean = compare_outputs(o[lo:hi].float().numpy(), o_ref, kind)
         check_lse(lse[:, lo:hi].numpy(), lse_ref, lse_bound(qw, kw, keep, ref["kbar"], lse_ref, c, cfg.block, P,
-                                                            rows=rows))
+                                                            rows=rows, kind=kind))
         say(f"  seq {b}: L={L} P={P} kept {keep.sum() / max(1, (np.tril(np.ones((nq, nb)), ref['i0']).sum()) * Hkv):.2%} "
             f"diffs {ndiff} (band {nband}) max|err| {mx:.2e} mean {mean:.2e}")
         row0 += Hkv * nq
@@ -368,7 +369,7 @@ def test_no_correction_variant(fp, tau, dtype):
     say(f"no-correction tau={tau} {dtype}")
     compare_outputs(b["o"][0].float().cpu().numpy(), o_ref, dtype)
     check_lse(b["lse"][0].cpu().numpy(), lse_ref,
-              lse_bound(qd, kd, keep, ref["kbar"], lse_ref, c, 128, 0, correction=False))
+              lse_bound(qd, kd, keep, ref["kbar"], lse_ref, c, 128, 0, correction=False, kind=dtype))
     assert not torch.equal(a["o"], b["o"])          # the correction changes the result
 
 

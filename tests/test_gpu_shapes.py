@@ -101,7 +101,8 @@ def test_softmax_scale(fp, dtype):
     compare_masks(keep, ref["keep"], ref["R"], tau)
     o_ref, lse_ref = oracle.attend(qd, kd, vd, keep, ref["kbar"], ref["vbar"], cscale, 128, 0)
     compare_outputs(out["o"][0].float().cpu().numpy(), o_ref, dtype)
-    check_lse(out["lse"][0].cpu().numpy(), lse_ref, lse_bound(qd, kd, keep, ref["kbar"], lse_ref, cscale, 128, 0))
+    check_lse(out["lse"][0].cpu().numpy(), lse_ref, lse_bound(qd, kd, keep, ref["kbar"], lse_ref, cscale, 128, 0,
+                                                             kind=dtype))
 
 
 @pytest.mark.parametrize("cid,S", [(2, 4096 + 33), (1, 2048)])
