@@ -10,6 +10,7 @@ Entry points (same names as the C ABI):
   fp_select_blocks         max-based dynamic threshold -> CSR kept lists (E3-E5)
   fp_sparse_prefill        sparse attention + mean correction (E6)
   fp_sparse_prefill_paged  all of it for a paged varlen batch
+  fp_sparse_prefill_noalloc  fp_sparse_prefill without a workspace (static scratch)
 and sparse_prefill(), which chains the first three.
 """
 from __future__ import annotations
@@ -28,7 +29,7 @@ from ._native import FpError, FpProblem, FpVarlenProblem
 __all__ = [
     "FpError", "Problem", "make_problem", "fp_block_scores", "fp_select_blocks",
     "fp_sparse_prefill", "fp_sparse_prefill_paged", "sparse_prefill", "version",
-    "make_varlen_problem",
+    "make_varlen_problem", "fp_sparse_prefill_noalloc",
 ]
 
 
@@ -224,6 +225,38 @@ def fp_sparse_prefill(p: Problem, q, k, v, kbar, vbar, row_ptr, col_idx, sched=N
                                   _ptr(v_scale), _ptr(kbar), _ptr(vbar), _ptr(row_ptr),
                                   _ptr(col_idx), _ptr(sched), _ptr(o), _ptr(lse), _ptr(workspace),
                                   workspace.numel(), _stream()))
+    return o, lse
+
+
+def fp_sparse_prefill_noalloc(p: Problem, q, k, v, kbar, vbar, row_ptr, col_idx, sched=None,
+                              q_scale=None, k_scale=None, v_scale=None, o: Optional[torch.Tensor] = None,
+                              lse: Optional[torch.Tensor] = None):
+    """fp_sparse_prefill without a workspace: the library's static per-GPU
+    scratch array holds the summary operands. o (and lse, if wanted) are the
+    caller's, so nothing is allocated here either when they are passed; o is
+    allocated only when omitted. Calls that overlap on one GPU race."""
+    c = p.c
+    _check_qkv(p, q, k, v)
+    _check_scales(p.fp8, c.batch, c.num_q_heads, c.num_kv_heads, (c.seqlen + 127) // 128, q_scale, k_scale,
+                  v_scale)
+    pooled = (c.batch, c.num_kv_heads, p.nb, 128)
+    _check(kbar, "kbar", torch.float32, pooled, required=True)
+    _check(vbar, "vbar", torch.float32, pooled, required=True)
+    _check(row_ptr, "row_ptr", torch.int32, (p.rows + 1,), required=True)
+    _check(col_idx, "col_idx", torch.int32, required=True)
+    _check(sched, "sched", torch.int32, (p.rows,))
+    _check(lse, "lse", torch.float32, (c.batch, c.num_q_heads, c.seqlen))
+    odt = torch.float32 if c.out_dtype == N.FP_OUT_FP32 else torch.bfloat16
+    oshape = (c.batch, c.seqlen, c.num_q_heads, 128)
+    if o is None:
+        if tuple(c.o_stride) != (c.seqlen * c.num_q_heads * 128, c.num_q_heads * 128, 128):
+            raise FpError(N.FP_ERR_INVALID, "the problem was built for a strided o: pass that o")
+        o = torch.empty(oshape, dtype=odt, device=q.device)
+    else:
+        _check_view(o, "o", odt, oshape, tuple(c.o_stride))
+    N.check(N.load().fp_sparse_prefill_noalloc(p.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(q_scale), _ptr(k_scale),
+                                               _ptr(v_scale), _ptr(kbar), _ptr(vbar), _ptr(row_ptr),
+                                               _ptr(col_idx), _ptr(sched), _ptr(o), _ptr(lse), _stream()))
     return o, lse
 
 

@@ -26,8 +26,9 @@ EXPORTS = (
     "fp_prefill_workspace_size",
     "fp_block_scores", "fp_select_blocks", "fp_sparse_prefill",
     "fp_varlen_num_rows", "fp_varlen_max_nnz", "fp_varlen_workspace_size",
-    "fp_sparse_prefill_paged",
+    "fp_sparse_prefill_paged", "fp_sparse_prefill_noalloc",
 )
+FP_NOALLOC_MAX_POOLED_ROWS = 32768
 
 
 class FpProblem(ctypes.Structure):
@@ -85,6 +86,8 @@ def load() -> ctypes.CDLL:
     lib.fp_sparse_prefill.restype = ctypes.c_int
     lib.fp_sparse_prefill.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                       ctypes.c_size_t, vp]
+    lib.fp_sparse_prefill_noalloc.restype = ctypes.c_int
+    lib.fp_sparse_prefill_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.fp_sparse_prefill_paged.restype = ctypes.c_int
     lib.fp_sparse_prefill_paged.argtypes = [VP, vp, i32p, i32p, vp, vp, vp, vp, vp, vp, ctypes.c_float,
                                             vp, vp, ctypes.c_int64, vp, vp, vp, ctypes.c_size_t, vp]

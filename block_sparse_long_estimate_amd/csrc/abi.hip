@@ -9,6 +9,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "../../include/fp_prefill.h"
@@ -293,27 +294,40 @@ int fp_select_blocks(const fp_problem* p, const float* scores, float tau, int32_
     return ok();
 }
 
-int fp_sparse_prefill(const fp_problem* p, const void* q, const void* k, const void* v,
-                      const float* q_scale, const float* k_scale, const float* v_scale,
-                      const float* kbar, const float* vbar, const int32_t* row_ptr,
-                      const int32_t* col_idx, const int32_t* sched, void* o, float* lse,
-                      void* workspace, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of fp_sparse_prefill and its allocation-free variant (no HIP call).
+int check_prefill(const char* fn, const fp_problem* p, const void* q, const void* k, const void* v,
+                  const float* q_scale, const float* k_scale, const float* v_scale, const float* kbar,
+                  const float* vbar, const int32_t* row_ptr, const int32_t* col_idx, const void* o) {
     int rc = check_fixed(p);
     if (rc) return rc;
-    if (!q || !k || !v || !kbar || !vbar || !row_ptr || !col_idx || !o || !workspace)
-        return fail(FP_ERR_INVALID, "fp_sparse_prefill: NULL pointer");
-    const long long prow = (long long)p->batch * p->num_kv_heads * cdiv(p->seqlen, p->block);
-    if (ws_bytes < summary_ws_bytes(prow))
-        return fail(FP_ERR_CAPACITY, "fp_sparse_prefill: workspace %zu < %zu bytes", ws_bytes,
-                    summary_ws_bytes(prow));
-    if (misaligned(workspace, ALIGN)) return fail(FP_ERR_INVALID, "workspace must be 256-byte aligned");
+    if (!q || !k || !v || !kbar || !vbar || !row_ptr || !col_idx || !o)
+        return fail(FP_ERR_INVALID, "%s: NULL pointer", fn);
     const bool fp8 = p->dtype == FP_DTYPE_FP8_E4M3;
     if (fp8 && (!q_scale || !k_scale || !v_scale))
-        return fail(FP_ERR_INVALID, "fp_sparse_prefill: fp8 needs q_scale, k_scale and v_scale");
+        return fail(FP_ERR_INVALID, "%s: fp8 needs q_scale, k_scale and v_scale", fn);
     // fp32 o rows are written with 16-byte stores, bf16 rows with 8-byte stores
     if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(kbar, 16) ||
         misaligned(vbar, 16) || misaligned(o, p->out_dtype == FP_OUT_FP32 ? 16 : 8))
-        return fail(FP_ERR_INVALID, "fp_sparse_prefill: misaligned tensor");
+        return fail(FP_ERR_INVALID, "%s: misaligned tensor", fn);
+    return FP_OK;
+}
+
+long long fixed_pooled_rows(const fp_problem* p) {
+    return (long long)p->batch * p->num_kv_heads * cdiv(p->seqlen, p->block);
+}
+
+// Launches of E6 on a checked problem; `workspace` (256-byte aligned) holds
+// the bf16 summary operands, summary_ws_bytes(pooled rows) bytes.
+int launch_prefill(const fp_problem* p, const void* q, const void* k, const void* v, const float* q_scale,
+                   const float* k_scale, const float* v_scale, const float* kbar, const float* vbar,
+                   const int32_t* row_ptr, const int32_t* col_idx, const int32_t* sched, void* o, float* lse,
+                   void* workspace, hipStream_t st) {
+    const long long prow = fixed_pooled_rows(p);
+    const bool fp8 = p->dtype == FP_DTYPE_FP8_E4M3;
     GeoFixed geo = geo_fixed(p);
     const int nsb = cdiv(p->seqlen, SCALE_TOK);
     const int G = p->num_q_heads / p->num_kv_heads;
@@ -343,11 +357,85 @@ int fp_sparse_prefill(const fp_problem* p, const void* q, const void* k, const v
     a.slices = cdiv(G * p->block, 128);
     a.scale_log2 = default_scale(p->softmax_scale, p->head_dim) * 1.4426950408889634f;
     hipError_t e = launch_summary_prep(kbar, vbar, (__bf16*)a.kbar_hi, (__bf16*)a.kbar_lo,
-                                       (__bf16*)a.vbar_bf, prow * D, (hipStream_t)stream);
+                                       (__bf16*)a.vbar_bf, prow * D, st);
     if (e != hipSuccess) return fail(FP_ERR_HIP, "summary prep launch: %s", hipGetErrorString(e));
-    e = launch_attn(&geo, nullptr, a, p->block, fp8, 0, (hipStream_t)stream);
+    e = launch_attn(&geo, nullptr, a, p->block, fp8, 0, st);
     if (e != hipSuccess) return fail(FP_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
     return ok();
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free entry point: the bf16 summary operands live
+// in this device array instead of a caller workspace. Each GPU the library
+// runs on holds its own copy until the process ends. In host code the name
+// is only a handle: its device address on the current device comes from
+// hipGetSymbolAddress, looked up once per device on the first call there.
+// ---------------------------------------------------------------------------
+__device__ __align__(256) uint8_t scratch[FP_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+int scratch_address(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(FP_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= MAX_DEVICES) return fail(FP_ERR_UNSUPPORTED, "device %d beyond %d", dev, MAX_DEVICES);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(FP_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return FP_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int fp_sparse_prefill(const fp_problem* p, const void* q, const void* k, const void* v,
+                      const float* q_scale, const float* k_scale, const float* v_scale,
+                      const float* kbar, const float* vbar, const int32_t* row_ptr,
+                      const int32_t* col_idx, const int32_t* sched, void* o, float* lse,
+                      void* workspace, size_t ws_bytes, void* stream) {
+    int rc = check_prefill("fp_sparse_prefill", p, q, k, v, q_scale, k_scale, v_scale, kbar, vbar, row_ptr,
+                           col_idx, o);
+    if (rc) return rc;
+    if (!workspace) return fail(FP_ERR_INVALID, "fp_sparse_prefill: NULL workspace");
+    const size_t need = summary_ws_bytes(fixed_pooled_rows(p));
+    if (ws_bytes < need)
+        return fail(FP_ERR_CAPACITY, "fp_sparse_prefill: workspace %zu < %zu bytes", ws_bytes, need);
+    if (misaligned(workspace, ALIGN)) return fail(FP_ERR_INVALID, "workspace must be 256-byte aligned");
+    return launch_prefill(p, q, k, v, q_scale, k_scale, v_scale, kbar, vbar, row_ptr, col_idx, sched, o, lse,
+                          workspace, (hipStream_t)stream);
+}
+
+int fp_sparse_prefill_noalloc(const fp_problem* p, const void* q, const void* k, const void* v,
+                              const float* q_scale, const float* k_scale, const float* v_scale,
+                              const float* kbar, const float* vbar, const int32_t* row_ptr,
+                              const int32_t* col_idx, const int32_t* sched, void* o, float* lse,
+                              void* stream) {
+    int rc = check_prefill("fp_sparse_prefill_noalloc", p, q, k, v, q_scale, k_scale, v_scale, kbar, vbar,
+                           row_ptr, col_idx, o);
+    if (rc) return rc;
+    const size_t need = summary_ws_bytes(fixed_pooled_rows(p));
+    if (need > (size_t)FP_NOALLOC_SCRATCH_BYTES)
+        return fail(FP_ERR_CAPACITY,
+                    "fp_sparse_prefill_noalloc: the problem needs %zu bytes of scratch, above the %d-byte static "
+                    "array (batch x KV heads x blocks at most %d)", need, FP_NOALLOC_SCRATCH_BYTES,
+                    FP_NOALLOC_MAX_POOLED_ROWS);
+    void* ws = nullptr;
+    rc = scratch_address(&ws);
+    if (rc) return rc;
+    return launch_prefill(p, q, k, v, q_scale, k_scale, v_scale, kbar, vbar, row_ptr, col_idx, sched, o, lse,
+                          ws, (hipStream_t)stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -173,6 +173,27 @@ int fp_sparse_prefill(const fp_problem* p, const void* q, const void* k, const v
                       const int32_t* row_ptr, const int32_t* col_idx, const int32_t* sched,
                       void* o, float* lse, void* workspace, size_t ws_bytes, void* stream);
 
+/* Allocation-free variant of fp_sparse_prefill, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same kernels and results,
+ * with the workspace replaced by a static device array of
+ * FP_NOALLOC_SCRATCH_BYTES that each GPU holds from the library's load
+ * until the process ends. It accepts problems with batch x num_kv_heads x
+ * ceil(seqlen / block) <= FP_NOALLOC_MAX_POOLED_ROWS pooled rows and returns
+ * FP_ERR_CAPACITY above that. It calls no hipMalloc or hipFree; the first
+ * call on a device looks the array's address up there (hipGetSymbolAddress),
+ * with that device current, which must be the device of `stream`. Every call
+ * on one GPU uses that GPU's one array: calls that overlap in time on the same
+ * GPU (other streams, other threads) race and must be serialised by the
+ * caller. Arguments as for fp_sparse_prefill. */
+#define FP_NOALLOC_MAX_POOLED_ROWS 32768
+#define FP_NOALLOC_SCRATCH_BYTES (3 * FP_NOALLOC_MAX_POOLED_ROWS * 256)
+int fp_sparse_prefill_noalloc(const fp_problem* p, const void* q, const void* k, const void* v,
+                              const float* q_scale, const float* k_scale, const float* v_scale,
+                              const float* kbar, const float* vbar,
+                              const int32_t* row_ptr, const int32_t* col_idx, const int32_t* sched,
+                              void* o, float* lse, void* stream);
+
 /* Sizing of a paged varlen call (host only). cu_seqlens_q int32 [num_seqs+1]
  * and seqlens_k int32 [num_seqs] are HOST arrays. */
 int64_t fp_varlen_num_rows(const fp_varlen_problem* p, const int32_t* cu_seqlens_q,

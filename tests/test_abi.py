@@ -377,3 +377,24 @@ def test_binding_argument_checks():
         fp.fp_sparse_prefill_paged(vp, qp[:30], cache, cache, bt, 1.0)
     with pytest.raises(fp.FpError, match="on the GPU"):
         fp.fp_sparse_prefill_paged(vp, qp, cache, cache, bt, 1.0)
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch():
+    """The allocation-free entry point refuses, before any HIP call, a problem
+    whose summary operands exceed its static scratch array (batch x KV heads
+    x blocks above FP_NOALLOC_MAX_POOLED_ROWS), and accepts the argument
+    checks of fp_sparse_prefill."""
+    lib = N.load()
+    nb = 1024
+    p = problem(seqlen=nb * 128, num_q_heads=8, num_kv_heads=8)
+    for arr in (p.q_stride, p.k_stride, p.v_stride, p.o_stride):
+        arr[0], arr[1], arr[2] = nb * 128 * 8 * 128, 8 * 128, 128
+    p.batch = N.FP_NOALLOC_MAX_POOLED_ROWS // (8 * nb) + 1
+    fake = ctypes.c_void_p(1 << 20)          # never dereferenced: the call fails before any device work
+    args = [fake] * 3 + [None] * 3 + [fake] * 4 + [None, fake, None, None]
+    rc = lib.fp_sparse_prefill_noalloc(ctypes.byref(p), *args)
+    assert rc == N.FP_ERR_CAPACITY
+    assert b"static" in lib.fp_last_error()
+    p.batch = 1
+    args_null = [fake] * 3 + [None] * 3 + [None] + [fake] * 3 + [None, fake, None, None]
+    assert lib.fp_sparse_prefill_noalloc(ctypes.byref(p), *args_null) == N.FP_ERR_INVALID
