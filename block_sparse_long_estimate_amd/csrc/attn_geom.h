@@ -1,0 +1,240 @@
+// Address arithmetic of the sparse attention kernel (k_attn.hip), callable
+// from host code as well: the kernel computes every global and LDS address
+// through these functions, and a host replay (tests/c/attn_replay.cpp) runs
+// the same functions over whole launches to check each access against the
+// extents of the buffers and of the LDS allocation.
+#pragma once
+
+#include "fp_internal.h"
+
+#if defined(__HIP_DEVICE_COMPILE__)
+#define FP_UNIFORM(x) __builtin_amdgcn_readfirstlane(x)
+#else
+#define FP_UNIFORM(x) (x)
+#endif
+
+namespace fp {
+
+// ---------------------------------------------------------------------------
+// Tile layouts in LDS (128 dims per row; rows padded, not XOR-swizzled, so
+// every operand address is lane_base + immediate):
+//   bf16 K rows every 272 bytes: the QK^T operand read (16 lanes = 16 rows
+//     at one 16-byte chunk) lands on 16 distinct 4-bank groups;
+//   bf16 V rows every 320 bytes: a transpose read covers 8 rows x 64 bytes,
+//     served 32 lanes (4 rows) at a time; a stride of 64 bytes mod 256 puts
+//     those rows on disjoint banks;
+//   fp8 K rows every 144 bytes (16 mod 256, as bf16 K);
+//   fp8 V rows every 160 bytes, keys permuted inside each 64-key step (bits 2
+//     and 3 swapped) so that each 32-lane half of a transpose read covers 8
+//     consecutive rows x 32 bytes, on 8 disjoint 8-bank groups.
+// Summary tiles (pooled keys hi/lo and pooled values) use the bf16 layouts.
+// ---------------------------------------------------------------------------
+constexpr int KSTR = 272;
+constexpr int VSTR = 320;
+constexpr int KSTR8 = 144;
+constexpr int VSTR8 = 160;
+constexpr int PIECE = 1024;                 // LDS bytes one wavefront load instruction fills
+
+// swap bits 2 and 3 of a key index
+FP_HD int vt_slot(int key) { return (key & ~0xC) | ((key >> 1) & 4) | ((key << 1) & 8); }
+
+template <int BLK, bool FP8>
+struct TileGeom {
+    static constexpr int ESZ = FP8 ? 1 : 2;
+    static constexpr int KS = FP8 ? KSTR8 : KSTR;
+    static constexpr int VS = FP8 ? VSTR8 : VSTR;
+    static constexpr int NKB = BLK / 32;             // 32-key blocks per tile
+    static constexpr int SUMC = BLK / 2;             // pooled columns per summary sub-tile
+    static constexpr int SB = NKB / 2;               // 32-column blocks per summary sub-tile
+    static constexpr int KTILE = BLK * KSTR;         // bytes: a bf16 or fp8 K tile, or a summary K tile
+    static constexpr int VTILE_KEPT = BLK * VS;
+    static constexpr int VTILE_SUM = SUMC * VSTR;
+    static constexpr int VTILE = VTILE_KEPT > VTILE_SUM ? VTILE_KEPT : VTILE_SUM;
+    static constexpr int KPIECES = BLK * KS / PIECE;
+    static constexpr int VPIECES = BLK * VS / PIECE;
+    static constexpr int SKPIECES = BLK * KSTR / PIECE;   // summary K: hi rows then lo rows
+    static constexpr int SVPIECES = SUMC * VSTR / PIECE;
+    static_assert(BLK * KS % PIECE == 0 && BLK * VS % PIECE == 0 && SUMC * VSTR % PIECE == 0, "whole pieces");
+};
+
+// Lane `lane` of the load of piece t (stride STR) fills LDS bytes
+// t * 1024 + 16 lane .. + 15: tile row `row`, 16-byte chunk `ch` of it.
+struct PieceLoc {
+    int row, ch;
+};
+FP_HD PieceLoc piece_loc(int STR, int t, int lane) {
+    const int pb = t * PIECE + lane * 16;
+    const int row = pb / STR;
+    return PieceLoc{row, (pb - row * STR) >> 4};
+}
+
+// Per-lane byte offsets (from the tile's first key row) of the pieces this
+// lane loads for contiguous K/V, computed once per workgroup; wavefront w of
+// NW loads pieces w, w + NW, ... Unsigned 32-bit offsets from a uniform base
+// let each load use the scalar-base addressing form.
+template <int STR, int BLK, int ESZ, bool PERM, int NW>
+struct TileOffs {
+    static constexpr int PIECES = BLK * STR / PIECE;
+    static constexpr int NP = (PIECES + NW - 1) / NW;
+    static constexpr uint32_t PAD = 0xFFFFFFFFu;     // lane lands on row padding (or past the last piece)
+    uint32_t off[NP];
+    FP_HD void init(long long tok_stride, int wave, int lane) {
+#pragma unroll
+        for (int k = 0; k < NP; ++k) {
+            const int t = k * NW + wave;
+            const PieceLoc pl = piece_loc(STR, t, lane);
+            const int key = PERM ? vt_slot(pl.row) : pl.row;
+            off[k] = (t < PIECES && pl.ch < 8 * ESZ) ? (uint32_t)(key * tok_stride * ESZ + pl.ch * 16) : PAD;
+        }
+    }
+    // Paged K/V: key `key` of a tile lies in page slot key >> lshift of the
+    // tile (lshift = log2 min(page, BLK)) at in-page row key & (2^lshift - 1);
+    // off packs the in-page byte offset (low 24 bits) with the slot.
+    FP_HD void init_paged(long long tok_stride, int lshift, int wave, int lane) {
+#pragma unroll
+        for (int k = 0; k < NP; ++k) {
+            const int t = k * NW + wave;
+            const PieceLoc pl = piece_loc(STR, t, lane);
+            const int key = PERM ? vt_slot(pl.row) : pl.row;
+            const uint32_t inpage = (uint32_t)((key & ((1 << lshift) - 1)) * tok_stride * ESZ + pl.ch * 16);
+            off[k] = (t < PIECES && pl.ch < 8 * ESZ) ? (inpage | ((uint32_t)(key >> lshift) << 24)) : PAD;
+        }
+    }
+    FP_HD bool active(int k) const { return off[k] != PAD; }
+    // byte address, relative to the tensor base, of piece k of a full
+    // contiguous tile whose first key row is at byte tile_base
+    FP_HD long long src_full(long long tile_base, int k) const { return tile_base + off[k]; }
+    // paged: the page slot of piece k within the tile and its in-page byte offset
+    FP_HD int page_slot(int k) const { return (int)(off[k] >> 24); }
+    FP_HD uint32_t in_page(int k) const { return off[k] & 0xFFFFFFu; }
+};
+
+// Byte offset (relative to the tensor base) of the 16 bytes lane `lane`
+// loads for piece t of key block j in the generic path (ragged tile, or a
+// paged tile without the fast offsets), or -1 when the lane lands on row
+// padding. Rows past the sequence repeat its last key. pages: the
+// sequence's page ids (staged), or null to read the block table.
+template <int STR, int BLK, int ESZ, bool PERM, bool PAGED, typename PageFn>
+FP_HD long long tile_src(const KVAddr& ka, int b, int L, int g, int j, int t, int lane, PageFn pages,
+                         bool have_pages) {
+    constexpr int PIECES = BLK * STR / PIECE;
+    const PieceLoc pl = piece_loc(STR, t, lane);
+    if (t >= PIECES || pl.ch >= 8 * ESZ) return -1;
+    const int key = PERM ? vt_slot(pl.row) : pl.row;
+    const int rmax = L - 1 - j * BLK;
+    const int sk = j * BLK + (key < rmax ? key : rmax);
+    const long long off = PAGED && have_pages ? ka.off_page(pages(sk >> ka.page_shift), sk, g)
+                                              : ka.template off<PAGED>(b, sk, g);
+    return off * ESZ + pl.ch * 16;
+}
+
+// Summary sub-tile m (pooled columns [SUMC m, SUMC m + SUMC)): lane `lane`
+// of piece t of the K (w = 0) or V (w = 1) part. K rows 0 .. SUMC-1 hold the
+// bf16 hi parts of those pooled keys, rows SUMC .. BLK-1 the lo parts; V rows
+// the bf16 pooled values. Returns the element offset into the hi / lo / V
+// array (which = 0, 1, 2) or -1 for row padding. Columns past the sequence's
+// last block repeat it (they are masked out).
+struct SummarySrc {
+    int which;
+    long long off;
+};
+template <int BLK>
+FP_HD SummarySrc summary_src(const SeqDesc& s, int Hkv, int g, int m, int w, int t, int lane) {
+    constexpr int SUMC = BLK / 2;
+    const PieceLoc pl = piece_loc(w == 0 ? KSTR : VSTR, t, lane);
+    if (pl.ch >= 16) return SummarySrc{-1, -1};
+    const int part = w == 0 && pl.row >= SUMC;          // 0 hi / 1 lo (K rows)
+    const int jc = SUMC * m + pl.row - part * SUMC;
+    const int jp = jc < s.nbk - 1 ? jc : s.nbk - 1;
+    return SummarySrc{w == 0 ? part : 2, kbar_row(s, Hkv, g, jp) * D + pl.ch * 8};
+}
+
+// ---------------------------------------------------------------------------
+// Work units. Unit u of the grid runs one 256-row slice of one kept-list row:
+// u % 8 picks the XCD, and the row's slices sit on one XCD so they share its
+// L2 copy of the K/V tiles.
+// ---------------------------------------------------------------------------
+struct UnitMap {
+    int pidx, slice;
+};
+FP_HD UnitMap unit_map(int u, int slices) {
+    const int xcd = u & 7, k8 = u >> 3;
+    return UnitMap{8 * (k8 / slices) + xcd, k8 % slices};
+}
+
+// Packed query row of (slice, wavefront, row group, lane): NW wavefronts x RG
+// groups x 32 rows = 256 rows per slice, token-major over the G heads.
+template <int NW>
+FP_HD int packed_row(int slice, int wave, int rg, int n) {
+    constexpr int RG = 8 / NW;
+    return slice * 256 + wave * (32 * RG) + rg * 32 + n;
+}
+
+// ---------------------------------------------------------------------------
+// Tile sequence of a row: the kept blocks in column order (codes >= 0 are
+// block indices), then the summary sub-tiles holding at least one pruned
+// column (code -1 - m for sub-tile m), then NONE. `kept` is the row's kept
+// bitmap (bit j of word j / 32), i the row's diagonal block.
+// ---------------------------------------------------------------------------
+constexpr int TILE_NONE = -0x7fffffff;
+
+FP_HD uint32_t range_bits(int c0, int lo, int hi) {
+    const int a = lo - c0 > 0 ? lo - c0 : 0, z = hi - c0 < 31 ? hi - c0 : 31;
+    if (a > z) return 0u;
+    return (0xFFFFFFFFu >> (31 - z)) & (0xFFFFFFFFu << a);
+}
+
+template <int SUMC, typename Bits>
+FP_HD int next_summary(const Bits& kept, int i, int m0, bool no_correction) {
+    if (no_correction) return TILE_NONE;                  // ablation: no pseudo-tokens
+    for (int mm = m0; mm * SUMC <= i - 1; ++mm) {
+        const int c_lo = mm * SUMC > 1 ? mm * SUMC : 1;
+        const int c_hi = mm * SUMC + SUMC - 1 < i - 1 ? mm * SUMC + SUMC - 1 : i - 1;
+        uint32_t anyw = 0u;
+        for (int wd = c_lo >> 5; wd <= (c_hi >> 5); ++wd) anyw |= ~kept[wd] & range_bits(wd * 32, c_lo, c_hi);
+        if (anyw) return -1 - mm;
+    }
+    return TILE_NONE;
+}
+
+template <int SUMC, typename Bits>
+FP_HD int next_code(const Bits& kept, int i, int code, bool no_correction) {
+    if (code >= 0) {
+        int wd = (code + 1) >> 5;
+        uint32_t w = code + 1 <= i ? kept[wd] & (~0u << ((code + 1) & 31)) : 0u;
+        while (w == 0u && wd < (i >> 5)) w = kept[++wd];
+        w = FP_UNIFORM(w);
+        wd = FP_UNIFORM(wd);
+        if (w != 0u) return wd * 32 + __builtin_ctz(w);
+        return next_summary<SUMC>(kept, i, 0, no_correction);
+    }
+    return next_summary<SUMC>(kept, i, -code, no_correction);
+}
+
+// ---------------------------------------------------------------------------
+// LDS operand reads of the tile compute, as byte offsets within a tile
+// buffer, for lane (n = lane & 31, lh = lane >> 5).
+// ---------------------------------------------------------------------------
+// bf16 K operand of key block kb, dim step ks: 16 bytes.
+// DORD 0: dims 16 ks + 8 lh .. +8; DORD 1: dims 64 (ks / 4) + 32 lh + 8 (ks % 4) .. +8
+template <int DORD>
+FP_HD int k_read_off(int kb, int ks, int n, int lh) {
+    const int d0 = DORD ? 64 * (ks >> 2) + 32 * lh + 8 * (ks & 3) : 16 * ks + 8 * lh;
+    return (kb * 32 + n) * KSTR + d0 * 2;
+}
+// bf16 V^T transpose read aa (0, 1) of key block kb, 16-key step s2, dim block db: 8 bytes
+FP_HD int v_read_off(int kb, int s2, int aa, int db, int lane) {
+    const int jj = lane & 15, q = lane >> 4;
+    const int rsub = 4 * (q >> 1) + (jj >> 2);
+    const int dsub = 16 * (q & 1) + 4 * (jj & 3);
+    return (kb * 32 + 16 * s2 + 8 * aa + rsub) * VSTR + (32 * db + dsub) * 2;
+}
+// fp8 K operand of key block kb, 64-dim step ks: 32 bytes (two 16-byte reads)
+FP_HD int k8_read_off(int kb, int ks, int n, int lh) { return (kb * 32 + n) * KSTR8 + ks * 64 + lh * 32; }
+// fp8 V^T transpose read c (0..3) of 64-key step s2, dim block db: 8 bytes
+FP_HD int v8_read_off(int s2, int c, int db, int lane) {
+    const int a = lane & 15, half = (lane >> 4) & 1, lh = lane >> 5;
+    return (s2 * 64 + 8 * lh + (a >> 1)) * VSTR8 + 16 * half + 8 * (a & 1) + 16 * c * VSTR8 + db * 32;
+}
+
+}  // namespace fp

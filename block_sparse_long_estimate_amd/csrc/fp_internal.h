@@ -5,6 +5,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Index arithmetic is callable from host code too (FP_HD), so host programs
+// can replay a launch's addresses and check them against buffer extents.
+#define FP_HD __host__ __device__ __forceinline__
+
 namespace fp {
 
 constexpr int D = 128;            // head dim
@@ -43,17 +47,17 @@ __host__ __device__ inline int score_tiles(int nq, int nbk) {
 struct GeoFixed {
     static constexpr bool PAGED_KV = false;   // contiguous K/V
     int nseq, S, Hq, Hkv, blk, nb, ntile;
-    __device__ __forceinline__ SeqDesc seq(int b) const {
+    FP_HD SeqDesc seq(int b) const {
         SeqDesc s;
         s.L = S; s.P = 0; s.i0 = 0; s.nq = nb; s.nbk = nb; s.q0 = 0;
         s.qb0 = b * nb; s.kb0 = b * nb; s.row0 = b * Hkv * nb; s.tile0 = b * ntile;
         s.sc0 = (long long)b * Hq * nb * nb;
         return s;
     }
-    __device__ __forceinline__ int seq_of_qblock(int u) const { return u / nb; }
-    __device__ __forceinline__ int seq_of_kblock(int u) const { return u / nb; }
-    __device__ __forceinline__ int seq_of_row(int r) const { return r / (Hkv * nb); }
-    __device__ __forceinline__ int seq_of_tile(int u) const { return u / ntile; }
+    FP_HD int seq_of_qblock(int u) const { return u / nb; }
+    FP_HD int seq_of_kblock(int u) const { return u / nb; }
+    FP_HD int seq_of_row(int r) const { return r / (Hkv * nb); }
+    FP_HD int seq_of_tile(int u) const { return u / ntile; }
 };
 
 // Varlen: a table of nseq descriptors in device memory, entry nseq holding
@@ -62,7 +66,7 @@ struct GeoTable {
     static constexpr bool PAGED_KV = true;    // K/V in the paged cache
     const SeqDesc* t;
     int nseq, Hq, Hkv, blk;
-    __device__ __forceinline__ SeqDesc seq(int b) const { return t[b]; }
+    FP_HD SeqDesc seq(int b) const { return t[b]; }
     // largest b in [0, nseq) with field(b) <= u (empty sequences share the
     // next one's offset, so ties resolve to the last, non-empty, one)
 #define FP_SEARCH(FIELD)                                              \
@@ -72,10 +76,10 @@ struct GeoTable {
         if (t[mid].FIELD <= u) lo = mid; else hi = mid;               \
     }                                                                 \
     return lo;
-    __device__ __forceinline__ int seq_of_qblock(int u) const { FP_SEARCH(qb0) }
-    __device__ __forceinline__ int seq_of_kblock(int u) const { FP_SEARCH(kb0) }
-    __device__ __forceinline__ int seq_of_row(int r) const { int u = r; FP_SEARCH(row0) }
-    __device__ __forceinline__ int seq_of_tile(int u) const { FP_SEARCH(tile0) }
+    FP_HD int seq_of_qblock(int u) const { FP_SEARCH(qb0) }
+    FP_HD int seq_of_kblock(int u) const { FP_SEARCH(kb0) }
+    FP_HD int seq_of_row(int r) const { int u = r; FP_SEARCH(row0) }
+    FP_HD int seq_of_tile(int u) const { FP_SEARCH(tile0) }
 #undef FP_SEARCH
 };
 
@@ -83,7 +87,7 @@ struct GeoTable {
 // q / o / lse rows: b * sb + (q0 + t - P) * st + h * sh   (varlen: sb = 0)
 struct RowAddr {
     long long sb, st, sh;
-    __device__ __forceinline__ long long off(int b, const SeqDesc& s, int t, int h) const {
+    FP_HD long long off(int b, const SeqDesc& s, int t, int h) const {
         return (long long)b * sb + (long long)(s.q0 + t - s.P) * st + (long long)h * sh;
     }
 };
@@ -95,7 +99,7 @@ struct KVAddr {
     const int* table;
     int maxp, page_shift;
     template <bool PAGED>
-    __device__ __forceinline__ long long off(int b, int s, int g) const {
+    FP_HD long long off(int b, int s, int g) const {
         if (PAGED) {
             int pg = table[(long long)b * maxp + (s >> page_shift)];
             return (long long)pg * spage + (long long)(s & ((1 << page_shift) - 1)) * st +
@@ -104,20 +108,20 @@ struct KVAddr {
         return (long long)b * sb + (long long)s * st + (long long)g * sh;
     }
     // paged offset with the page id already looked up
-    __device__ __forceinline__ long long off_page(int pg, int s, int g) const {
+    FP_HD long long off_page(int pg, int s, int g) const {
         return (long long)pg * spage + (long long)(s & ((1 << page_shift) - 1)) * st + (long long)g * sh;
     }
 };
 
 // Pooled tensors: Qbar [qb0*Hq + h*nq + il], Kbar/Vbar [kb0*Hkv + g*nbk + j], rows of D floats.
-__device__ __forceinline__ long long qbar_row(const SeqDesc& s, int Hq, int h, int il) {
+FP_HD long long qbar_row(const SeqDesc& s, int Hq, int h, int il) {
     return (long long)s.qb0 * Hq + (long long)h * s.nq + il;
 }
-__device__ __forceinline__ long long kbar_row(const SeqDesc& s, int Hkv, int g, int j) {
+FP_HD long long kbar_row(const SeqDesc& s, int Hkv, int g, int j) {
     return (long long)s.kb0 * Hkv + (long long)g * s.nbk + j;
 }
 // Scores: [sc0 + (h*nq + il) * nbk + j]
-__device__ __forceinline__ long long score_off(const SeqDesc& s, int h, int il, int j) {
+FP_HD long long score_off(const SeqDesc& s, int h, int il, int j) {
     return s.sc0 + ((long long)h * s.nq + il) * s.nbk + j;
 }
 
@@ -125,7 +129,7 @@ __device__ __forceinline__ long long score_off(const SeqDesc& s, int h, int il, 
 struct ScaleAddr {
     const float* p;
     long long sb, sh;
-    __device__ __forceinline__ float at(int b, int h, int t) const {
+    FP_HD float at(int b, int h, int t) const {
         return p[(long long)b * sb + (long long)h * sh + (t >> 7)];
     }
 };
