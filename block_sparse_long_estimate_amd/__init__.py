@@ -11,6 +11,7 @@ Entry points (same names as the C ABI):
   fp_sparse_prefill        sparse attention + mean correction (E6)
   fp_sparse_prefill_paged  all of it for a paged varlen batch
   fp_sparse_prefill_noalloc  fp_sparse_prefill without a workspace (static scratch)
+  fp_dense_prefill         dense causal attention on the same kernel (the baseline)
 and sparse_prefill(), which chains the first three.
 """
 from __future__ import annotations
@@ -29,7 +30,7 @@ from ._native import FpError, FpProblem, FpVarlenProblem
 __all__ = [
     "FpError", "Problem", "make_problem", "fp_block_scores", "fp_select_blocks",
     "fp_sparse_prefill", "fp_sparse_prefill_paged", "sparse_prefill", "version",
-    "make_varlen_problem", "fp_sparse_prefill_noalloc",
+    "make_varlen_problem", "fp_sparse_prefill_noalloc", "fp_dense_prefill",
 ]
 
 
@@ -225,6 +226,29 @@ def fp_sparse_prefill(p: Problem, q, k, v, kbar, vbar, row_ptr, col_idx, sched=N
                                   _ptr(v_scale), _ptr(kbar), _ptr(vbar), _ptr(row_ptr),
                                   _ptr(col_idx), _ptr(sched), _ptr(o), _ptr(lse), _ptr(workspace),
                                   workspace.numel(), _stream()))
+    return o, lse
+
+
+def fp_dense_prefill(p: Problem, q, k, v, q_scale=None, k_scale=None, v_scale=None, with_lse: bool = True,
+                     o: Optional[torch.Tensor] = None):
+    """Dense causal attention on the same kernel (every block kept; no
+    estimate, selection or correction) -> (o, lse)."""
+    c = p.c
+    _check_qkv(p, q, k, v)
+    _check_scales(p.fp8, c.batch, c.num_q_heads, c.num_kv_heads, (c.seqlen + 127) // 128, q_scale, k_scale,
+                  v_scale)
+    odt = torch.float32 if c.out_dtype == N.FP_OUT_FP32 else torch.bfloat16
+    oshape = (c.batch, c.seqlen, c.num_q_heads, 128)
+    if o is None:
+        if tuple(c.o_stride) != (c.seqlen * c.num_q_heads * 128, c.num_q_heads * 128, 128):
+            raise FpError(N.FP_ERR_INVALID, "the problem was built for a strided o: pass that o")
+        o = torch.empty(oshape, dtype=odt, device=q.device)
+    else:
+        _check_view(o, "o", odt, oshape, tuple(c.o_stride))
+    lse = torch.empty((c.batch, c.num_q_heads, c.seqlen), dtype=torch.float32,
+                      device=q.device) if with_lse else None
+    N.check(N.load().fp_dense_prefill(p.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(q_scale), _ptr(k_scale),
+                                      _ptr(v_scale), _ptr(o), _ptr(lse), _stream()))
     return o, lse
 
 

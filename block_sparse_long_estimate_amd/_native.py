@@ -26,7 +26,7 @@ EXPORTS = (
     "fp_prefill_workspace_size",
     "fp_block_scores", "fp_select_blocks", "fp_sparse_prefill",
     "fp_varlen_num_rows", "fp_varlen_max_nnz", "fp_varlen_workspace_size",
-    "fp_sparse_prefill_paged", "fp_sparse_prefill_noalloc",
+    "fp_sparse_prefill_paged", "fp_sparse_prefill_noalloc", "fp_dense_prefill",
 )
 FP_NOALLOC_MAX_POOLED_ROWS = 32768
 
@@ -86,6 +86,8 @@ def load() -> ctypes.CDLL:
     lib.fp_sparse_prefill.restype = ctypes.c_int
     lib.fp_sparse_prefill.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                       ctypes.c_size_t, vp]
+    lib.fp_dense_prefill.restype = ctypes.c_int
+    lib.fp_dense_prefill.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.fp_sparse_prefill_noalloc.restype = ctypes.c_int
     lib.fp_sparse_prefill_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.fp_sparse_prefill_paged.restype = ctypes.c_int

@@ -417,6 +417,42 @@ int fp_sparse_prefill(const fp_problem* p, const void* q, const void* k, const v
                           workspace, (hipStream_t)stream);
 }
 
+int fp_dense_prefill(const fp_problem* p, const void* q, const void* k, const void* v, const float* q_scale,
+                     const float* k_scale, const float* v_scale, void* o, float* lse, void* stream) {
+    int rc = check_fixed(p);
+    if (rc) return rc;
+    if (!q || !k || !v || !o) return fail(FP_ERR_INVALID, "fp_dense_prefill: NULL pointer");
+    const bool fp8 = p->dtype == FP_DTYPE_FP8_E4M3;
+    if (fp8 && (!q_scale || !k_scale || !v_scale))
+        return fail(FP_ERR_INVALID, "fp_dense_prefill: fp8 needs q_scale, k_scale and v_scale");
+    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) ||
+        misaligned(o, p->out_dtype == FP_OUT_FP32 ? 16 : 8))
+        return fail(FP_ERR_INVALID, "fp_dense_prefill: misaligned tensor");
+    GeoFixed geo = geo_fixed(p);
+    const int nsb = cdiv(p->seqlen, SCALE_TOK);
+    const int G = p->num_q_heads / p->num_kv_heads;
+    AttnArgs a{};
+    a.q = q; a.k = k; a.v = v;
+    a.qa = RowAddr{p->q_stride[0], p->q_stride[1], p->q_stride[2]};
+    a.oa = RowAddr{p->o_stride[0], p->o_stride[1], p->o_stride[2]};
+    a.o_f32 = p->out_dtype == FP_OUT_FP32;
+    a.no_correction = 1;                 // nothing is pruned
+    a.dense = 1;
+    a.ka = KVAddr{p->k_stride[0], p->k_stride[1], p->k_stride[2], 0, nullptr, 0, 0};
+    a.va = KVAddr{p->v_stride[0], p->v_stride[1], p->v_stride[2], 0, nullptr, 0, 0};
+    a.qs = ScaleAddr{q_scale, (long long)p->num_q_heads * nsb, nsb};
+    a.ks = ScaleAddr{k_scale, (long long)p->num_kv_heads * nsb, nsb};
+    a.vs = ScaleAddr{v_scale, (long long)p->num_kv_heads * nsb, nsb};
+    a.o = o; a.lse = lse;
+    a.la = RowAddr{(long long)p->num_q_heads * p->seqlen, 1, p->seqlen};
+    a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads; a.G = G;
+    a.rows = p->batch * p->num_kv_heads * geo.nb;
+    a.scale_log2 = default_scale(p->softmax_scale, p->head_dim) * 1.4426950408889634f;
+    hipError_t e = launch_attn(&geo, nullptr, a, p->block, fp8, 0, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(FP_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
 int fp_sparse_prefill_noalloc(const fp_problem* p, const void* q, const void* k, const void* v,
                               const float* q_scale, const float* k_scale, const float* v_scale,
                               const float* kbar, const float* vbar, const int32_t* row_ptr,

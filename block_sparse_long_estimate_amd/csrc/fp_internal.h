@@ -189,6 +189,7 @@ struct AttnArgs {
     int o_f32;                         // o in fp32 (diagnostic) instead of bf16
     int paged_fast;                    // paged: in-page offsets of a tile fit 24 bits (precomputed per lane)
     int no_correction;                 // ablation: pruned blocks dropped (no summary tiles)
+    int dense;                         // every block j <= i kept, no kept lists read (dense causal attention)
 };
 
 hipError_t launch_pool(const GeoFixed* gf, const GeoTable* gt, const PoolArgs& a, hipStream_t st);

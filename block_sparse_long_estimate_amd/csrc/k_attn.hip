@@ -435,7 +435,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_tile_kernel(Geo geo, AttnArgs
 
     const UnitMap um = unit_map(blockIdx.x, a.slices);
     if (um.pidx >= a.rows) return;
-    const int r = a.sched ? a.sched[um.pidx] : um.pidx;
+    // dense: rows in reverse order, so every (sequence, KV head) runs its
+    // longest rows (latest query blocks) first
+    const int r = a.dense ? a.rows - 1 - um.pidx : (a.sched ? a.sched[um.pidx] : um.pidx);
     const int b = geo.seq_of_row(r);
     const SeqDesc s = geo.seq(b);
     const int rl = r - s.row0;
@@ -462,8 +464,10 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_tile_kernel(Geo geo, AttnArgs
         h[rg] = g * G + (prow - tl * G);
     }
 
-    const int rp0 = a.row_ptr[r], nnz = a.row_ptr[r + 1] - rp0;
-    const int j0 = a.col_idx[rp0];
+    // kept list of the row: from the CSR, or every block j <= i when dense
+    const int rp0 = a.dense ? 0 : a.row_ptr[r];
+    const int nnz = a.dense ? i + 1 : a.row_ptr[r + 1] - rp0;
+    const int j0 = a.dense ? 0 : a.col_idx[rp0];
     KVOffs<BLK, FP8, NW> kvo;
     if (!PAGED) {
         kvo.k.init(a.ka.st, wave, lane);
@@ -534,7 +538,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_tile_kernel(Geo geo, AttnArgs
     __syncthreads();
     float svm = 0.f;
     for (int e = tid; e < nnz; e += NT) {
-        const int j = a.col_idx[rp0 + e];
+        const int j = a.dense ? e : a.col_idx[rp0 + e];
         atomicOr(&kept[j >> 5], 1u << (j & 31));
         if (FP8) svm = fmaxf(svm, vsp[(j * BLK) >> 7]);
     }

@@ -173,6 +173,18 @@ int fp_sparse_prefill(const fp_problem* p, const void* q, const void* k, const v
                       const int32_t* row_ptr, const int32_t* col_idx, const int32_t* sched,
                       void* o, float* lse, void* workspace, size_t ws_bytes, void* stream);
 
+/* Dense causal attention with the same kernel: every key block j <= i of
+ * every row is attended (no estimate, no selection, no correction), tiles in
+ * order, rows longest first. It is the dense baseline the sparse path is
+ * measured against (the pages quote their speedups against dense
+ * FlashAttention kernels: lode.cx page, "Why It Matters"; aimodeling.com
+ * page, "The Numbers That Matter") and equals fp_sparse_prefill on the
+ * lists of tau = +inf bit for bit. Arguments as for fp_sparse_prefill (the
+ * problem's variant is ignored); no kept lists, no workspace. */
+int fp_dense_prefill(const fp_problem* p, const void* q, const void* k, const void* v,
+                     const float* q_scale, const float* k_scale, const float* v_scale,
+                     void* o, float* lse, void* stream);
+
 /* Allocation-free variant of fp_sparse_prefill, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc): the same kernels and results,

@@ -398,3 +398,21 @@ def test_noalloc_rejects_problems_beyond_its_scratch():
     p.batch = 1
     args_null = [fake] * 3 + [None] * 3 + [None] + [fake] * 3 + [None, fake, None, None]
     assert lib.fp_sparse_prefill_noalloc(ctypes.byref(p), *args_null) == N.FP_ERR_INVALID
+
+
+def test_dense_entry_point_checks():
+    """fp_dense_prefill validates its problem and pointers before any HIP call."""
+    lib = N.load()
+    p = problem()
+    fake = ctypes.c_void_p(1 << 20)
+    assert lib.fp_dense_prefill(ctypes.byref(p), None, fake, fake, None, None, None, fake, None, None) \
+        == N.FP_ERR_INVALID
+    p8 = problem(dtype=N.FP_DTYPE_FP8_E4M3)
+    for arr in (p8.q_stride, p8.k_stride, p8.v_stride):
+        arr[0], arr[1], arr[2] = arr[0] // 2, arr[1] // 2, arr[2] // 2
+    assert lib.fp_dense_prefill(ctypes.byref(p8), fake, fake, fake, None, None, None, fake, None, None) \
+        == N.FP_ERR_INVALID
+    assert b"scale" in lib.fp_last_error()
+    bad = problem(head_dim=64)
+    assert lib.fp_dense_prefill(ctypes.byref(bad), fake, fake, fake, None, None, None, fake, None, None) \
+        == N.FP_ERR_UNSUPPORTED
