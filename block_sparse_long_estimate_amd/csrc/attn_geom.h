@@ -59,32 +59,37 @@ struct TileGeom {
 
 // Lane `lane` of the load of piece t (stride STR) fills LDS bytes
 // t * 1024 + 16 lane .. + 15: tile row `row`, 16-byte chunk `ch` of it.
+// Chunks past the row's data (the row padding, never read) take a copy of
+// the row's last data chunk: the lane's source then shares a cache line with
+// its neighbour's, and no lane of a load has to be masked off.
 struct PieceLoc {
     int row, ch;
 };
-FP_HD PieceLoc piece_loc(int STR, int t, int lane) {
+FP_HD PieceLoc piece_loc(int STR, int t, int lane, int data_chunks) {
     const int pb = t * PIECE + lane * 16;
     const int row = pb / STR;
-    return PieceLoc{row, (pb - row * STR) >> 4};
+    const int ch = (pb - row * STR) >> 4;
+    return PieceLoc{row, ch < data_chunks ? ch : data_chunks - 1};
 }
 
 // Per-lane byte offsets (from the tile's first key row) of the pieces this
 // lane loads for contiguous K/V, computed once per workgroup; wavefront w of
-// NW loads pieces w, w + NW, ... Unsigned 32-bit offsets from a uniform base
-// let each load use the scalar-base addressing form.
+// NW loads pieces w, w + NW, ... (piece k * NW + w exists for k < NP - 1 on
+// every wavefront, for the last k only when has(k, w)). Unsigned 32-bit
+// offsets from a uniform base let each load use the scalar-base form.
 template <int STR, int BLK, int ESZ, bool PERM, int NW>
 struct TileOffs {
     static constexpr int PIECES = BLK * STR / PIECE;
     static constexpr int NP = (PIECES + NW - 1) / NW;
-    static constexpr uint32_t PAD = 0xFFFFFFFFu;     // lane lands on row padding (or past the last piece)
     uint32_t off[NP];
+    // whether wavefront `wave` loads a k-th piece (uniform; compile-time true but for the last k)
+    static FP_HD bool has(int k, int wave) { return k < NP - 1 || PIECES % NW == 0 || k * NW + wave < PIECES; }
     FP_HD void init(long long tok_stride, int wave, int lane) {
 #pragma unroll
         for (int k = 0; k < NP; ++k) {
-            const int t = k * NW + wave;
-            const PieceLoc pl = piece_loc(STR, t, lane);
+            const PieceLoc pl = piece_loc(STR, k * NW + wave, lane, 8 * ESZ);
             const int key = PERM ? vt_slot(pl.row) : pl.row;
-            off[k] = (t < PIECES && pl.ch < 8 * ESZ) ? (uint32_t)(key * tok_stride * ESZ + pl.ch * 16) : PAD;
+            off[k] = has(k, wave) ? (uint32_t)(key * tok_stride * ESZ + pl.ch * 16) : 0u;
         }
     }
     // Paged K/V: key `key` of a tile lies in page slot key >> lshift of the
@@ -93,14 +98,12 @@ struct TileOffs {
     FP_HD void init_paged(long long tok_stride, int lshift, int wave, int lane) {
 #pragma unroll
         for (int k = 0; k < NP; ++k) {
-            const int t = k * NW + wave;
-            const PieceLoc pl = piece_loc(STR, t, lane);
+            const PieceLoc pl = piece_loc(STR, k * NW + wave, lane, 8 * ESZ);
             const int key = PERM ? vt_slot(pl.row) : pl.row;
             const uint32_t inpage = (uint32_t)((key & ((1 << lshift) - 1)) * tok_stride * ESZ + pl.ch * 16);
-            off[k] = (t < PIECES && pl.ch < 8 * ESZ) ? (inpage | ((uint32_t)(key >> lshift) << 24)) : PAD;
+            off[k] = has(k, wave) ? (inpage | ((uint32_t)(key >> lshift) << 24)) : 0u;
         }
     }
-    FP_HD bool active(int k) const { return off[k] != PAD; }
     // byte address, relative to the tensor base, of piece k of a full
     // contiguous tile whose first key row is at byte tile_base
     FP_HD long long src_full(long long tile_base, int k) const { return tile_base + off[k]; }
@@ -110,16 +113,14 @@ struct TileOffs {
 };
 
 // Byte offset (relative to the tensor base) of the 16 bytes lane `lane`
-// loads for piece t of key block j in the generic path (ragged tile, or a
-// paged tile without the fast offsets), or -1 when the lane lands on row
-// padding. Rows past the sequence repeat its last key. pages: the
-// sequence's page ids (staged), or null to read the block table.
+// loads for piece t (< the tile's pieces) of key block j in the generic path
+// (ragged tile, or a paged tile without the fast offsets). Rows past the
+// sequence repeat its last key. pages: the sequence's page ids (staged), or
+// have_pages false to read the block table.
 template <int STR, int BLK, int ESZ, bool PERM, bool PAGED, typename PageFn>
 FP_HD long long tile_src(const KVAddr& ka, int b, int L, int g, int j, int t, int lane, PageFn pages,
                          bool have_pages) {
-    constexpr int PIECES = BLK * STR / PIECE;
-    const PieceLoc pl = piece_loc(STR, t, lane);
-    if (t >= PIECES || pl.ch >= 8 * ESZ) return -1;
+    const PieceLoc pl = piece_loc(STR, t, lane, 8 * ESZ);
     const int key = PERM ? vt_slot(pl.row) : pl.row;
     const int rmax = L - 1 - j * BLK;
     const int sk = j * BLK + (key < rmax ? key : rmax);
@@ -132,8 +133,8 @@ FP_HD long long tile_src(const KVAddr& ka, int b, int L, int g, int j, int t, in
 // of piece t of the K (w = 0) or V (w = 1) part. K rows 0 .. SUMC-1 hold the
 // bf16 hi parts of those pooled keys, rows SUMC .. BLK-1 the lo parts; V rows
 // the bf16 pooled values. Returns the element offset into the hi / lo / V
-// array (which = 0, 1, 2) or -1 for row padding. Columns past the sequence's
-// last block repeat it (they are masked out).
+// array (which = 0, 1, 2). Columns past the sequence's last block repeat it
+// (they are masked out).
 struct SummarySrc {
     int which;
     long long off;
@@ -141,8 +142,7 @@ struct SummarySrc {
 template <int BLK>
 FP_HD SummarySrc summary_src(const SeqDesc& s, int Hkv, int g, int m, int w, int t, int lane) {
     constexpr int SUMC = BLK / 2;
-    const PieceLoc pl = piece_loc(w == 0 ? KSTR : VSTR, t, lane);
-    if (pl.ch >= 16) return SummarySrc{-1, -1};
+    const PieceLoc pl = piece_loc(w == 0 ? KSTR : VSTR, t, lane, 16);
     const int part = w == 0 && pl.row >= SUMC;          // 0 hi / 1 lo (K rows)
     const int jc = SUMC * m + pl.row - part * SUMC;
     const int jp = jc < s.nbk - 1 ? jc : s.nbk - 1;

@@ -160,7 +160,7 @@ __device__ __forceinline__ void issue_full(const TileOffs<STR, BLK, ESZ, PERM, N
                                            lds_u8* buf, int wave) {
 #pragma unroll
     for (int k = 0; k < o.NP; ++k)
-        if (o.active(k))
+        if (o.has(k, wave))
             __builtin_amdgcn_global_load_lds((const void*)(tile_base + o.off[k]),
                                              (lds_void*)(buf + (k * NW + wave) * PIECE), 16, 0, 0);
 }
@@ -172,9 +172,9 @@ __device__ __forceinline__ void issue_full(const TileOffs<STR, BLK, ESZ, PERM, N
 // them (it cannot tell the page list from the buffers being filled).
 template <int STR, int BLK, int ESZ, bool PERM, int NW>
 __device__ __forceinline__ void read_pages(const TileOffs<STR, BLK, ESZ, PERM, NW>& o, const lds_int* pages,
-                                           int (&pg)[TileOffs<STR, BLK, ESZ, PERM, NW>::NP]) {
+                                           int (&pg)[TileOffs<STR, BLK, ESZ, PERM, NW>::NP], int wave) {
 #pragma unroll
-    for (int k = 0; k < o.NP; ++k) pg[k] = o.active(k) ? pages[o.page_slot(k)] : 0;
+    for (int k = 0; k < o.NP; ++k) pg[k] = o.has(k, wave) ? pages[o.page_slot(k)] : 0;
 }
 template <int STR, int BLK, int ESZ, bool PERM, int NW>
 __device__ __forceinline__ void issue_paged(const TileOffs<STR, BLK, ESZ, PERM, NW>& o, const uint8_t* base,
@@ -182,7 +182,7 @@ __device__ __forceinline__ void issue_paged(const TileOffs<STR, BLK, ESZ, PERM, 
                                             unsigned long long page_bytes, lds_u8* buf, int wave) {
 #pragma unroll
     for (int k = 0; k < o.NP; ++k)
-        if (o.active(k))
+        if (o.has(k, wave))
             __builtin_amdgcn_global_load_lds(
                 (const void*)(base + (unsigned long long)pg[k] * page_bytes + o.in_page(k)),
                 (lds_void*)(buf + (k * NW + wave) * PIECE), 16, 0, 0);
@@ -193,20 +193,21 @@ __device__ __forceinline__ void issue_paged(const TileOffs<STR, BLK, ESZ, PERM, 
 template <int STR, int BLK, int ESZ, bool PERM, bool PAGED, int NW>
 __device__ __forceinline__ void issue_generic(const uint8_t* base, const KVAddr& ka, int b, int L, int g, int j,
                                               lds_u8* buf, int wave, int lane, const lds_int* pages) {
-    constexpr int PIECES = BLK * STR / PIECE;
-    constexpr int NP = (PIECES + NW - 1) / NW;
+    using TO = TileOffs<STR, BLK, ESZ, PERM, NW>;
     asm volatile("" : "+v"(lane));   // recompute addresses per call, keep none live
-    long long src[NP];
+    const uint8_t* src[TO::NP];
     auto pg = [&](int slot) { return pages[slot]; };
 #pragma unroll
-    for (int k = 0; k < NP; ++k)
-        src[k] = tile_src<STR, BLK, ESZ, PERM, PAGED>(ka, b, L, g, j, k * NW + wave, lane, pg, pages != nullptr);
+    for (int k = 0; k < TO::NP; ++k)
+        src[k] = TO::has(k, wave) ? base + tile_src<STR, BLK, ESZ, PERM, PAGED>(ka, b, L, g, j, k * NW + wave, lane,
+                                                                                 pg, pages != nullptr)
+                                  : base;
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int k = 0; k < NP; ++k)
-        if (src[k] >= 0)
-            __builtin_amdgcn_global_load_lds((const void*)(base + src[k]),
-                                             (lds_void*)(buf + (k * NW + wave) * PIECE), 16, 0, 0);
+    for (int k = 0; k < TO::NP; ++k)
+        if (TO::has(k, wave))
+            __builtin_amdgcn_global_load_lds((const void*)src[k], (lds_void*)(buf + (k * NW + wave) * PIECE), 16,
+                                             0, 0);
 }
 
 template <int BLK, bool FP8, int NW>
@@ -227,8 +228,8 @@ __device__ __forceinline__ void issue_kv(const AttnArgs& a, int b, int L, int g,
         const long long ub = (long long)((j * BLK) & ((1 << sh) - 1)) * a.ka.st + (long long)g * a.ka.sh;
         const lds_int* pt = pages + ((j * BLK) >> sh);
         int pgk[KVOffs<BLK, FP8, NW>::NPK], pgv[KVOffs<BLK, FP8, NW>::NPV];
-        read_pages(o.k, pt, pgk);
-        read_pages(o.v, pt, pgv);
+        read_pages(o.k, pt, pgk, wave);
+        read_pages(o.v, pt, pgv, wave);
         __builtin_amdgcn_sched_barrier(0);
         issue_paged(o.k, (const uint8_t*)a.k + ub * ESZ, pgk, (unsigned long long)a.ka.spage * ESZ, kbuf, wave);
         issue_paged(o.v, (const uint8_t*)a.v + ub * ESZ, pgv, (unsigned long long)a.va.spage * ESZ, vbuf, wave);
@@ -266,7 +267,6 @@ __device__ __forceinline__ void issue_summary(const AttnArgs& a, const SeqDesc& 
             const int t = t0 + wave;
             if (t < (w == 0 ? KP : VP)) {
                 const SummarySrc src = summary_src<BLK>(s, a.Hkv, g, m, w, t, lane);
-                if (src.which < 0) continue;
                 const __bf16* arr = src.which == 0 ? a.kbar_hi : (src.which == 1 ? a.kbar_lo : a.vbar_bf);
                 __builtin_amdgcn_global_load_lds((const void*)(arr + src.off), (lds_void*)(buf + t * PIECE), 16, 0,
                                                  0);

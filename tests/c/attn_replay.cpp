@@ -252,12 +252,12 @@ static void replay(const Launch& L) {
                             const long long k0 = ka.template off<false>(b, code * BLK, g) * ESZ;
                             const long long v0 = va.template off<false>(b, code * BLK, g) * ESZ;
                             for (int k = 0; k < ko.NP; ++k)
-                                if (ko.active(k)) {
+                                if (ko.has(k, wave)) {
                                     check_kv(ko.src_full(k0, k), kbytes, "K tile");
                                     CHECK((k * NW + wave) * PIECE + 16 * lane + 16 <= TG::KTILE, "K LDS piece");
                                 }
                             for (int k = 0; k < vo.NP; ++k)
-                                if (vo.active(k)) {
+                                if (vo.has(k, wave)) {
                                     check_kv(vo.src_full(v0, k), vbytes, "V tile");
                                     CHECK((k * NW + wave) * PIECE + 16 * lane + 16 <= TG::VTILE, "V LDS piece");
                                 }
@@ -270,14 +270,14 @@ static void replay(const Launch& L) {
                                 (long long)((code * BLK) & ((1 << sh) - 1)) * ka.st + (long long)g * ka.sh;
                             const int slot0 = (code * BLK) >> sh;
                             for (int k = 0; k < ko.NP; ++k)
-                                if (ko.active(k)) {
+                                if (ko.has(k, wave)) {
                                     const int pg = page_of(slot0 + ko.page_slot(k));
                                     check_kv(ub * ESZ + (long long)pg * ka.spage * ESZ + ko.in_page(k), kbytes,
                                              "K paged tile");
                                     CHECK((k * NW + wave) * PIECE + 16 * lane + 16 <= TG::KTILE, "K LDS piece");
                                 }
                             for (int k = 0; k < vo.NP; ++k)
-                                if (vo.active(k)) {
+                                if (vo.has(k, wave)) {
                                     const int pg = page_of(slot0 + vo.page_slot(k));
                                     check_kv(ub * ESZ + (long long)pg * va.spage * ESZ + vo.in_page(k), vbytes,
                                              "V paged tile");
@@ -286,17 +286,19 @@ static void replay(const Launch& L) {
                         } else {
                             auto pf = [&](int slot) { return page_of(slot); };
                             for (int k = 0; k < ko.NP; ++k) {
+                                if (!ko.has(k, wave)) continue;
                                 const long long src = tile_src<TG::KS, BLK, ESZ, false, PAGED>(
                                     ka, b, s.L, g, code, k * NW + wave, lane, pf, staged);
-                                if (src >= 0) {
+                                {
                                     check_kv(src, kbytes, "K generic tile");
                                     CHECK((k * NW + wave) * PIECE + 16 * lane + 16 <= TG::KTILE, "K LDS piece");
                                 }
                             }
                             for (int k = 0; k < vo.NP; ++k) {
+                                if (!vo.has(k, wave)) continue;
                                 const long long src = tile_src<TG::VS, BLK, ESZ, FP8, PAGED>(
                                     va, b, s.L, g, code, k * NW + wave, lane, pf, staged);
-                                if (src >= 0) {
+                                {
                                     check_kv(src, vbytes, "V generic tile");
                                     CHECK((k * NW + wave) * PIECE + 16 * lane + 16 <= TG::VTILE, "V LDS piece");
                                 }
@@ -314,7 +316,7 @@ static void replay(const Launch& L) {
                             if (t >= P) continue;
                             for (int lane = 0; lane < 64; ++lane) {
                                 const SummarySrc src = summary_src<BLK>(s, L.Hkv, g, m, w, t, lane);
-                                if (src.which < 0) continue;
+                                CHECK(src.which >= 0 && src.which <= 2, "summary array %d", src.which);
                                 CHECK(src.off >= 0 && src.off + 8 <= L.pooled_rows * D, "summary source %lld",
                                       src.off);
                                 CHECK(t * PIECE + 16 * lane + 16 <= (w == 0 ? TG::KTILE : TG::VTILE),

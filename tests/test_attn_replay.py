@@ -47,8 +47,10 @@ MUTANTS = [
      "const int sk = j * BLK + (key < rmax ? key : rmax);", "const int sk = j * BLK + key;"),
     ("summary column not clamped to the last block",
      "const int jp = jc < s.nbk - 1 ? jc : s.nbk - 1;", "const int jp = jc;"),
-    ("pieces past the tile not masked",
-     "off[k] = (t < PIECES && pl.ch < 8 * ESZ) ? (uint32_t)(key * tok_stride", "off[k] = (pl.ch < 8 * ESZ) ? (uint32_t)(key * tok_stride"),
+    ("pieces past the tile loaded",
+     "return k < NP - 1 || PIECES % NW == 0 || k * NW + wave < PIECES;", "return true;"),
+    ("padding chunks not redirected to the row's data",
+     "return PieceLoc{row, ch < data_chunks ? ch : data_chunks - 1};", "return PieceLoc{row, ch};"),
     ("packed rows of a 4-wavefront slice overlap",
      "return slice * 256 + wave * (32 * RG) + rg * 32 + n;", "return slice * 256 + wave * 32 + rg * 32 + n;"),
 ]
