@@ -144,12 +144,12 @@ def graph_replay_ms(fp, inp, tau, replays=20):
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        fp.sparse_prefill(q, k, v, inp.cfg.block, tau)
+        fp.sparse_prefill_fused(q, k, v, inp.cfg.block, tau)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        fp.sparse_prefill(q, k, v, inp.cfg.block, tau)
+        fp.sparse_prefill_fused(q, k, v, inp.cfg.block, tau)
     g.replay()
     torch.cuda.synchronize()
     ts = []
@@ -202,12 +202,14 @@ def ablation_vs_dense(fp, inp, taus=(2.0, 4.0, 8.0), chunk=8192):
     return res
 
 
-def time_path(fp, N, inp, tau, steps, warmup, label, flush_bytes=0, keep_outputs=False):
+def time_path(fp, N, inp, tau, steps, warmup, label, flush_bytes=0, keep_outputs=False, fused=True):
     """Run the path `warmup` + `steps` times; HIP events per stage on the
-    current stream (the library launches on it). flush_bytes > 0: before each
-    timed step a buffer of that size is overwritten (outside the events), so
-    L2 and the memory-side cache start cold. keep_outputs: also return the
-    outputs of KV head 0's query heads (host, fp32) and lse."""
+    current stream (the library launches on it). fused: fp_estimate_select +
+    fp_sparse_prefill (no score matrix); otherwise the three calls
+    fp_block_scores + fp_select_blocks + fp_sparse_prefill. flush_bytes > 0:
+    before each timed step a buffer of that size is overwritten (outside the
+    events), so L2 and the memory-side cache start cold. keep_outputs: also
+    return the outputs of KV head 0's query heads (host, fp32) and lse."""
     import torch
     dev = torch.device("cuda:0")
     q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
@@ -220,12 +222,13 @@ def time_path(fp, N, inp, tau, steps, warmup, label, flush_bytes=0, keep_outputs
     qbar = torch.empty((c.batch, c.num_q_heads, p.nb, 128), **f32)
     kbar = torch.empty((c.batch, c.num_kv_heads, p.nb, 128), **f32)
     vbar = torch.empty((c.batch, c.num_kv_heads, p.nb, 128), **f32)
-    scores = torch.empty((c.batch, c.num_q_heads, p.nb, p.nb), **f32)
+    scores = None if fused else torch.empty((c.batch, c.num_q_heads, p.nb, p.nb), **f32)
     row_ptr = torch.empty(p.rows + 1, **i32)
     col_idx = torch.empty(p.max_nnz, **i32)
     sched = torch.empty(p.rows, **i32)
     lib = N.load()
-    ws = torch.empty(N.check_size(lib.fp_workspace_size(p.ref)), dtype=torch.uint8, device=dev)
+    ws = torch.empty(N.check_size(lib.fp_estimate_select_workspace_size(p.ref) if fused
+                                  else lib.fp_workspace_size(p.ref)), dtype=torch.uint8, device=dev)
     ws2 = torch.empty(N.check_size(lib.fp_prefill_workspace_size(p.ref)), dtype=torch.uint8, device=dev)
     o = torch.empty((c.batch, c.seqlen, c.num_q_heads, 128), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((c.batch, c.num_q_heads, c.seqlen), **f32)
@@ -234,12 +237,19 @@ def time_path(fp, N, inp, tau, steps, warmup, label, flush_bytes=0, keep_outputs
     sh = stream.cuda_stream
 
     def step():
-        N.check(lib.fp_block_scores(p.ref, P(q), P(k), P(v), P(sc[0]), P(sc[1]), P(sc[2]), P(qbar),
-                                    P(kbar), P(vbar), P(scores), sh))
-        ev[1].record(stream)
-        N.check(lib.fp_select_blocks(p.ref, P(scores), float(tau), P(row_ptr), P(col_idx), p.max_nnz,
-                                     P(sched), P(ws), ws.numel(), sh))
-        ev[2].record(stream)
+        if fused:
+            N.check(lib.fp_estimate_select(p.ref, P(q), P(k), P(v), P(sc[0]), P(sc[1]), P(sc[2]), float(tau),
+                                           P(qbar), P(kbar), P(vbar), P(row_ptr), P(col_idx), p.max_nnz,
+                                           P(sched), P(ws), ws.numel(), sh))
+            ev[1].record(stream)
+            ev[2].record(stream)
+        else:
+            N.check(lib.fp_block_scores(p.ref, P(q), P(k), P(v), P(sc[0]), P(sc[1]), P(sc[2]), P(qbar),
+                                        P(kbar), P(vbar), P(scores), sh))
+            ev[1].record(stream)
+            N.check(lib.fp_select_blocks(p.ref, P(scores), float(tau), P(row_ptr), P(col_idx), p.max_nnz,
+                                         P(sched), P(ws), ws.numel(), sh))
+            ev[2].record(stream)
         N.check(lib.fp_sparse_prefill(p.ref, P(q), P(k), P(v), P(sc[0]), P(sc[1]), P(sc[2]), P(kbar),
                                       P(vbar), P(row_ptr), P(col_idx), P(sched), P(o), P(lse), P(ws2),
                                       ws2.numel(), sh))
@@ -291,13 +301,21 @@ def time_path(fp, N, inp, tau, steps, warmup, label, flush_bytes=0, keep_outputs
     res["dense_equiv_tflops"] = dense / (res["ms_per_step"] * 1e-3) / 1e12
     res["attn_kept_tflops"] = kept / (res["ms_attention"] * 1e-3) / 1e12
     res["attn_executed_tflops"] = (kept + corr) / (res["ms_attention"] * 1e-3) / 1e12
-    # estimator: reads Q, K, V once and writes pooled rows + full score matrix
+    # estimator: reads Q, K, V once and writes pooled rows (+ the full score
+    # matrix on the three-call path); selection reads the causal half of the
+    # scores there and writes the CSR and schedule
     esz = 1 if inp.q.dtype == torch.uint8 else 2
+    n_s = 0 if scores is None else scores.numel()
     est_bytes = (q.numel() + k.numel() + v.numel()) * esz + (qbar.numel() + kbar.numel() + vbar.numel()
-                                                             + scores.numel()) * 4
-    res["estimate_gbs"] = est_bytes / (res["ms_estimate"] * 1e-3) / 1e9
-    sel_bytes = scores.numel() * 4 // 2 + (len(ci) + 3 * p.rows) * 4
-    res["select_gbs"] = sel_bytes / (res["ms_select"] * 1e-3) / 1e9
+                                                             + n_s) * 4
+    sel_bytes = n_s * 4 // 2 + (len(ci) + 3 * p.rows) * 4
+    res["ms_estimate_select"] = res["ms_estimate"] + res["ms_select"]
+    if fused:
+        res["estimate_gbs"] = (est_bytes + sel_bytes) / (res["ms_estimate_select"] * 1e-3) / 1e9
+        res["select_gbs"] = None
+    else:
+        res["estimate_gbs"] = est_bytes / (res["ms_estimate"] * 1e-3) / 1e9
+        res["select_gbs"] = sel_bytes / (res["ms_select"] * 1e-3) / 1e9
     outs = None
     if keep_outputs:
         outs = (o[0, :, :G].float().cpu().numpy(), lse[0, :G].cpu().numpy())
@@ -473,6 +491,8 @@ def main():
                     help="skip the smaller fixed-shape configurations (S=2048 and S=32768)")
     ap.add_argument("--no-ablation", action="store_true",
                     help="skip the error-vs-dense comparison with and without the mean correction")
+    ap.add_argument("--no-unfused", action="store_true",
+                    help="skip the three-call path (fp_block_scores + fp_select_blocks, score matrix in HBM)")
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the dense baseline legs (fp_dense_prefill in bf16 and fp8)")
     ap.add_argument("--no-sweep", action="store_true",
@@ -549,6 +569,18 @@ def main():
             log(f"sweep tau={tau}: {json.dumps(sweep[str(tau)])}")
         dense, _ = time_path(fp, N, inputs["bf16"], float("inf"), 2, 1, "bf16 dense")
         log(f"dense (tau=inf): {json.dumps(dense)}")
+    three_call = {}
+    if not args.no_unfused:
+        # the same workload through the three-call path (score matrix in HBM)
+        for kind in ("bf16", "fp8"):
+            if kind not in inputs:
+                continue
+            r, _ = time_path(fp, N, inputs[kind], args.tau, 10, 3, f"{kind} three calls", fused=False)
+            three_call[kind] = {"ms_per_layer_median": round(r["ms_step_median"], 4),
+                                "ms_estimate": round(r["ms_estimate"], 4), "ms_select": round(r["ms_select"], 4),
+                                "estimator_gbs": round(r["estimate_gbs"], 1),
+                                "select_gbs": round(r["select_gbs"], 1)}
+            log(f"three-call path {kind}: {json.dumps(three_call[kind])}")
     dense_base = {}
     if not args.no_dense:
         for kind, res in (("bf16", bf), ("fp8", f8)):
@@ -584,15 +616,17 @@ def main():
                                f"16 planted blocks per KV head, seed {cfg.seed}",
                    "seq_len": cfg.S, "batch": 1, "tau": args.tau, "block": 128},
         "kept_fraction": round(bf["kept_fraction"], 5),
-        "ms_per_layer": {"total": round(bf["ms_per_step"], 4), "estimate": round(bf["ms_estimate"], 4),
-                         "select": round(bf["ms_select"], 4), "attention": round(bf["ms_attention"], 4)},
+        "path": "fp_estimate_select (pooling + fused block scores/threshold/CSR/schedule, no score matrix) "
+                "+ fp_sparse_prefill",
+        "ms_per_layer": {"total": round(bf["ms_per_step"], 4),
+                         "estimate_select": round(bf["ms_estimate_select"], 4),
+                         "attention": round(bf["ms_attention"], 4)},
         "ms_per_layer_median": {"total": round(bf["ms_step_median"], 4),
                                 "attention": round(bf["ms_attention_median"], 4)},
         "mfma_util_kept": round(bf["attn_kept_tflops"] / att_peak, 4),
         "mfma_util_executed": round(bf["attn_executed_tflops"] / att_peak, 4),
-        "estimator_gbs": round(bf["estimate_gbs"], 1), "select_gbs": round(bf["select_gbs"], 1),
-        "estimator_hbm_frac": round(bf["estimate_gbs"] / HBM_GBS, 4),
-        "select_hbm_frac": round(bf["select_gbs"] / HBM_GBS, 4),
+        "estimate_select_gbs": round(bf["estimate_gbs"], 1),
+        "estimate_select_hbm_frac": round(bf["estimate_gbs"] / HBM_GBS, 4),
         "roofline": {"bound": "mfma", "kernel": "attn_tile_kernel<128, bf16> (fp_sparse_prefill)",
                      "achieved": round(bf["attn_kept_tflops"], 2), "peak": att_peak,
                      "unit": "TFLOP/s", "frac": round(bf["attn_kept_tflops"] / att_peak, 4),
@@ -605,7 +639,8 @@ def main():
                        "kept_fraction": round(f8["kept_fraction"], 5),
                        "attn_kept_tflops": round(f8["attn_kept_tflops"], 2),
                        "mfma_util_kept": round(f8["attn_kept_tflops"] / PEAK_TFLOPS["fp8"], 4),
-                       "estimator_gbs": round(f8["estimate_gbs"], 1)}
+                       "ms_estimate_select": round(f8["ms_estimate_select"], 4),
+                       "estimate_select_gbs": round(f8["estimate_gbs"], 1)}
     if cold is not None:
         line["cold_cache"] = {"runs": 5, "flush": "1 GiB written before each step",
                               "ms_per_layer_median": round(cold["ms_step_median"], 4),
@@ -625,6 +660,8 @@ def main():
                                    "attn_tflops": round(dense["attn_kept_tflops"], 2),
                                    "mfma_util": round(dense["attn_kept_tflops"] / att_peak, 4),
                                    "sparse_speedup": round(dense["ms_per_step"] / bf["ms_per_step"], 2)}
+    if three_call:
+        line["three_call_path"] = three_call
     if dense_base:
         # fp_dense_prefill: every block kept, no estimate/selection/correction
         dense_base["context"] = ("the pages' H20 speedups at 128K, for context only (other hardware, other "

@@ -12,6 +12,7 @@ Entry points (same names as the C ABI):
   fp_sparse_prefill_paged  all of it for a paged varlen batch
   fp_sparse_prefill_noalloc  fp_sparse_prefill without a workspace (static scratch)
   fp_dense_prefill         dense causal attention on the same kernel (the baseline)
+  fp_estimate_select       E1-E5 without a score matrix (fused estimate + selection)
 and sparse_prefill(), which chains the first three.
 """
 from __future__ import annotations
@@ -30,7 +31,8 @@ from ._native import FpError, FpProblem, FpVarlenProblem
 __all__ = [
     "FpError", "Problem", "make_problem", "fp_block_scores", "fp_select_blocks",
     "fp_sparse_prefill", "fp_sparse_prefill_paged", "sparse_prefill", "version",
-    "make_varlen_problem", "fp_sparse_prefill_noalloc", "fp_dense_prefill",
+    "make_varlen_problem", "fp_sparse_prefill_noalloc", "fp_dense_prefill", "fp_estimate_select",
+    "sparse_prefill_fused",
 ]
 
 
@@ -227,6 +229,46 @@ def fp_sparse_prefill(p: Problem, q, k, v, kbar, vbar, row_ptr, col_idx, sched=N
                                   _ptr(col_idx), _ptr(sched), _ptr(o), _ptr(lse), _ptr(workspace),
                                   workspace.numel(), _stream()))
     return o, lse
+
+
+def fp_estimate_select(p: Problem, q, k, v, tau: float, q_scale=None, k_scale=None, v_scale=None,
+                       with_sched: bool = True, workspace: Optional[torch.Tensor] = None):
+    """E1-E5 without a score matrix -> (qbar, kbar, vbar, row_ptr, col_idx, sched);
+    the kept lists equal fp_block_scores + fp_select_blocks bit for bit."""
+    c = p.c
+    _check_qkv(p, q, k, v)
+    _check_scales(p.fp8, c.batch, c.num_q_heads, c.num_kv_heads, (c.seqlen + 127) // 128, q_scale, k_scale,
+                  v_scale)
+    dev = q.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    qbar = torch.empty((c.batch, c.num_q_heads, p.nb, 128), **f32)
+    kbar = torch.empty((c.batch, c.num_kv_heads, p.nb, 128), **f32)
+    vbar = torch.empty((c.batch, c.num_kv_heads, p.nb, 128), **f32)
+    row_ptr = torch.empty(p.rows + 1, **i32)
+    col_idx = torch.empty(p.max_nnz, **i32)
+    sched = torch.empty(p.rows, **i32) if with_sched else None
+    lib = N.load()
+    if workspace is None:
+        workspace = torch.empty(N.check_size(lib.fp_estimate_select_workspace_size(p.ref)), dtype=torch.uint8,
+                                device=dev)
+    N.check(lib.fp_estimate_select(p.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale),
+                                   float(tau), _ptr(qbar), _ptr(kbar), _ptr(vbar), _ptr(row_ptr), _ptr(col_idx),
+                                   p.max_nnz, _ptr(sched), _ptr(workspace), workspace.numel(), _stream()))
+    return qbar, kbar, vbar, row_ptr, col_idx, sched
+
+
+def sparse_prefill_fused(q, k, v, block: int, tau: float, softmax_scale: float = 0.0,
+                         q_scale=None, k_scale=None, v_scale=None, with_lse: bool = True,
+                         out_fp32: bool = False, correction: bool = True):
+    """The path in two calls: fp_estimate_select (no score matrix) then
+    fp_sparse_prefill. Returns a dict of device tensors."""
+    p = make_problem(q, k, v, block, softmax_scale, out_fp32=out_fp32, correction=correction)
+    qbar, kbar, vbar, row_ptr, col_idx, sched = fp_estimate_select(p, q, k, v, tau, q_scale, k_scale, v_scale)
+    o, lse = fp_sparse_prefill(p, q, k, v, kbar, vbar, row_ptr, col_idx, sched,
+                               q_scale, k_scale, v_scale, with_lse)
+    return dict(problem=p, qbar=qbar, kbar=kbar, vbar=vbar, row_ptr=row_ptr, col_idx=col_idx, sched=sched,
+                o=o, lse=lse)
 
 
 def fp_dense_prefill(p: Problem, q, k, v, q_scale=None, k_scale=None, v_scale=None, with_lse: bool = True,

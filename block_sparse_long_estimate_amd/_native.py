@@ -27,6 +27,7 @@ EXPORTS = (
     "fp_block_scores", "fp_select_blocks", "fp_sparse_prefill",
     "fp_varlen_num_rows", "fp_varlen_max_nnz", "fp_varlen_workspace_size",
     "fp_sparse_prefill_paged", "fp_sparse_prefill_noalloc", "fp_dense_prefill",
+    "fp_estimate_select", "fp_estimate_select_workspace_size",
 )
 FP_NOALLOC_MAX_POOLED_ROWS = 32768
 
@@ -72,7 +73,8 @@ def load() -> ctypes.CDLL:
     vp, i32p = ctypes.c_void_p, ctypes.c_void_p
     lib.fp_version.restype = ctypes.c_char_p
     lib.fp_last_error.restype = ctypes.c_char_p
-    for name in ("fp_num_rows", "fp_max_nnz", "fp_workspace_size", "fp_prefill_workspace_size"):
+    for name in ("fp_num_rows", "fp_max_nnz", "fp_workspace_size", "fp_prefill_workspace_size",
+                 "fp_estimate_select_workspace_size"):
         f = getattr(lib, name)
         f.restype, f.argtypes = ctypes.c_int64, [P]
     for name in ("fp_varlen_num_rows", "fp_varlen_max_nnz", "fp_varlen_workspace_size"):
@@ -86,6 +88,9 @@ def load() -> ctypes.CDLL:
     lib.fp_sparse_prefill.restype = ctypes.c_int
     lib.fp_sparse_prefill.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                       ctypes.c_size_t, vp]
+    lib.fp_estimate_select.restype = ctypes.c_int
+    lib.fp_estimate_select.argtypes = [P, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp,
+                                       ctypes.c_int64, vp, vp, ctypes.c_size_t, vp]
     lib.fp_dense_prefill.restype = ctypes.c_int
     lib.fp_dense_prefill.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.fp_sparse_prefill_noalloc.restype = ctypes.c_int

@@ -217,19 +217,14 @@ int64_t fp_workspace_size(const fp_problem* p) {
     return (int64_t)select_ws((long long)p->batch * p->num_kv_heads * nb, nb, fixed_sort_plan(p).ngrp).total;
 }
 
-int fp_block_scores(const fp_problem* p, const void* q, const void* k, const void* v,
-                    const float* q_scale, const float* k_scale, const float* v_scale,
-                    float* qbar, float* kbar, float* vbar, float* scores, void* stream) {
-    int rc = check_fixed(p);
-    if (rc) return rc;
-    if (!q || !k || !v || !qbar || !kbar || !vbar || !scores)
-        return fail(FP_ERR_INVALID, "fp_block_scores: NULL tensor pointer");
-    const bool fp8 = p->dtype == FP_DTYPE_FP8_E4M3;
-    if (fp8 && (!q_scale || !k_scale || !v_scale))
-        return fail(FP_ERR_INVALID, "fp_block_scores: fp8 needs q_scale, k_scale and v_scale");
-    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(qbar, 16) ||
-        misaligned(kbar, 16) || misaligned(vbar, 16))
-        return fail(FP_ERR_INVALID, "fp_block_scores: tensors must be 16-byte aligned");
+}  // extern "C"
+
+namespace {
+
+// Pooling (E1) of a checked fixed-shape problem.
+hipError_t fixed_pool(const fp_problem* p, const void* q, const void* k, const void* v, const float* q_scale,
+                      const float* k_scale, const float* v_scale, float* qbar, float* kbar, float* vbar,
+                      hipStream_t st) {
     GeoFixed geo = geo_fixed(p);
     const int nsb = cdiv(p->seqlen, SCALE_TOK);
     PoolArgs a;
@@ -242,17 +237,107 @@ int fp_block_scores(const fp_problem* p, const void* q, const void* k, const voi
     a.vs = ScaleAddr{v_scale, (long long)p->num_kv_heads * nsb, nsb};
     a.qbar = qbar; a.kbar = kbar; a.vbar = vbar;
     a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads; a.blk = p->block;
-    a.fp8 = fp8; a.paged = 0;
+    a.fp8 = p->dtype == FP_DTYPE_FP8_E4M3; a.paged = 0;
     a.total_qblocks = a.total_kblocks = p->batch * geo.nb;
-    hipStream_t st = (hipStream_t)stream;
-    hipError_t e = launch_pool(&geo, nullptr, a, st);
-    if (e != hipSuccess) return fail(FP_ERR_HIP, "pool launch: %s", hipGetErrorString(e));
+    return launch_pool(&geo, nullptr, a, st);
+}
+
+// Block scores (E2) of a checked fixed-shape problem into `scores`.
+hipError_t fixed_scores(const fp_problem* p, const float* qbar, const float* kbar, float* scores, hipStream_t st) {
+    GeoFixed geo = geo_fixed(p);
     ScoreArgs sa;
     sa.qbar = qbar; sa.kbar = kbar; sa.scores = scores;
     sa.Hq = p->num_q_heads; sa.Hkv = p->num_kv_heads;
     sa.total_tiles = p->batch * geo.ntile;
     sa.scale = default_scale(p->softmax_scale, p->head_dim);
-    e = launch_scores(&geo, nullptr, sa, st);
+    return launch_scores(&geo, nullptr, sa, st);
+}
+
+// Shared checks of the pooled-input arguments.
+int check_pool_args(const char* fn, const fp_problem* p, const void* q, const void* k, const void* v,
+                    const float* q_scale, const float* k_scale, const float* v_scale, const float* qbar,
+                    const float* kbar, const float* vbar) {
+    if (!q || !k || !v || !qbar || !kbar || !vbar) return fail(FP_ERR_INVALID, "%s: NULL tensor pointer", fn);
+    if (p->dtype == FP_DTYPE_FP8_E4M3 && (!q_scale || !k_scale || !v_scale))
+        return fail(FP_ERR_INVALID, "%s: fp8 needs q_scale, k_scale and v_scale", fn);
+    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(qbar, 16) ||
+        misaligned(kbar, 16) || misaligned(vbar, 16))
+        return fail(FP_ERR_INVALID, "%s: tensors must be 16-byte aligned", fn);
+    return FP_OK;
+}
+
+// Checks of the kept-list outputs and workspace of a selection; fills the
+// workspace carve.
+int check_select_args(const char* fn, const fp_problem* p, float tau, const int32_t* row_ptr,
+                      const int32_t* col_idx, int64_t capacity, const void* workspace, size_t ws_bytes,
+                      size_t ws_need) {
+    if (!row_ptr || !col_idx || !workspace) return fail(FP_ERR_INVALID, "%s: NULL pointer", fn);
+    if (isnan(tau)) return fail(FP_ERR_INVALID, "%s: tau is NaN", fn);
+    const int nb = cdiv(p->seqlen, p->block);
+    const long long rows = (long long)p->batch * p->num_kv_heads * nb;
+    const long long need = rows * (nb + 1) / 2;
+    if (capacity < need)
+        return fail(FP_ERR_CAPACITY, "%s: capacity %lld < max nnz %lld", fn, (long long)capacity, need);
+    if (ws_bytes < ws_need) return fail(FP_ERR_CAPACITY, "%s: workspace %zu < %zu bytes", fn, ws_bytes, ws_need);
+    if (misaligned(workspace, ALIGN)) return fail(FP_ERR_INVALID, "workspace must be 256-byte aligned");
+    return FP_OK;
+}
+
+SelectArgs fixed_select_args(const fp_problem* p, const SelectWs& w, const SortPlan& sp, void* workspace,
+                             float tau, int32_t* row_ptr, int32_t* col_idx, int32_t* sched) {
+    const int nb = cdiv(p->seqlen, p->block);
+    SelectArgs a{};
+    a.counts = (int32_t*)((char*)workspace + w.counts);
+    a.bits = (uint32_t*)((char*)workspace + w.bits);
+    a.keys = (int32_t*)((char*)workspace + w.keys);
+    a.maxc = (int32_t*)((char*)workspace + w.maxc);
+    a.hist = (int32_t*)((char*)workspace + w.hist);
+    a.nbw = w.nbw;
+    a.row_ptr = row_ptr; a.col_idx = col_idx; a.sched = sched;
+    a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads;
+    a.rows = p->batch * p->num_kv_heads * nb; a.max_nbk = nb;
+    a.ngrp = sp.ngrp; a.grp_units = sp.grp_units;
+    a.neg_tau = -tau;
+    a.scale = default_scale(p->softmax_scale, p->head_dim);
+    return a;
+}
+
+SelectWs fixed_select_ws(const fp_problem* p) {
+    const int nb = cdiv(p->seqlen, p->block);
+    return select_ws((long long)p->batch * p->num_kv_heads * nb, nb, fixed_sort_plan(p).ngrp);
+}
+
+// Workspace of fp_estimate_select: the selection's, plus the score matrix
+// when the sequence is too long for the fused kernel.
+size_t estimate_select_ws(const fp_problem* p) {
+    const int nb = cdiv(p->seqlen, p->block);
+    size_t total = fixed_select_ws(p).total;
+    if (nb > FUSED_MAX_NBK) total = align_up(total) + (size_t)p->batch * p->num_q_heads * nb * nb * 4;
+    return total;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t fp_estimate_select_workspace_size(const fp_problem* p) {
+    int rc = check_fixed(p);
+    if (rc) return rc;
+    return (int64_t)estimate_select_ws(p);
+}
+
+int fp_block_scores(const fp_problem* p, const void* q, const void* k, const void* v,
+                    const float* q_scale, const float* k_scale, const float* v_scale,
+                    float* qbar, float* kbar, float* vbar, float* scores, void* stream) {
+    int rc = check_fixed(p);
+    if (rc) return rc;
+    rc = check_pool_args("fp_block_scores", p, q, k, v, q_scale, k_scale, v_scale, qbar, kbar, vbar);
+    if (rc) return rc;
+    if (!scores) return fail(FP_ERR_INVALID, "fp_block_scores: NULL tensor pointer");
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = fixed_pool(p, q, k, v, q_scale, k_scale, v_scale, qbar, kbar, vbar, st);
+    if (e != hipSuccess) return fail(FP_ERR_HIP, "pool launch: %s", hipGetErrorString(e));
+    e = fixed_scores(p, qbar, kbar, scores, st);
     if (e != hipSuccess) return fail(FP_ERR_HIP, "scores launch: %s", hipGetErrorString(e));
     return ok();
 }
@@ -262,34 +347,47 @@ int fp_select_blocks(const fp_problem* p, const float* scores, float tau, int32_
                      size_t ws_bytes, void* stream) {
     int rc = check_fixed(p);
     if (rc) return rc;
-    if (!scores || !row_ptr || !col_idx || !workspace)
-        return fail(FP_ERR_INVALID, "fp_select_blocks: NULL pointer");
-    if (isnan(tau)) return fail(FP_ERR_INVALID, "fp_select_blocks: tau is NaN");
-    const int nb = cdiv(p->seqlen, p->block);
-    const long long rows = (long long)p->batch * p->num_kv_heads * nb;
-    const long long need = rows * (nb + 1) / 2;
-    if (capacity < need)
-        return fail(FP_ERR_CAPACITY, "fp_select_blocks: capacity %lld < max nnz %lld", (long long)capacity, need);
-    const SortPlan sp = fixed_sort_plan(p);
-    const SelectWs w = select_ws(rows, nb, sp.ngrp);
-    if (ws_bytes < w.total)
-        return fail(FP_ERR_CAPACITY, "fp_select_blocks: workspace %zu < %zu bytes", ws_bytes, w.total);
-    if (misaligned(workspace, ALIGN)) return fail(FP_ERR_INVALID, "workspace must be 256-byte aligned");
+    if (!scores) return fail(FP_ERR_INVALID, "fp_select_blocks: NULL pointer");
+    const SelectWs w = fixed_select_ws(p);
+    rc = check_select_args("fp_select_blocks", p, tau, row_ptr, col_idx, capacity, workspace, ws_bytes, w.total);
+    if (rc) return rc;
     GeoFixed geo = geo_fixed(p);
-    SelectArgs a;
+    SelectArgs a = fixed_select_args(p, w, fixed_sort_plan(p), workspace, tau, row_ptr, col_idx, sched);
     a.scores = scores;
-    a.counts = (int32_t*)((char*)workspace + w.counts);
-    a.bits = (uint32_t*)((char*)workspace + w.bits);
-    a.keys = (int32_t*)((char*)workspace + w.keys);
-    a.maxc = (int32_t*)((char*)workspace + w.maxc);
-    a.hist = (int32_t*)((char*)workspace + w.hist);
-    a.nbw = w.nbw;
-    a.row_ptr = row_ptr; a.col_idx = col_idx; a.sched = sched;
-    a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads;
-    a.rows = (int)rows; a.max_nbk = nb;
-    a.ngrp = sp.ngrp; a.grp_units = sp.grp_units;
-    a.neg_tau = -tau;
     hipError_t e = launch_select(&geo, nullptr, a, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(FP_ERR_HIP, "select launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int fp_estimate_select(const fp_problem* p, const void* q, const void* k, const void* v,
+                       const float* q_scale, const float* k_scale, const float* v_scale, float tau,
+                       float* qbar, float* kbar, float* vbar, int32_t* row_ptr, int32_t* col_idx,
+                       int64_t capacity, int32_t* sched, void* workspace, size_t ws_bytes, void* stream) {
+    int rc = check_fixed(p);
+    if (rc) return rc;
+    rc = check_pool_args("fp_estimate_select", p, q, k, v, q_scale, k_scale, v_scale, qbar, kbar, vbar);
+    if (rc) return rc;
+    rc = check_select_args("fp_estimate_select", p, tau, row_ptr, col_idx, capacity, workspace, ws_bytes,
+                           estimate_select_ws(p));
+    if (rc) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = fixed_pool(p, q, k, v, q_scale, k_scale, v_scale, qbar, kbar, vbar, st);
+    if (e != hipSuccess) return fail(FP_ERR_HIP, "pool launch: %s", hipGetErrorString(e));
+    const SelectWs w = fixed_select_ws(p);
+    GeoFixed geo = geo_fixed(p);
+    SelectArgs a = fixed_select_args(p, w, fixed_sort_plan(p), workspace, tau, row_ptr, col_idx, sched);
+    if (geo.nb <= FUSED_MAX_NBK) {
+        a.qbar = qbar; a.kbar = kbar;
+        e = launch_select_fused(geo, a, st);
+        if (e != hipSuccess) return fail(FP_ERR_HIP, "fused select launch: %s", hipGetErrorString(e));
+        return ok();
+    }
+    // longer sequences: the score rows do not fit the fused kernel's LDS
+    float* scores = (float*)((char*)workspace + align_up(w.total));
+    e = fixed_scores(p, qbar, kbar, scores, st);
+    if (e != hipSuccess) return fail(FP_ERR_HIP, "scores launch: %s", hipGetErrorString(e));
+    a.scores = scores;
+    e = launch_select(&geo, nullptr, a, st);
     if (e != hipSuccess) return fail(FP_ERR_HIP, "select launch: %s", hipGetErrorString(e));
     return ok();
 }

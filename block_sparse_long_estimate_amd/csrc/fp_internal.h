@@ -165,7 +165,14 @@ struct SelectArgs {
     int ngrp;                                   // schedule groups (rows sharing a K/V working set)
     long long grp_units;                        // group size in (key block x KV head) units
     float neg_tau;
+    // fused estimate + threshold (scores == nullptr): pooled rows and the softmax scale
+    const float* qbar; const float* kbar; float scale;
 };
+
+// Fused block scores + threshold: the workgroup's S columns (query block x
+// query head) and the largest key-block count whose S rows fit its LDS.
+constexpr int FUSED_COLS = 32;
+constexpr int FUSED_MAX_NBK = 1024;
 
 // Schedule group of the rows of (sequence s, KV head g): the (sequence, KV
 // head) pairs in row order are cut into groups of grp_units key blocks' worth
@@ -195,6 +202,8 @@ struct AttnArgs {
 hipError_t launch_pool(const GeoFixed* gf, const GeoTable* gt, const PoolArgs& a, hipStream_t st);
 hipError_t launch_scores(const GeoFixed* gf, const GeoTable* gt, const ScoreArgs& a, hipStream_t st);
 hipError_t launch_select(const GeoFixed* gf, const GeoTable* gt, const SelectArgs& a, hipStream_t st);
+// E2-E5 without a score matrix (fixed shape, key blocks <= FUSED_MAX_NBK), then the same compaction
+hipError_t launch_select_fused(const GeoFixed& gf, const SelectArgs& a, hipStream_t st);
 hipError_t launch_attn(const GeoFixed* gf, const GeoTable* gt, const AttnArgs& a, int blk,
                        int fp8, int paged, hipStream_t st);
 hipError_t launch_summary_prep(const float* kbar, const float* vbar, __bf16* hi, __bf16* lo,

@@ -77,6 +77,131 @@ __global__ __launch_bounds__(256) void select_rows_kernel(Geo geo, SelectArgs a)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Fused E2-E5 (fixed shape): the scores of a row are computed from the pooled
+// rows where they are needed and never written to HBM. One workgroup per
+// (sequence, KV head, QB = 32 / G query blocks): its S columns are the QB x G
+// (query block, query head) pairs, the rows are all key blocks, kept in LDS
+// (32 x (nbk + 1) floats). Each of the 8 wavefronts takes every 8th 32-key
+// tile and computes S^T = Kbar Qbar^T on v_mfma_f32_32x32x2_f32 with the
+// query side in registers and the next tile's pooled keys loaded while the
+// current one is multiplied; the dims are summed in the same order, pairing and scale as
+// scores_kernel, so every S value -- and every decision -- is the one the
+// unfused path makes. Then the row maxima (E3) per column, the group union
+// (E4) and the threshold (E5) per query block, ballot-compacted into the
+// same bit rows and counts select_rows_kernel writes.
+// ---------------------------------------------------------------------------
+constexpr int FUSED_WAVES = 8;
+
+__global__ __launch_bounds__(FUSED_WAVES * 64) void select_fused_kernel(GeoFixed geo, SelectArgs a) {
+    extern __shared__ __align__(16) float S_sh[];   // [FUSED_COLS][nbk + 1]
+    __shared__ float M_sh[FUSED_COLS];
+    typedef __attribute__((ext_vector_type(16))) float f32x16;
+    const float NEG_INF = -__builtin_inff();
+    const int G = a.Hq / a.Hkv;
+    const int QB = FUSED_COLS / G;
+    const int nb = geo.nb;
+    const int ntq = cdiv(nb, QB);
+    const int u = blockIdx.x;
+    const int bg = u / ntq, qt = u % ntq;
+    const int b = bg / a.Hkv, g = bg % a.Hkv;
+    const SeqDesc s = geo.seq(b);
+    const int il0 = qt * QB;
+    const int nql = min(QB, s.nq - il0);
+    const int cols = nql * G;
+    const int imax = s.i0 + il0 + nql - 1;
+    const int sst = nb + 1;                          // padded row stride of S_sh
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 31, lh = lane >> 5;
+
+    // query side of the MFMA: column n = (query block n / G, head n % G);
+    // step (pass p, t, component c) takes dim 32 p + 4 t + c from lanes 0-31
+    // and dim 32 p + 16 + 4 t + c from lanes 32-63, as scores_kernel does
+    float4 qv[4][4];
+    {
+        const bool ok = n < cols;
+        const int ql = ok ? n / G : 0, hh = ok ? n % G : 0;
+        const float* qr = a.qbar + qbar_row(s, a.Hq, g * G + hh, il0 + ql) * D;
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                qv[p][t] = ok ? *(const float4*)(qr + 32 * p + 16 * lh + 4 * t) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    const int nkt = imax / 32 + 1;
+    // pooled keys of key tile kt for this lane: row kt * 32 + n, the dims of qv
+    auto load_tile = [&](int kt, float4 (&kv)[4][4]) {
+        const int jrow = min(kt * 32 + n, s.nbk - 1);
+        const float* kr = a.kbar + kbar_row(s, a.Hkv, g, jrow) * D;
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) kv[p][t] = *(const float4*)(kr + 32 * p + 16 * lh + 4 * t);
+    };
+    float4 kn[4][4];
+    if (wave < nkt) load_tile(wave, kn);
+    for (int kt = wave; kt < nkt; kt += FUSED_WAVES) {
+        float4 kv[4][4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) kv[p][t] = kn[p][t];
+        if (kt + FUSED_WAVES < nkt) load_tile(kt + FUSED_WAVES, kn);
+        f32x16 acc;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(kv[p][t].x, qv[p][t].x, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(kv[p][t].y, qv[p][t].y, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(kv[p][t].z, qv[p][t].z, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(kv[p][t].w, qv[p][t].w, acc, 0, 0, 0);
+            }
+        // accumulator: lane holds column n, key rows 8 (v / 4) + 4 lh + v % 4
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int j = kt * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
+            if (j < nb) S_sh[n * sst + j] = acc[v] * a.scale;
+        }
+    }
+    __syncthreads();
+    // E3: row maximum of each column over its visible key blocks j <= i
+    for (int c = wave; c < cols; c += FUSED_WAVES) {
+        const int i = s.i0 + il0 + c / G;
+        float m = NEG_INF;
+        for (int j = lane; j <= i; j += 64) m = fmaxf(m, S_sh[c * sst + j]);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+        if (lane == 0) M_sh[c] = m;
+    }
+    __syncthreads();
+    // E4-E5 per query block: union over the group's heads, threshold, ballot
+    for (int ql = wave; ql < nql; ql += FUSED_WAVES) {
+        const int i = s.i0 + il0 + ql;
+        const int r = s.row0 + g * s.nq + il0 + ql;
+        uint32_t* bits = a.bits + (long long)r * a.nbw;
+        int count = 0;
+        for (int jc = 0; jc <= i; jc += 64) {
+            const int j = jc + lane;
+            bool keep = false;
+            if (j <= i) {
+                float R = NEG_INF;
+                for (int hh = 0; hh < G; ++hh) R = fmaxf(R, S_sh[(ql * G + hh) * sst + j] - M_sh[ql * G + hh]);
+                keep = (R >= a.neg_tau) || j == 0 || j == i;
+            }
+            const unsigned long long bal = __ballot(keep);
+            count += __popcll(bal);
+            if (lane == 0) bits[jc >> 5] = (uint32_t)bal;
+            if (lane == 1 && (jc >> 5) + 1 < a.nbw) bits[(jc >> 5) + 1] = (uint32_t)(bal >> 32);
+        }
+        if (lane == 0) {
+            a.counts[r] = count;
+            a.keys[r] = row_group(s, g, a.Hkv, a.grp_units, a.ngrp);
+        }
+    }
+}
+
 // Exclusive scan of counts into row_ptr[0..rows]; one workgroup of 1024.
 __global__ __launch_bounds__(1024) void scan_rows_kernel(SelectArgs a) {
     __shared__ int part[1024];
@@ -204,9 +329,9 @@ __global__ __launch_bounds__(SORT_CHUNK) void sort_scatter_kernel(SelectArgs a) 
 }
 
 template <typename Geo>
-static hipError_t select_dispatch(const Geo& geo, const SelectArgs& a, hipStream_t st) {
+static hipError_t select_dispatch(const Geo& geo, const SelectArgs& a, hipStream_t st, bool fused = false) {
     const int wg = cdiv(a.rows, 4);
-    select_rows_kernel<Geo><<<wg, 256, 0, st>>>(geo, a);
+    if (!fused) select_rows_kernel<Geo><<<wg, 256, 0, st>>>(geo, a);
     scan_rows_kernel<<<1, 1024, 0, st>>>(a);
     expand_rows_kernel<Geo><<<wg, 256, 0, st>>>(geo, a);
     if (a.sched) {
@@ -227,6 +352,21 @@ static hipError_t select_dispatch(const Geo& geo, const SelectArgs& a, hipStream
 hipError_t launch_select(const GeoFixed* gf, const GeoTable* gt, const SelectArgs& a, hipStream_t st) {
     if (a.rows == 0) return hipSuccess;
     return gf ? select_dispatch(*gf, a, st) : select_dispatch(*gt, a, st);
+}
+
+hipError_t launch_select_fused(const GeoFixed& gf, const SelectArgs& a, hipStream_t st) {
+    if (a.rows == 0) return hipSuccess;
+    if (gf.nb > FUSED_MAX_NBK) return hipErrorInvalidValue;
+    const int G = a.Hq / a.Hkv;
+    const int ntq = cdiv(gf.nb, FUSED_COLS / G);
+    const size_t shm = (size_t)FUSED_COLS * (gf.nb + 1) * sizeof(float);
+    if (shm > 65536) {
+        hipError_t e = hipFuncSetAttribute((const void*)select_fused_kernel,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+        if (e != hipSuccess) return e;
+    }
+    select_fused_kernel<<<gf.nseq * a.Hkv * ntq, FUSED_WAVES * 64, shm, st>>>(gf, a);
+    return select_dispatch(gf, a, st, true);
 }
 
 }  // namespace fp

@@ -152,6 +152,23 @@ int fp_select_blocks(const fp_problem* p, const float* scores, float tau,
                      int32_t* row_ptr, int32_t* col_idx, int64_t capacity,
                      int32_t* sched, void* workspace, size_t ws_bytes, void* stream);
 
+/* E1-E5 in one call, without a score matrix: pools Q, K, V per block (as
+ * fp_block_scores), then computes each row's block scores from the pooled
+ * rows inside the selection and emits the kept lists and schedule (as
+ * fp_select_blocks). The estimate has to be cheap next to the attention it
+ * prunes (aipulsen.com article body: the search latency of earlier sparse
+ * methods). The scores are summed in the same order as fp_block_scores, so
+ * the kept lists equal those of fp_block_scores + fp_select_blocks bit for
+ * bit. Sequences of more than 1024 key blocks fall back to a score matrix in
+ * the workspace. Outputs: qbar, kbar, vbar (device, as fp_block_scores),
+ * row_ptr, col_idx (capacity >= fp_max_nnz), sched (nullable); workspace of
+ * ws_bytes >= fp_estimate_select_workspace_size(p), 256-byte aligned. */
+int64_t fp_estimate_select_workspace_size(const fp_problem* p);
+int fp_estimate_select(const fp_problem* p, const void* q, const void* k, const void* v,
+                       const float* q_scale, const float* k_scale, const float* v_scale, float tau,
+                       float* qbar, float* kbar, float* vbar, int32_t* row_ptr, int32_t* col_idx,
+                       int64_t capacity, int32_t* sched, void* workspace, size_t ws_bytes, void* stream);
+
 /* E6: the sparse flash-attention operator over the kept blocks (lode.cx
  * page, implementation paragraph and bullet list; aimodeling.com page,
  * "Operator alignment" bullet) plus the mean correction for the pruned

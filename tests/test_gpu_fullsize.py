@@ -64,7 +64,13 @@ def run_and_check(fp, inp, tau, kind, full=True, every=8):
     qs, ks, vs = mv(inp.q_scale), mv(inp.k_scale), mv(inp.v_scale)
     say(f"  S={cfg.S} tau={tau} {kind}: GPU run")
     out = fp.sparse_prefill(q, k, v, cfg.block, tau, q_scale=qs, k_scale=ks, v_scale=vs)
+    # the fused estimate + selection (no score matrix) makes the same decisions
+    fused = fp.fp_estimate_select(out["problem"], q, k, v, tau, q_scale=qs, k_scale=ks, v_scale=vs)
     torch.cuda.synchronize()
+    nnz = int(out["row_ptr"][-1])
+    assert torch.equal(fused[3], out["row_ptr"]) and torch.equal(fused[4][:nnz], out["col_idx"][:nnz])
+    assert torch.equal(fused[5], out["sched"])
+    del fused
     o = out["o"][0].float().cpu().numpy()
     lse = out["lse"][0].cpu().numpy()
     assert np.isfinite(o).all() and np.isfinite(lse).all()

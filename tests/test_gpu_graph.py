@@ -137,3 +137,36 @@ def test_two_streams_at_once(fp):
         nnz = int(outs[n]["row_ptr"][-1])
         assert torch.equal(outs[n]["col_idx"][:nnz], serial[n]["col_idx"])
     say("two problems on two streams at once: bit-identical to serial runs")
+
+
+def test_fused_path_graph_replays(fp):
+    """fp_estimate_select + fp_sparse_prefill captured and replayed, at a
+    length whose score rows need more than 64 KiB of LDS (the fused kernel
+    raises its dynamic LDS limit at launch, also under capture)."""
+    cfg = synth.config(2, S=600 * 128 + 5, Hq=4, Hkv=1, seed=93, tau=2.0)
+    inp = synth.gen_fixed(cfg)
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in (inp.q, inp.k, inp.v))
+    keys = ("row_ptr", "sched", "o", "lse")
+    ref = fp.sparse_prefill(q, k, v, 128, cfg.tau)          # the three-call path, eager
+    torch.cuda.synchronize()
+    n = int(ref["row_ptr"][-1])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fp.sparse_prefill_fused(q, k, v, 128, cfg.tau)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cap = fp.sparse_prefill_fused(q, k, v, 128, cfg.tau)
+    for r in range(3):
+        cap["o"].zero_()
+        cap["row_ptr"].fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for key in keys:
+            assert torch.equal(cap[key], ref[key]), f"fused replay {r}: {key} differs"
+        assert torch.equal(cap["col_idx"][:n], ref["col_idx"][:n])
+    say("fused path: 3 graph replays bit-identical to the eager three-call path")
