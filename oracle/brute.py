@@ -27,11 +27,19 @@ def block_mean_logit(q, k, c, P, L, B, h, g, i, j) -> float:
     return acc / n
 
 
-def select_enum(q, k, c, P, L, B, G, tau) -> np.ndarray:
+def select_enum(q, k, c, P, L, B, G, tau, per_head=False) -> np.ndarray:
     """Kept-block mask [Hkv, nq, nb] by enumeration: for every (g, i, j) test
     whether some head of the group has a block score within tau of its own row
-    maximum, or j is the sink or the diagonal."""
+    maximum, or j is the sink or the diagonal. per_head: one list per query
+    head ([Hq, nq, nb]), each head judged on its own scores."""
     Hq = q.shape[1]
+    if per_head:
+        Hkv_real = k.shape[1]
+        out = []
+        for h in range(Hq):
+            kk = k[:, [h // (Hq // Hkv_real)]]
+            out.append(select_enum(q[:, [h]], kk, c, P, L, B, 1, tau)[0])
+        return np.array(out)
     Hkv = Hq // G
     i0 = P // B
     i1 = (L - 1) // B
@@ -53,11 +61,14 @@ def select_enum(q, k, c, P, L, B, G, tau) -> np.ndarray:
     return keep
 
 
-def attend_augmented(q, k, v, keep, c, P, L, B, G) -> Tuple[np.ndarray, np.ndarray]:
+def attend_augmented(q, k, v, keep, c, P, L, B, G, block_score=False) -> Tuple[np.ndarray, np.ndarray]:
     """Softmax attention of every present row over an explicitly built list of
     (logit, value) entries: each causal token of a kept block, and one entry
     per pruned block whose key and value are the block's token means and whose
-    logit carries + ln(block size)."""
+    logit carries + ln(block size). keep is [Hkv, ...] (one list per KV head)
+    or [Hq, ...] (one per query head). block_score: the pruned block's logit
+    is the block pair's mean token logit (the block score) + ln(block size),
+    the same for every row of the query block."""
     Hq, d = q.shape[1], q.shape[2]
     Hkv = Hq // G
     o = np.zeros((L - P, Hq, d))
@@ -66,17 +77,20 @@ def attend_augmented(q, k, v, keep, c, P, L, B, G) -> Tuple[np.ndarray, np.ndarr
         i = t // B
         for h in range(Hq):
             g = h // G
+            lst = h if keep.shape[0] == Hq else g
             entries: List[Tuple[float, List[float]]] = []
             for j in range(i + 1):
                 toks = list(range(j * B, min((j + 1) * B, L)))
-                if keep[g, i - P // B, j]:
+                if keep[lst, i - P // B, j]:
                     for s in toks:
                         if s <= t:
                             entries.append((c * _dot(q[t - P, h], k[s, g]), list(v[s, g])))
                 else:
                     kb = [sum(float(k[s, g, e]) for s in toks) / len(toks) for e in range(d)]
                     vb = [sum(float(v[s, g, e]) for s in toks) / len(toks) for e in range(d)]
-                    entries.append((c * _dot(q[t - P, h], kb) + math.log(len(toks)), vb))
+                    z = (block_mean_logit(q, k, c, P, L, B, h, g, i, j) if block_score
+                         else c * _dot(q[t - P, h], kb))
+                    entries.append((z + math.log(len(toks)), vb))
             m = max(z for z, _ in entries)
             den = sum(math.exp(z - m) for z, _ in entries)
             for e in range(d):

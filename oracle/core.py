@@ -72,14 +72,18 @@ def block_scores(qbar: np.ndarray, kbar: np.ndarray, c: float, i0: int) -> np.nd
     return S
 
 
-def select(S: np.ndarray, G: int, tau: float, i0: int) -> Tuple[np.ndarray, np.ndarray]:
+def select(S: np.ndarray, G: int, tau: float, i0: int, per_head: bool = False) -> Tuple[np.ndarray, np.ndarray]:
     """E3-E5: max-based dynamic threshold (lode.cx page, "How It Works";
     aimodeling.com page, "From Prototype to Production").
 
     Returns (keep bool [Hkv, nq, nb], R float [Hkv, nq, nb]) with R = -inf and
-    keep = False for j > i.  Sink j = 0 and diagonal j = i are always kept."""
+    keep = False for j > i.  Sink j = 0 and diagonal j = i are always kept.
+    per_head: the variant without the GQA union (E4 over one head): each
+    query head keeps its own list, keep and R are [Hq, nq, nb]."""
     if isinstance(tau, float) and math.isnan(tau):
         raise ValueError("tau is NaN")
+    if per_head:
+        return select(S, 1, tau, i0)
     Hq, nq, nb = S.shape
     Hkv = Hq // G
     M = S.max(axis=2)                                # E3, over visible j only (rest -inf)
@@ -100,7 +104,8 @@ def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, keep: np.ndarray,
            kbar: np.ndarray, vbar: np.ndarray, c: float, B: int, P: int,
            rows: Optional[Sequence[Tuple[int, int]]] = None,
            correction: bool = True,
-           out: Optional[Tuple[np.ndarray, np.ndarray]] = None) -> Tuple[np.ndarray, np.ndarray]:
+           out: Optional[Tuple[np.ndarray, np.ndarray]] = None,
+           block_scores: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
     """E6: sparse attention over kept blocks plus the mean-correction pseudo-tokens.
 
     Sparse operator over kept blocks: lode.cx page, "How It Works" and the
@@ -113,9 +118,31 @@ def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, keep: np.ndarray,
     are dropped (no pseudo-tokens).
     out: optional preallocated (o, lse) to fill instead (only the rows
     evaluated are written; callers may split the rows over threads).
+    Per-head lists (keep [Hq, nq, nb], the variant without the GQA union):
+    each query head h attends its own list; rows are then (h, il) pairs.
+    block_scores (S [Hq, nq, nb] of E2): the variant whose pruned block j
+    stands in with the logit S[h, i, j] + ln|J_j| for every row of query
+    block i, instead of c<q_t, Kbar_j> + ln|J_j|.
     Returns o [L-P, Hq, d] and lse [Hq, L-P]."""
     L, Hkv, d = k.shape
     Hq = q.shape[1]
+    if keep.shape[0] == Hq and Hq != Hkv:
+        # per-head lists: each head is its own group of one, reading KV head h // G
+        G = Hq // Hkv
+        todo = rows if rows is not None else [(h, il) for h in range(Hq)
+                                              for il in range(query_blocks(P, L, B)[1])]
+        if out is None:
+            out = (np.full((L - P, Hq, d), np.nan), np.full((Hq, L - P), np.nan))
+        for h, il in todo:
+            sub = attend(q[:, h:h + 1], k[:, h // G:h // G + 1], v[:, h // G:h // G + 1], keep[h:h + 1],
+                         kbar[h // G:h // G + 1], vbar[h // G:h // G + 1], c, B, P, rows=[(0, il)],
+                         correction=correction,
+                         block_scores=None if block_scores is None else block_scores[h:h + 1])
+            i0, _ = query_blocks(P, L, B)
+            lo, hi = max((i0 + il) * B, P), min((i0 + il + 1) * B, L)
+            out[0][lo - P:hi - P, h] = sub[0][lo - P:hi - P, 0]
+            out[1][h, lo - P:hi - P] = sub[1][0, lo - P:hi - P]
+        return out
     G = Hq // Hkv
     i0, nq = query_blocks(P, L, B)
     if out is None:
@@ -141,7 +168,10 @@ def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, keep: np.ndarray,
             Q = q[lo - P:hi - P, h, :]               # [rows, d]
             z = c * (Q @ Kx.T)
             z[future] = NEG_INF
-            zp = c * (Q @ Kp.T) + bias[None, :]
+            if block_scores is None:
+                zp = c * (Q @ Kp.T) + bias[None, :]
+            else:                                    # one logit per block pair, the same for every row
+                zp = np.repeat(block_scores[h, il, pruned_j][None, :] + bias[None, :], hi - lo, axis=0)
             m = np.maximum(z.max(axis=1), zp.max(axis=1) if len(pruned_j) else NEG_INF)
             w = np.exp(z - m[:, None])
             wp = np.exp(zp - m[:, None])
@@ -151,14 +181,25 @@ def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, keep: np.ndarray,
     return o, lse
 
 
+VARIANTS = ("mean", "none", "per_head", "block_score")
+
+
 def prefill(q: np.ndarray, k: np.ndarray, v: np.ndarray, B: int, tau: float,
             c: Optional[float] = None, P: int = 0,
             keep: Optional[np.ndarray] = None,
             rows: Optional[Sequence[Tuple[int, int]]] = None,
-            with_output: bool = True, correction: bool = True) -> Dict[str, np.ndarray]:
+            with_output: bool = True, correction: bool = True,
+            variant: str = "mean") -> Dict[str, np.ndarray]:
     """E1-E6 for one sequence.  keep overrides the oracle's own mask (used to
     evaluate E6 under another, validated mask); correction=False evaluates the
-    ablation without the mean correction."""
+    ablation without the mean correction. variant: "mean" (E1-E6 as stated),
+    "none" (no correction), "per_head" (one kept list per query head, no GQA
+    union; keep and R are [Hq, nq, nb]) or "block_score" (the pruned blocks'
+    pseudo-tokens take the block score S[h, i, j] + ln|J_j| as logit)."""
+    if variant not in VARIANTS:
+        raise ValueError(f"unknown variant {variant}")
+    if variant == "none":
+        correction = False
     L, Hkv, d = k.shape
     Hq = q.shape[1]
     assert q.shape[0] == L - P and Hq % Hkv == 0 and v.shape == k.shape
@@ -170,11 +211,12 @@ def prefill(q: np.ndarray, k: np.ndarray, v: np.ndarray, B: int, tau: float,
     kbar = pool_keys(k, B)
     vbar = pool_keys(v, B)
     S = block_scores(qbar, kbar, c, i0)
-    own_keep, R = select(S, G, tau, i0)
+    own_keep, R = select(S, G, tau, i0, per_head=variant == "per_head")
     out = dict(qbar=qbar, kbar=kbar, vbar=vbar, S=S, R=R, keep=own_keep, i0=i0, nq=nq)
     if with_output:
         use = own_keep if keep is None else keep
-        out["o"], out["lse"] = attend(q, k, v, use, kbar, vbar, c, B, P, rows=rows, correction=correction)
+        out["o"], out["lse"] = attend(q, k, v, use, kbar, vbar, c, B, P, rows=rows, correction=correction,
+                                      block_scores=S if variant == "block_score" else None)
     return out
 
 

@@ -428,3 +428,99 @@ def test_query_blocks_without_present_rows():
     k = rng.standard_normal((700, 1, 8))
     ref = prefill(np.zeros((0, 2, 8)), k, k, 128, 1.0, P=700)
     assert ref["keep"].shape == (1, 0, 6) and ref["o"].shape[0] == 0
+
+
+# --------------------------------------------------------------------------
+# Variants: per-query-head lists (no GQA union) and the block-score correction
+# --------------------------------------------------------------------------
+def walk_inputs(L, Hq, Hkv, d, seed, P=0):
+    q = rnd((L - P, Hq, d), seed) + 0.8
+    k = rnd((L, Hkv, d), seed + 1) + np.cumsum(rnd((L, Hkv, d), seed + 2, 0.6), axis=0)
+    v = rnd((L, Hkv, d), seed + 3)
+    return q, k, v
+
+
+@pytest.mark.parametrize("P,tau", [(0, 0.3), (0, 1.0), (9, 0.5)])
+def test_per_head_lists_union_is_the_group_list(P, tau):
+    """The group's list (E4 with the union) is exactly the OR of its heads'
+    own lists, each head's list is a subset of it, and per-head lists come
+    out of an independent enumeration."""
+    L, B, Hq, Hkv, d = 80, 8, 4, 2, 8
+    q, k, v = walk_inputs(L, Hq, Hkv, d, 40, P)
+    union = prefill(q, k, v, B, tau, 0.5, P=P, with_output=False)
+    ph = prefill(q, k, v, B, tau, 0.5, P=P, with_output=False, variant="per_head")
+    G = Hq // Hkv
+    assert ph["keep"].shape[0] == Hq
+    for g in range(Hkv):
+        assert np.array_equal(union["keep"][g], ph["keep"][g * G:(g + 1) * G].any(axis=0))
+    assert (union["keep"].sum() < ph["keep"].reshape(Hkv, G, *ph["keep"].shape[1:]).sum())  # heads differ
+    enum = brute.select_enum(q, k, 0.5, P, L, B, G, tau, per_head=True)
+    assert np.array_equal(ph["keep"], enum)
+
+
+def test_per_head_lists_of_identical_heads_equal_the_union():
+    L, B, d = 64, 8, 8
+    q1 = rnd((L, 1, d), 44) + 0.7
+    k = rnd((L, 1, d), 45) + np.cumsum(rnd((L, 1, d), 46, 0.5), axis=0)
+    v = rnd((L, 1, d), 47)
+    qG = np.repeat(q1, 4, axis=1)
+    a = prefill(qG, k, v, B, 0.5, 0.3)
+    b = prefill(qG, k, v, B, 0.5, 0.3, variant="per_head")
+    for h in range(4):
+        assert np.array_equal(b["keep"][h], a["keep"][0])
+    assert np.abs(a["o"] - b["o"]).max() < 1e-12 and np.abs(a["lse"] - b["lse"]).max() < 1e-12
+
+
+@pytest.mark.parametrize("P,tau", [(0, 0.3), (7, 1.0)])
+def test_per_head_attend_matches_augmented_loops(P, tau):
+    L, B, Hq, Hkv, d = 34, 4, 4, 2, 4
+    q, k, v = walk_inputs(L, Hq, Hkv, d, 48, P)
+    out = prefill(q, k, v, B, tau, 0.5, P=P, variant="per_head")
+    o, lse = brute.attend_augmented(q, k, v, out["keep"], 0.5, P, L, B, Hq // Hkv)
+    assert np.abs(out["o"] - o).max() < 1e-12 and np.abs(out["lse"] - lse).max() < 1e-12
+
+
+@pytest.mark.parametrize("variant", ["per_head", "block_score"])
+@pytest.mark.parametrize("tau", [-1.0, 0.3, 2.0])
+def test_variants_exact_for_block_size_one(variant, tau):
+    """With 1-token blocks a pruned block's pseudo-token is its token (and the
+    block score is that token's logit), so every variant equals dense attention."""
+    L, Hq, Hkv, d = 30, 4, 2, 8
+    q, k, v = walk_inputs(L, Hq, Hkv, d, 52)
+    out = prefill(q, k, v, 1, tau, 0.4, variant=variant)
+    ref, lse = dense_numpy(q, k, v, 0.4)
+    assert np.abs(out["o"] - ref).max() < 1e-12 and np.abs(out["lse"] - lse).max() < 1e-12
+
+
+@pytest.mark.parametrize("tau", [-1.0, 0.5, 3.0])
+def test_block_score_equals_mean_correction_for_block_constant_queries(tau):
+    """When q is constant inside every query block, the block score of (i, j)
+    is every row's own pseudo-token logit: the two corrections coincide (any
+    K, V); with block-constant K and V too, both equal dense attention."""
+    L, B, Hq, Hkv, d = 96, 8, 4, 2, 8
+    nb = L // B
+    qb = rnd((nb, Hq, d), 55) + 0.5
+    q = np.repeat(qb, B, axis=0)
+    _, k, v = walk_inputs(L, Hq, Hkv, d, 56)
+    a = prefill(q, k, v, B, tau, 0.3)
+    b = prefill(q, k, v, B, tau, 0.3, variant="block_score")
+    assert np.abs(a["o"] - b["o"]).max() < 1e-12 and np.abs(a["lse"] - b["lse"]).max() < 1e-12
+    kc = np.repeat(rnd((nb, Hkv, d), 57), B, axis=0)
+    vc = np.repeat(rnd((nb, Hkv, d), 58), B, axis=0)
+    c_ = prefill(q, kc, vc, B, tau, 0.3, variant="block_score")
+    ref, lse = dense_numpy(q, kc, vc, 0.3)
+    assert np.abs(c_["o"] - ref).max() < 1e-12 and np.abs(c_["lse"] - lse).max() < 1e-12
+
+
+@pytest.mark.parametrize("P,tau", [(0, 0.3), (7, 1.0), (0, -1.0)])
+def test_block_score_matches_augmented_loops(P, tau):
+    """The block-score pseudo-token logit is the block pair's mean token logit
+    (E2's closed form, summed pair by pair here) plus ln |J|."""
+    L, B, Hq, Hkv, d = 34, 4, 4, 2, 4
+    q, k, v = walk_inputs(L, Hq, Hkv, d, 60, P)
+    out = prefill(q, k, v, B, tau, 0.5, P=P, variant="block_score")
+    assert (~out["keep"]).any()
+    o, lse = brute.attend_augmented(q, k, v, out["keep"], 0.5, P, L, B, Hq // Hkv, block_score=True)
+    assert np.abs(out["o"] - o).max() < 1e-12 and np.abs(out["lse"] - lse).max() < 1e-12
+    mean = prefill(q, k, v, B, tau, 0.5, P=P)
+    assert np.abs(out["o"] - mean["o"]).max() > 1e-6     # a different correction on these inputs

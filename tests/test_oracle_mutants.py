@@ -94,7 +94,14 @@ MUTANTS = [
     ("select", "keep[g, il, 0] = True", "pass", "E5: sink block not forced"),
     ("select", "keep[g, il, i] = True", "pass", "E5: diagonal block not forced"),
     ("select", "M = S.max(axis=2)", "M = S[:, :, :1].max(axis=2)", "E3: row maximum over the sink only"),
-    ("attend", "+ bias[None, :]", "", "E6: ln|J| multiplicity of the pseudo-tokens dropped"),
+    ("attend", "zp = c * (Q @ Kp.T) + bias[None, :]", "zp = c * (Q @ Kp.T)",
+     "E6: ln|J| multiplicity of the pseudo-tokens dropped"),
+    ("attend", "block_scores[h, il, pruned_j][None, :] + bias[None, :]", "block_scores[h, il, pruned_j][None, :]",
+     "block-score variant: ln|J| multiplicity dropped"),
+    ("attend", "block_scores[h, il, pruned_j]", "block_scores[h, max(il - 1, 0), pruned_j]",
+     "block-score variant: the previous query block's scores"),
+    ("select", "return select(S, 1, tau, i0)", "return select(S, 2, tau, i0)",
+     "per-head variant: lists shared by pairs of heads"),
     ("attend", "future = tok[None, :] > t[:, None]", "future = tok[None, :] >= t[:, None]",
      "E6: causal mask excludes the query's own position"),
     ("attend", "Kp = kbar[g, pruned_j, :]", "Kp = vbar[g, pruned_j, :]", "E6: pooled keys and values swapped"),
