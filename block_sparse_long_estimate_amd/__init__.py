@@ -32,7 +32,7 @@ __all__ = [
     "FpError", "Problem", "make_problem", "fp_block_scores", "fp_select_blocks",
     "fp_sparse_prefill", "fp_sparse_prefill_paged", "sparse_prefill", "version",
     "make_varlen_problem", "fp_sparse_prefill_noalloc", "fp_dense_prefill", "fp_estimate_select",
-    "sparse_prefill_fused",
+    "sparse_prefill_fused", "fp_sparse_prefill_scored", "VARIANTS",
 ]
 
 
@@ -119,13 +119,23 @@ class Problem:
         return ctypes.byref(self.c)
 
 
+VARIANTS = {"mean": N.FP_VARIANT_MEAN_CORRECTION, "none": N.FP_VARIANT_NO_CORRECTION,
+            "per_head": N.FP_VARIANT_PER_HEAD_LISTS, "block_score": N.FP_VARIANT_BLOCK_SCORE}
+
+
 def make_problem(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block: int,
                  softmax_scale: float = 0.0, o: Optional[torch.Tensor] = None,
-                 out_fp32: bool = False, correction: bool = True) -> Problem:
+                 out_fp32: bool = False, correction: bool = True, variant: Optional[str] = None) -> Problem:
     """Descriptor of a fixed-shape batch: q [batch, S, Hq, 128], k/v [batch, S, Hkv, 128]
     (bf16, or uint8 E4M3FN codes), last dim contiguous. out_fp32: fp_sparse_prefill
     writes o in float32 (diagnostic) instead of bfloat16. correction=False: the
-    ablation without the mean correction (pruned blocks dropped)."""
+    ablation without the mean correction (pruned blocks dropped). variant: one of
+    VARIANTS ("mean" is E1-E6 as stated; "none", "per_head" and "block_score"
+    are ablations)."""
+    if variant is None:
+        variant = "mean" if correction else "none"
+    if variant not in VARIANTS:
+        raise FpError(N.FP_ERR_INVALID, f"unknown variant {variant!r} (one of {sorted(VARIANTS)})")
     fp8 = q.dtype == torch.uint8
     if q.dtype not in (torch.bfloat16, torch.uint8) or k.dtype != q.dtype or v.dtype != q.dtype:
         raise FpError(N.FP_ERR_INVALID, f"q, k, v must all be bfloat16 or all uint8 E4M3FN codes "
@@ -135,7 +145,7 @@ def make_problem(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block: int,
                                         f"(got {tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)})")
     c = FpProblem()
     c.out_dtype = N.FP_OUT_FP32 if out_fp32 else N.FP_OUT_BF16
-    c.variant = N.FP_VARIANT_MEAN_CORRECTION if correction else N.FP_VARIANT_NO_CORRECTION
+    c.variant = VARIANTS[variant]
     c.batch, c.seqlen, c.num_q_heads, c.head_dim = q.shape[0], q.shape[1], q.shape[2], q.shape[3]
     c.num_kv_heads = k.shape[2]
     c.block = block
@@ -260,10 +270,11 @@ def fp_estimate_select(p: Problem, q, k, v, tau: float, q_scale=None, k_scale=No
 
 def sparse_prefill_fused(q, k, v, block: int, tau: float, softmax_scale: float = 0.0,
                          q_scale=None, k_scale=None, v_scale=None, with_lse: bool = True,
-                         out_fp32: bool = False, correction: bool = True):
+                         out_fp32: bool = False, correction: bool = True, variant: Optional[str] = None):
     """The path in two calls: fp_estimate_select (no score matrix) then
-    fp_sparse_prefill. Returns a dict of device tensors."""
-    p = make_problem(q, k, v, block, softmax_scale, out_fp32=out_fp32, correction=correction)
+    fp_sparse_prefill. Returns a dict of device tensors. (The block-score
+    variant needs the score matrix: use sparse_prefill.)"""
+    p = make_problem(q, k, v, block, softmax_scale, out_fp32=out_fp32, correction=correction, variant=variant)
     qbar, kbar, vbar, row_ptr, col_idx, sched = fp_estimate_select(p, q, k, v, tau, q_scale, k_scale, v_scale)
     o, lse = fp_sparse_prefill(p, q, k, v, kbar, vbar, row_ptr, col_idx, sched,
                                q_scale, k_scale, v_scale, with_lse)
@@ -326,15 +337,55 @@ def fp_sparse_prefill_noalloc(p: Problem, q, k, v, kbar, vbar, row_ptr, col_idx,
     return o, lse
 
 
+def fp_sparse_prefill_scored(p: Problem, q, k, v, scores, vbar, row_ptr, col_idx, sched=None,
+                             q_scale=None, k_scale=None, v_scale=None, with_lse: bool = True,
+                             o: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """E6 under the block-score correction (a problem of variant
+    "block_score"): pruned blocks stand in with logit S[h,i,j] + ln|block| ->
+    (o, lse)."""
+    c = p.c
+    _check_qkv(p, q, k, v)
+    _check_scales(p.fp8, c.batch, c.num_q_heads, c.num_kv_heads, (c.seqlen + 127) // 128, q_scale, k_scale,
+                  v_scale)
+    _check(scores, "scores", torch.float32, (c.batch, c.num_q_heads, p.nb, p.nb), required=True)
+    _check(vbar, "vbar", torch.float32, (c.batch, c.num_kv_heads, p.nb, 128), required=True)
+    _check(row_ptr, "row_ptr", torch.int32, (p.rows + 1,), required=True)
+    _check(col_idx, "col_idx", torch.int32, required=True)
+    _check(sched, "sched", torch.int32, (p.rows,))
+    odt = torch.float32 if c.out_dtype == N.FP_OUT_FP32 else torch.bfloat16
+    oshape = (c.batch, c.seqlen, c.num_q_heads, 128)
+    if o is None:
+        if tuple(c.o_stride) != (c.seqlen * c.num_q_heads * 128, c.num_q_heads * 128, 128):
+            raise FpError(N.FP_ERR_INVALID, "the problem was built for a strided o: pass that o")
+        o = torch.empty(oshape, dtype=odt, device=q.device)
+    else:
+        _check_view(o, "o", odt, oshape, tuple(c.o_stride))
+    lse = torch.empty((c.batch, c.num_q_heads, c.seqlen), dtype=torch.float32,
+                      device=q.device) if with_lse else None
+    lib = N.load()
+    if workspace is None:
+        workspace = torch.empty(N.check_size(lib.fp_prefill_workspace_size(p.ref)), dtype=torch.uint8,
+                                device=q.device)
+    N.check(lib.fp_sparse_prefill_scored(p.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(q_scale), _ptr(k_scale),
+                                         _ptr(v_scale), _ptr(scores), _ptr(vbar), _ptr(row_ptr), _ptr(col_idx),
+                                         _ptr(sched), _ptr(o), _ptr(lse), _ptr(workspace), workspace.numel(),
+                                         _stream()))
+    return o, lse
+
+
 def sparse_prefill(q, k, v, block: int, tau: float, softmax_scale: float = 0.0,
                    q_scale=None, k_scale=None, v_scale=None, with_lse: bool = True,
-                   out_fp32: bool = False, correction: bool = True):
+                   out_fp32: bool = False, correction: bool = True, variant: Optional[str] = None):
     """All three stages on the current stream. Returns a dict of device tensors."""
-    p = make_problem(q, k, v, block, softmax_scale, out_fp32=out_fp32, correction=correction)
+    p = make_problem(q, k, v, block, softmax_scale, out_fp32=out_fp32, correction=correction, variant=variant)
     qbar, kbar, vbar, scores = fp_block_scores(p, q, k, v, q_scale, k_scale, v_scale)
     row_ptr, col_idx, sched = fp_select_blocks(p, scores, tau)
-    o, lse = fp_sparse_prefill(p, q, k, v, kbar, vbar, row_ptr, col_idx, sched,
-                               q_scale, k_scale, v_scale, with_lse)
+    if p.c.variant == N.FP_VARIANT_BLOCK_SCORE:
+        o, lse = fp_sparse_prefill_scored(p, q, k, v, scores, vbar, row_ptr, col_idx, sched,
+                                          q_scale, k_scale, v_scale, with_lse)
+    else:
+        o, lse = fp_sparse_prefill(p, q, k, v, kbar, vbar, row_ptr, col_idx, sched,
+                                   q_scale, k_scale, v_scale, with_lse)
     return dict(problem=p, qbar=qbar, kbar=kbar, vbar=vbar, scores=scores, row_ptr=row_ptr,
                 col_idx=col_idx, sched=sched, o=o, lse=lse)
 

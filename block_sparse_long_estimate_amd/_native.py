@@ -20,6 +20,8 @@ FP_OUT_BF16 = 0
 FP_OUT_FP32 = 2
 FP_VARIANT_MEAN_CORRECTION = 0
 FP_VARIANT_NO_CORRECTION = 1
+FP_VARIANT_PER_HEAD_LISTS = 2
+FP_VARIANT_BLOCK_SCORE = 3
 
 EXPORTS = (
     "fp_version", "fp_last_error", "fp_num_rows", "fp_max_nnz", "fp_workspace_size",
@@ -27,7 +29,7 @@ EXPORTS = (
     "fp_block_scores", "fp_select_blocks", "fp_sparse_prefill",
     "fp_varlen_num_rows", "fp_varlen_max_nnz", "fp_varlen_workspace_size",
     "fp_sparse_prefill_paged", "fp_sparse_prefill_noalloc", "fp_dense_prefill",
-    "fp_estimate_select", "fp_estimate_select_workspace_size",
+    "fp_estimate_select", "fp_estimate_select_workspace_size", "fp_sparse_prefill_scored",
 )
 FP_NOALLOC_MAX_POOLED_ROWS = 32768
 
@@ -91,6 +93,9 @@ def load() -> ctypes.CDLL:
     lib.fp_estimate_select.restype = ctypes.c_int
     lib.fp_estimate_select.argtypes = [P, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp,
                                        ctypes.c_int64, vp, vp, ctypes.c_size_t, vp]
+    lib.fp_sparse_prefill_scored.restype = ctypes.c_int
+    lib.fp_sparse_prefill_scored.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                             ctypes.c_size_t, vp]
     lib.fp_dense_prefill.restype = ctypes.c_int
     lib.fp_dense_prefill.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.fp_sparse_prefill_noalloc.restype = ctypes.c_int

@@ -73,7 +73,7 @@ int check_fixed(const fp_problem* p) {
             if ((st[t][e] * esz) % 16) return fail(FP_ERR_INVALID, "strides must be multiples of 16 bytes");
     if (p->out_dtype != FP_OUT_BF16 && p->out_dtype != FP_OUT_FP32)
         return fail(FP_ERR_UNSUPPORTED, "out_dtype %d unsupported", p->out_dtype);
-    if (p->variant != FP_VARIANT_MEAN_CORRECTION && p->variant != FP_VARIANT_NO_CORRECTION)
+    if (p->variant < FP_VARIANT_MEAN_CORRECTION || p->variant > FP_VARIANT_BLOCK_SCORE)
         return fail(FP_ERR_UNSUPPORTED, "variant %d unsupported", p->variant);
     const int osz = p->out_dtype == FP_OUT_FP32 ? 4 : 2;
     for (int e = 0; e < 3; ++e)
@@ -144,6 +144,15 @@ SelectWs select_ws(long long rows, int max_nbk, int ngrp) {
     return w;
 }
 
+// The kept lists' view of a problem: one list per (sequence, KV head, query
+// block), or per (sequence, query head, query block) for the per-head
+// variant -- there each query head is its own group of one.
+fp_problem lists_of(const fp_problem* p) {
+    fp_problem v = *p;
+    if (p->variant == FP_VARIANT_PER_HEAD_LISTS) v.num_kv_heads = p->num_q_heads;
+    return v;
+}
+
 SortPlan fixed_sort_plan(const fp_problem* p) {
     const int nb = cdiv(p->seqlen, p->block);
     return sort_plan((long long)p->batch * p->num_kv_heads * nb, nb, p->block,
@@ -194,14 +203,14 @@ const char* fp_last_error(void) { return g_err; }
 int64_t fp_num_rows(const fp_problem* p) {
     int rc = check_fixed(p);
     if (rc) return rc;
-    return (int64_t)p->batch * p->num_kv_heads * cdiv(p->seqlen, p->block);
+    return (int64_t)p->batch * lists_of(p).num_kv_heads * cdiv(p->seqlen, p->block);
 }
 
 int64_t fp_max_nnz(const fp_problem* p) {
     int rc = check_fixed(p);
     if (rc) return rc;
     const int64_t nb = cdiv(p->seqlen, p->block);
-    return (int64_t)p->batch * p->num_kv_heads * nb * (nb + 1) / 2;
+    return (int64_t)p->batch * lists_of(p).num_kv_heads * nb * (nb + 1) / 2;
 }
 
 int64_t fp_prefill_workspace_size(const fp_problem* p) {
@@ -213,8 +222,9 @@ int64_t fp_prefill_workspace_size(const fp_problem* p) {
 int64_t fp_workspace_size(const fp_problem* p) {
     int rc = check_fixed(p);
     if (rc) return rc;
+    const fp_problem lv = lists_of(p);
     const int nb = cdiv(p->seqlen, p->block);
-    return (int64_t)select_ws((long long)p->batch * p->num_kv_heads * nb, nb, fixed_sort_plan(p).ngrp).total;
+    return (int64_t)select_ws((long long)p->batch * lv.num_kv_heads * nb, nb, fixed_sort_plan(&lv).ngrp).total;
 }
 
 }  // extern "C"
@@ -274,7 +284,7 @@ int check_select_args(const char* fn, const fp_problem* p, float tau, const int3
     if (!row_ptr || !col_idx || !workspace) return fail(FP_ERR_INVALID, "%s: NULL pointer", fn);
     if (isnan(tau)) return fail(FP_ERR_INVALID, "%s: tau is NaN", fn);
     const int nb = cdiv(p->seqlen, p->block);
-    const long long rows = (long long)p->batch * p->num_kv_heads * nb;
+    const long long rows = (long long)p->batch * lists_of(p).num_kv_heads * nb;
     const long long need = rows * (nb + 1) / 2;
     if (capacity < need)
         return fail(FP_ERR_CAPACITY, "%s: capacity %lld < max nnz %lld", fn, (long long)capacity, need);
@@ -283,10 +293,16 @@ int check_select_args(const char* fn, const fp_problem* p, float tau, const int3
     return FP_OK;
 }
 
+// Selection arguments over the kept lists' view (lists_of) of a problem.
 SelectArgs fixed_select_args(const fp_problem* p, const SelectWs& w, const SortPlan& sp, void* workspace,
                              float tau, int32_t* row_ptr, int32_t* col_idx, int32_t* sched) {
     const int nb = cdiv(p->seqlen, p->block);
+    const int Hkv_pool = p->num_kv_heads;
+    const fp_problem lv = lists_of(p);
+    p = &lv;
     SelectArgs a{};
+    a.Hkv_pool = Hkv_pool;
+    a.kv_div = p->num_kv_heads / Hkv_pool;
     a.counts = (int32_t*)((char*)workspace + w.counts);
     a.bits = (uint32_t*)((char*)workspace + w.bits);
     a.keys = (int32_t*)((char*)workspace + w.keys);
@@ -303,8 +319,9 @@ SelectArgs fixed_select_args(const fp_problem* p, const SelectWs& w, const SortP
 }
 
 SelectWs fixed_select_ws(const fp_problem* p) {
+    const fp_problem lv = lists_of(p);
     const int nb = cdiv(p->seqlen, p->block);
-    return select_ws((long long)p->batch * p->num_kv_heads * nb, nb, fixed_sort_plan(p).ngrp);
+    return select_ws((long long)p->batch * lv.num_kv_heads * nb, nb, fixed_sort_plan(&lv).ngrp);
 }
 
 // Workspace of fp_estimate_select: the selection's, plus the score matrix
@@ -351,8 +368,9 @@ int fp_select_blocks(const fp_problem* p, const float* scores, float tau, int32_
     const SelectWs w = fixed_select_ws(p);
     rc = check_select_args("fp_select_blocks", p, tau, row_ptr, col_idx, capacity, workspace, ws_bytes, w.total);
     if (rc) return rc;
-    GeoFixed geo = geo_fixed(p);
-    SelectArgs a = fixed_select_args(p, w, fixed_sort_plan(p), workspace, tau, row_ptr, col_idx, sched);
+    const fp_problem lv = lists_of(p);
+    GeoFixed geo = geo_fixed(&lv);
+    SelectArgs a = fixed_select_args(p, w, fixed_sort_plan(&lv), workspace, tau, row_ptr, col_idx, sched);
     a.scores = scores;
     hipError_t e = launch_select(&geo, nullptr, a, (hipStream_t)stream);
     if (e != hipSuccess) return fail(FP_ERR_HIP, "select launch: %s", hipGetErrorString(e));
@@ -374,8 +392,9 @@ int fp_estimate_select(const fp_problem* p, const void* q, const void* k, const 
     hipError_t e = fixed_pool(p, q, k, v, q_scale, k_scale, v_scale, qbar, kbar, vbar, st);
     if (e != hipSuccess) return fail(FP_ERR_HIP, "pool launch: %s", hipGetErrorString(e));
     const SelectWs w = fixed_select_ws(p);
-    GeoFixed geo = geo_fixed(p);
-    SelectArgs a = fixed_select_args(p, w, fixed_sort_plan(p), workspace, tau, row_ptr, col_idx, sched);
+    const fp_problem lv = lists_of(p);
+    GeoFixed geo = geo_fixed(&lv);
+    SelectArgs a = fixed_select_args(p, w, fixed_sort_plan(&lv), workspace, tau, row_ptr, col_idx, sched);
     if (geo.nb <= FUSED_MAX_NBK) {
         a.qbar = qbar; a.kbar = kbar;
         e = launch_select_fused(geo, a, st);
@@ -423,13 +442,17 @@ long long fixed_pooled_rows(const fp_problem* p) {
 int launch_prefill(const fp_problem* p, const void* q, const void* k, const void* v, const float* q_scale,
                    const float* k_scale, const float* v_scale, const float* kbar, const float* vbar,
                    const int32_t* row_ptr, const int32_t* col_idx, const int32_t* sched, void* o, float* lse,
-                   void* workspace, hipStream_t st) {
+                   void* workspace, hipStream_t st, const float* scores = nullptr) {
     const long long prow = fixed_pooled_rows(p);
     const bool fp8 = p->dtype == FP_DTYPE_FP8_E4M3;
-    GeoFixed geo = geo_fixed(p);
+    // rows of the kept lists: (sequence, KV head, query block), or per query head
+    const fp_problem lv = lists_of(p);
+    GeoFixed geo = geo_fixed(&lv);
     const int nsb = cdiv(p->seqlen, SCALE_TOK);
-    const int G = p->num_q_heads / p->num_kv_heads;
+    const int G = p->num_q_heads / lv.num_kv_heads;   // query heads sharing one list
     AttnArgs a{};
+    a.kv_div = lv.num_kv_heads / p->num_kv_heads;
+    a.scores = scores;
     a.q = q; a.k = k; a.v = v;
     a.qa = RowAddr{p->q_stride[0], p->q_stride[1], p->q_stride[2]};
     a.oa = RowAddr{p->o_stride[0], p->o_stride[1], p->o_stride[2]};
@@ -451,10 +474,11 @@ int launch_prefill(const fp_problem* p, const void* q, const void* k, const void
     a.o = o; a.lse = lse;
     a.la = RowAddr{(long long)p->num_q_heads * p->seqlen, 1, p->seqlen};
     a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads; a.G = G;
-    a.rows = p->batch * p->num_kv_heads * geo.nb;
+    a.rows = p->batch * lv.num_kv_heads * geo.nb;
     a.slices = cdiv(G * p->block, 128);
     a.scale_log2 = default_scale(p->softmax_scale, p->head_dim) * 1.4426950408889634f;
-    hipError_t e = launch_summary_prep(kbar, vbar, (__bf16*)a.kbar_hi, (__bf16*)a.kbar_lo,
+    // the block-score correction needs no pooled keys (kbar may be null)
+    hipError_t e = launch_summary_prep(scores ? nullptr : kbar, vbar, (__bf16*)a.kbar_hi, (__bf16*)a.kbar_lo,
                                        (__bf16*)a.vbar_bf, prow * D, st);
     if (e != hipSuccess) return fail(FP_ERR_HIP, "summary prep launch: %s", hipGetErrorString(e));
     e = launch_attn(&geo, nullptr, a, p->block, fp8, 0, st);
@@ -506,6 +530,9 @@ int fp_sparse_prefill(const fp_problem* p, const void* q, const void* k, const v
     int rc = check_prefill("fp_sparse_prefill", p, q, k, v, q_scale, k_scale, v_scale, kbar, vbar, row_ptr,
                            col_idx, o);
     if (rc) return rc;
+    if (p->variant == FP_VARIANT_BLOCK_SCORE)
+        return fail(FP_ERR_INVALID, "fp_sparse_prefill: the block-score variant takes the block scores "
+                                    "(fp_sparse_prefill_scored)");
     if (!workspace) return fail(FP_ERR_INVALID, "fp_sparse_prefill: NULL workspace");
     const size_t need = summary_ws_bytes(fixed_pooled_rows(p));
     if (ws_bytes < need)
@@ -536,6 +563,7 @@ int fp_dense_prefill(const fp_problem* p, const void* q, const void* k, const vo
     a.o_f32 = p->out_dtype == FP_OUT_FP32;
     a.no_correction = 1;                 // nothing is pruned
     a.dense = 1;
+    a.kv_div = 1;
     a.ka = KVAddr{p->k_stride[0], p->k_stride[1], p->k_stride[2], 0, nullptr, 0, 0};
     a.va = KVAddr{p->v_stride[0], p->v_stride[1], p->v_stride[2], 0, nullptr, 0, 0};
     a.qs = ScaleAddr{q_scale, (long long)p->num_q_heads * nsb, nsb};
@@ -551,6 +579,27 @@ int fp_dense_prefill(const fp_problem* p, const void* q, const void* k, const vo
     return ok();
 }
 
+int fp_sparse_prefill_scored(const fp_problem* p, const void* q, const void* k, const void* v,
+                             const float* q_scale, const float* k_scale, const float* v_scale,
+                             const float* scores, const float* vbar, const int32_t* row_ptr,
+                             const int32_t* col_idx, const int32_t* sched, void* o, float* lse,
+                             void* workspace, size_t ws_bytes, void* stream) {
+    int rc = check_prefill("fp_sparse_prefill_scored", p, q, k, v, q_scale, k_scale, v_scale, vbar, vbar,
+                           row_ptr, col_idx, o);
+    if (rc) return rc;
+    if (p->variant != FP_VARIANT_BLOCK_SCORE)
+        return fail(FP_ERR_INVALID, "fp_sparse_prefill_scored: the problem's variant must be "
+                                    "FP_VARIANT_BLOCK_SCORE");
+    if (!scores || misaligned(scores, 16)) return fail(FP_ERR_INVALID, "fp_sparse_prefill_scored: scores");
+    if (!workspace) return fail(FP_ERR_INVALID, "fp_sparse_prefill_scored: NULL workspace");
+    const size_t need = summary_ws_bytes(fixed_pooled_rows(p));
+    if (ws_bytes < need)
+        return fail(FP_ERR_CAPACITY, "fp_sparse_prefill_scored: workspace %zu < %zu bytes", ws_bytes, need);
+    if (misaligned(workspace, ALIGN)) return fail(FP_ERR_INVALID, "workspace must be 256-byte aligned");
+    return launch_prefill(p, q, k, v, q_scale, k_scale, v_scale, nullptr, vbar, row_ptr, col_idx, sched, o, lse,
+                          workspace, (hipStream_t)stream, scores);
+}
+
 int fp_sparse_prefill_noalloc(const fp_problem* p, const void* q, const void* k, const void* v,
                               const float* q_scale, const float* k_scale, const float* v_scale,
                               const float* kbar, const float* vbar, const int32_t* row_ptr,
@@ -559,6 +608,9 @@ int fp_sparse_prefill_noalloc(const fp_problem* p, const void* q, const void* k,
     int rc = check_prefill("fp_sparse_prefill_noalloc", p, q, k, v, q_scale, k_scale, v_scale, kbar, vbar,
                            row_ptr, col_idx, o);
     if (rc) return rc;
+    if (p->variant == FP_VARIANT_BLOCK_SCORE)
+        return fail(FP_ERR_INVALID, "fp_sparse_prefill_noalloc: the block-score variant takes the block scores "
+                                    "(fp_sparse_prefill_scored)");
     const size_t need = summary_ws_bytes(fixed_pooled_rows(p));
     if (need > (size_t)FP_NOALLOC_SCRATCH_BYTES)
         return fail(FP_ERR_CAPACITY,
@@ -779,6 +831,7 @@ int fp_sparse_prefill_paged(const fp_varlen_problem* p, const void* q, const int
     se.rows = (int)plan.rows; se.max_nbk = std::max(plan.max_nbk, 1);
     se.ngrp = plan.sort.ngrp; se.grp_units = plan.sort.grp_units;
     se.neg_tau = -tau;
+    se.kv_div = 1; se.Hkv_pool = p->num_kv_heads;
     e = launch_select(nullptr, &geo, se, st);
     if (e != hipSuccess) return fail(FP_ERR_HIP, "select launch: %s", hipGetErrorString(e));
 
@@ -788,6 +841,7 @@ int fp_sparse_prefill_paged(const fp_varlen_problem* p, const void* q, const int
     a.qa = RowAddr{0, p->q_stride[0], p->q_stride[1]};
     a.oa = RowAddr{0, p->o_stride[0], p->o_stride[1]};
     a.ka = kva; a.va = kva;
+    a.kv_div = 1;
     // per-lane in-page offsets of a tile are kept in 24 bits
     a.paged_fast = (long long)std::min(p->page_size, p->block) * p->kv_stride[1] * (fp8 ? 1 : 2) < (1LL << 24);
     a.qs = pa.qs; a.ks = pa.ks; a.vs = pa.vs;

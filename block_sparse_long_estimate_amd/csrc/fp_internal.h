@@ -167,6 +167,7 @@ struct SelectArgs {
     float neg_tau;
     // fused estimate + threshold (scores == nullptr): pooled rows and the softmax scale
     const float* qbar; const float* kbar; float scale;
+    int kv_div, Hkv_pool;                       // pooled keys of list group g: KV head g / kv_div of Hkv_pool
 };
 
 // Fused block scores + threshold: the workgroup's S columns (query block x
@@ -197,6 +198,8 @@ struct AttnArgs {
     int paged_fast;                    // paged: in-page offsets of a tile fit 24 bits (precomputed per lane)
     int no_correction;                 // ablation: pruned blocks dropped (no summary tiles)
     int dense;                         // every block j <= i kept, no kept lists read (dense causal attention)
+    int kv_div;                        // KV head of kept-list row group g: g / kv_div (G with per-head lists, else 1)
+    const float* scores;               // block-score correction: pseudo-token logit S[b,h,i,j] + ln|J| (else null)
 };
 
 hipError_t launch_pool(const GeoFixed* gf, const GeoTable* gt, const PoolArgs& a, hipStream_t st);

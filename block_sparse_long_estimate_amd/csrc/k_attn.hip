@@ -261,6 +261,7 @@ __device__ __forceinline__ void issue_summary(const AttnArgs& a, const SeqDesc& 
 #pragma unroll
     for (int w = 0; w < 2; ++w) {
         constexpr int KP = TG::SKPIECES, VP = TG::SVPIECES;
+        if (w == 0 && a.scores) continue;           // block-score correction: no pooled keys needed
         lds_u8* buf = w == 0 ? kbuf : vbuf;
 #pragma unroll
         for (int t0 = 0; t0 < (w == 0 ? KP : VP); t0 += NW) {
@@ -441,7 +442,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_tile_kernel(Geo geo, AttnArgs
     const int b = geo.seq_of_row(r);
     const SeqDesc s = geo.seq(b);
     const int rl = r - s.row0;
-    const int g = rl / s.nq, il = rl % s.nq;
+    const int g = rl / s.nq, il = rl % s.nq;       // g: the row's group of query heads
+    const int gk = g / a.kv_div;                     // its KV head
     const int i = s.i0 + il;
     const int t_lo = max(i * BLK, s.P), t_hi = min((i + 1) * BLK, s.L);
     const int G = a.G;
@@ -478,7 +480,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_tile_kernel(Geo geo, AttnArgs
         kvo.k.init_paged(a.ka.st, lshift, wave, lane);
         kvo.v.init_paged(a.va.st, lshift, wave, lane);
     }
-    issue_kv<BLK, FP8, PAGED, NW>(a, b, s.L, g, j0, kA, vA, wave, lane, kvo, nullptr);
+    issue_kv<BLK, FP8, PAGED, NW>(a, b, s.L, gk, j0, kA, vA, wave, lane, kvo, nullptr);
     // paged: stage the page ids for the later tiles (visible after the
     // barrier that follows the kept-bitmap build)
     const lds_int* pages = nullptr;
@@ -524,8 +526,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_tile_kernel(Geo geo, AttnArgs
         }
     }
     // fp8 tile scales of this row's (sequence, KV head): one per 128 keys
-    const float* ksp = FP8 ? a.ks.p + (long long)b * a.ks.sb + (long long)g * a.ks.sh : nullptr;
-    const float* vsp = FP8 ? a.vs.p + (long long)b * a.vs.sb + (long long)g * a.vs.sh : nullptr;
+    const float* ksp = FP8 ? a.ks.p + (long long)b * a.ks.sb + (long long)gk * a.ks.sh : nullptr;
+    const float* vsp = FP8 ? a.vs.p + (long long)b * a.vs.sb + (long long)gk * a.vs.sh : nullptr;
     float ksA = 1.f, vsA = 1.f, ksB = 1.f, vsB = 1.f;
     if constexpr (FP8) {
         ksA = load_scale(ksp, (j0 * BLK) >> 7);
@@ -570,13 +572,13 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_tile_kernel(Geo geo, AttnArgs
 
     auto issue = [&](int code, lds_u8* kb, lds_u8* vb, float& ksn, float& vsn) __attribute__((always_inline)) {
         if (code >= 0) {
-            issue_kv<BLK, FP8, PAGED, NW>(a, b, s.L, g, code, kb, vb, wave, lane, kvo, pages);
+            issue_kv<BLK, FP8, PAGED, NW>(a, b, s.L, gk, code, kb, vb, wave, lane, kvo, pages);
             if constexpr (FP8) {
                 ksn = load_scale(ksp, (code * BLK) >> 7);
                 vsn = load_scale(vsp, (code * BLK) >> 7);
             }
         } else {
-            issue_summary<BLK, NW>(a, s, g, -1 - code, kb, vb, wave, lane);
+            issue_summary<BLK, NW>(a, s, gk, -1 - code, kb, vb, wave, lane);
         }
     };
     // causal mask inside the diagonal tile: keys after the row's token
@@ -636,8 +638,29 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_tile_kernel(Geo geo, AttnArgs
     auto compute_summary = [&](int code, const lds_u8* kc, const lds_u8* vc) __attribute__((always_inline)) {
         const int mm = -1 - code;
         f32x16 sh[RG][SB];
-        qk_pad<RG, SB, FP8 ? 1 : 0, false>(kc, qf, n, lh, 0, sh);    // hi rows
-        qk_pad<RG, SB, FP8 ? 1 : 0, true>(kc, qf, n, lh, SB, sh);    // lo rows, same columns
+        float fs[RG];
+        if (a.scores) {
+            // block-score correction: the pseudo-token logit of column j is the
+            // block score S[h, i, j] (scale included), the same for every row
+            // of the query block
+#pragma unroll
+            for (int rg = 0; rg < RG; ++rg) {
+                const float* srow = a.scores + score_off(s, h[rg], il, 0);
+#pragma unroll
+                for (int kb = 0; kb < SB; ++kb)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int col = min(mm * TG::SUMC + kb * 32 + 8 * (v >> 2) + 4 * lh + (v & 3), s.nbk - 1);
+                        sh[rg][kb][v] = srow[col];
+                    }
+                fs[rg] = 1.4426950408889634f;                        // log2(e): S is in natural-log units
+            }
+        } else {
+            qk_pad<RG, SB, FP8 ? 1 : 0, false>(kc, qf, n, lh, 0, sh);    // hi rows
+            qk_pad<RG, SB, FP8 ? 1 : 0, true>(kc, qf, n, lh, SB, sh);    // lo rows, same columns
+#pragma unroll
+            for (int rg = 0; rg < RG; ++rg) fs[rg] = f_row[rg];
+        }
 #pragma unroll
         for (int kb = 0; kb < SB; ++kb) {
             const int c0 = mm * TG::SUMC + kb * 32;
@@ -652,7 +675,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_tile_kernel(Geo geo, AttnArgs
         float mn[RG], ts[RG];
         bool nd[RG];
 #pragma unroll
-        for (int rg = 0; rg < RG; ++rg) softmax_probs<SB, 8>(sh[rg], f_row[rg], lnb2, lw_sum, m[rg], mn[rg], ts[rg], nd[rg]);
+        for (int rg = 0; rg < RG; ++rg) softmax_probs<SB, 8>(sh[rg], fs[rg], lnb2, lw_sum, m[rg], mn[rg], ts[rg], nd[rg]);
         softmax_commit<RG>(nd, m, mn, lsum, ts, lw_sum, oacc);
         pv_tr<RG, SB>(sh, vc, lane, 0, oacc);
     };
@@ -692,19 +715,19 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_tile_kernel(Geo geo, AttnArgs
     // Summary phase: realign so the loop below always starts on buffer A.
     if (in_b && nxt != TILE_NONE) {
         const int cn = next_summary<TG::SUMC>(kbits, i, -nxt, no_corr);
-        if (cn != TILE_NONE) issue_summary<BLK, NW>(a, s, g, -1 - cn, kA, vA, wave, lane);
+        if (cn != TILE_NONE) issue_summary<BLK, NW>(a, s, gk, -1 - cn, kA, vA, wave, lane);
         compute_summary(nxt, kB, vB);
         __syncthreads();
         nxt = cn;
     }
     while (nxt != TILE_NONE) {
         const int cb = next_summary<TG::SUMC>(kbits, i, -nxt, no_corr);
-        if (cb != TILE_NONE) issue_summary<BLK, NW>(a, s, g, -1 - cb, kB, vB, wave, lane);
+        if (cb != TILE_NONE) issue_summary<BLK, NW>(a, s, gk, -1 - cb, kB, vB, wave, lane);
         compute_summary(nxt, kA, vA);
         __syncthreads();
         if (cb == TILE_NONE) break;
         const int cn = next_summary<TG::SUMC>(kbits, i, -cb, no_corr);
-        if (cn != TILE_NONE) issue_summary<BLK, NW>(a, s, g, -1 - cn, kA, vA, wave, lane);
+        if (cn != TILE_NONE) issue_summary<BLK, NW>(a, s, gk, -1 - cn, kA, vA, wave, lane);
         compute_summary(cb, kB, vB);
         __syncthreads();
         nxt = cn;
@@ -743,23 +766,26 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_tile_kernel(Geo geo, AttnArgs
     }
 }
 
-// bf16 operands of the summary tiles: Kbar = hi + lo (two bf16 terms), Vbar.
+// bf16 operands of the summary tiles: Kbar = hi + lo (two bf16 terms), Vbar
+// (only Vbar when kbar is null).
 __global__ __launch_bounds__(256) void summary_prep_kernel(const float* kbar, const float* vbar, __bf16* hi,
                                                            __bf16* lo, __bf16* vb, long long n4) {
     const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
     if (e >= n4) return;
-    const float4 k = ((const float4*)kbar)[e];
     const float4 v = ((const float4*)vbar)[e];
-    uint2 h, l, w;
+    uint2 w;
+    w.x = pk_bf16(v.x, v.y);
+    w.y = pk_bf16(v.z, v.w);
+    ((uint2*)vb)[e] = w;
+    if (!kbar) return;                  // pooled values only
+    const float4 k = ((const float4*)kbar)[e];
+    uint2 h, l;
     h.x = pk_bf16(k.x, k.y);
     h.y = pk_bf16(k.z, k.w);
     l.x = pk_bf16(k.x - bf16_round(k.x), k.y - bf16_round(k.y));
     l.y = pk_bf16(k.z - bf16_round(k.z), k.w - bf16_round(k.w));
-    w.x = pk_bf16(v.x, v.y);
-    w.y = pk_bf16(v.z, v.w);
     ((uint2*)hi)[e] = h;
     ((uint2*)lo)[e] = l;
-    ((uint2*)vb)[e] = w;
 }
 
 hipError_t launch_summary_prep(const float* kbar, const float* vbar, __bf16* hi, __bf16* lo, __bf16* vb,

@@ -131,7 +131,7 @@ __global__ __launch_bounds__(FUSED_WAVES * 64) void select_fused_kernel(GeoFixed
     // pooled keys of key tile kt for this lane: row kt * 32 + n, the dims of qv
     auto load_tile = [&](int kt, float4 (&kv)[4][4]) {
         const int jrow = min(kt * 32 + n, s.nbk - 1);
-        const float* kr = a.kbar + kbar_row(s, a.Hkv, g, jrow) * D;
+        const float* kr = a.kbar + kbar_row(s, a.Hkv_pool, g / a.kv_div, jrow) * D;
 #pragma unroll
         for (int p = 0; p < 4; ++p)
 #pragma unroll

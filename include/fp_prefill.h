@@ -69,6 +69,11 @@ extern "C" {
 #define FP_OUT_FP32 2            /* ... in float32 (diagnostic: no output rounding) */
 #define FP_VARIANT_MEAN_CORRECTION 0   /* E6 as specified: pruned blocks as pooled pseudo-tokens */
 #define FP_VARIANT_NO_CORRECTION 1     /* ablation: pruned blocks simply dropped        */
+#define FP_VARIANT_PER_HEAD_LISTS 2    /* ablation: one kept list per query head (E4 without the
+                                          GQA union); kept-list rows are (b, query head, i)  */
+#define FP_VARIANT_BLOCK_SCORE 3       /* ablation: a pruned block's pseudo-token takes the block
+                                          score S[h,i,j] + ln|block| as logit for every row of
+                                          query block i (fp_sparse_prefill_scored)            */
 
 /* Fixed-shape batch: `batch` sequences of `seqlen` tokens each, one-shot
  * prefill (no cached prefix). q [batch, seqlen, Hq, 128], k and v
@@ -88,8 +93,9 @@ typedef struct fp_problem {
     int64_t v_stride[3];
     int64_t o_stride[3];
     int32_t out_dtype;       /* FP_OUT_BF16 (0, default) or FP_OUT_FP32: diagnostic fp32 o */
-    int32_t variant;         /* FP_VARIANT_MEAN_CORRECTION (0, default) or FP_VARIANT_NO_CORRECTION:
-                                an ablation of the mean correction (fp_sparse_prefill only) */
+    int32_t variant;         /* FP_VARIANT_MEAN_CORRECTION (0, default) or an ablation: NO_CORRECTION
+                                and BLOCK_SCORE change E6 only; PER_HEAD_LISTS changes the kept
+                                lists (sizes, selection and attention rows) */
 } fp_problem;
 
 /* Paged varlen batch (continuous batching with cached prefixes). Sequence b
@@ -116,7 +122,7 @@ const char* fp_version(void);
 const char* fp_last_error(void);
 
 /* Sizing (host only, no HIP call). Return < 0 with fp_last_error() set on an
- * invalid problem. */
+ * invalid problem. With FP_VARIANT_PER_HEAD_LISTS, Hq replaces Hkv below. */
 int64_t fp_num_rows(const fp_problem* p);       /* batch * Hkv * nb           */
 int64_t fp_max_nnz(const fp_problem* p);        /* batch * Hkv * nb(nb+1)/2   */
 int64_t fp_workspace_size(const fp_problem* p); /* bytes for fp_select_blocks */
@@ -189,6 +195,19 @@ int fp_sparse_prefill(const fp_problem* p, const void* q, const void* k, const v
                       const float* kbar, const float* vbar,
                       const int32_t* row_ptr, const int32_t* col_idx, const int32_t* sched,
                       void* o, float* lse, void* workspace, size_t ws_bytes, void* stream);
+
+/* E6 under the block-score correction (FP_VARIANT_BLOCK_SCORE, an ablation
+ * of the mean correction of the lode.cx page, "How It Works", and the
+ * aimodeling.com page, "Error correction" bullet): a pruned block j stands in
+ * as one pseudo-token with value Vbar[g,j] and logit scores[b,h,i,j] +
+ * ln|block j| for every row of query block i. scores (device) as written by
+ * fp_block_scores; no pooled keys are read. Other arguments as for
+ * fp_sparse_prefill; the problem's variant must be FP_VARIANT_BLOCK_SCORE. */
+int fp_sparse_prefill_scored(const fp_problem* p, const void* q, const void* k, const void* v,
+                             const float* q_scale, const float* k_scale, const float* v_scale,
+                             const float* scores, const float* vbar,
+                             const int32_t* row_ptr, const int32_t* col_idx, const int32_t* sched,
+                             void* o, float* lse, void* workspace, size_t ws_bytes, void* stream);
 
 /* Dense causal attention with the same kernel: every key block j <= i of
  * every row is attended (no estimate, no selection, no correction), tiles in

@@ -37,6 +37,8 @@ static const char* g_case = "";
 struct Launch {
     bool paged = false;
     int nseq = 0, Hq = 0, Hkv = 0, G = 0, blk = 128;
+    int kv_div = 1;                  // per-head lists: list groups are query heads, KV head = g / kv_div
+    int Hlist = 0;                   // list groups per sequence (Hkv, or Hq with per-head lists)
     std::vector<SeqDesc> table;      // nseq + 1 (the last entry: totals)
     RowAddr qa{}, oa{}, la{};
     KVAddr ka{}, va{};
@@ -65,7 +67,7 @@ static void make_lists(Launch& L, std::mt19937_64& rng, double density) {
     L.col_idx.clear();
     for (int b = 0; b < L.nseq; ++b) {
         const SeqDesc& s = L.table[b];
-        for (int g = 0; g < L.Hkv; ++g)
+        for (int g = 0; g < L.Hlist; ++g)
             for (int il = 0; il < s.nq; ++il) {
                 const int i = s.i0 + il;
                 for (int j = 0; j <= i; ++j)
@@ -95,14 +97,14 @@ static void make_table(Launch& L, const std::vector<int>& Ls, const std::vector<
         s.q0 = L.paged ? (int)qrows : 0;
         s.qb0 = (int)qb;
         s.kb0 = (int)kb;
-        s.row0 = (int)(qb * L.Hkv);
+        s.row0 = (int)(qb * L.Hlist);
         qb += s.nq;
         kb += s.nbk;
         qrows += ql;
     }
     L.table[L.nseq].qb0 = (int)qb;
     L.table[L.nseq].kb0 = (int)kb;
-    L.table[L.nseq].row0 = (int)(qb * L.Hkv);
+    L.table[L.nseq].row0 = (int)(qb * L.Hlist);
     L.pooled_rows = kb * L.Hkv;
 }
 
@@ -162,6 +164,7 @@ static void replay(const Launch& L) {
         const SeqDesc s = L.table[b];
         const int rl = r - s.row0;
         const int g = rl / s.nq, il = rl % s.nq;
+        const int gk = g / L.kv_div;
         const int i = s.i0 + il;
         const int t_lo = std::max(i * BLK, s.P), t_hi = std::min((i + 1) * BLK, s.L);
         const int npk = L.G * (t_hi - t_lo);
@@ -238,7 +241,7 @@ static void replay(const Launch& L) {
             if (code >= 0) {
                 CHECK(code <= i, "kept code %d > %d", code, i);
                 if (FP8) {
-                    const long long ksi = (long long)b * L.ks.sb + (long long)g * L.ks.sh + ((code * BLK) >> 7);
+                    const long long ksi = (long long)b * L.ks.sb + (long long)gk * L.ks.sh + ((code * BLK) >> 7);
                     CHECK(ksi >= 0 && ksi < L.kvs_elems, "k scale %lld", ksi);
                 }
                 const bool full = (code + 1) * BLK <= s.L;
@@ -249,8 +252,8 @@ static void replay(const Launch& L) {
                         if (!PAGED && full) {
                             ko.init(ka.st, wave, lane);
                             vo.init(va.st, wave, lane);
-                            const long long k0 = ka.template off<false>(b, code * BLK, g) * ESZ;
-                            const long long v0 = va.template off<false>(b, code * BLK, g) * ESZ;
+                            const long long k0 = ka.template off<false>(b, code * BLK, gk) * ESZ;
+                            const long long v0 = va.template off<false>(b, code * BLK, gk) * ESZ;
                             for (int k = 0; k < ko.NP; ++k)
                                 if (ko.has(k, wave)) {
                                     check_kv(ko.src_full(k0, k), kbytes, "K tile");
@@ -267,7 +270,7 @@ static void replay(const Launch& L) {
                             vo.init_paged(va.st, lshift, wave, lane);
                             const int sh = ka.page_shift;
                             const long long ub =
-                                (long long)((code * BLK) & ((1 << sh) - 1)) * ka.st + (long long)g * ka.sh;
+                                (long long)((code * BLK) & ((1 << sh) - 1)) * ka.st + (long long)gk * ka.sh;
                             const int slot0 = (code * BLK) >> sh;
                             for (int k = 0; k < ko.NP; ++k)
                                 if (ko.has(k, wave)) {
@@ -288,7 +291,7 @@ static void replay(const Launch& L) {
                             for (int k = 0; k < ko.NP; ++k) {
                                 if (!ko.has(k, wave)) continue;
                                 const long long src = tile_src<TG::KS, BLK, ESZ, false, PAGED>(
-                                    ka, b, s.L, g, code, k * NW + wave, lane, pf, staged);
+                                    ka, b, s.L, gk, code, k * NW + wave, lane, pf, staged);
                                 {
                                     check_kv(src, kbytes, "K generic tile");
                                     CHECK((k * NW + wave) * PIECE + 16 * lane + 16 <= TG::KTILE, "K LDS piece");
@@ -297,7 +300,7 @@ static void replay(const Launch& L) {
                             for (int k = 0; k < vo.NP; ++k) {
                                 if (!vo.has(k, wave)) continue;
                                 const long long src = tile_src<TG::VS, BLK, ESZ, FP8, PAGED>(
-                                    va, b, s.L, g, code, k * NW + wave, lane, pf, staged);
+                                    va, b, s.L, gk, code, k * NW + wave, lane, pf, staged);
                                 {
                                     check_kv(src, vbytes, "V generic tile");
                                     CHECK((k * NW + wave) * PIECE + 16 * lane + 16 <= TG::VTILE, "V LDS piece");
@@ -315,7 +318,7 @@ static void replay(const Launch& L) {
                             const int t = t0 + wave;
                             if (t >= P) continue;
                             for (int lane = 0; lane < 64; ++lane) {
-                                const SummarySrc src = summary_src<BLK>(s, L.Hkv, g, m, w, t, lane);
+                                const SummarySrc src = summary_src<BLK>(s, L.Hkv, gk, m, w, t, lane);
                                 CHECK(src.which >= 0 && src.which <= 2, "summary array %d", src.which);
                                 CHECK(src.off >= 0 && src.off + 8 <= L.pooled_rows * D, "summary source %lld",
                                       src.off);
@@ -350,17 +353,19 @@ static void replay(const Launch& L) {
 // problem builders
 // ---------------------------------------------------------------------------
 static Launch fixed_launch(int batch, int S, int Hq, int Hkv, int blk, bool fp8, double density, uint64_t seed,
-                           bool fused_qkv) {
+                           bool fused_qkv, bool per_head = false) {
     Launch L;
     L.nseq = batch;
     L.Hq = Hq;
     L.Hkv = Hkv;
-    L.G = Hq / Hkv;
+    L.G = per_head ? 1 : Hq / Hkv;
+    L.kv_div = per_head ? Hq / Hkv : 1;
+    L.Hlist = per_head ? Hq : Hkv;
     L.blk = blk;
     make_table(L, std::vector<int>(batch, S), std::vector<int>(batch, 0));
     // fixed shape: every sequence has nb query and key blocks; the descriptor
-    // offsets are the same arithmetic GeoFixed uses
-    GeoFixed gf{batch, S, Hq, Hkv, blk, cdiv(S, blk), 0};
+    // offsets are the same arithmetic GeoFixed uses (over the list groups)
+    GeoFixed gf{batch, S, Hq, L.Hlist, blk, cdiv(S, blk), 0};
     for (int b = 0; b < batch; ++b) L.table[b] = gf.seq(b);
     long long qst = (long long)Hq * D, kst = (long long)Hkv * D;
     if (fused_qkv) qst = kst = (long long)(Hq + 2 * Hkv) * D;    // one [S, Hq + 2 Hkv, D] buffer
@@ -394,6 +399,7 @@ static Launch paged_launch(const std::vector<int>& Ls, const std::vector<int>& P
     L.Hq = Hq;
     L.Hkv = Hkv;
     L.G = Hq / Hkv;
+    L.Hlist = Hkv;
     L.blk = blk;
     make_table(L, Ls, Ps);
     int shift = 0;
@@ -469,6 +475,13 @@ int main(int argc, char** argv) {
                     replay_all<8>(L, fp8);
                     replay_all<4>(L, fp8);
                     if (quick) goto paged_cases;
+                    if (fused == 0 && f.Hq != f.Hkv) {      // one kept list per query head
+                        snprintf(name, sizeof name, "fixed per-head lists B=%d S=%d %d/%d blk=%d dens=%.1f %s",
+                                 f.batch, f.S, f.Hq, f.Hkv, f.blk, dens, fp8 ? "fp8" : "bf16");
+                        const Launch P = fixed_launch(f.batch, f.S, f.Hq, f.Hkv, f.blk, fp8, dens, seed++, false,
+                                                      true);
+                        replay_all<8>(P, fp8);
+                    }
                 }
 paged_cases:
     // paged varlen: cached prefixes (mid-block, on a block boundary, one new

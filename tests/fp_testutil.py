@@ -55,7 +55,7 @@ def attend_threaded(q, k, v, keep, kbar, vbar, c, B, P, rows=None, correction=Tr
 KEPT_REL = {"bf16": 2.0 ** -17, "fp8": 2.0 ** -11}
 
 
-def lse_bound(q, k, keep, kbar, lse_ref, c, B, P, rows=None, correction=True, kind="bf16"):
+def lse_bound(q, k, keep, kbar, lse_ref, c, B, P, rows=None, correction=True, kind="bf16", pruned=None):
     """Per-element bound on |lse_gpu - lse_oracle| [Hq, L-P], from the data.
 
     lse is 1-Lipschitz in every logit (max norm), so the bound is the largest
@@ -70,7 +70,9 @@ def lse_bound(q, k, keep, kbar, lse_ref, c, B, P, rows=None, correction=True, ki
                       approximations: 2^-19 * (1 + |lse|).
     sum_d |q_d| |k_sd| is bounded by sum_d |q_d| max_s |k_sd| over the row's
     kept tokens (pruned blocks: exact per block). Rows not evaluated are NaN.
-    correction=False: the ablation without pseudo-tokens."""
+    correction=False: the ablation without pseudo-tokens. pruned: a separate
+    mask of the pseudo-token blocks (default: every block keep leaves out),
+    e.g. the blocks any head of a group prunes when lists are per head."""
     L, Hkv, d = k.shape
     Hq = q.shape[1]
     G = Hq // Hkv
@@ -79,18 +81,18 @@ def lse_bound(q, k, keep, kbar, lse_ref, c, B, P, rows=None, correction=True, ki
     todo = list(rows) if rows is not None else [(g, il) for il in range(nq) for g in range(Hkv)]
     with ThreadPoolExecutor(workers()) as ex:
         list(ex.map(lambda ch: _lse_bound_rows(q, k, keep, kbar, lse_ref, c, B, P, G, i0, ch, bound, correction,
-                                               KEPT_REL[kind]),
+                                               KEPT_REL[kind], ~keep if pruned is None else pruned),
                     _row_chunks(todo, workers())))
     return bound
 
 
-def _lse_bound_rows(q, k, keep, kbar, lse_ref, c, B, P, G, i0, todo, bound, correction, kept_rel):
+def _lse_bound_rows(q, k, keep, kbar, lse_ref, c, B, P, G, i0, todo, bound, correction, kept_rel, pruned):
     L = k.shape[0]
     for g, il in todo:
         i = i0 + il
         lo, hi = max(i * B, P), min((i + 1) * B, L)
         kj = np.nonzero(keep[g, il, :i + 1])[0]
-        pj = np.nonzero(~keep[g, il, :i + 1])[0] if correction else []
+        pj = np.nonzero(pruned[g, il, :i + 1])[0] if correction else []
         kmax = np.max([np.abs(k[j * B:min((j + 1) * B, L), g]).max(axis=0) for j in kj], axis=0)
         qa = np.abs(q[lo - P:hi - P, g * G:(g + 1) * G])          # [rows, G, d]
         a_kept = c * (qa @ kmax)                                   # [rows, G]

@@ -240,6 +240,28 @@ def test_variant_validation():
     assert ctypes.sizeof(N.FpProblem) == 136
     assert lib.fp_num_rows(ctypes.byref(problem(variant=N.FP_VARIANT_NO_CORRECTION))) > 0
     assert lib.fp_num_rows(ctypes.byref(problem(variant=7))) == N.FP_ERR_UNSUPPORTED
+    # per-head lists: one row per (query head, query block), sizes follow
+    base = problem()
+    ph = problem(variant=N.FP_VARIANT_PER_HEAD_LISTS)
+    G = base.num_q_heads // base.num_kv_heads
+    assert lib.fp_num_rows(ctypes.byref(ph)) == G * lib.fp_num_rows(ctypes.byref(base))
+    assert lib.fp_max_nnz(ctypes.byref(ph)) == G * lib.fp_max_nnz(ctypes.byref(base))
+    assert lib.fp_workspace_size(ctypes.byref(ph)) > lib.fp_workspace_size(ctypes.byref(base))
+    assert lib.fp_prefill_workspace_size(ctypes.byref(ph)) == lib.fp_prefill_workspace_size(ctypes.byref(base))
+
+
+def test_block_score_variant_takes_scores():
+    """The block-score variant runs through fp_sparse_prefill_scored only; the
+    other entry points refuse it, and the scored entry refuses other variants
+    (all before any HIP call)."""
+    lib = N.load()
+    fake = ctypes.c_void_p(1 << 20)
+    args = [fake] * 3 + [None] * 3 + [fake] * 4 + [None, fake, None, fake, 1 << 30, None]
+    bs = problem(variant=N.FP_VARIANT_BLOCK_SCORE)
+    assert lib.fp_sparse_prefill(ctypes.byref(bs), *args) == N.FP_ERR_INVALID
+    assert b"fp_sparse_prefill_scored" in lib.fp_last_error()
+    assert lib.fp_sparse_prefill_scored(ctypes.byref(problem()), *args) == N.FP_ERR_INVALID
+    assert b"FP_VARIANT_BLOCK_SCORE" in lib.fp_last_error()
 
 
 def test_out_dtype_validation():
