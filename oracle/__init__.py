@@ -46,7 +46,8 @@ so E1-E6 themselves are "parity unpinned" against the paper: they are the
 stated reading.
 """
 from .core import (
-    nblocks, query_blocks, pool_queries, pool_keys, block_scores, select,
+    nblocks, query_blocks, pool_queries, pool_keys, pool_update, pool_means, prefill_chunked,
+    block_scores, select,
     attend, prefill, kept_fraction, threshold_margin, causal_block_pairs,
     dense_flops, kept_flops, correction_flops,
 )
@@ -54,7 +55,8 @@ from .fp8 import decode_e4m3, widen_fp8
 from .batch import prefill_fixed, prefill_varlen, varlen_sequence, widen_bf16
 
 __all__ = [
-    "nblocks", "query_blocks", "pool_queries", "pool_keys", "block_scores", "select",
+    "nblocks", "query_blocks", "pool_queries", "pool_keys", "pool_update", "pool_means", "prefill_chunked",
+    "block_scores", "select",
     "attend", "prefill", "kept_fraction", "threshold_margin", "causal_block_pairs",
     "dense_flops", "kept_flops", "correction_flops", "decode_e4m3", "widen_fp8",
     "prefill_fixed", "prefill_varlen", "varlen_sequence", "widen_bf16",

@@ -54,6 +54,37 @@ def pool_keys(k: np.ndarray, B: int) -> np.ndarray:
     return out
 
 
+def pool_update(sums: np.ndarray, counts: np.ndarray, x_new: np.ndarray, start: int,
+                B: int) -> Tuple[np.ndarray, np.ndarray]:
+    """E1 kept incrementally across chunks (the pages' chunked prefill over a
+    paged KV cache: lode.cx page, "How It Works", implementation paragraph;
+    aimodeling.com page, "Framework integration" bullet). sums [H, nb, d] and
+    counts [nb] are the running per-block sums and token counts of the keys
+    (or values) seen so far; x_new [n, H, d] holds the keys at positions
+    start .. start+n-1. Each new token is added to the sum of its block. The
+    block means are sums / counts (pool_means). Returns new arrays, grown as
+    far as the new tokens reach."""
+    n, H, d = x_new.shape
+    nb = nblocks(start + n, B)
+    S = np.zeros((H, max(nb, sums.shape[1]), d))
+    C = np.zeros(S.shape[1], dtype=np.int64)
+    S[:, :sums.shape[1]] = sums
+    C[:counts.shape[0]] = counts
+    for t in range(n):
+        j = (start + t) // B
+        S[:, j] += x_new[t]
+        C[j] += 1
+    return S, C
+
+
+def pool_means(sums: np.ndarray, counts: np.ndarray, L: int, B: int) -> np.ndarray:
+    """The pooled keys of blocks 0 .. nblocks(L)-1 from running sums: the mean
+    over each block's present tokens (E1)."""
+    nb = nblocks(L, B)
+    assert counts.shape[0] >= nb and counts[:nb].min() > 0
+    return sums[:, :nb] / counts[:nb, None]
+
+
 def block_scores(qbar: np.ndarray, kbar: np.ndarray, c: float, i0: int) -> np.ndarray:
     """E2: S[h, il, j] = c <Qbar[h, il], Kbar[g(h), j]> for j <= i0 + il, -inf above.
 
@@ -189,13 +220,16 @@ def prefill(q: np.ndarray, k: np.ndarray, v: np.ndarray, B: int, tau: float,
             keep: Optional[np.ndarray] = None,
             rows: Optional[Sequence[Tuple[int, int]]] = None,
             with_output: bool = True, correction: bool = True,
-            variant: str = "mean") -> Dict[str, np.ndarray]:
+            variant: str = "mean",
+            pooled_kv: Optional[Tuple[np.ndarray, np.ndarray]] = None) -> Dict[str, np.ndarray]:
     """E1-E6 for one sequence.  keep overrides the oracle's own mask (used to
     evaluate E6 under another, validated mask); correction=False evaluates the
     ablation without the mean correction. variant: "mean" (E1-E6 as stated),
     "none" (no correction), "per_head" (one kept list per query head, no GQA
     union; keep and R are [Hq, nq, nb]) or "block_score" (the pruned blocks'
-    pseudo-tokens take the block score S[h, i, j] + ln|J_j| as logit)."""
+    pseudo-tokens take the block score S[h, i, j] + ln|J_j| as logit).
+    pooled_kv: (Kbar, Vbar) [Hkv, nblocks(L), d] kept from earlier chunks
+    (prefill_chunked), used in place of pooling k and v here."""
     if variant not in VARIANTS:
         raise ValueError(f"unknown variant {variant}")
     if variant == "none":
@@ -208,8 +242,11 @@ def prefill(q: np.ndarray, k: np.ndarray, v: np.ndarray, B: int, tau: float,
         c = 1.0 / math.sqrt(d)
     i0, nq = query_blocks(P, L, B)
     qbar = pool_queries(q, B, P, L)
-    kbar = pool_keys(k, B)
-    vbar = pool_keys(v, B)
+    if pooled_kv is None:
+        kbar, vbar = pool_keys(k, B), pool_keys(v, B)
+    else:
+        kbar, vbar = pooled_kv
+        assert kbar.shape == (Hkv, nblocks(L, B), d) and vbar.shape == kbar.shape
     S = block_scores(qbar, kbar, c, i0)
     own_keep, R = select(S, G, tau, i0, per_head=variant == "per_head")
     out = dict(qbar=qbar, kbar=kbar, vbar=vbar, S=S, R=R, keep=own_keep, i0=i0, nq=nq)
@@ -217,6 +254,30 @@ def prefill(q: np.ndarray, k: np.ndarray, v: np.ndarray, B: int, tau: float,
         use = own_keep if keep is None else keep
         out["o"], out["lse"] = attend(q, k, v, use, kbar, vbar, c, B, P, rows=rows, correction=correction,
                                       block_scores=S if variant == "block_score" else None)
+    return out
+
+
+def prefill_chunked(q: np.ndarray, k: np.ndarray, v: np.ndarray, B: int, tau: float,
+                    ends: Sequence[int], c: Optional[float] = None,
+                    variant: str = "mean") -> list:
+    """Chunked prefill of one sequence with a pooled-KV cache: chunk n holds
+    the query rows [ends[n-1], ends[n]) (ends[-1] = L) and sees the keys
+    [0, ends[n]). The per-block sums of K and V are carried from chunk to
+    chunk and each chunk adds only its own keys (pool_update); E2-E6 then run
+    on the cached means (prefill with pooled_kv). q, k, v hold the whole
+    sequence. Returns one prefill result per chunk."""
+    L, Hkv, d = k.shape
+    sk = np.zeros((Hkv, 0, d)); sv = np.zeros((Hkv, 0, d)); cnt = np.zeros(0, dtype=np.int64)
+    out, P = [], 0
+    for end in ends:
+        assert P < end <= L
+        sk, cnt_k = pool_update(sk, cnt, k[P:end], P, B)
+        sv, cnt = pool_update(sv, cnt, v[P:end], P, B)
+        assert np.array_equal(cnt_k, cnt)
+        pooled = (pool_means(sk, cnt, end, B), pool_means(sv, cnt, end, B))
+        out.append(prefill(q[P:end], k[:end], v[:end], B, tau, c=c, P=P, variant=variant,
+                           pooled_kv=pooled))
+        P = end
     return out
 
 

@@ -321,6 +321,47 @@ def test_chunk_rows_equal_one_shot_rows():
         assert np.array_equal(part["keep"][:, il0:], full["keep"][:, first_full // B:])
 
 
+@pytest.mark.parametrize("ends", [(37,), (16, 40, 75), (5, 6, 64, 65, 100), (48, 96, 113)])
+def test_pool_update_chunks_equal_one_shot_pooling(ends):
+    """Running per-block sums fed chunk by chunk give exactly the one-shot
+    block means (E1) once every token is in: dyadic inputs make every sum
+    exact, so the comparison is bit for bit; the counts are the block sizes."""
+    L, B, H, d = ends[-1], 16, 3, 5
+    x = np.random.default_rng(44).integers(-64, 64, (L, H, d)) / 8.0
+    sums, counts, P = np.zeros((H, 0, d)), np.zeros(0, dtype=np.int64), 0
+    for end in ends:
+        sums, counts = oracle.pool_update(sums, counts, x[P:end], P, B)
+        # after each chunk the means cover exactly the keys seen so far
+        assert np.array_equal(oracle.pool_means(sums, counts, end, B), pool_keys(x[:end], B))
+        sizes = [min((j + 1) * B, end) - j * B for j in range(-(-end // B))]
+        assert counts.tolist() == sizes
+        P = end
+
+
+def test_prefill_chunked_equals_uncached_chunks_and_one_shot_rows():
+    """A chunked prefill that carries the pooled K/V from chunk to chunk
+    equals, chunk by chunk, a prefill that pools all of the chunk's keys
+    afresh, and its rows in full query blocks equal the one-shot prefill's."""
+    L, B, Hq, Hkv, d = 150, 16, 4, 2, 8
+    q = rnd((L, Hq, d), 45) + 0.5
+    k = rnd((L, Hkv, d), 46) + np.cumsum(rnd((L, Hkv, d), 47, 0.5), axis=0)
+    v = rnd((L, Hkv, d), 48)
+    full = prefill(q, k, v, B, 0.5, 0.4)
+    ends = (40, 41, 100, 150)
+    chunks = oracle.prefill_chunked(q, k, v, B, 0.5, ends, c=0.4)
+    P = 0
+    for end, ch in zip(ends, chunks):
+        fresh = prefill(q[P:end], k[:end], v[:end], B, 0.5, 0.4, P=P)
+        assert np.abs(ch["kbar"] - pool_keys(k[:end], B)).max() < 1e-12
+        assert np.array_equal(ch["keep"], fresh["keep"])
+        assert np.abs(ch["o"] - fresh["o"]).max() < 1e-12
+        first_full = -(-P // B) * B
+        last_full = end // B * B                    # rows of blocks complete within the chunk
+        if last_full > first_full:
+            assert np.abs(ch["o"][first_full - P:last_full - P] - full["o"][first_full:last_full]).max() < 1e-12
+        P = end
+
+
 def test_varlen_paged_batch_equals_per_sequence():
     import synth
     cfg = synth.config(5, Hq=4, Hkv=2, len_range=(150, 400), n_seqs=3, block=64, page_size=16)

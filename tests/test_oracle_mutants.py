@@ -113,6 +113,10 @@ MUTANTS = [
      "E6: correction mass dropped from the denominator"),
     ("attend", "kept_j = [j for j in range(i + 1) if keep[g, il, j]]",
      "kept_j = [j for j in range(i) if keep[g, il, j]]", "E6: exact tokens of the diagonal block dropped"),
+    ("pool_update", "j = (start + t) // B", "j = t // B",
+     "E1 cache: new tokens placed by their offset in the chunk, not their position"),
+    ("pool_update", "C[:counts.shape[0]] = counts", "pass", "E1 cache: earlier chunks' token counts dropped"),
+    ("pool_means", "sums[:, :nb] / counts[:nb, None]", "sums[:, :nb] / B", "E1 cache: partial block divided by B"),
 ]
 
 
