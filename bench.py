@@ -17,9 +17,11 @@ the same tensors (skipped with --no-sweep): bf16 at tau 2, 6, 8, and tau=inf,
 where every block is kept and the path is this library's own dense causal
 attention. The paged varlen entry point is timed on its own 8-sequence
 batch (skipped with --no-paged), and the S=2048 and S=32768 configurations
-on their own (skipped with --no-configs). The error of the sparse outputs against
-that dense attention, with and without the mean correction, is reported at
-tau 2, 4, 8 (skipped with --no-ablation).
+on their own (skipped with --no-configs). A chunked prefill of the same sequence in three chunks is timed
+with and without the pooled-KV cache (skipped with --no-chunked). The error
+of the sparse outputs against that dense attention is reported at tau 2, 4, 8 for four variants: mean
+correction, none, per-query-head lists, block-score correction (skipped
+with --no-ablation).
 """
 from __future__ import annotations
 
@@ -135,6 +137,68 @@ def time_paged(fp, N, steps, warmup, dtype="bf16"):
     return res
 
 
+def time_chunked(fp, inp, tau, ends=(43690, 87380, 131072), page=64, reps=5):
+    """Chunked prefill of the S=131072 sequence in three chunks through the
+    paged entry points (the fixed-shape tensors moved into a shuffled cache of
+    64-token pages): each chunk timed with the pooled-KV cache
+    (fp_sparse_prefill_paged_cached: cached blocks are not re-pooled) and
+    without it (fp_sparse_prefill_paged: all keys pooled on every call)."""
+    import torch
+    dev = torch.device("cuda:0")
+    S, Hkv = inp.k.shape[1], inp.k.shape[2]
+    assert ends[-1] == S and S % page == 0
+    npg = S // page
+    perm = torch.from_numpy(np.random.default_rng(5).permutation(npg)).to(dev)
+    kc = torch.empty((npg, page, Hkv, 128), dtype=inp.k.dtype, device=dev)
+    vc = torch.empty_like(kc)
+    kc[perm] = inp.k[0].to(dev).view(npg, page, Hkv, 128)
+    vc[perm] = inp.v[0].to(dev).view(npg, page, Hkv, 128)
+    bt = perm.to(torch.int32).view(1, npg).contiguous()
+    q = inp.q[0].to(dev)
+    B = inp.cfg.block
+    slots = fp.pooled_kv_slots(kc, B)
+    kbc = torch.zeros((slots, Hkv, 128), device=dev)
+    vbc = torch.zeros_like(kbc)
+    stream = torch.cuda.current_stream()
+    calls, P = [], 0
+    for E in ends:
+        qc = q[P:E].contiguous()
+        vp = fp.make_varlen_problem(qc, np.array([0, E - P], dtype=np.int32), np.array([E], dtype=np.int32),
+                                    kc, bt, B)
+        ws = torch.empty(vp.ws_bytes, dtype=torch.uint8, device=dev)
+        calls.append((P, E, vp, qc, ws))
+        P = E
+
+    def run(c, cached):
+        _, _, vp, qc, ws = c
+        if cached:
+            return fp.fp_sparse_prefill_paged_cached(vp, qc, kc, vc, bt, kbc, vbc, tau, with_lse=False, workspace=ws)
+        return fp.fp_sparse_prefill_paged(vp, qc, kc, vc, bt, tau, with_lse=False, workspace=ws)
+
+    for c in calls:                              # fills the pooled cache chunk by chunk
+        run(c, True)
+        run(c, False)
+    torch.cuda.synchronize()
+    res = []
+    for c in calls:
+        row = {"rows": [c[0], c[1]]}
+        for name, cached in (("ms_cached", True), ("ms_uncached", False)):
+            ts = []
+            for _ in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                run(c, cached)
+                e1.record(stream)
+                ts.append((e0, e1))
+            torch.cuda.synchronize()
+            row[name] = round(float(np.median([a.elapsed_time(b) for a, b in ts])), 4)
+        res.append(row)
+    del kc, vc, kbc, vbc, calls, q
+    torch.cuda.empty_cache()
+    return {"workload": f"S={S} in chunks ending at {list(ends)}, {page}-token shuffled pages, "
+                        f"32/8 heads, 128x128 blocks, tau={tau}, bf16", "chunks": res}
+
+
 def graph_replay_ms(fp, inp, tau, replays=20):
     """The whole path captured once in a HIP graph and replayed: median ms per
     replay (for small prefills, where launch overhead dominates)."""
@@ -166,16 +230,24 @@ def graph_replay_ms(fp, inp, tau, replays=20):
     return ms
 
 
+ABLATION_VARIANTS = ("mean", "none", "per_head", "block_score")
+
+
 def ablation_vs_dense(fp, inp, taus=(2.0, 4.0, 8.0), chunk=8192):
     """Error of the sparse path against this library's dense causal attention
-    (tau = inf: every block kept) on the same tensors, with and without the
-    mean correction: max and mean |o - o_dense| (V is in units of max|V|) and
-    the relative Frobenius norm. A synthetic stand-in for the pages' accuracy
-    claim, which needs trained weights to check."""
+    (tau = inf: every block kept) on the same tensors, for the four variants
+    of the method: the mean correction over GQA-union lists ("mean"), no
+    correction ("none"), one list per query head with the mean correction
+    ("per_head"), and the block score as each pruned block's logit
+    ("block_score"). Max and mean |o - o_dense| (V is in units of max|V|),
+    the relative Frobenius norm, the kept fraction of the causal block pairs
+    (per list) and the wall time of one whole call (allocation included). A synthetic stand-in for the
+    pages' accuracy claim, which needs trained weights to check."""
     import torch
     dev = torch.device("cuda:0")
     q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
     B = inp.cfg.block
+    nb = -(-q.shape[1] // B)
     dense = fp.sparse_prefill(q, k, v, B, float("inf"), with_lse=False)["o"]
     ref_sq = 0.0
     for t0 in range(0, dense.shape[1], chunk):
@@ -183,9 +255,16 @@ def ablation_vs_dense(fp, inp, taus=(2.0, 4.0, 8.0), chunk=8192):
     res = {}
     for tau in taus:
         row = {}
-        for name, corr in (("with_correction", True), ("without_correction", False)):
-            out = fp.sparse_prefill(q, k, v, B, tau, with_lse=False, correction=corr)
+        for name in ABLATION_VARIANTS:
+            fp.sparse_prefill(q, k, v, B, tau, with_lse=False, variant=name)   # warm
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            out = fp.sparse_prefill(q, k, v, B, tau, with_lse=False, variant=name)
+            torch.cuda.synchronize()
+            ms = (time.perf_counter() - t0) * 1e3
             o = out["o"]
+            lists = out["row_ptr"].numel() - 1
+            kept = int(out["row_ptr"][-1]) / (lists // nb * nb * (nb + 1) // 2)
             mx, sm, sq, n = 0.0, 0.0, 0.0, 0
             for t0 in range(0, o.shape[1], chunk):
                 d = (o[:, t0:t0 + chunk].float() - dense[:, t0:t0 + chunk].float()).abs_()
@@ -194,8 +273,10 @@ def ablation_vs_dense(fp, inp, taus=(2.0, 4.0, 8.0), chunk=8192):
                 sq += float(d.pow_(2).sum())
                 n += d.numel()
             row[name] = {"max_abs": round(mx, 5), "mean_abs": round(sm / n, 6),
-                         "rel_fro": round(math.sqrt(sq / ref_sq), 6)}
+                         "rel_fro": round(math.sqrt(sq / ref_sq), 6), "kept": round(kept, 5),
+                         "ms_call": round(ms, 2)}
             del out, o
+            torch.cuda.empty_cache()
         res[str(tau)] = row
     del q, k, v, dense
     torch.cuda.empty_cache()
@@ -446,7 +527,7 @@ def sample_parity(gpu, keep, R, o_or, lse_or, il_list, nb, B, tau):
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_S131072_tau4_traffic.md")
 # the attention kernel and the selection stage that orders its work (both shape its traffic)
-KERNEL_SOURCES = [os.path.join(ROOT, "block_sparse_long_estimate_amd", "csrc", f) for f in ("k_attn.hip", "k_select.hip")]
+KERNEL_SOURCES = [os.path.join(ROOT, "block_sparse_long_estimate_amd", "csrc", f) for f in ("k_attn.hip", "attn_geom.h", "k_select.hip")]
 
 
 def measured_traffic(S, tau):
@@ -495,6 +576,10 @@ def main():
                     help="skip the three-call path (fp_block_scores + fp_select_blocks, score matrix in HBM)")
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the dense baseline legs (fp_dense_prefill in bf16 and fp8)")
+    ap.add_argument("--no-chunked", action="store_true",
+                    help="skip the chunked-prefill leg (three chunks, with and without the pooled-KV cache)")
+    ap.add_argument("--only-chunked", action="store_true",
+                    help="run only the chunked-prefill leg and print its result")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the context legs (bf16 at tau 2/6/8, and tau=inf: every block kept)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -526,6 +611,9 @@ def main():
     t0 = time.time()
     inputs = synth.gen_fixed_multi(cfg, ("bf16",) if args.no_fp8 else ("bf16", "fp8"))
     log(f"generated S={cfg.S} inputs in {time.time() - t0:.1f} s")
+    if args.only_chunked:
+        print(json.dumps({"chunked_prefill_bf16": time_chunked(fp, inputs["bf16"], args.tau)}), flush=True)
+        return
     bf, bf_csr = time_path(fp, N, inputs["bf16"], args.tau, args.steps, args.warmup, "bf16",
                            keep_outputs=not args.no_cpu_baseline)
     log(f"bf16: {json.dumps(bf)}")
@@ -559,6 +647,10 @@ def main():
         if not args.no_fp8:
             paged8 = time_paged(fp, N, 5, 1, "fp8")
             log(f"paged varlen fp8: {json.dumps(paged8)}")
+    chunked = None
+    if not args.no_chunked:
+        chunked = time_chunked(fp, inputs["bf16"], args.tau)
+        log(f"chunked prefill: {json.dumps(chunked)}")
     sweep, dense = {}, None
     if not args.no_sweep:
         for tau in (2.0, 6.0, 8.0):
@@ -651,6 +743,8 @@ def main():
         line["paged_varlen_bf16"] = paged
     if paged8:
         line["paged_varlen_fp8"] = paged8
+    if chunked is not None:
+        line["chunked_prefill_bf16"] = chunked
     if sweep:
         line["tau_sweep_bf16"] = sweep
     if dense is not None:

@@ -32,7 +32,8 @@ __all__ = [
     "FpError", "Problem", "make_problem", "fp_block_scores", "fp_select_blocks",
     "fp_sparse_prefill", "fp_sparse_prefill_paged", "sparse_prefill", "version",
     "make_varlen_problem", "fp_sparse_prefill_noalloc", "fp_dense_prefill", "fp_estimate_select",
-    "sparse_prefill_fused", "fp_sparse_prefill_scored", "VARIANTS",
+    "sparse_prefill_fused", "fp_sparse_prefill_scored", "VARIANTS", "fp_sparse_prefill_paged_cached",
+    "pooled_kv_slots",
 ]
 
 
@@ -436,12 +437,8 @@ def make_varlen_problem(q: torch.Tensor, cu_seqlens_q, seqlens_k, k_cache: torch
     return VarlenProblem(c, cu, lk, rows, nnz, ws)
 
 
-def fp_sparse_prefill_paged(vp: VarlenProblem, q, k_cache, v_cache, block_table, tau: float,
-                            with_lse: bool = True, workspace: Optional[torch.Tensor] = None,
-                            q_scale=None, k_scale=None, v_scale=None):
-    """E1-E6 on a paged varlen batch -> (o, lse, row_ptr, col_idx). fp8
-    (uint8 E4M3FN codes) takes fp32 scales [num_seqs, H, nsb], one per 128
-    positions of each sequence."""
+def _paged_call(entry: str, vp: VarlenProblem, q, k_cache, v_cache, block_table, tau, with_lse, workspace,
+                q_scale, k_scale, v_scale, pooled=()):
     c = vp.c
     dt = torch.uint8 if c.dtype == N.FP_DTYPE_FP8_E4M3 else torch.bfloat16
     if q.dim() != 3 or q.shape[0] != int(vp.cu[-1]) or q.shape[1] != c.num_q_heads:
@@ -458,6 +455,10 @@ def fp_sparse_prefill_paged(vp: VarlenProblem, q, k_cache, v_cache, block_table,
     nsb = (c.max_pages_per_seq * c.page_size + 127) // 128
     _check_scales(c.dtype == N.FP_DTYPE_FP8_E4M3, c.num_seqs, c.num_q_heads, c.num_kv_heads, nsb,
                   q_scale, k_scale, v_scale)
+    if pooled:
+        slots = k_cache.shape[0] * max(1, c.page_size // c.block)
+        for t, name in zip(pooled, ("kbar_cache", "vbar_cache")):
+            _check(t, name, torch.float32, (slots, c.num_kv_heads, 128), required=True)
     dev = q.device
     i32 = dict(dtype=torch.int32, device=dev)
     row_ptr = torch.empty(vp.rows + 1, **i32)
@@ -467,9 +468,37 @@ def fp_sparse_prefill_paged(vp: VarlenProblem, q, k_cache, v_cache, block_table,
     if workspace is None:
         workspace = torch.empty(vp.ws_bytes, dtype=torch.uint8, device=dev)
     cup, lkp = vp.host_ptrs()
-    N.check(N.load().fp_sparse_prefill_paged(vp.ref, _ptr(q), cup, lkp, _ptr(k_cache), _ptr(v_cache),
-                                             _ptr(block_table), _ptr(q_scale), _ptr(k_scale),
-                                             _ptr(v_scale), float(tau), _ptr(row_ptr),
-                                             _ptr(col_idx), vp.max_nnz, _ptr(o), _ptr(lse),
-                                             _ptr(workspace), workspace.numel(), _stream()))
+    N.check(getattr(N.load(), entry)(vp.ref, _ptr(q), cup, lkp, _ptr(k_cache), _ptr(v_cache),
+                                     _ptr(block_table), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale),
+                                     *[_ptr(t) for t in pooled], float(tau), _ptr(row_ptr),
+                                     _ptr(col_idx), vp.max_nnz, _ptr(o), _ptr(lse),
+                                     _ptr(workspace), workspace.numel(), _stream()))
     return o, lse, row_ptr, col_idx
+
+
+def fp_sparse_prefill_paged(vp: VarlenProblem, q, k_cache, v_cache, block_table, tau: float,
+                            with_lse: bool = True, workspace: Optional[torch.Tensor] = None,
+                            q_scale=None, k_scale=None, v_scale=None):
+    """E1-E6 on a paged varlen batch -> (o, lse, row_ptr, col_idx). fp8
+    (uint8 E4M3FN codes) takes fp32 scales [num_seqs, H, nsb], one per 128
+    positions of each sequence."""
+    return _paged_call("fp_sparse_prefill_paged", vp, q, k_cache, v_cache, block_table, tau, with_lse,
+                       workspace, q_scale, k_scale, v_scale)
+
+
+def pooled_kv_slots(k_cache: torch.Tensor, block: int) -> int:
+    """Slots of the pooled-KV cache beside a page cache [pages, page_size, Hkv, 128]:
+    one per page, or page_size / block per page when pages hold several blocks."""
+    return k_cache.shape[0] * max(1, k_cache.shape[1] // block)
+
+
+def fp_sparse_prefill_paged_cached(vp: VarlenProblem, q, k_cache, v_cache, block_table, kbar_cache,
+                                   vbar_cache, tau: float, with_lse: bool = True,
+                                   workspace: Optional[torch.Tensor] = None,
+                                   q_scale=None, k_scale=None, v_scale=None):
+    """fp_sparse_prefill_paged with the pooled-KV cache kbar_cache / vbar_cache
+    (fp32 [pooled_kv_slots(k_cache, block), Hkv, 128], kept across calls):
+    complete blocks of each sequence's cached prefix are read from it, and
+    complete blocks this call pools are written to it."""
+    return _paged_call("fp_sparse_prefill_paged_cached", vp, q, k_cache, v_cache, block_table, tau, with_lse,
+                       workspace, q_scale, k_scale, v_scale, pooled=(kbar_cache, vbar_cache))

@@ -30,6 +30,7 @@ EXPORTS = (
     "fp_varlen_num_rows", "fp_varlen_max_nnz", "fp_varlen_workspace_size",
     "fp_sparse_prefill_paged", "fp_sparse_prefill_noalloc", "fp_dense_prefill",
     "fp_estimate_select", "fp_estimate_select_workspace_size", "fp_sparse_prefill_scored",
+    "fp_sparse_prefill_paged_cached",
 )
 FP_NOALLOC_MAX_POOLED_ROWS = 32768
 
@@ -103,6 +104,10 @@ def load() -> ctypes.CDLL:
     lib.fp_sparse_prefill_paged.restype = ctypes.c_int
     lib.fp_sparse_prefill_paged.argtypes = [VP, vp, i32p, i32p, vp, vp, vp, vp, vp, vp, ctypes.c_float,
                                             vp, vp, ctypes.c_int64, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.fp_sparse_prefill_paged_cached.restype = ctypes.c_int
+    lib.fp_sparse_prefill_paged_cached.argtypes = [VP, vp, i32p, i32p, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                   ctypes.c_float, vp, vp, ctypes.c_int64, vp, vp, vp,
+                                                   ctypes.c_size_t, vp]
     _lib = lib
     return lib
 

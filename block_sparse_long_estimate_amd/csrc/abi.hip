@@ -237,7 +237,7 @@ hipError_t fixed_pool(const fp_problem* p, const void* q, const void* k, const v
                       hipStream_t st) {
     GeoFixed geo = geo_fixed(p);
     const int nsb = cdiv(p->seqlen, SCALE_TOK);
-    PoolArgs a;
+    PoolArgs a{};
     a.q = q; a.k = k; a.v = v;
     a.qa = RowAddr{p->q_stride[0], p->q_stride[1], p->q_stride[2]};
     a.ka = KVAddr{p->k_stride[0], p->k_stride[1], p->k_stride[2], 0, nullptr, 0, 0};
@@ -738,33 +738,37 @@ int64_t fp_varlen_workspace_size(const fp_varlen_problem* p, const int32_t* cu, 
     return rc ? rc : (int64_t)plan.total;
 }
 
-int fp_sparse_prefill_paged(const fp_varlen_problem* p, const void* q, const int32_t* cu,
-                            const int32_t* lk, const void* k_cache, const void* v_cache,
-                            const int32_t* block_table, const float* q_scale, const float* k_scale,
-                            const float* v_scale, float tau, int32_t* row_ptr, int32_t* col_idx,
-                            int64_t capacity, void* o, float* lse, void* workspace, size_t ws_bytes,
-                            void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The paged varlen path; kc / vc: the pooled-KV cache (both NULL: none).
+int paged_impl(const char* who, const fp_varlen_problem* p, const void* q, const int32_t* cu,
+               const int32_t* lk, const void* k_cache, const void* v_cache,
+               const int32_t* block_table, const float* q_scale, const float* k_scale,
+               const float* v_scale, float* kc, float* vc, float tau, int32_t* row_ptr, int32_t* col_idx,
+               int64_t capacity, void* o, float* lse, void* workspace, size_t ws_bytes, void* stream) {
     VarPlan plan;
     int rc = check_varlen(p, cu, lk, plan);
     if (rc) return rc;
     if (!k_cache || !v_cache || !block_table || !row_ptr || !col_idx || !workspace)
-        return fail(FP_ERR_INVALID, "fp_sparse_prefill_paged: NULL pointer");
+        return fail(FP_ERR_INVALID, "%s: NULL pointer", who);
     // q and o hold sum q_len rows: they may be empty (NULL) when every sequence is fully cached
-    if (plan.sum_q > 0 && (!q || !o)) return fail(FP_ERR_INVALID, "fp_sparse_prefill_paged: NULL q or o");
+    if (plan.sum_q > 0 && (!q || !o)) return fail(FP_ERR_INVALID, "%s: NULL q or o", who);
     const bool fp8 = p->dtype == FP_DTYPE_FP8_E4M3;
     if (fp8 && (!q_scale || !k_scale || !v_scale))
-        return fail(FP_ERR_INVALID, "fp_sparse_prefill_paged: fp8 needs q_scale, k_scale and v_scale");
+        return fail(FP_ERR_INVALID, "%s: fp8 needs q_scale, k_scale and v_scale", who);
     // fp8 scales: [num_seqs, H, nsb], one per 128 positions of each sequence
     const long long nsb = ((long long)p->max_pages_per_seq * p->page_size + SCALE_TOK - 1) / SCALE_TOK;
-    if (isnan(tau)) return fail(FP_ERR_INVALID, "fp_sparse_prefill_paged: tau is NaN");
+    if (isnan(tau)) return fail(FP_ERR_INVALID, "%s: tau is NaN", who);
     if (capacity < plan.max_nnz)
-        return fail(FP_ERR_CAPACITY, "fp_sparse_prefill_paged: capacity %lld < max nnz %lld",
-                    (long long)capacity, plan.max_nnz);
+        return fail(FP_ERR_CAPACITY, "%s: capacity %lld < max nnz %lld", who, (long long)capacity, plan.max_nnz);
     if (ws_bytes < plan.total)
-        return fail(FP_ERR_CAPACITY, "fp_sparse_prefill_paged: workspace %zu < %zu bytes", ws_bytes, plan.total);
+        return fail(FP_ERR_CAPACITY, "%s: workspace %zu < %zu bytes", who, ws_bytes, plan.total);
     if (misaligned(workspace, ALIGN)) return fail(FP_ERR_INVALID, "workspace must be 256-byte aligned");
-    if (misaligned(q, 16) || misaligned(k_cache, 16) || misaligned(v_cache, 16) || misaligned(o, 8))
-        return fail(FP_ERR_INVALID, "fp_sparse_prefill_paged: misaligned tensor");
+    if (misaligned(q, 16) || misaligned(k_cache, 16) || misaligned(v_cache, 16) || misaligned(o, 8) ||
+        misaligned(kc, 16) || misaligned(vc, 16))
+        return fail(FP_ERR_INVALID, "%s: misaligned tensor", who);
     if (plan.rows == 0) {
         // nothing to attend: the kept lists are empty, row_ptr = {0}
         hipError_t e = launch_zero_first(row_ptr, (hipStream_t)stream);
@@ -796,7 +800,7 @@ int fp_sparse_prefill_paged(const fp_varlen_problem* p, const void* q, const int
     hipError_t e = launch_table_copy(plan.table.data(), p->num_seqs + 1, dtable, st);
     if (e != hipSuccess) return fail(FP_ERR_HIP, "table copy: %s", hipGetErrorString(e));
 
-    PoolArgs pa;
+    PoolArgs pa{};
     pa.q = q; pa.k = k_cache; pa.v = v_cache;
     pa.qa = RowAddr{0, p->q_stride[0], p->q_stride[1]};
     pa.ka = kva; pa.va = kva;
@@ -807,6 +811,8 @@ int fp_sparse_prefill_paged(const fp_varlen_problem* p, const void* q, const int
     pa.Hq = p->num_q_heads; pa.Hkv = p->num_kv_heads; pa.blk = p->block;
     pa.fp8 = fp8; pa.paged = 1;
     pa.total_qblocks = plan.total_qblocks; pa.total_kblocks = plan.total_kblocks;
+    pa.kc = kc; pa.vc = vc;
+    pa.spp = std::max(1, p->page_size / p->block);
     e = launch_pool(nullptr, &geo, pa, st);
     if (e != hipSuccess) return fail(FP_ERR_HIP, "pool launch: %s", hipGetErrorString(e));
 
@@ -865,6 +871,34 @@ int fp_sparse_prefill_paged(const fp_varlen_problem* p, const void* q, const int
     e = launch_attn(nullptr, &geo, a, p->block, fp8, 1, st);
     if (e != hipSuccess) return fail(FP_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp_sparse_prefill_paged(const fp_varlen_problem* p, const void* q, const int32_t* cu,
+                            const int32_t* lk, const void* k_cache, const void* v_cache,
+                            const int32_t* block_table, const float* q_scale, const float* k_scale,
+                            const float* v_scale, float tau, int32_t* row_ptr, int32_t* col_idx,
+                            int64_t capacity, void* o, float* lse, void* workspace, size_t ws_bytes,
+                            void* stream) {
+    return paged_impl("fp_sparse_prefill_paged", p, q, cu, lk, k_cache, v_cache, block_table, q_scale, k_scale,
+                      v_scale, nullptr, nullptr, tau, row_ptr, col_idx, capacity, o, lse, workspace, ws_bytes,
+                      stream);
+}
+
+int fp_sparse_prefill_paged_cached(const fp_varlen_problem* p, const void* q, const int32_t* cu,
+                                   const int32_t* lk, const void* k_cache, const void* v_cache,
+                                   const int32_t* block_table, const float* q_scale, const float* k_scale,
+                                   const float* v_scale, float* kbar_cache, float* vbar_cache, float tau,
+                                   int32_t* row_ptr, int32_t* col_idx, int64_t capacity, void* o, float* lse,
+                                   void* workspace, size_t ws_bytes, void* stream) {
+    if (!kbar_cache || !vbar_cache)
+        return fail(FP_ERR_INVALID, "fp_sparse_prefill_paged_cached: NULL kbar_cache or vbar_cache");
+    return paged_impl("fp_sparse_prefill_paged_cached", p, q, cu, lk, k_cache, v_cache, block_table, q_scale,
+                      k_scale, v_scale, kbar_cache, vbar_cache, tau, row_ptr, col_idx, capacity, o, lse, workspace,
+                      ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -144,6 +144,16 @@ struct PoolArgs {
     float* qbar; float* kbar; float* vbar;
     int Hq, Hkv, blk, fp8, paged;
     int total_qblocks, total_kblocks;
+    // pooled-KV cache beside the page cache (NULL: none): fp32 [slots, Hkv, D]
+    float* kc; float* vc;
+    int spp;                                    // slots per page: max(1, page / blk)
+    // slot of complete key block j of sequence b: the page of its last token
+    FP_HD long long cache_row(int b, int j, int head) const {
+        const int e = (j + 1) * blk - 1;
+        const long long pg = ka.table[(long long)b * ka.maxp + (e >> ka.page_shift)];
+        const int in_page = (e & ((1 << ka.page_shift) - 1)) / blk;
+        return ((pg * spp + in_page) * Hkv + head) * D;
+    }
 };
 
 struct ScoreArgs {

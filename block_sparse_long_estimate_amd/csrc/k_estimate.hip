@@ -60,6 +60,14 @@ __global__ __launch_bounds__(256) void pool_kernel(Geo geo, PoolArgs a) {
     const char* base = (const char*)(isq ? a.q : (isv ? a.v : a.k));
     const ScaleAddr& sa = isq ? a.qs : (isv ? a.vs : a.ks);
     constexpr int ESZ = FP8 ? 1 : 2;
+    float* cache = isq ? nullptr : (isv ? a.vc : a.kc);
+    if (PAGED && cache && (blk + 1) * B <= s.P) {
+        // a complete block of the cached prefix: its mean was kept by an earlier chunk
+        if (tid < D)
+            (isv ? a.vbar : a.kbar)[kbar_row(s, a.Hkv, head, blk) * D + tid] =
+                cache[a.cache_row(b, blk, head) + tid];
+        return;
+    }
 
     for (int t = lo + tl; t < hi; t += TL) {
         long long off;
@@ -99,6 +107,7 @@ __global__ __launch_bounds__(256) void pool_kernel(Geo geo, PoolArgs a) {
         const float mean = (FP8 ? sum * sa.at(b, head, lo) : sum) / (float)(hi - lo);
         if (isq) a.qbar[qbar_row(s, a.Hq, head, blk) * D + tid] = mean;
         else (isv ? a.vbar : a.kbar)[kbar_row(s, a.Hkv, head, blk) * D + tid] = mean;
+        if (PAGED && cache && hi - lo == B) cache[a.cache_row(b, blk, head) + tid] = mean;
     }
 }
 
@@ -162,6 +171,17 @@ __global__ __launch_bounds__(256) void pool_rows_fp8_kernel(Geo geo, PoolArgs a)
     const ScaleAddr& sa = isq ? a.qs : (isv ? a.vs : a.ks);
     const KVAddr& kva = isv ? a.va : a.ka;
     constexpr int ESZ = FP8 ? 1 : 2;
+    float* cache = isq ? nullptr : (isv ? a.vc : a.kc);
+    if (PAGED && cache && (blk + 1) * B <= s.P) {
+        // a complete block of the cached prefix: its mean was kept by an earlier chunk
+        if (tl == 0 && act) {
+            const float* src = cache + a.cache_row(b, blk, head) + ch * EPC;
+            float* dst = (isv ? a.vbar : a.kbar) + kbar_row(s, a.Hkv, head, blk) * D + ch * EPC;
+#pragma unroll
+            for (int e = 0; e < EPC; e += 4) *(float4*)(dst + e) = *(const float4*)(src + e);
+        }
+        return;
+    }
 
     for (int t0 = lo + tl; t0 < hi; t0 += NLD * TL) {
         uint4 wv[NLD];
@@ -218,6 +238,11 @@ __global__ __launch_bounds__(256) void pool_rows_fp8_kernel(Geo geo, PoolArgs a)
 #pragma unroll
     for (int e = 0; e < EPC; e += 4)
         *(float4*)(dst + ch * EPC + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+    if (PAGED && cache && hi - lo == B) {
+        float* cdst = cache + a.cache_row(b, blk, head) + ch * EPC;
+#pragma unroll
+        for (int e = 0; e < EPC; e += 4) *(float4*)(cdst + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+    }
 }
 
 // ---------------------------------------------------------------------------

@@ -282,6 +282,41 @@ int fp_sparse_prefill_paged(const fp_varlen_problem* p, const void* q,
                             void* o, float* lse, void* workspace, size_t ws_bytes,
                             void* stream);
 
+/* fp_sparse_prefill_paged with a pooled-KV cache for chunked prefill: the
+ * block means of K and V (E1) are kept beside the page cache, so a chunk
+ * pools only the blocks its new keys fall in (the pages' chunked prefill over
+ * a paged KV cache with continuous batching: lode.cx page, "How It Works",
+ * implementation paragraph; aimodeling.com page, "Framework integration"
+ * bullet).
+ * kbar_cache, vbar_cache (device, 16-byte aligned): fp32 [slots, Hkv, 128],
+ * slots = (pages of the cache) * spp with spp = max(1, page_size / block).
+ * The complete key block j of sequence b (tokens [j*block, (j+1)*block)) has
+ * slot block_table[b][e / page_size] * spp + (e % page_size) / block, where
+ * e = (j+1)*block - 1 is its last token: the slot travels with the page that
+ * holds the block's last token, so sequences that share that page share the
+ * block's tokens and its slot.
+ * Read: each block complete within the cached prefix ((j+1)*block <= L_b -
+ * q_len_b) is taken from its slot and its keys are not re-read. Its slot
+ * must hold what an earlier call of this entry point wrote when the block
+ * was complete (that call's chunk ended at or past the block's last token);
+ * a slot never written holds garbage, which the call cannot detect.
+ * Write: every complete block this call pools ((j+1)*block > L_b - q_len_b
+ * and <= L_b) is written to its slot. A block still partial at the chunk's
+ * end is pooled from the page cache on each call and never written.
+ * Sequences without present rows read and write nothing. Every other
+ * argument, output and error is as for fp_sparse_prefill_paged; the outputs
+ * are bit-identical to its own on the same call when the read slots hold
+ * what this entry point wrote. Calls that overlap on the same slots race. */
+int fp_sparse_prefill_paged_cached(const fp_varlen_problem* p, const void* q,
+                                   const int32_t* cu_seqlens_q, const int32_t* seqlens_k,
+                                   const void* k_cache, const void* v_cache,
+                                   const int32_t* block_table,
+                                   const float* q_scale, const float* k_scale, const float* v_scale,
+                                   float* kbar_cache, float* vbar_cache,
+                                   float tau, int32_t* row_ptr, int32_t* col_idx, int64_t capacity,
+                                   void* o, float* lse, void* workspace, size_t ws_bytes,
+                                   void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -259,7 +259,7 @@ def prefill(q: np.ndarray, k: np.ndarray, v: np.ndarray, B: int, tau: float,
 
 def prefill_chunked(q: np.ndarray, k: np.ndarray, v: np.ndarray, B: int, tau: float,
                     ends: Sequence[int], c: Optional[float] = None,
-                    variant: str = "mean") -> list:
+                    variant: str = "mean", with_output: bool = True) -> list:
     """Chunked prefill of one sequence with a pooled-KV cache: chunk n holds
     the query rows [ends[n-1], ends[n]) (ends[-1] = L) and sees the keys
     [0, ends[n]). The per-block sums of K and V are carried from chunk to
@@ -276,7 +276,7 @@ def prefill_chunked(q: np.ndarray, k: np.ndarray, v: np.ndarray, B: int, tau: fl
         assert np.array_equal(cnt_k, cnt)
         pooled = (pool_means(sk, cnt, end, B), pool_means(sv, cnt, end, B))
         out.append(prefill(q[P:end], k[:end], v[:end], B, tau, c=c, P=P, variant=variant,
-                           pooled_kv=pooled))
+                           pooled_kv=pooled, with_output=with_output))
         P = end
     return out
 

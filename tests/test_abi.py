@@ -234,6 +234,50 @@ def test_paged_fp8_needs_scales():
     assert lib.fp_varlen_num_rows(ctypes.byref(p), cup, lkp) == N.FP_ERR_INVALID
 
 
+def test_paged_cached_needs_its_cache_and_checks_like_paged():
+    """The pooled-KV entry point refuses a missing or misaligned cache and
+    otherwise checks its arguments exactly as the plain paged one, before any
+    HIP call."""
+    lib = N.load()
+    p = vproblem()
+    _, cup = arr([0, 300, 400, 1000])
+    _, lkp = arr([500, 200, 1000])
+    nnz = lib.fp_varlen_max_nnz(ctypes.byref(p), cup, lkp)
+    ws = lib.fp_varlen_workspace_size(ctypes.byref(p), cup, lkp)
+    fake = ctypes.c_void_p(1 << 20)
+    call = lambda kc, vc, tau=4.0, cap=nnz, wsb=ws: lib.fp_sparse_prefill_paged_cached(
+        ctypes.byref(p), fake, cup, lkp, fake, fake, fake, None, None, None, kc, vc, tau, fake, fake, cap, fake,
+        None, fake, wsb, None)
+    assert call(None, fake) == N.FP_ERR_INVALID
+    assert call(fake, None) == N.FP_ERR_INVALID
+    assert call(fake, ctypes.c_void_p((1 << 20) + 4)) == N.FP_ERR_INVALID       # not 16-byte aligned
+    assert "misaligned" in lib.fp_last_error().decode()
+    assert call(fake, fake, tau=float("nan")) == N.FP_ERR_INVALID
+    assert call(fake, fake, cap=nnz - 1) == N.FP_ERR_CAPACITY
+    assert call(fake, fake, wsb=ws - 1) == N.FP_ERR_CAPACITY
+
+
+def test_binding_checks_pooled_kv_cache():
+    """The pooled-KV cache is fp32 [pages * max(1, page_size / block), Hkv, 128]."""
+    import torch
+    import block_sparse_long_estimate_amd as fp
+    Hkv, pages = 2, 8
+    q = torch.zeros((40, 4, 128), dtype=torch.bfloat16)
+    for page, block, slots in ((16, 64, 8), (256, 64, 32), (64, 64, 8)):
+        kc = torch.zeros((pages, page, Hkv, 128), dtype=torch.bfloat16)
+        bt = torch.arange(pages, dtype=torch.int32).reshape(2, 4)
+        cu, lk = np.array([0, 20, 40], dtype=np.int32), np.array([30, 50], dtype=np.int32)
+        vp = fp.make_varlen_problem(q, cu, lk, kc, bt, block)
+        assert fp.pooled_kv_slots(kc, block) == slots
+        good = torch.zeros((slots, Hkv, 128))
+        with pytest.raises(fp.FpError, match="kbar_cache has shape"):
+            fp.fp_sparse_prefill_paged_cached(vp, q, kc, kc, bt, good[:-1], good, 1.0)
+        with pytest.raises(fp.FpError, match="vbar_cache must be torch.float32"):
+            fp.fp_sparse_prefill_paged_cached(vp, q, kc, kc, bt, good, good.bfloat16(), 1.0)
+        with pytest.raises(fp.FpError, match="vbar_cache is required"):
+            fp.fp_sparse_prefill_paged_cached(vp, q, kc, kc, bt, good, None, 1.0)
+
+
 def test_variant_validation():
     """variant (the ablation of the mean correction) sits where the padding was."""
     lib = N.load()
