@@ -16,23 +16,28 @@
 namespace fp {
 
 // ---------------------------------------------------------------------------
-// Tile layouts in LDS (128 dims per row; rows padded, not XOR-swizzled, so
-// every operand address is lane_base + immediate):
+// Tile layouts in LDS (128 dims per row). The LDS banks repeat every 256
+// bytes; reads that would land on one bank group are spread either by
+// padding the rows or by rotating each row's bytes:
 //   bf16 K rows every 272 bytes: the QK^T operand read (16 lanes = 16 rows
 //     at one 16-byte chunk) lands on 16 distinct 4-bank groups;
-//   bf16 V rows every 320 bytes: a transpose read covers 8 rows x 64 bytes,
-//     served 32 lanes (4 rows) at a time; a stride of 64 bytes mod 256 puts
-//     those rows on disjoint banks;
+//   bf16 V rows every 256 bytes (no padding), row r's bytes rotated by
+//     64 (r mod 4): a transpose read covers 8 rows x 64 bytes, served 32 lanes
+//     (4 rows, r mod 4 = 0..3) at a time, on 4 disjoint 64-byte bank groups;
 //   fp8 K rows every 144 bytes (16 mod 256, as bf16 K);
-//   fp8 V rows every 160 bytes, keys permuted inside each 64-key step (bits 2
+//   fp8 V rows every 128 bytes, keys permuted inside each 64-key step (bits 2
 //     and 3 swapped) so that each 32-lane half of a transpose read covers 8
-//     consecutive rows x 32 bytes, on 8 disjoint 8-bank groups.
+//     consecutive rows x 32 bytes, and row r's bytes rotated by
+//     32 ((r / 2) mod 4): those 8 rows land on 8 disjoint 32-byte bank groups.
+// Padding keeps an operand address lane_base + immediate; a rotation needs
+// one lane base per 32-dim block of V (4), which the V reads can afford, and
+// it saves the direct loads of the padding (V: 20% of its pieces).
 // Summary tiles (pooled keys hi/lo and pooled values) use the bf16 layouts.
 // ---------------------------------------------------------------------------
 constexpr int KSTR = 272;
-constexpr int VSTR = 320;
+constexpr int VSTR = 256;
 constexpr int KSTR8 = 144;
-constexpr int VSTR8 = 160;
+constexpr int VSTR8 = 128;
 constexpr int PIECE = 1024;                 // LDS bytes one wavefront load instruction fills
 
 // swap bits 2 and 3 of a key index
@@ -58,10 +63,12 @@ struct TileGeom {
 };
 
 // Lane `lane` of the load of piece t (stride STR) fills LDS bytes
-// t * 1024 + 16 lane .. + 15: tile row `row`, 16-byte chunk `ch` of it.
-// Chunks past the row's data (the row padding, never read) take a copy of
-// the row's last data chunk: the lane's source then shares a cache line with
-// its neighbour's, and no lane of a load has to be masked off.
+// t * 1024 + 16 lane .. + 15: tile row `row`, 16-byte data chunk `ch` of it.
+// Padded rows: chunks past the row's data (the padding, never read) take a
+// copy of the row's last data chunk, so the lane's source shares a cache line
+// with its neighbour's and no lane of a load has to be masked off. Rotated
+// rows (the V layouts): LDS chunk position p of row r holds data chunk
+// p - rot(r), modulo the chunks per row.
 struct PieceLoc {
     int row, ch;
 };
@@ -69,6 +76,8 @@ FP_HD PieceLoc piece_loc(int STR, int t, int lane, int data_chunks) {
     const int pb = t * PIECE + lane * 16;
     const int row = pb / STR;
     const int ch = (pb - row * STR) >> 4;
+    if (STR == VSTR) return PieceLoc{row, (ch - 4 * (row & 3)) & 15};
+    if (STR == VSTR8) return PieceLoc{row, (ch - 2 * ((row >> 1) & 3)) & 7};
     return PieceLoc{row, ch < data_chunks ? ch : data_chunks - 1};
 }
 
@@ -223,18 +232,20 @@ FP_HD int k_read_off(int kb, int ks, int n, int lh) {
     return (kb * 32 + n) * KSTR + d0 * 2;
 }
 // bf16 V^T transpose read aa (0, 1) of key block kb, 16-key step s2, dim block db: 8 bytes
+// (row kb * 32 + 16 s2 + 8 aa + rsub, whose rotation is 64 (rsub mod 4) bytes)
 FP_HD int v_read_off(int kb, int s2, int aa, int db, int lane) {
     const int jj = lane & 15, q = lane >> 4;
     const int rsub = 4 * (q >> 1) + (jj >> 2);
     const int dsub = 16 * (q & 1) + 4 * (jj & 3);
-    return (kb * 32 + 16 * s2 + 8 * aa + rsub) * VSTR + (32 * db + dsub) * 2;
+    return (kb * 32 + 16 * s2 + 8 * aa + rsub) * VSTR + 64 * ((db + rsub) & 3) + 2 * dsub;
 }
 // fp8 K operand of key block kb, 64-dim step ks: 32 bytes (two 16-byte reads)
 FP_HD int k8_read_off(int kb, int ks, int n, int lh) { return (kb * 32 + n) * KSTR8 + ks * 64 + lh * 32; }
 // fp8 V^T transpose read c (0..3) of 64-key step s2, dim block db: 8 bytes
+// (row s2 * 64 + 16 c + 8 lh + a / 2, whose rotation is 32 (a / 4) bytes)
 FP_HD int v8_read_off(int s2, int c, int db, int lane) {
     const int a = lane & 15, half = (lane >> 4) & 1, lh = lane >> 5;
-    return (s2 * 64 + 8 * lh + (a >> 1)) * VSTR8 + 16 * half + 8 * (a & 1) + 16 * c * VSTR8 + db * 32;
+    return (s2 * 64 + 16 * c + 8 * lh + (a >> 1)) * VSTR8 + 32 * ((db + (a >> 2)) & 3) + 16 * half + 8 * (a & 1);
 }
 
 }  // namespace fp

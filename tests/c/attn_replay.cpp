@@ -440,6 +440,154 @@ static Launch paged_launch(const std::vector<int>& Ls, const std::vector<int>& P
     return L;
 }
 
+// ---------------------------------------------------------------------------
+// Operand layout: fill a tagged image of each LDS tile through the load
+// functions (piece_loc, with the fp8 V key permutation; summary_src for the
+// summary tiles), then emulate every operand read of the tile compute --
+// plain 16/32-byte reads for K, the transpose reads for V^T with the lane
+// semantics of ds_read_b64_tr_b16 (16-lane group: lane i's element e is
+// element i mod 4 of the 8 bytes lane 4e + i / 4 addresses) and
+// ds_read_b64_tr_b8 (lane i's byte e is byte i mod 8 of the 8 bytes lane
+// 2e + i / 8 addresses) -- and check that each lane receives the (key, dim)
+// the MFMA step expects: K[key kb*32 + n][dims of its k slot] for QK^T; for
+// PV, the A operand's k index must hold the key that the P operand (taken in
+// the order of the S^T accumulator, key 8 (v/4) + 4 lh + v mod 4 for
+// accumulator element v of lane half lh) holds there.
+// ---------------------------------------------------------------------------
+struct Tag {
+    int key = -1, dim = -1;          // dim: element index within the 128 dims
+    bool operator==(const Tag& o) const { return key == o.key && dim == o.dim; }
+};
+
+static void tag_tile(std::vector<Tag>& img, int STR, int rows, int esz, bool perm, int key_of_row_lo = 0,
+                     bool summary_k = false, int sumc = 0) {
+    const int pieces = rows * STR / PIECE;
+    img.assign((size_t)pieces * PIECE, Tag{});
+    for (int t = 0; t < pieces; ++t)
+        for (int lane = 0; lane < 64; ++lane) {
+            const PieceLoc pl = piece_loc(STR, t, lane, 8 * esz);
+            int key = perm ? vt_slot(pl.row) : pl.row;
+            if (summary_k) key = pl.row >= sumc ? 1000000 + (pl.row - sumc) : pl.row;   // lo rows: tagged apart
+            for (int b = 0; b < 16; ++b)
+                img[(size_t)t * PIECE + lane * 16 + b] = Tag{key + key_of_row_lo, (pl.ch * 16 + b) / esz};
+        }
+}
+
+
+
+#define LAYOUT(cond, ...)                                                 \
+    do {                                                                  \
+        ++g_checks;                                                       \
+        if (!(cond)) {                                                    \
+            fprintf(stderr, "[operand layout] ");                        \
+            fprintf(stderr, __VA_ARGS__);                                 \
+            fputc('\n', stderr);                                          \
+            if (++g_fail > 20) exit(1);                                   \
+        }                                                                 \
+    } while (0)
+
+// A kept K or V tile as the contiguous-tile loads fill it: the per-lane
+// source offsets of TileOffs (rows of 128 elements) decoded back to (key, dim).
+template <int STR, int BLK, int ESZ, bool PERM, int NW>
+static void tag_loaded_tile(std::vector<Tag>& img) {
+    using TO = TileOffs<STR, BLK, ESZ, PERM, NW>;
+    img.assign((size_t)TO::PIECES * PIECE, Tag{});
+    for (int wave = 0; wave < NW; ++wave)
+        for (int lane = 0; lane < 64; ++lane) {
+            TO o;
+            o.init(128, wave, lane);
+            for (int k = 0; k < TO::NP; ++k) {
+                if (!TO::has(k, wave)) continue;
+                if (k * NW + wave >= TO::PIECES) {
+                    LAYOUT(false, "piece %d of wave %d lies past the %d-piece tile", k * NW + wave, wave, TO::PIECES);
+                    continue;
+                }
+                const long long src = o.src_full(0, k);
+                const int key = (int)(src / (128 * ESZ)), d0 = (int)(src % (128 * ESZ)) / ESZ;
+                for (int b = 0; b < 16; ++b)
+                    img[(size_t)(k * NW + wave) * PIECE + lane * 16 + b] = Tag{key, d0 + b / ESZ};
+            }
+        }
+}
+
+template <int BLK, bool FP8>
+static void check_operand_layout() {
+    using TG = TileGeom<BLK, FP8>;
+    constexpr int ESZ = TG::ESZ;
+    std::vector<Tag> K, V, SK, SV;
+    tag_loaded_tile<TG::KS, BLK, ESZ, false, 8>(K);
+    tag_loaded_tile<TG::VS, BLK, ESZ, FP8, 8>(V);
+    tag_tile(SK, KSTR, BLK, 2, false, 0, true, TG::SUMC);
+    tag_tile(SV, VSTR, TG::SUMC, 2, false);
+    auto at = [](const std::vector<Tag>& img, int byte, int esz) -> Tag {
+        if (byte < 0 || byte + esz > (int)img.size()) return Tag{-2, -2};
+        return img[byte];
+    };
+    for (int lane = 0; lane < 64; ++lane) {
+        const int n = lane & 31, lh = lane >> 5;
+        for (int kb = 0; kb < TG::NKB; ++kb) {
+            if (FP8) {
+                for (int ks = 0; ks < 2; ++ks)
+                    for (int e = 0; e < 32; ++e)
+                        LAYOUT(at(K, k8_read_off(kb, ks, n, lh) + e, 1) == (Tag{kb * 32 + n, 64 * ks + 32 * lh + e}),
+                               "fp8 K blk=%d kb=%d ks=%d lane=%d byte %d", BLK, kb, ks, lane, e);
+            } else {
+                for (int ks = 0; ks < 8; ++ks)
+                    for (int e = 0; e < 8; ++e)
+                        LAYOUT(at(K, k_read_off<0>(kb, ks, n, lh) + 2 * e, 2) == (Tag{kb * 32 + n, 16 * ks + 8 * lh + e}),
+                               "bf16 K blk=%d kb=%d ks=%d lane=%d elem %d", BLK, kb, ks, lane, e);
+            }
+        }
+        // summary K: row kb*32+n holds hi of column kb*32+n for kb < SB, lo of column (kb-SB)*32+n after
+        for (int kb = 0; kb < 2 * TG::SB; ++kb)
+            for (int dord = 0; dord < 2; ++dord)
+                for (int ks = 0; ks < 8; ++ks) {
+                    const int col = (kb % TG::SB) * 32 + n + (kb >= TG::SB ? 1000000 : 0);
+                    const int d0 = dord ? 64 * (ks >> 2) + 32 * lh + 8 * (ks & 3) : 16 * ks + 8 * lh;
+                    const int off = dord ? k_read_off<1>(kb, ks, n, lh) : k_read_off<0>(kb, ks, n, lh);
+                    for (int e = 0; e < 8; ++e)
+                        LAYOUT(at(SK, off + 2 * e, 2) == (Tag{col, d0 + e}), "summary K blk=%d kb=%d ks=%d lane=%d",
+                               BLK, kb, ks, lane);
+                }
+    }
+    // V^T transpose reads, whole wavefront at a time
+    for (int db = 0; db < 4; ++db) {
+        if (FP8) {
+            for (int s2 = 0; s2 < TG::NKB / 2; ++s2)
+                for (int c = 0; c < 4; ++c)
+                    for (int lane = 0; lane < 64; ++lane) {
+                        const int g = lane / 16, i = lane % 16;
+                        for (int e = 0; e < 8; ++e) {
+                            const int src = 16 * g + 2 * e + i / 8;
+                            const Tag got = at(V, v8_read_off(s2, c, db, src) + i % 8, 1);
+                            const int key = s2 * 64 + 16 * c + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                            LAYOUT(got == (Tag{key, 32 * db + (lane & 31)}), "fp8 V blk=%d s2=%d c=%d db=%d lane=%d",
+                                   BLK, s2, c, db, lane);
+                        }
+                    }
+        }
+        const int nkb_v = FP8 ? 0 : TG::NKB;
+        for (int part = 0; part < 2; ++part) {          // 0: kept V tile (bf16), 1: summary V tile
+            const std::vector<Tag>& img = part ? SV : V;
+            for (int kb = 0; kb < (part ? TG::SB : nkb_v); ++kb)
+                for (int s2 = 0; s2 < 2; ++s2)
+                    for (int aa = 0; aa < 2; ++aa)
+                        for (int lane = 0; lane < 64; ++lane) {
+                            const int g = lane / 16, i = lane % 16;
+                            for (int e4 = 0; e4 < 4; ++e4) {
+                                const int src = 16 * g + 4 * e4 + i / 4;
+                                const Tag got = at(img, v_read_off(kb, s2, aa, db, src) + 2 * (i % 4), 2);
+                                const int e = 4 * aa + e4;
+                                const int key = kb * 32 + 16 * s2 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                                LAYOUT(got == (Tag{key, 32 * db + (lane & 31)}),
+                                       "%s V blk=%d kb=%d s2=%d aa=%d db=%d lane=%d", part ? "summary" : "bf16", BLK,
+                                       kb, s2, aa, db, lane);
+                            }
+                        }
+        }
+    }
+}
+
 template <int NW>
 static void replay_all(const Launch& L, bool fp8) {
     if (L.paged) {
@@ -457,6 +605,10 @@ int main(int argc, char** argv) {
     const bool quick = argc > 1 && argv[1][0] == 'q';
     char name[256];
     uint64_t seed = 1;
+    check_operand_layout<128, false>();
+    check_operand_layout<128, true>();
+    check_operand_layout<64, false>();
+    check_operand_layout<64, true>();
     // fixed shapes: tiny and ragged lengths, GQA ratios, densities from
     // "sink and diagonal only" to "everything kept", fused q/k/v strides;
     // among them the launch that once faulted: S = 4173, 8/2 heads, block 128

@@ -4,7 +4,9 @@ LDS address the kernel computes -- through the same functions of
 csrc/attn_geom.h -- stays inside its buffer over whole launches of many shapes,
 for the launched 8-wavefront shape and the 4-wavefront one; every packed query
 row is owned by one lane, every kept block is visited once as a tile and every
-pruned column lies in exactly one visited summary sub-tile. A second test
+pruned column lies in exactly one visited summary sub-tile; and every MFMA
+operand read of the tile compute returns the (key, dim) the contraction
+expects, from an LDS image filled through the load functions. A second test
 plants mistakes in a copy of the address functions and checks the replay
 reports them. CPU only."""
 import os
@@ -53,6 +55,12 @@ MUTANTS = [
      "return PieceLoc{row, ch < data_chunks ? ch : data_chunks - 1};", "return PieceLoc{row, ch};"),
     ("packed rows of a 4-wavefront slice overlap",
      "return slice * 256 + wave * (32 * RG) + rg * 32 + n;", "return slice * 256 + wave * 32 + rg * 32 + n;"),
+    ("bf16 V rows read without their rotation", "64 * ((db + rsub) & 3) + 2 * dsub", "64 * db + 2 * dsub"),
+    ("fp8 V rows loaded without their rotation", "(ch - 2 * ((row >> 1) & 3)) & 7", "ch & 7"),
+    ("K operand dim halves swapped", ": 16 * ks + 8 * lh;", ": 16 * ks + 8 * (lh ^ 1);"),
+    ("fp8 V key permutation dropped from the contiguous loads",
+     "const int key = PERM ? vt_slot(pl.row) : pl.row;\n            off[k] = has(k, wave) ? (uint32_t)",
+     "const int key = pl.row;\n            off[k] = has(k, wave) ? (uint32_t)"),
 ]
 
 
@@ -70,7 +78,7 @@ def test_planted_mistakes_are_reported(tmp_path, have_clang, what, old, new):
     exe = str(tmp_path / "replay")
     build(str(src), exe)
     r = subprocess.run([exe, "quick"], capture_output=True, text=True, timeout=300)
-    assert r.returncode != 0 and ("out of bounds" in r.stderr or "owned" in r.stderr), what
+    assert r.returncode != 0 and any(m in r.stderr for m in ("out of bounds", "owned", "operand layout")), what
 
 
 def test_tile_sequence_mistake_is_reported(tmp_path, have_clang):
