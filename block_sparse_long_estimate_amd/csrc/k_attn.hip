@@ -639,38 +639,55 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_tile_kernel(Geo geo, AttnArgs
         const int mm = -1 - code;
         f32x16 sh[RG][SB];
         float fs[RG];
+        // Pseudo-tokens of kept, future, sink and diagonal columns are masked by
+        // an additive bias, 0 or -inf per column: accumulator element v of lane
+        // half lh holds column 8 (v / 4) + 4 lh + v % 4 of the 32-column block,
+        // so one sign-extended bit of the lane's shifted word gives the bias
+        // bits (0 or those of -inf), and the bias starts the QK^T accumulation.
+        auto set_bias = [&]() __attribute__((always_inline)) {
+#pragma unroll
+            for (int kb = 0; kb < SB; ++kb) {
+                const int c0 = mm * TG::SUMC + kb * 32;
+                const uint32_t pw = ~kept[min(c0 >> 5, MAX_NB / 32 - 1)] & range_bits(c0, 1, i - 1);
+                const uint32_t masked = ~(lh ? pw >> 4 : pw);     // bit 8 q + r: column 8 q + 4 lh + r masked
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    // the empty asm keeps the extract and the and as two instructions
+                    // (the compiler would otherwise rebuild a compare and a select)
+                    int ext = __builtin_amdgcn_sbfe((int)masked, 8 * (v >> 2) + (v & 3), 1);
+                    asm volatile("" : "+v"(ext));
+                    const float bias = __int_as_float(ext & (int)0xFF800000);
+#pragma unroll
+                    for (int rg = 0; rg < RG; ++rg) sh[rg][kb][v] = bias;
+                }
+            }
+        };
         if (a.scores) {
             // block-score correction: the pseudo-token logit of column j is the
             // block score S[h, i, j] (scale included), the same for every row
-            // of the query block
+            // of the query block; masked columns are selected out
 #pragma unroll
             for (int rg = 0; rg < RG; ++rg) {
                 const float* srow = a.scores + score_off(s, h[rg], il, 0);
 #pragma unroll
-                for (int kb = 0; kb < SB; ++kb)
+                for (int kb = 0; kb < SB; ++kb) {
+                    const int c0 = mm * TG::SUMC + kb * 32;
+                    const uint32_t pw = ~kept[min(c0 >> 5, MAX_NB / 32 - 1)] & range_bits(c0, 1, i - 1);
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
-                        const int col = min(mm * TG::SUMC + kb * 32 + 8 * (v >> 2) + 4 * lh + (v & 3), s.nbk - 1);
-                        sh[rg][kb][v] = srow[col];
+                        const int bit = 8 * (v >> 2) + 4 * lh + (v & 3);
+                        const float sc = srow[min(c0 + bit, s.nbk - 1)];
+                        sh[rg][kb][v] = ((pw >> bit) & 1u) ? sc : NEG_INF;
                     }
+                }
                 fs[rg] = 1.4426950408889634f;                        // log2(e): S is in natural-log units
             }
         } else {
-            qk_pad<RG, SB, FP8 ? 1 : 0, false>(kc, qf, n, lh, 0, sh);    // hi rows
+            set_bias();
+            qk_pad<RG, SB, FP8 ? 1 : 0, true>(kc, qf, n, lh, 0, sh);     // hi rows
             qk_pad<RG, SB, FP8 ? 1 : 0, true>(kc, qf, n, lh, SB, sh);    // lo rows, same columns
 #pragma unroll
             for (int rg = 0; rg < RG; ++rg) fs[rg] = f_row[rg];
-        }
-#pragma unroll
-        for (int kb = 0; kb < SB; ++kb) {
-            const int c0 = mm * TG::SUMC + kb * 32;
-            const uint32_t pw = ~kept[min(c0 >> 5, MAX_NB / 32 - 1)] & range_bits(c0, 1, i - 1);
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int bit = 8 * (v >> 2) + 4 * lh + (v & 3);
-#pragma unroll
-                for (int rg = 0; rg < RG; ++rg) sh[rg][kb][v] = ((pw >> bit) & 1u) ? sh[rg][kb][v] : NEG_INF;
-            }
         }
         float mn[RG], ts[RG];
         bool nd[RG];
