@@ -96,6 +96,42 @@ int main(void) {
     vp.page_size = 48;
     CHECK(fp_varlen_num_rows(&vp, cu, lk) == FP_ERR_UNSUPPORTED);
 
+    /* every other entry point refuses bad arguments before any device work */
+    p = fixed_problem(2048, 4, 1, 64);
+    char* fake = (char*)dummy;               /* never dereferenced: the checks fail first */
+    CHECK(fp_estimate_select_workspace_size(&p) > 0);
+    CHECK(fp_estimate_select(&p, fake, fake, fake, NULL, NULL, NULL, nanf(""), dummy, dummy, dummy, ibuf, ibuf,
+                             1 << 20, ibuf, fake, 1 << 30, NULL) == FP_ERR_INVALID);
+    CHECK(fp_estimate_select(&p, fake, fake, fake, NULL, NULL, NULL, 1.f, dummy, dummy, dummy, ibuf, ibuf, 10, ibuf,
+                             fake, 1 << 30, NULL) == FP_ERR_CAPACITY);
+    CHECK(fp_sparse_prefill(&p, NULL, fake, fake, NULL, NULL, NULL, dummy, dummy, ibuf, ibuf, NULL, fake, NULL,
+                            fake, 1 << 30, NULL) == FP_ERR_INVALID);
+    CHECK(fp_sparse_prefill(&p, fake, fake, fake, NULL, NULL, NULL, dummy, dummy, ibuf, ibuf, NULL, fake, NULL,
+                            fake, 1, NULL) == FP_ERR_CAPACITY);
+    CHECK(fp_dense_prefill(&p, fake, NULL, fake, NULL, NULL, NULL, fake, NULL, NULL) == FP_ERR_INVALID);
+    /* the block-score correction has its own entry point, and only it takes scores */
+    CHECK(fp_sparse_prefill_scored(&p, fake, fake, fake, NULL, NULL, NULL, dummy, dummy, ibuf, ibuf, NULL, fake,
+                                   NULL, fake, 1 << 30, NULL) == FP_ERR_INVALID);
+    p.variant = FP_VARIANT_BLOCK_SCORE;
+    CHECK(fp_sparse_prefill(&p, fake, fake, fake, NULL, NULL, NULL, dummy, dummy, ibuf, ibuf, NULL, fake, NULL,
+                            fake, 1 << 30, NULL) == FP_ERR_INVALID);
+    CHECK(fp_sparse_prefill_noalloc(&p, fake, fake, fake, NULL, NULL, NULL, dummy, dummy, ibuf, ibuf, NULL, fake,
+                                    NULL, NULL) == FP_ERR_INVALID);
+    /* the allocation-free entry point refuses problems beyond its static scratch */
+    p = fixed_problem(1 << 20, 32, 8, 64);
+    CHECK(fp_num_rows(&p) > 0);
+    CHECK(fp_sparse_prefill_noalloc(&p, fake, fake, fake, NULL, NULL, NULL, dummy, dummy, ibuf, ibuf, NULL, fake,
+                                    NULL, NULL) == FP_ERR_CAPACITY);
+    /* paged: NaN tau, a short workspace, a missing pooled-KV cache */
+    vp.page_size = 16;
+    const int64_t vnnz = fp_varlen_max_nnz(&vp, cu, lk), vws = fp_varlen_workspace_size(&vp, cu, lk);
+    CHECK(fp_sparse_prefill_paged(&vp, fake, cu, lk, fake, fake, ibuf, NULL, NULL, NULL, nanf(""), ibuf, ibuf, vnnz,
+                                  fake, NULL, fake, (size_t)vws, NULL) == FP_ERR_INVALID);
+    CHECK(fp_sparse_prefill_paged(&vp, fake, cu, lk, fake, fake, ibuf, NULL, NULL, NULL, 1.f, ibuf, ibuf, vnnz,
+                                  fake, NULL, fake, (size_t)vws - 1, NULL) == FP_ERR_CAPACITY);
+    CHECK(fp_sparse_prefill_paged_cached(&vp, fake, cu, lk, fake, fake, ibuf, NULL, NULL, NULL, NULL, dummy, 1.f,
+                                         ibuf, ibuf, vnnz, fake, NULL, fake, (size_t)vws, NULL) == FP_ERR_INVALID);
+
     if (failures) return 1;
     printf("ok\n");
     return 0;

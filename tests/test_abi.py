@@ -367,6 +367,49 @@ def test_plain_c_program_uses_the_abi(tmp_path):
     assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
 
 
+def test_abi_host_code_under_sanitizers(tmp_path):
+    """The library's host code (argument checks, sizing, workspace carving)
+    built with AddressSanitizer and UndefinedBehaviorSanitizer (host pass
+    only: -Xarch_host), driven by tests/c/abi_host.c built the same way. No
+    GPU: every call in the program returns before any device work."""
+    import shutil
+    import subprocess
+    from concurrent.futures import ThreadPoolExecutor
+    hipcc, clang = "/opt/rocm/bin/hipcc", "/opt/rocm/llvm/bin/clang"
+    if not (os.path.exists(hipcc) and os.path.exists(clang)):
+        pytest.skip("ROCm hipcc/clang not found")
+    csrc = os.path.join(ROOT, "block_sparse_long_estimate_amd", "csrc")
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=undefined"]
+    flags = ["--offload-arch=gfx950", "-O1", "-g", "-std=c++17", "-fPIC", "-Xclang", "-target-feature",
+             "-Xclang", "-packed-fp32-ops", "-Wno-unused-command-line-argument"]
+
+    def compile_one(name):
+        obj = str(tmp_path / (name + ".o"))
+        extra = san if name == "abi" else []        # the host-side checks live in abi.hip
+        r = subprocess.run([hipcc] + flags + extra + ["-c", os.path.join(csrc, name + ".hip"), "-o", obj],
+                           capture_output=True, text=True, timeout=600)
+        assert r.returncode == 0, r.stderr[-2000:]
+        return obj
+
+    with ThreadPoolExecutor(4) as ex:
+        objs = list(ex.map(compile_one, ["abi", "k_estimate", "k_select", "k_attn"]))
+    lib = str(tmp_path / "libfp_prefill.so")
+    r = subprocess.run([hipcc] + flags + san + ["-shared"] + objs + ["-o", lib], capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    exe = str(tmp_path / "abi_host")
+    r = subprocess.run([clang, "-std=c99", "-Wall", "-Wextra", "-Werror", "-g", "-fsanitize=address,undefined",
+                        "-fno-sanitize-recover=undefined", "-I", os.path.join(ROOT, "include"),
+                        os.path.join(ROOT, "tests", "c", "abi_host.c"), "-L", str(tmp_path), "-lfp_prefill",
+                        f"-Wl,-rpath,{tmp_path}", "-lm", "-o", exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr[-2000:]
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0",
+               UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120, env=env)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr[-3000:]
+
+
 def test_binding_argument_checks():
     """The binding refuses, before any device call, tensors that the kernels
     would misread: mixed q/k/v dtypes, missing or misshapen fp8 scales,
