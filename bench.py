@@ -283,20 +283,23 @@ def ablation_vs_dense(fp, inp, taus=(2.0, 4.0, 8.0), chunk=8192):
     return res
 
 
-def time_path(fp, N, inp, tau, steps, warmup, label, flush_bytes=0, keep_outputs=False, fused=True):
+def time_path(fp, N, inp, tau, steps, warmup, label, flush_bytes=0, keep_outputs=False, fused=True,
+              split_small=False):
     """Run the path `warmup` + `steps` times; HIP events per stage on the
     current stream (the library launches on it). fused: fp_estimate_select +
     fp_sparse_prefill (no score matrix); otherwise the three calls
     fp_block_scores + fp_select_blocks + fp_sparse_prefill. flush_bytes > 0:
     before each timed step a buffer of that size is overwritten (outside the
     events), so L2 and the memory-side cache start cold. keep_outputs: also
-    return the outputs of KV head 0's query heads (host, fp32) and lse."""
+    return the outputs of KV head 0's query heads (host, fp32) and lse.
+    split_small: a problem too small for the chip splits its rows' tiles
+    (FP_SPLIT_SMALL_GRIDS)."""
     import torch
     dev = torch.device("cuda:0")
     q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
     sc = [None if t is None else t.to(dev) for t in (inp.q_scale, inp.k_scale, inp.v_scale)]
     block = inp.cfg.block
-    p = fp.make_problem(q, k, v, block)
+    p = fp.make_problem(q, k, v, block, split_small=split_small)
     c = p.c
     f32 = dict(dtype=torch.float32, device=dev)
     i32 = dict(dtype=torch.int32, device=dev)
@@ -639,6 +642,13 @@ def main():
                                "kept_fraction": round(r["kept_fraction"], 5),
                                "mfma_util_kept": round(r["attn_kept_tflops"] / PEAK_TFLOPS["bf16"], 4),
                                "ms_per_layer_graph_replay": round(graph_replay_ms(fp, ci_inp, c.tau), 4)}
+            if cid == 1:
+                # the same problem with its rows split over several workgroups (it has 32 units)
+                rs, _ = time_path(fp, N, ci_inp, c.tau, 10, 3, f"config {cid} split", split_small=True)
+                configs[c.name]["split_small"] = {"ms_per_layer_median": round(rs["ms_step_median"], 4),
+                                                  "ms_attention_median": round(rs["ms_attention_median"], 4),
+                                                  "mfma_util_kept": round(rs["attn_kept_tflops"] / PEAK_TFLOPS["bf16"],
+                                                                          4)}
             log(f"config {cid}: {json.dumps(configs[c.name])}")
     paged = paged8 = None
     if not args.no_paged:

@@ -126,13 +126,16 @@ VARIANTS = {"mean": N.FP_VARIANT_MEAN_CORRECTION, "none": N.FP_VARIANT_NO_CORREC
 
 def make_problem(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block: int,
                  softmax_scale: float = 0.0, o: Optional[torch.Tensor] = None,
-                 out_fp32: bool = False, correction: bool = True, variant: Optional[str] = None) -> Problem:
+                 out_fp32: bool = False, correction: bool = True, variant: Optional[str] = None,
+                 split_small: bool = False) -> Problem:
     """Descriptor of a fixed-shape batch: q [batch, S, Hq, 128], k/v [batch, S, Hkv, 128]
     (bf16, or uint8 E4M3FN codes), last dim contiguous. out_fp32: fp_sparse_prefill
     writes o in float32 (diagnostic) instead of bfloat16. correction=False: the
     ablation without the mean correction (pruned blocks dropped). variant: one of
     VARIANTS ("mean" is E1-E6 as stated; "none", "per_head" and "block_score"
-    are ablations)."""
+    are ablations). split_small: a problem too small to fill the chip splits each
+    row's tiles over several workgroups (FP_SPLIT_SMALL_GRIDS; lower latency, but
+    the rounding then depends on the problem's size)."""
     if variant is None:
         variant = "mean" if correction else "none"
     if variant not in VARIANTS:
@@ -147,6 +150,7 @@ def make_problem(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block: int,
     c = FpProblem()
     c.out_dtype = N.FP_OUT_FP32 if out_fp32 else N.FP_OUT_BF16
     c.variant = VARIANTS[variant]
+    c.split = N.FP_SPLIT_SMALL_GRIDS if split_small else N.FP_SPLIT_OFF
     c.batch, c.seqlen, c.num_q_heads, c.head_dim = q.shape[0], q.shape[1], q.shape[2], q.shape[3]
     c.num_kv_heads = k.shape[2]
     c.block = block
@@ -271,11 +275,13 @@ def fp_estimate_select(p: Problem, q, k, v, tau: float, q_scale=None, k_scale=No
 
 def sparse_prefill_fused(q, k, v, block: int, tau: float, softmax_scale: float = 0.0,
                          q_scale=None, k_scale=None, v_scale=None, with_lse: bool = True,
-                         out_fp32: bool = False, correction: bool = True, variant: Optional[str] = None):
+                         out_fp32: bool = False, correction: bool = True, variant: Optional[str] = None,
+                         split_small: bool = False):
     """The path in two calls: fp_estimate_select (no score matrix) then
     fp_sparse_prefill. Returns a dict of device tensors. (The block-score
     variant needs the score matrix: use sparse_prefill.)"""
-    p = make_problem(q, k, v, block, softmax_scale, out_fp32=out_fp32, correction=correction, variant=variant)
+    p = make_problem(q, k, v, block, softmax_scale, out_fp32=out_fp32, correction=correction, variant=variant,
+                     split_small=split_small)
     qbar, kbar, vbar, row_ptr, col_idx, sched = fp_estimate_select(p, q, k, v, tau, q_scale, k_scale, v_scale)
     o, lse = fp_sparse_prefill(p, q, k, v, kbar, vbar, row_ptr, col_idx, sched,
                                q_scale, k_scale, v_scale, with_lse)
@@ -376,9 +382,11 @@ def fp_sparse_prefill_scored(p: Problem, q, k, v, scores, vbar, row_ptr, col_idx
 
 def sparse_prefill(q, k, v, block: int, tau: float, softmax_scale: float = 0.0,
                    q_scale=None, k_scale=None, v_scale=None, with_lse: bool = True,
-                   out_fp32: bool = False, correction: bool = True, variant: Optional[str] = None):
+                   out_fp32: bool = False, correction: bool = True, variant: Optional[str] = None,
+                   split_small: bool = False):
     """All three stages on the current stream. Returns a dict of device tensors."""
-    p = make_problem(q, k, v, block, softmax_scale, out_fp32=out_fp32, correction=correction, variant=variant)
+    p = make_problem(q, k, v, block, softmax_scale, out_fp32=out_fp32, correction=correction, variant=variant,
+                     split_small=split_small)
     qbar, kbar, vbar, scores = fp_block_scores(p, q, k, v, q_scale, k_scale, v_scale)
     row_ptr, col_idx, sched = fp_select_blocks(p, scores, tau)
     if p.c.variant == N.FP_VARIANT_BLOCK_SCORE:

@@ -22,6 +22,8 @@ FP_VARIANT_MEAN_CORRECTION = 0
 FP_VARIANT_NO_CORRECTION = 1
 FP_VARIANT_PER_HEAD_LISTS = 2
 FP_VARIANT_BLOCK_SCORE = 3
+FP_SPLIT_OFF = 0
+FP_SPLIT_SMALL_GRIDS = 1
 
 EXPORTS = (
     "fp_version", "fp_last_error", "fp_num_rows", "fp_max_nnz", "fp_workspace_size",
@@ -33,6 +35,7 @@ EXPORTS = (
     "fp_sparse_prefill_paged_cached",
 )
 FP_NOALLOC_MAX_POOLED_ROWS = 32768
+FP_NOALLOC_SCRATCH_BYTES = 36 << 20
 
 
 class FpProblem(ctypes.Structure):
@@ -44,6 +47,7 @@ class FpProblem(ctypes.Structure):
         ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3),
         ("v_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3),
         ("out_dtype", ctypes.c_int32), ("variant", ctypes.c_int32),
+        ("split", ctypes.c_int32), ("reserved_", ctypes.c_int32),
     ]
 
 

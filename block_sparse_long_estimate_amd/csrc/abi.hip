@@ -13,7 +13,7 @@
 #include <vector>
 
 #include "../../include/fp_prefill.h"
-#include "fp_internal.h"
+#include "attn_geom.h"
 
 using namespace fp;
 
@@ -75,6 +75,9 @@ int check_fixed(const fp_problem* p) {
         return fail(FP_ERR_UNSUPPORTED, "out_dtype %d unsupported", p->out_dtype);
     if (p->variant < FP_VARIANT_MEAN_CORRECTION || p->variant > FP_VARIANT_BLOCK_SCORE)
         return fail(FP_ERR_UNSUPPORTED, "variant %d unsupported", p->variant);
+    if (p->split != FP_SPLIT_OFF && p->split != FP_SPLIT_SMALL_GRIDS)
+        return fail(FP_ERR_UNSUPPORTED, "split %d unsupported", p->split);
+    if (p->reserved_ != 0) return fail(FP_ERR_INVALID, "fp_problem.reserved_ must be 0");
     const int osz = p->out_dtype == FP_OUT_FP32 ? 4 : 2;
     for (int e = 0; e < 3; ++e)
         if ((p->o_stride[e] * osz) % (osz == 4 ? 16 : 8))
@@ -162,6 +165,22 @@ SortPlan fixed_sort_plan(const fp_problem* p) {
 // bf16 copies of the pooled keys (hi, lo) and values used by the summary tiles
 size_t summary_ws_bytes(long long pooled_rows) { return 3 * align_up((size_t)pooled_rows * D * 2); }
 
+// Split rows (small grids, fixed shape): parts per row and the bytes of their partial results.
+int fixed_split(const fp_problem* p) {
+    if (p->split != FP_SPLIT_SMALL_GRIDS) return 1;
+    const fp_problem lv = lists_of(p);
+    const int rows = p->batch * lv.num_kv_heads * cdiv(p->seqlen, p->block);
+    return split_count(rows, attn_slices(p->num_q_heads / lv.num_kv_heads, p->block));
+}
+size_t split_ws_bytes(const fp_problem* p) {
+    const int ns = fixed_split(p);
+    if (ns < 2) return 0;
+    const fp_problem lv = lists_of(p);
+    const int rows = p->batch * lv.num_kv_heads * cdiv(p->seqlen, p->block);
+    return align_up((size_t)split_floats(split_parts(rows, attn_slices(p->num_q_heads / lv.num_kv_heads, p->block),
+                                                     ns)) * 4);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -216,7 +235,8 @@ int64_t fp_max_nnz(const fp_problem* p) {
 int64_t fp_prefill_workspace_size(const fp_problem* p) {
     int rc = check_fixed(p);
     if (rc) return rc;
-    return (int64_t)summary_ws_bytes((long long)p->batch * p->num_kv_heads * cdiv(p->seqlen, p->block));
+    return (int64_t)(summary_ws_bytes((long long)p->batch * p->num_kv_heads * cdiv(p->seqlen, p->block)) +
+                     split_ws_bytes(p));
 }
 
 int64_t fp_workspace_size(const fp_problem* p) {
@@ -475,7 +495,14 @@ int launch_prefill(const fp_problem* p, const void* q, const void* k, const void
     a.la = RowAddr{(long long)p->num_q_heads * p->seqlen, 1, p->seqlen};
     a.Hq = p->num_q_heads; a.Hkv = p->num_kv_heads; a.G = G;
     a.rows = p->batch * lv.num_kv_heads * geo.nb;
-    a.slices = cdiv(G * p->block, 128);
+    a.slices = attn_slices(G, p->block);
+    // a grid too small for the chip splits each row's tiles; the parts' results follow the summary operands
+    a.nsplit = fixed_split(p);
+    if (a.nsplit > 1) {
+        const long long parts = split_parts(a.rows, a.slices, a.nsplit);
+        a.part_o = (float*)((char*)workspace + summary_ws_bytes(prow));
+        a.part_ml = a.part_o + split_o_floats(parts);
+    }
     a.scale_log2 = default_scale(p->softmax_scale, p->head_dim) * 1.4426950408889634f;
     // the block-score correction needs no pooled keys (kbar may be null)
     hipError_t e = launch_summary_prep(scores ? nullptr : kbar, vbar, (__bf16*)a.kbar_hi, (__bf16*)a.kbar_lo,
@@ -534,7 +561,7 @@ int fp_sparse_prefill(const fp_problem* p, const void* q, const void* k, const v
         return fail(FP_ERR_INVALID, "fp_sparse_prefill: the block-score variant takes the block scores "
                                     "(fp_sparse_prefill_scored)");
     if (!workspace) return fail(FP_ERR_INVALID, "fp_sparse_prefill: NULL workspace");
-    const size_t need = summary_ws_bytes(fixed_pooled_rows(p));
+    const size_t need = summary_ws_bytes(fixed_pooled_rows(p)) + split_ws_bytes(p);
     if (ws_bytes < need)
         return fail(FP_ERR_CAPACITY, "fp_sparse_prefill: workspace %zu < %zu bytes", ws_bytes, need);
     if (misaligned(workspace, ALIGN)) return fail(FP_ERR_INVALID, "workspace must be 256-byte aligned");
@@ -592,7 +619,7 @@ int fp_sparse_prefill_scored(const fp_problem* p, const void* q, const void* k, 
                                     "FP_VARIANT_BLOCK_SCORE");
     if (!scores || misaligned(scores, 16)) return fail(FP_ERR_INVALID, "fp_sparse_prefill_scored: scores");
     if (!workspace) return fail(FP_ERR_INVALID, "fp_sparse_prefill_scored: NULL workspace");
-    const size_t need = summary_ws_bytes(fixed_pooled_rows(p));
+    const size_t need = summary_ws_bytes(fixed_pooled_rows(p)) + split_ws_bytes(p);
     if (ws_bytes < need)
         return fail(FP_ERR_CAPACITY, "fp_sparse_prefill_scored: workspace %zu < %zu bytes", ws_bytes, need);
     if (misaligned(workspace, ALIGN)) return fail(FP_ERR_INVALID, "workspace must be 256-byte aligned");
@@ -611,12 +638,12 @@ int fp_sparse_prefill_noalloc(const fp_problem* p, const void* q, const void* k,
     if (p->variant == FP_VARIANT_BLOCK_SCORE)
         return fail(FP_ERR_INVALID, "fp_sparse_prefill_noalloc: the block-score variant takes the block scores "
                                     "(fp_sparse_prefill_scored)");
-    const size_t need = summary_ws_bytes(fixed_pooled_rows(p));
-    if (need > (size_t)FP_NOALLOC_SCRATCH_BYTES)
+    const size_t need = summary_ws_bytes(fixed_pooled_rows(p)) + split_ws_bytes(p);
+    if (fixed_pooled_rows(p) > FP_NOALLOC_MAX_POOLED_ROWS || need > (size_t)FP_NOALLOC_SCRATCH_BYTES)
         return fail(FP_ERR_CAPACITY,
-                    "fp_sparse_prefill_noalloc: the problem needs %zu bytes of scratch, above the %d-byte static "
-                    "array (batch x KV heads x blocks at most %d)", need, FP_NOALLOC_SCRATCH_BYTES,
-                    FP_NOALLOC_MAX_POOLED_ROWS);
+                    "fp_sparse_prefill_noalloc: the problem has %lld pooled rows (batch x KV heads x blocks, at "
+                    "most %d) and needs %zu bytes of the %d-byte static array", fixed_pooled_rows(p),
+                    FP_NOALLOC_MAX_POOLED_ROWS, need, FP_NOALLOC_SCRATCH_BYTES);
     void* ws = nullptr;
     rc = scratch_address(&ws);
     if (rc) return rc;

@@ -159,16 +159,49 @@ FP_HD SummarySrc summary_src(const SeqDesc& s, int Hkv, int g, int m, int w, int
 }
 
 // ---------------------------------------------------------------------------
-// Work units. Unit u of the grid runs one 256-row slice of one kept-list row:
-// u % 8 picks the XCD, and the row's slices sit on one XCD so they share its
-// L2 copy of the K/V tiles.
+// Work units. Unit u of the grid runs one 256-row slice of one kept-list row,
+// or, when the row's tiles are split, one part of that slice's tile sequence:
+// u % 8 picks the XCD, and the slices and parts of a row sit on one XCD so
+// they share its L2 copy of the K/V tiles.
 // ---------------------------------------------------------------------------
 struct UnitMap {
-    int pidx, slice;
+    int pidx, slice, split;
 };
-FP_HD UnitMap unit_map(int u, int slices) {
-    const int xcd = u & 7, k8 = u >> 3;
-    return UnitMap{8 * (k8 / slices) + xcd, k8 % slices};
+FP_HD UnitMap unit_map(int u, int slices, int nsplit = 1) {
+    const int xcd = u & 7, k8 = u >> 3, per = slices * nsplit;
+    const int rem = k8 % per;
+    return UnitMap{8 * (k8 / per) + xcd, rem % slices, rem / slices};
+}
+
+// 256-row slices per kept-list row: G query heads x BLK tokens, packed
+constexpr int SLICE_ROWS = 256;
+FP_HD int attn_slices(int G, int blk) { return (G * blk + SLICE_ROWS - 1) / SLICE_ROWS; }
+
+// Split rows: a grid with fewer units than the chip's 256 compute units
+// splits each row's tile sequence into parts run by separate workgroups, as
+// many as bring the grid to about 256 units (at most SPLIT_MAX); each part
+// leaves its unnormalised (O, m, l) and a merge pass combines them. 1 = off.
+constexpr int SPLIT_MAX = 8;
+constexpr int SPLIT_TARGET_UNITS = 256;
+FP_HD int split_count(int rows, int slices) {
+    const long long units = (long long)((rows + 7) / 8) * 8 * slices;
+    const long long n = units > 0 ? SPLIT_TARGET_UNITS / units : 1;
+    return n < 2 ? 1 : (n > SPLIT_MAX ? SPLIT_MAX : (int)n);
+}
+// floats of the partial results: O [parts][256][128], then (m, l) [parts][256][2]
+FP_HD long long split_parts(int rows, int slices, int nsplit) { return (long long)rows * slices * nsplit; }
+FP_HD long long split_o_floats(long long parts) { return parts * SLICE_ROWS * D; }
+FP_HD long long split_floats(long long parts) { return parts * SLICE_ROWS * (D + 2); }
+FP_HD long long split_part(int pidx, int slices, int slice, int nsplit, int split) {
+    return ((long long)pidx * slices + slice) * nsplit + split;
+}
+// tiles [first, first + count) of a sequence of T tiles for part `split`
+struct SplitRange {
+    int first, count;
+};
+FP_HD SplitRange split_range(int T, int split, int nsplit) {
+    const int a = (int)((long long)T * split / nsplit), z = (int)((long long)T * (split + 1) / nsplit);
+    return SplitRange{a, z - a};
 }
 
 // Packed query row of (slice, wavefront, row group, lane): NW wavefronts x RG
@@ -204,6 +237,22 @@ FP_HD int next_summary(const Bits& kept, int i, int m0, bool no_correction) {
         if (anyw) return -1 - mm;
     }
     return TILE_NONE;
+}
+
+// number of summary sub-tiles of a row, and the code of its k-th one (k < that number)
+template <int SUMC, typename Bits>
+FP_HD int count_summary(const Bits& kept, int i, bool no_correction) {
+    int n = 0;
+    for (int c = next_summary<SUMC>(kept, i, 0, no_correction); c != TILE_NONE;
+         c = next_summary<SUMC>(kept, i, -c, no_correction))
+        ++n;
+    return n;
+}
+template <int SUMC, typename Bits>
+FP_HD int nth_summary(const Bits& kept, int i, int k, bool no_correction) {
+    int c = next_summary<SUMC>(kept, i, 0, no_correction);
+    for (int e = 0; e < k && c != TILE_NONE; ++e) c = next_summary<SUMC>(kept, i, -c, no_correction);
+    return c;
 }
 
 template <int SUMC, typename Bits>

@@ -210,6 +210,8 @@ struct AttnArgs {
     int dense;                         // every block j <= i kept, no kept lists read (dense causal attention)
     int kv_div;                        // KV head of kept-list row group g: g / kv_div (G with per-head lists, else 1)
     const float* scores;               // block-score correction: pseudo-token logit S[b,h,i,j] + ln|J| (else null)
+    int nsplit;                        // parts per row's tile sequence (split_count; 0 or 1: off)
+    float* part_o; float* part_ml;     // split: per-part unnormalised O and (m, l), merged afterwards
 };
 
 hipError_t launch_pool(const GeoFixed* gf, const GeoTable* gt, const PoolArgs& a, hipStream_t st);

@@ -406,7 +406,7 @@ __device__ __forceinline__ float load_scale(const float* p, long long idx) {
     return p[idx + z];
 }
 
-template <int BLK, bool FP8, bool PAGED, typename Geo, int NW>
+template <int BLK, bool FP8, bool PAGED, typename Geo, int NW, bool SPLIT>
 __global__ __launch_bounds__(NW * 64, 1) void attn_tile_kernel(Geo geo, AttnArgs a) {
     using TG = TileGeom<BLK, FP8>;
     constexpr int RG = 8 / NW;                      // 32-row groups per wavefront
@@ -434,7 +434,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_tile_kernel(Geo geo, AttnArgs
     const int n = lane & 31, lh = lane >> 5;
     const float NEG_INF = -__builtin_inff();
 
-    const UnitMap um = unit_map(blockIdx.x, a.slices);
+    const UnitMap um = unit_map(blockIdx.x, a.slices, SPLIT ? a.nsplit : 1);
     if (um.pidx >= a.rows) return;
     // dense: rows in reverse order, so every (sequence, KV head) runs its
     // longest rows (latest query blocks) first
@@ -480,7 +480,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_tile_kernel(Geo geo, AttnArgs
         kvo.k.init_paged(a.ka.st, lshift, wave, lane);
         kvo.v.init_paged(a.va.st, lshift, wave, lane);
     }
-    issue_kv<BLK, FP8, PAGED, NW>(a, b, s.L, gk, j0, kA, vA, wave, lane, kvo, nullptr);
+    // the first tile; a split row's part learns its first tile from the kept bitmap
+    if (!SPLIT) issue_kv<BLK, FP8, PAGED, NW>(a, b, s.L, gk, j0, kA, vA, wave, lane, kvo, nullptr);
     // paged: stage the page ids for the later tiles (visible after the
     // barrier that follows the kept-bitmap build)
     const lds_int* pages = nullptr;
@@ -529,7 +530,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_tile_kernel(Geo geo, AttnArgs
     const float* ksp = FP8 ? a.ks.p + (long long)b * a.ks.sb + (long long)gk * a.ks.sh : nullptr;
     const float* vsp = FP8 ? a.vs.p + (long long)b * a.vs.sb + (long long)gk * a.vs.sh : nullptr;
     float ksA = 1.f, vsA = 1.f, ksB = 1.f, vsB = 1.f;
-    if constexpr (FP8) {
+    if constexpr (FP8 && !SPLIT) {
         ksA = load_scale(ksp, (j0 * BLK) >> 7);
         vsA = load_scale(vsp, (j0 * BLK) >> 7);
     }
@@ -697,22 +698,66 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_tile_kernel(Geo geo, AttnArgs
         pv_tr<RG, SB>(sh, vc, lane, 0, oacc);
     };
 
+    // A split row's part runs tiles [first, first + count) of the row's
+    // sequence (kept blocks, then summary sub-tiles): `remaining` counts them
+    // down and ends the sequence after the last.
+    int code0 = j0, remaining = 0x7fffffff;
+    if constexpr (SPLIT) {
+        const int T = __builtin_amdgcn_readfirstlane(nnz + (no_corr ? 0 : count_summary<TG::SUMC>(kbits, i, no_corr)));
+        const SplitRange sr = split_range(T, um.split, a.nsplit);
+        remaining = __builtin_amdgcn_readfirstlane(sr.count);
+        if (remaining == 0) {
+            // an empty part: nothing to add (m = -inf, l = 0, O = 0)
+            const long long pu = split_part(um.pidx, a.slices, um.slice, a.nsplit, um.split);
+#pragma unroll
+            for (int rg = 0; rg < RG; ++rg) {
+                if (!valid[rg]) continue;
+                const int pl = packed_row<NW>(0, wave, rg, n);
+                float* po = a.part_o + (pu * SLICE_ROWS + pl) * D;
+#pragma unroll
+                for (int db = 0; db < 4; ++db)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4)
+                        *(float4*)(po + db * 32 + q4 * 8 + lh * 4) = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (lh == 0) *(float2*)(a.part_ml + (pu * SLICE_ROWS + pl) * 2) = make_float2(NEG_INF, 0.f);
+            }
+            return;
+        }
+        code0 = sr.first < nnz ? a.col_idx[rp0 + sr.first] : nth_summary<TG::SUMC>(kbits, i, sr.first - nnz, no_corr);
+        code0 = __builtin_amdgcn_readfirstlane(code0);
+        issue(code0, kA, vA, ksA, vsA);
+        __syncthreads();                              // the part's first tile landed
+    }
+    // the code after `code` in the sequence (kept block or summary sub-tile)
+    auto next_tile = [&](int code) __attribute__((always_inline)) {
+        if (SPLIT && --remaining <= 0) return TILE_NONE;
+        return next_code<TG::SUMC>(kbits, i, code, no_corr);
+    };
+    auto next_sum = [&](int code) __attribute__((always_inline)) {
+        if (SPLIT && --remaining <= 0) return TILE_NONE;
+        return next_summary<TG::SUMC>(kbits, i, -code, no_corr);
+    };
+
     // Kept phase. Buffers alternate A, B; the loop ends once the code of the
     // following tile is a summary code (already issued) or NONE (both < 0).
-    int nxt, ca = j0;
-    bool in_b;
-    while (true) {
-        const int cb = next_code<TG::SUMC>(kbits, i, ca, no_corr);
-        if (cb != TILE_NONE) issue(cb, kB, vB, ksB, vsB);
-        compute_kept(ca, kA, vA, ksA, vsA);
-        __syncthreads();                              // next tile landed; A is free
-        if (cb < 0) { nxt = cb; in_b = true; break; }
-        const int cn = next_code<TG::SUMC>(kbits, i, cb, no_corr);
-        if (cn != TILE_NONE) issue(cn, kA, vA, ksA, vsA);
-        compute_kept(cb, kB, vB, ksB, vsB);
-        __syncthreads();
-        if (cn < 0) { nxt = cn; in_b = false; break; }
-        ca = cn;
+    int nxt, ca = code0;
+    bool in_b = false;
+    if (!SPLIT || code0 >= 0) {
+        while (true) {
+            const int cb = next_tile(ca);
+            if (cb != TILE_NONE) issue(cb, kB, vB, ksB, vsB);
+            compute_kept(ca, kA, vA, ksA, vsA);
+            __syncthreads();                          // next tile landed; A is free
+            if (cb < 0) { nxt = cb; in_b = true; break; }
+            const int cn = next_tile(cb);
+            if (cn != TILE_NONE) issue(cn, kA, vA, ksA, vsA);
+            compute_kept(cb, kB, vB, ksB, vsB);
+            __syncthreads();
+            if (cn < 0) { nxt = cn; in_b = false; break; }
+            ca = cn;
+        }
+    } else {
+        nxt = code0;                                  // the part starts among the summary sub-tiles (in A)
     }
     if constexpr (FP8) {
         // widen the query codes to bf16 (exact) in the fp8 fragment's dim order
@@ -731,19 +776,19 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_tile_kernel(Geo geo, AttnArgs
     }
     // Summary phase: realign so the loop below always starts on buffer A.
     if (in_b && nxt != TILE_NONE) {
-        const int cn = next_summary<TG::SUMC>(kbits, i, -nxt, no_corr);
+        const int cn = next_sum(nxt);
         if (cn != TILE_NONE) issue_summary<BLK, NW>(a, s, gk, -1 - cn, kA, vA, wave, lane);
         compute_summary(nxt, kB, vB);
         __syncthreads();
         nxt = cn;
     }
     while (nxt != TILE_NONE) {
-        const int cb = next_summary<TG::SUMC>(kbits, i, -nxt, no_corr);
+        const int cb = next_sum(nxt);
         if (cb != TILE_NONE) issue_summary<BLK, NW>(a, s, gk, -1 - cb, kB, vB, wave, lane);
         compute_summary(nxt, kA, vA);
         __syncthreads();
         if (cb == TILE_NONE) break;
-        const int cn = next_summary<TG::SUMC>(kbits, i, -cb, no_corr);
+        const int cn = next_sum(cb);
         if (cn != TILE_NONE) issue_summary<BLK, NW>(a, s, gk, -1 - cn, kA, vA, wave, lane);
         compute_summary(cb, kB, vB);
         __syncthreads();
@@ -754,6 +799,26 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_tile_kernel(Geo geo, AttnArgs
     float ltot[RG];
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) ltot[rg] = lsum[rg] + other_half(lsum[rg]);
+    if constexpr (SPLIT) {
+        // the part's unnormalised O (fp8: in value units) and (m, l), for the merge
+        const long long pu = split_part(um.pidx, a.slices, um.slice, a.nsplit, um.split);
+        const float sc = FP8 ? svmax * 0.00390625f : 1.f;
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg) {
+            if (!valid[rg]) continue;
+            const int pl = packed_row<NW>(0, wave, rg, n);
+            float* po = a.part_o + (pu * SLICE_ROWS + pl) * D;
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+                    *(float4*)(po + db * 32 + q4 * 8 + lh * 4) =
+                        make_float4(oacc[rg][db][4 * q4] * sc, oacc[rg][db][4 * q4 + 1] * sc,
+                                    oacc[rg][db][4 * q4 + 2] * sc, oacc[rg][db][4 * q4 + 3] * sc);
+            if (lh == 0) *(float2*)(a.part_ml + (pu * SLICE_ROWS + pl) * 2) = make_float2(m[rg], ltot[rg]);
+        }
+        return;
+    }
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
         if (!valid[rg]) continue;
@@ -813,16 +878,86 @@ hipError_t launch_summary_prep(const float* kbar, const float* vbar, __bf16* hi,
     return hipGetLastError();
 }
 
+// Merge of a split row's parts: one workgroup per 8 packed rows of a (row,
+// slice), 32 threads per packed row (4 dims each). With M = max m_s and
+// w_s = 2^(m_s - M): o = sum w_s O_s / sum w_s l_s, lse = (M + log2 sum w_s l_s)
+// ln 2; the parts are added in their order, so the result does not depend on
+// timing. Every part's (m, l), then every part's O, is loaded before use.
+constexpr int MERGE_ROWS = 8;
+template <typename Geo>
+__global__ __launch_bounds__(256) void split_merge_kernel(Geo geo, AttnArgs a, int blk) {
+    constexpr int GROUPS = SLICE_ROWS / MERGE_ROWS;
+    const int grp = blockIdx.x % GROUPS, unit = blockIdx.x / GROUPS;
+    const int slice = unit % a.slices, pidx = unit / a.slices;
+    if (pidx >= a.rows) return;
+    const int r = a.sched ? a.sched[pidx] : pidx;
+    const int b = geo.seq_of_row(r);
+    const SeqDesc s = geo.seq(b);
+    const int rl = r - s.row0;
+    const int g = rl / s.nq, il = rl % s.nq;
+    const int i = s.i0 + il;
+    const int t_lo = max(i * blk, s.P), t_hi = min((i + 1) * blk, s.L);
+    const int npk = a.G * (t_hi - t_lo);
+    const int c = threadIdx.x & 31;
+    const int pl = grp * MERGE_ROWS + (threadIdx.x >> 5);
+    const int prow = slice * SLICE_ROWS + pl;
+    if (prow >= npk) return;
+    const int tl = prow / a.G;
+    const int t = t_lo + tl, h = g * a.G + (prow - tl * a.G);
+    const float NEG_INF = -__builtin_inff();
+    float2 ml[SPLIT_MAX];
+    float4 po[SPLIT_MAX];
+#pragma unroll
+    for (int sp = 0; sp < SPLIT_MAX; ++sp) {
+        const long long pu = split_part(pidx, a.slices, slice, a.nsplit, sp < a.nsplit ? sp : 0);
+        ml[sp] = sp < a.nsplit ? *(const float2*)(a.part_ml + (pu * SLICE_ROWS + pl) * 2) : make_float2(NEG_INF, 0.f);
+        po[sp] = *(const float4*)(a.part_o + (pu * SLICE_ROWS + pl) * D + 4 * c);
+    }
+    float M = NEG_INF;
+#pragma unroll
+    for (int sp = 0; sp < SPLIT_MAX; ++sp) M = fmaxf(M, ml[sp].x);
+    float L = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int sp = 0; sp < SPLIT_MAX; ++sp) {
+        // an empty part, or no key of this row in it, weighs nothing
+        const float w = ml[sp].x == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(ml[sp].x - M);
+        L += w * ml[sp].y;
+        acc.x += w * po[sp].x; acc.y += w * po[sp].y; acc.z += w * po[sp].z; acc.w += w * po[sp].w;
+    }
+    const float inv = 1.f / L;
+    if (a.o_f32) {
+        float* op = (float*)a.o + a.oa.off(b, s, t, h) + 4 * c;
+        *(float4*)op = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    } else {
+        __bf16* op = (__bf16*)a.o + a.oa.off(b, s, t, h) + 4 * c;
+        uint2 w2;
+        w2.x = pk_bf16(acc.x * inv, acc.y * inv);
+        w2.y = pk_bf16(acc.z * inv, acc.w * inv);
+        *(uint2*)op = w2;
+    }
+    if (a.lse && c == 0) a.lse[a.la.off(b, s, t, h)] = (M + __log2f(L)) * LN2;
+}
+
 template <int BLK, int NW, typename Geo>
 static void attn_launch(const Geo& geo, const AttnArgs& a, int fp8, hipStream_t st) {
     AttnArgs b2 = a;
-    b2.slices = cdiv(a.G * BLK, 256);
+    b2.slices = attn_slices(a.G, BLK);
     const int units = cdiv(a.rows, 8) * 8 * b2.slices;
     // contiguous K/V come with the fixed geometry, the paged cache with the
     // sequence table (the entry points pair them so)
     constexpr bool PG = Geo::PAGED_KV;
-    if (fp8) attn_tile_kernel<BLK, true, PG, Geo, NW><<<units, NW * 64, 0, st>>>(geo, b2);
-    else attn_tile_kernel<BLK, false, PG, Geo, NW><<<units, NW * 64, 0, st>>>(geo, b2);
+    if constexpr (!PG) {
+        if (a.nsplit > 1 && !a.dense) {
+            // a grid too small for the chip: each row's tiles in nsplit parts, then the merge
+            if (fp8) attn_tile_kernel<BLK, true, PG, Geo, NW, true><<<units * a.nsplit, NW * 64, 0, st>>>(geo, b2);
+            else attn_tile_kernel<BLK, false, PG, Geo, NW, true><<<units * a.nsplit, NW * 64, 0, st>>>(geo, b2);
+            split_merge_kernel<Geo><<<a.rows * b2.slices * (SLICE_ROWS / MERGE_ROWS), 256, 0, st>>>(geo, b2, BLK);
+            return;
+        }
+    }
+    if (fp8) attn_tile_kernel<BLK, true, PG, Geo, NW, false><<<units, NW * 64, 0, st>>>(geo, b2);
+    else attn_tile_kernel<BLK, false, PG, Geo, NW, false><<<units, NW * 64, 0, st>>>(geo, b2);
 }
 
 // The launched shape is NW = 8 (two wavefronts per SIMD, 32 rows each). The

@@ -74,6 +74,13 @@ extern "C" {
 #define FP_VARIANT_BLOCK_SCORE 3       /* ablation: a pruned block's pseudo-token takes the block
                                           score S[h,i,j] + ln|block| as logit for every row of
                                           query block i (fp_sparse_prefill_scored)            */
+#define FP_SPLIT_OFF 0           /* each (row, slice) runs in one workgroup: a row's results do not
+                                    depend on the other rows of the batch (default)            */
+#define FP_SPLIT_SMALL_GRIDS 1   /* a problem of at most 128 (row, 256-row slice) work units, too
+                                    few for the chip's 256 compute units, splits each row's tile
+                                    sequence over up to 8 workgroups and merges their partial
+                                    results: lower latency for short prompts; the rounding then
+                                    depends on the problem's size                              */
 
 /* Fixed-shape batch: `batch` sequences of `seqlen` tokens each, one-shot
  * prefill (no cached prefix). q [batch, seqlen, Hq, 128], k and v
@@ -96,6 +103,8 @@ typedef struct fp_problem {
     int32_t variant;         /* FP_VARIANT_MEAN_CORRECTION (0, default) or an ablation: NO_CORRECTION
                                 and BLOCK_SCORE change E6 only; PER_HEAD_LISTS changes the kept
                                 lists (sizes, selection and attention rows) */
+    int32_t split;           /* FP_SPLIT_OFF (0, default) or FP_SPLIT_SMALL_GRIDS (E6 only) */
+    int32_t reserved_;       /* must be 0 */
 } fp_problem;
 
 /* Paged varlen batch (continuous batching with cached prefixes). Sequence b
@@ -126,7 +135,14 @@ const char* fp_last_error(void);
 int64_t fp_num_rows(const fp_problem* p);       /* batch * Hkv * nb           */
 int64_t fp_max_nnz(const fp_problem* p);        /* batch * Hkv * nb(nb+1)/2   */
 int64_t fp_workspace_size(const fp_problem* p); /* bytes for fp_select_blocks */
-int64_t fp_prefill_workspace_size(const fp_problem* p); /* bytes for fp_sparse_prefill */
+/* bytes for fp_sparse_prefill: the bf16 summary operands and, with
+ * split = FP_SPLIT_SMALL_GRIDS on a problem of at most 128 (row, 256-row
+ * slice) work units, room for the partial results (unnormalised O, max,
+ * sum) of the up to 8 workgroups each row's tile sequence is split over,
+ * which a merge pass combines. The split is a function of the problem alone,
+ * so fp_sparse_prefill, fp_sparse_prefill_scored and fp_sparse_prefill_noalloc
+ * compute identical results on one problem. */
+int64_t fp_prefill_workspace_size(const fp_problem* p);
 
 /* E1-E2: the block-level score estimate (aipulsen.com article body: scores
  * estimated per block pair instead of per token; lode.cx page, "How It
@@ -235,7 +251,11 @@ int fp_dense_prefill(const fp_problem* p, const void* q, const void* k, const vo
  * GPU (other streams, other threads) race and must be serialised by the
  * caller. Arguments as for fp_sparse_prefill. */
 #define FP_NOALLOC_MAX_POOLED_ROWS 32768
-#define FP_NOALLOC_SCRATCH_BYTES (3 * FP_NOALLOC_MAX_POOLED_ROWS * 256)
+/* The array holds the bf16 summary operands (3 x 256 bytes per pooled row)
+ * and, for a problem of at most 128 workgroups, whose rows are split over
+ * several workgroups (see fp_prefill_workspace_size), the parts' partial
+ * results (at most 256 parts of 133,120 bytes). */
+#define FP_NOALLOC_SCRATCH_BYTES (36 << 20)
 int fp_sparse_prefill_noalloc(const fp_problem* p, const void* q, const void* k, const void* v,
                               const float* q_scale, const float* k_scale, const float* v_scale,
                               const float* kbar, const float* vbar,

@@ -109,7 +109,7 @@ static void make_table(Launch& L, const std::vector<int>& Ls, const std::vector<
 }
 
 template <int BLK, bool FP8, bool PAGED, int NW>
-static void replay(const Launch& L) {
+static void replay(const Launch& L, bool split_small) {
     using TG = TileGeom<BLK, FP8>;
     constexpr int RG = 8 / NW, ESZ = TG::ESZ;
     const int slices = cdiv(L.G * BLK, 256);
@@ -154,8 +154,24 @@ static void replay(const Launch& L) {
                         CHECK(v_read_off(kb, s2, aa, db, lane) + 8 <= TG::VTILE_SUM, "summary V read");
     }
 
-    for (int u = 0; u < units; ++u) {
-        const UnitMap um = unit_map(u, slices);
+    // a grid too small for the chip splits the rows of a fixed-shape launch
+    const int nsplit = PAGED || !split_small ? 1 : split_count(L.rows, slices);
+    const long long parts = split_parts(L.rows, slices, nsplit);
+    {
+        // the unit map covers each (row, slice, part) once
+        std::vector<int> seen((size_t)cdiv(L.rows, 8) * 8 * slices * nsplit, 0);
+        for (int u = 0; u < units * nsplit; ++u) {
+            const UnitMap um = unit_map(u, slices, nsplit);
+            CHECK(um.slice >= 0 && um.slice < slices && um.split >= 0 && um.split < nsplit && um.pidx >= 0,
+                  "unit %d", u);
+            const long long key = ((long long)um.pidx * slices + um.slice) * nsplit + um.split;
+            if (key >= 0 && key < (long long)seen.size()) ++seen[key];
+        }
+        for (size_t k = 0; k < seen.size(); ++k) CHECK(seen[k] == 1, "unit key %zu seen %d times", k, seen[k]);
+    }
+    for (int u = 0; u < units * nsplit; ++u) {
+        const UnitMap um = unit_map(u, slices, nsplit);
+        if (um.split != 0) continue;                 // all parts of a (row, slice) are replayed together
         if (um.pidx >= L.rows) continue;
         CHECK(um.pidx >= 0 && um.pidx < (int)L.sched.size(), "sched[%d]", um.pidx);
         const int r = L.sched[um.pidx];
@@ -234,8 +250,7 @@ static void replay(const Launch& L) {
         // ids are staged, so it reads the block table directly
         const bool no_corr = false;
         std::vector<char> visited(i + 1, 0), sub_visited(i / TG::SUMC + 1, 0);
-        for (int code = j0; code != TILE_NONE; code = next_code<TG::SUMC>(kept, i, code, no_corr)) {
-            const bool staged = have_pages && code != j0;
+        auto visit = [&](int code, bool staged) {
             if (code >= 0 && code <= i) ++visited[code];
             if (code < 0 && -1 - code <= i / TG::SUMC) ++sub_visited[-1 - code];
             if (code >= 0) {
@@ -328,6 +343,39 @@ static void replay(const Launch& L) {
                         }
                 }
             }
+        };
+        if (nsplit < 2) {
+            for (int code = j0; code != TILE_NONE; code = next_code<TG::SUMC>(kept, i, code, no_corr))
+                visit(code, have_pages && code != j0);
+        } else {
+            // the parts of a split row: tiles [first, first + count) each, first
+            // issued after the bitmap; partial results and their merge in bounds
+            const int T = nr + count_summary<TG::SUMC>(kept, i, no_corr);
+            int covered = 0;
+            for (int sp = 0; sp < nsplit; ++sp) {
+                const SplitRange sr = split_range(T, sp, nsplit);
+                CHECK(sr.first == covered && sr.count >= 0, "part %d of row %d: tiles [%d, +%d)", sp, i, sr.first,
+                      sr.count);
+                covered = sr.first + sr.count;
+                const long long pu = split_part(um.pidx, slices, um.slice, nsplit, sp);
+                CHECK(pu >= 0 && pu < parts, "part index %lld of %lld", pu, parts);
+                for (int pl = 0; pl < 256 && um.slice * 256 + pl < npk; ++pl) {
+                    CHECK((pu * SLICE_ROWS + pl) * D + D <= split_o_floats(parts), "partial O row %d", pl);
+                    CHECK((pu * SLICE_ROWS + pl) * 2 + 2 <= split_floats(parts) - split_o_floats(parts),
+                          "partial (m, l) row %d", pl);
+                }
+                if (sr.count == 0) continue;
+                int code = sr.first < nr ? L.col_idx[rp0 + sr.first]
+                                         : nth_summary<TG::SUMC>(kept, i, sr.first - nr, no_corr);
+                CHECK(code != TILE_NONE, "part %d of row %d starts past the sequence", sp, i);
+                for (int remaining = sr.count; code != TILE_NONE;) {
+                    visit(code, have_pages);
+                    if (--remaining <= 0) break;
+                    code = next_code<TG::SUMC>(kept, i, code, no_corr);
+                    CHECK(code != TILE_NONE, "part %d of row %d ends early", sp, i);
+                }
+            }
+            CHECK(covered == T, "parts of row %d cover %d of %d tiles", i, covered, T);
         }
         // every kept block visited once as a kept tile; every pruned column
         // (between the sink and the diagonal) inside a summary sub-tile that is
@@ -591,11 +639,15 @@ static void check_operand_layout() {
 template <int NW>
 static void replay_all(const Launch& L, bool fp8) {
     if (L.paged) {
-        if (L.blk == 128) fp8 ? replay<128, true, true, NW>(L) : replay<128, false, true, NW>(L);
-        else fp8 ? replay<64, true, true, NW>(L) : replay<64, false, true, NW>(L);
-    } else {
-        if (L.blk == 128) fp8 ? replay<128, true, false, NW>(L) : replay<128, false, false, NW>(L);
-        else fp8 ? replay<64, true, false, NW>(L) : replay<64, false, false, NW>(L);
+        if (L.blk == 128) fp8 ? replay<128, true, true, NW>(L, false) : replay<128, false, true, NW>(L, false);
+        else fp8 ? replay<64, true, true, NW>(L, false) : replay<64, false, true, NW>(L, false);
+        return;
+    }
+    // fixed shape: as launched by default, and with the split of small grids when it applies
+    const int slices = attn_slices(L.G, L.blk);
+    for (int sp = 0; sp < (split_count(L.rows, slices) > 1 ? 2 : 1); ++sp) {
+        if (L.blk == 128) fp8 ? replay<128, true, false, NW>(L, sp) : replay<128, false, false, NW>(L, sp);
+        else fp8 ? replay<64, true, false, NW>(L, sp) : replay<64, false, false, NW>(L, sp);
     }
 }
 
@@ -609,6 +661,17 @@ int main(int argc, char** argv) {
     check_operand_layout<128, true>();
     check_operand_layout<64, false>();
     check_operand_layout<64, true>();
+    // a launch small enough to split its rows into parts (first, so the quick mode runs it too)
+    for (int fp8 = 0; fp8 < 2; ++fp8) {
+        snprintf(name, sizeof name, "fixed split rows S=700 4/1 blk=128 %s", fp8 ? "fp8" : "bf16");
+        g_case = name;
+        const Launch L = fixed_launch(1, 700, 4, 1, 128, fp8, 0.3, seed++, false);
+        if (split_count(L.rows, attn_slices(L.G, 128)) < 2) {
+            fprintf(stderr, "[%s] expected a split launch\n", name);
+            return 1;
+        }
+        replay_all<8>(L, fp8);
+    }
     // fixed shapes: tiny and ragged lengths, GQA ratios, densities from
     // "sink and diagonal only" to "everything kept", fused q/k/v strides;
     // among them the launch that once faulted: S = 4173, 8/2 heads, block 128

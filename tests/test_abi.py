@@ -281,7 +281,7 @@ def test_binding_checks_pooled_kv_cache():
 def test_variant_validation():
     """variant (the ablation of the mean correction) sits where the padding was."""
     lib = N.load()
-    assert ctypes.sizeof(N.FpProblem) == 136
+    assert ctypes.sizeof(N.FpProblem) == 144
     assert lib.fp_num_rows(ctypes.byref(problem(variant=N.FP_VARIANT_NO_CORRECTION))) > 0
     assert lib.fp_num_rows(ctypes.byref(problem(variant=7))) == N.FP_ERR_UNSUPPORTED
     # per-head lists: one row per (query head, query block), sizes follow
@@ -292,6 +292,31 @@ def test_variant_validation():
     assert lib.fp_max_nnz(ctypes.byref(ph)) == G * lib.fp_max_nnz(ctypes.byref(base))
     assert lib.fp_workspace_size(ctypes.byref(ph)) > lib.fp_workspace_size(ctypes.byref(base))
     assert lib.fp_prefill_workspace_size(ctypes.byref(ph)) == lib.fp_prefill_workspace_size(ctypes.byref(base))
+
+
+def test_split_validation_and_workspace():
+    """split (FP_SPLIT_SMALL_GRIDS) only changes E6 on problems of at most 128
+    (row, 256-row slice) units: the prefill workspace then holds each part's
+    partial results (256 rows x (128 + 2) floats); larger problems, and the
+    default FP_SPLIT_OFF, need only the summary operands."""
+    lib = N.load()
+    assert lib.fp_num_rows(ctypes.byref(problem(split=7))) == N.FP_ERR_UNSUPPORTED
+    assert lib.fp_num_rows(ctypes.byref(problem(reserved_=1))) == N.FP_ERR_INVALID
+    ws = lambda **kw: lib.fp_prefill_workspace_size(ctypes.byref(problem(**kw)))
+    # 16 rows (8 query blocks x 2 KV heads) x 2 slices (G = 4, 128-token blocks) = 32 units: 8 parts
+    assert ws(split=N.FP_SPLIT_SMALL_GRIDS) - ws() == 16 * 2 * 8 * 256 * 130 * 4
+    # S = 2048, 4/1 heads, 64-token blocks: 32 rows x 1 slice = 32 units: 8 parts
+    small = dict(seqlen=2048, num_q_heads=4, num_kv_heads=1, block=64)
+    for name, H in (("q_stride", 4), ("k_stride", 1), ("v_stride", 1), ("o_stride", 4)):
+        small[name] = (ctypes.c_int64 * 3)(2048 * H * 128, H * 128, 128)
+    assert ws(split=N.FP_SPLIT_SMALL_GRIDS, **small) - ws(**small) == 32 * 8 * 256 * 130 * 4
+    # 128K tokens, 8 query / 2 KV heads: 2048 rows x 2 slices, far more than the chip: no split
+    big = dict(seqlen=131072)
+    for name, H in (("q_stride", 8), ("k_stride", 2), ("v_stride", 2), ("o_stride", 8)):
+        big[name] = (ctypes.c_int64 * 3)(131072 * H * 128, H * 128, 128)
+    assert ws(split=N.FP_SPLIT_SMALL_GRIDS, **big) == ws(**big)
+    # the allocation-free entry point's static array holds the largest split's partial results
+    assert 256 * 256 * 130 * 4 + 3 * 256 * 256 <= N.FP_NOALLOC_SCRATCH_BYTES
 
 
 def test_block_score_variant_takes_scores():
@@ -310,7 +335,7 @@ def test_block_score_variant_takes_scores():
 
 def test_out_dtype_validation():
     lib = N.load()
-    assert ctypes.sizeof(N.FpProblem) == 136
+    assert ctypes.sizeof(N.FpProblem) == 144
     p = problem(out_dtype=1)
     assert lib.fp_num_rows(ctypes.byref(p)) == N.FP_ERR_UNSUPPORTED
     p = problem(out_dtype=N.FP_OUT_FP32)

@@ -58,6 +58,10 @@ MUTANTS = [
     ("bf16 V rows read without their rotation", "64 * ((db + rsub) & 3) + 2 * dsub", "64 * db + 2 * dsub"),
     ("fp8 V rows loaded without their rotation", "(ch - 2 * ((row >> 1) & 3)) & 7", "ch & 7"),
     ("K operand dim halves swapped", ": 16 * ks + 8 * lh;", ": 16 * ks + 8 * (lh ^ 1);"),
+    ("split parts overlap by a tile", "z = (int)((long long)T * (split + 1) / nsplit);",
+     "z = (int)((long long)T * (split + 1) / nsplit) + (split + 1 < nsplit);"),
+    ("split units give two workgroups the same part", "return UnitMap{8 * (k8 / per) + xcd, rem % slices, rem / slices};",
+     "return UnitMap{8 * (k8 / per) + xcd, rem % slices, rem % nsplit};"),
     ("fp8 V key permutation dropped from the contiguous loads",
      "const int key = PERM ? vt_slot(pl.row) : pl.row;\n            off[k] = has(k, wave) ? (uint32_t)",
      "const int key = pl.row;\n            off[k] = has(k, wave) ? (uint32_t)"),
@@ -78,7 +82,7 @@ def test_planted_mistakes_are_reported(tmp_path, have_clang, what, old, new):
     exe = str(tmp_path / "replay")
     build(str(src), exe)
     r = subprocess.run([exe, "quick"], capture_output=True, text=True, timeout=300)
-    assert r.returncode != 0 and any(m in r.stderr for m in ("out of bounds", "owned", "operand layout")), what
+    assert r.returncode != 0 and any(m in r.stderr for m in ("out of bounds", "owned", "operand layout")), what + r.stderr[-500:]
 
 
 def test_tile_sequence_mistake_is_reported(tmp_path, have_clang):
