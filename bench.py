@@ -284,7 +284,7 @@ def ablation_vs_dense(fp, inp, taus=(2.0, 4.0, 8.0), chunk=8192):
 
 
 def time_path(fp, N, inp, tau, steps, warmup, label, flush_bytes=0, keep_outputs=False, fused=True,
-              split_small=False):
+              split_small=False, sampler=None):
     """Run the path `warmup` + `steps` times; HIP events per stage on the
     current stream (the library launches on it). fused: fp_estimate_select +
     fp_sparse_prefill (no score matrix); otherwise the three calls
@@ -293,7 +293,8 @@ def time_path(fp, N, inp, tau, steps, warmup, label, flush_bytes=0, keep_outputs
     events), so L2 and the memory-side cache start cold. keep_outputs: also
     return the outputs of KV head 0's query heads (host, fp32) and lse.
     split_small: a problem too small for the chip splits its rows' tiles
-    (FP_SPLIT_SMALL_GRIDS)."""
+    (FP_SPLIT_SMALL_GRIDS). sampler: started after the warm-up steps and
+    stopped once the timed steps have finished."""
     import torch
     dev = torch.device("cuda:0")
     q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
@@ -347,6 +348,8 @@ def time_path(fp, N, inp, tau, steps, warmup, label, flush_bytes=0, keep_outputs
     all0 = torch.cuda.Event(enable_timing=True)
     all1 = torch.cuda.Event(enable_timing=True)
     per = []
+    if sampler is not None:
+        sampler.start()
     all0.record(stream)
     for _ in range(steps):
         e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
@@ -359,6 +362,8 @@ def time_path(fp, N, inp, tau, steps, warmup, label, flush_bytes=0, keep_outputs
         per.append(e)
     all1.record(stream)
     torch.cuda.synchronize()
+    if sampler is not None:
+        sampler.stop()
     total_ms = all0.elapsed_time(all1)
     t_all = []
     for e in per:
@@ -560,6 +565,78 @@ def measured_traffic(S, tau, kind="bf16"):
         return None
 
 
+def input_hashes(inputs):
+    """SHA-256 of the bytes of every input tensor, per format (q, k, v and, for
+    fp8, the per-block scales), so a run can be matched to its inputs."""
+    import hashlib
+    import torch
+    out = {}
+    for kind, inp in inputs.items():
+        d = {}
+        for name in ("q", "k", "v", "q_scale", "k_scale", "v_scale"):
+            t = getattr(inp, name, None)
+            if t is None:
+                continue
+            t = t.contiguous()
+            raw = t.view(torch.int16) if t.dtype == torch.bfloat16 else t
+            d[name] = hashlib.sha256(memoryview(raw.numpy()).cast("B")).hexdigest()
+        out[kind] = d
+    return out
+
+
+class ClockSampler:
+    """Samples the GFX clock (MHz) of the GPU torch uses, through amdsmi, on a
+    background thread between start() and stop(). Best effort: when amdsmi is
+    missing or cannot identify the device, `result()` says why instead."""
+
+    def __init__(self, period_s=0.01):
+        import threading
+        self.period, self.samples, self.error, self.handle = period_s, [], None, None
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+        try:
+            import amdsmi
+            import torch
+            self._smi = amdsmi
+            amdsmi.amdsmi_init()
+            pr = torch.cuda.get_device_properties(0)
+            bdf = f"{pr.pci_domain_id:04x}:{pr.pci_bus_id:02x}:{pr.pci_device_id:02x}"
+            handles = amdsmi.amdsmi_get_processor_handles()
+            for h in handles:
+                if str(amdsmi.amdsmi_get_gpu_device_bdf(h)).lower().startswith(bdf):
+                    self.handle = h
+            if self.handle is None:
+                self.error = f"no amdsmi device at {bdf} among {len(handles)}"
+        except Exception as e:          # a reading, never a reason to fail the bench
+            self.error = f"amdsmi: {e!r}"
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(float(self._smi.amdsmi_get_clock_info(self.handle,
+                                                                          self._smi.AmdSmiClkType.GFX)["clk"]))
+            except Exception as e:
+                self.error = f"amdsmi: {e!r}"
+                return
+            self._stop.wait(self.period)
+
+    def start(self):
+        if self.handle is not None:
+            self._thread.start()
+
+    def stop(self):
+        self._stop.set()
+        if self._thread.is_alive():
+            self._thread.join()
+
+    def result(self):
+        if not self.samples:
+            return {"error": self.error or "no samples"}
+        x = np.array(self.samples)
+        return {"gfx_mhz_median": float(np.median(x)), "gfx_mhz_min": float(x.min()),
+                "gfx_mhz_max": float(x.max()), "samples": int(len(x)), "period_ms": self.period * 1e3}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -583,6 +660,8 @@ def main():
                     help="skip the chunked-prefill leg (three chunks, with and without the pooled-KV cache)")
     ap.add_argument("--only-chunked", action="store_true",
                     help="run only the chunked-prefill leg and print its result")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the clock leg (GFX clock sampled while the bf16 path runs back to back)")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the context legs (bf16 at tau 2/6/8, and tau=inf: every block kept)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -620,6 +699,15 @@ def main():
     bf, bf_csr = time_path(fp, N, inputs["bf16"], args.tau, args.steps, args.warmup, "bf16",
                            keep_outputs=not args.no_cpu_baseline)
     log(f"bf16: {json.dumps(bf)}")
+    # the clock the chip holds under this load: sampled over back-to-back steps
+    # of the same path, outside the timed steps above
+    clock = None
+    if not args.no_clock:
+        cs = ClockSampler()
+        time_path(fp, N, inputs["bf16"], args.tau, 80, 2, "bf16 clock", sampler=cs)
+        clock = {**cs.result(), "during": "80 back-to-back steps of the bf16 path above (about 1 s)",
+                 "source": "amdsmi GFX clock"}
+        log(f"clock: {json.dumps(clock)}")
     # cold caches: a 1 GiB write before each step evicts L2 and the memory-side cache
     cold = None
     if not args.no_cold:
@@ -747,6 +835,9 @@ def main():
                        "bf16_over_fp8_attention_time": round(bf["ms_attention_median"] / f8["ms_attention_median"], 3),
                        "bf16_over_fp8_context": "1.74x on H20 (47.26 / 27.19, the pages' speedups over "
                                                 "FlashAttention-2 in fp8 and bf16), other hardware"}
+    if clock is not None:
+        line["gpu_clock"] = clock
+    line["inputs_sha256"] = input_hashes(inputs)
     if cold is not None:
         line["cold_cache"] = {"runs": 5, "flush": "1 GiB written before each step",
                               "ms_per_layer_median": round(cold["ms_step_median"], 4),

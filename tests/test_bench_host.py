@@ -99,6 +99,29 @@ def test_traffic_record_requires_matching_workload():
     assert bench.measured_traffic(131072, 2.5) is None
 
 
+def test_input_hashes_are_sha256_of_the_tensor_bytes():
+    """The bench line's input hashes are plain SHA-256 over each tensor's
+    bytes (bf16 as its 16-bit patterns, fp8 codes and fp32 scales as stored)."""
+    import hashlib
+    import synth
+    out = bench.input_hashes({"bf16": synth.gen_fixed(synth.config(1)),
+                              "fp8": synth.gen_fixed(synth.config(4, S=300, Hq=4, Hkv=1))})
+    assert set(out["bf16"]) == {"q", "k", "v"}
+    assert set(out["fp8"]) == {"q", "k", "v", "q_scale", "k_scale", "v_scale"}
+    q = synth.gen_fixed(synth.config(1)).q
+    assert out["bf16"]["q"] == hashlib.sha256(q.view(__import__("torch").int16).numpy().tobytes()).hexdigest()
+    for d in out.values():
+        assert all(len(h) == 64 for h in d.values())
+
+
+def test_clock_sampler_reports_instead_of_failing_without_a_device():
+    cs = bench.ClockSampler(period_s=0.001)
+    cs.start()
+    cs.stop()
+    r = cs.result()
+    assert "error" in r or r["samples"] >= 1
+
+
 def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
