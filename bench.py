@@ -640,8 +640,8 @@ class ClockSampler:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--tau", type=float, default=4.0)
     ap.add_argument("--seqlen", type=int, default=131072)
     ap.add_argument("--no-fp8", action="store_true")
