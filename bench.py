@@ -461,28 +461,37 @@ def cpu_baseline(inp, tau, rows_sample=768, gpu=None):
     G = Hq // Hkv
     c = 1 / math.sqrt(128)
     nb = -(-S // B)
-    with threadpool_limits(limits=1):
-        g = 0
-        q = oracle.widen_bf16(inp.q[0, :, g * G:(g + 1) * G])
-        k = oracle.widen_bf16(inp.k[0, :, g:g + 1])
-        v = oracle.widen_bf16(inp.v[0, :, g:g + 1])
-        t0 = time.perf_counter()
-        qb = pool_queries(q, B, 0, S)
-        kb, vb = pool_keys(k, B), pool_keys(v, B)
-        Sc = block_scores(qb, kb, c, 0)
-        keep, R_or = select(Sc, G, tau, 0)
-        t_est = time.perf_counter() - t0
-        il_list = np.linspace(0, nb - 1, rows_sample).round().astype(int)
-        t0 = time.perf_counter()
-        o_or, lse_or = attend(q, k, v, keep, kb, vb, c, B, 0, rows=[(0, int(il)) for il in il_list])
-        t_att = time.perf_counter() - t0
+    # one BLAS thread, and this thread pinned to one of the cores it may use
+    prev = os.sched_getaffinity(0) if hasattr(os, "sched_getaffinity") else None
+    core = min(prev) if prev else None
+    if core is not None:
+        os.sched_setaffinity(0, {core})
+    try:
+        with threadpool_limits(limits=1):
+            g = 0
+            q = oracle.widen_bf16(inp.q[0, :, g * G:(g + 1) * G])
+            k = oracle.widen_bf16(inp.k[0, :, g:g + 1])
+            v = oracle.widen_bf16(inp.v[0, :, g:g + 1])
+            t0 = time.perf_counter()
+            qb = pool_queries(q, B, 0, S)
+            kb, vb = pool_keys(k, B), pool_keys(v, B)
+            Sc = block_scores(qb, kb, c, 0)
+            keep, R_or = select(Sc, G, tau, 0)
+            t_est = time.perf_counter() - t0
+            il_list = np.linspace(0, nb - 1, rows_sample).round().astype(int)
+            t0 = time.perf_counter()
+            o_or, lse_or = attend(q, k, v, keep, kb, vb, c, B, 0, rows=[(0, int(il)) for il in il_list])
+            t_att = time.perf_counter() - t0
+    finally:
+        if core is not None:
+            os.sched_setaffinity(0, prev)
     parity = None if gpu is None else sample_parity(gpu, keep, R_or, o_or, lse_or, il_list, nb, B, tau)
     # projection: estimator time per group x Hkv; E6 time per row (evenly spaced
     # rows average the linear growth of row cost in i) x all rows
     t_layer = t_est * Hkv + t_att / rows_sample * (Hkv * nb)
     dense = 4.0 * 128 * Hq * S * (S + 1) / 2.0
     return dict(value=dense / t_layer / 1e12, unit="TFLOP/s (dense-equivalent)", cores=1,
-                kind="oracle", host_cores=os.cpu_count(), host_cpu=host_cpu_model(),
+                kind="oracle", host_cores=os.cpu_count(), host_cpu=host_cpu_model(), pinned_core=core,
                 sample=(f"E1-E5 for KV head 0 (4 query heads, all {nb} query blocks): {t_est:.2f} s; "
                         f"E6 for {rows_sample} evenly spaced query blocks of KV head 0: {t_att:.2f} s; "
                         f"projected layer time {t_layer:.0f} s (x{Hkv} heads, x{nb} rows)"),
@@ -871,7 +880,7 @@ def main():
         line["error_vs_dense_bf16"] = ablation
     if cpu is not None:
         line["cpu_baseline"] = {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample", "host_cores",
-                                                    "host_cpu")}
+                                                    "host_cpu", "pinned_core")}
         line["cpu_baseline"]["value"] = round(cpu["value"], 6)
         line["parity_sample"] = cpu["parity"]
     print(json.dumps(line), flush=True)
