@@ -283,6 +283,19 @@ def ablation_vs_dense(fp, inp, taus=(2.0, 4.0, 8.0), chunk=8192):
     return res
 
 
+def plants_kept(metas, rp, ci, Hkv, nb):
+    """How many of the planted (KV head, query block, key block) pairs of the
+    synthetic inputs the produced kept lists hold, as [kept, planted]; rows
+    of the fixed layout are (sequence, KV head, query block)."""
+    kept = total = 0
+    for b, meta in enumerate(metas):
+        for g, ip, jp, _ in meta.plants:
+            r = (b * Hkv + g) * nb + ip
+            kept += int(jp in set(ci[rp[r]:rp[r + 1]].tolist()))
+            total += 1
+    return [kept, total]
+
+
 def time_path(fp, N, inp, tau, steps, warmup, label, flush_bytes=0, keep_outputs=False, fused=True,
               split_small=False, sampler=None):
     """Run the path `warmup` + `steps` times; HIP events per stage on the
@@ -388,6 +401,8 @@ def time_path(fp, N, inp, tau, steps, warmup, label, flush_bytes=0, keep_outputs
         kept_tflop=kept / 1e12, correction_tflop=corr / 1e12, dense_tflop=dense / 1e12,
     )
     res["dense_equiv_tflops"] = dense / (res["ms_per_step"] * 1e-3) / 1e12
+    if getattr(inp, "meta", None):
+        res["plants_kept"] = plants_kept(inp.meta, rp, ci, c.num_kv_heads, p.nb)
     res["attn_kept_tflops"] = kept / (res["ms_attention"] * 1e-3) / 1e12
     res["attn_executed_tflops"] = (kept + corr) / (res["ms_attention"] * 1e-3) / 1e12
     # estimator: reads Q, K, V once and writes pooled rows (+ the full score
@@ -763,7 +778,7 @@ def main():
         for tau in (2.0, 6.0, 8.0):
             r, _ = time_path(fp, N, inputs["bf16"], tau, 5, 1, f"bf16 tau={tau}")
             sweep[str(tau)] = {"ms_per_layer": round(r["ms_per_step"], 4), "ms_attention": round(r["ms_attention"], 4),
-                               "kept_fraction": round(r["kept_fraction"], 5),
+                               "kept_fraction": round(r["kept_fraction"], 5), "plants_kept": r.get("plants_kept"),
                                "attn_kept_tflops": round(r["attn_kept_tflops"], 2)}
             log(f"sweep tau={tau}: {json.dumps(sweep[str(tau)])}")
         dense, _ = time_path(fp, N, inputs["bf16"], float("inf"), 2, 1, "bf16 dense")
@@ -815,6 +830,7 @@ def main():
                                f"16 planted blocks per KV head, seed {cfg.seed}",
                    "seq_len": cfg.S, "batch": 1, "tau": args.tau, "block": 128},
         "kept_fraction": round(bf["kept_fraction"], 5),
+        "plants_kept": bf.get("plants_kept"),
         "path": "fp_estimate_select (pooling + fused block scores/threshold/CSR/schedule, no score matrix) "
                 "+ fp_sparse_prefill",
         "ms_per_layer": {"total": round(bf["ms_per_step"], 4),

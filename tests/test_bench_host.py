@@ -114,6 +114,22 @@ def test_input_hashes_are_sha256_of_the_tensor_bytes():
         assert all(len(h) == 64 for h in d.values())
 
 
+def test_plants_kept_reads_the_row_of_each_plant():
+    """Rows are (sequence, KV head, query block): a plant (g, i, j) is kept
+    when column j is in row (b * Hkv + g) * nb + i."""
+    from types import SimpleNamespace as NS
+    Hkv, nb = 2, 4
+    keep = np.zeros((2 * Hkv * nb, nb), dtype=bool)
+    keep[(0 * Hkv + 1) * nb + 3, 1] = True            # sequence 0, head 1, block 3 keeps column 1
+    keep[(1 * Hkv + 0) * nb + 2, 0] = True            # sequence 1, head 0, block 2 keeps column 0
+    rp, ci = [0], []
+    for r in range(keep.shape[0]):
+        ci.extend(np.nonzero(keep[r])[0].tolist())
+        rp.append(len(ci))
+    metas = [NS(plants=[(1, 3, 1, 1.0), (1, 3, 2, 1.0)]), NS(plants=[(0, 2, 0, 1.0), (1, 2, 0, 1.0)])]
+    assert bench.plants_kept(metas, np.array(rp), np.array(ci), Hkv, nb) == [2, 4]
+
+
 def test_clock_sampler_reports_instead_of_failing_without_a_device():
     cs = bench.ClockSampler(period_s=0.001)
     cs.start()
