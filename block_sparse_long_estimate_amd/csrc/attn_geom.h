@@ -158,6 +158,39 @@ FP_HD SummarySrc summary_src(const SeqDesc& s, int Hkv, int g, int m, int w, int
     return SummarySrc{w == 0 ? part : 2, kbar_row(s, Hkv, g, jp) * D + pl.ch * 8};
 }
 
+// Per-lane byte offsets of a whole summary sub-tile's loads (every pooled
+// column of it inside the sequence, so none repeats), computed once per
+// workgroup. Relative to the sub-tile's first hi row in the hi array, K piece
+// k * NW + w (wavefront w) reads at k_off[k]: its lo rows sit lo_delta bytes
+// further (the distance from the hi array to the lo array). The V pieces repeat
+// one pattern (4 rows of 256 bytes per piece, rotation period 4 rows): piece t
+// reads at v_off + t * PIECE from the sub-tile's first row in the V array.
+// summary_src gives the same addresses for these sub-tiles.
+template <int BLK, int NW>
+struct SumOffs {
+    using TG = TileGeom<BLK, false>;
+    static constexpr int NPK = (TG::SKPIECES + NW - 1) / NW;
+    static constexpr int NPV = (TG::SVPIECES + NW - 1) / NW;
+    uint32_t k_off[NPK];
+    uint32_t v_off;
+    static FP_HD bool has_k(int k, int wave) { return k * NW + wave < TG::SKPIECES; }
+    static FP_HD bool has_v(int k, int wave) { return k * NW + wave < TG::SVPIECES; }
+    FP_HD void init(uint32_t lo_delta, int wave, int lane) {
+#pragma unroll
+        for (int k = 0; k < NPK; ++k) {
+            const PieceLoc pl = piece_loc(KSTR, k * NW + wave, lane, 16);
+            const int part = pl.row >= TG::SUMC;
+            k_off[k] = has_k(k, wave) ? (part ? lo_delta : 0u) + (uint32_t)((pl.row - part * TG::SUMC) * D * 2 +
+                                                                           pl.ch * 16)
+                                      : 0u;
+        }
+        const PieceLoc pv = piece_loc(VSTR, 0, lane, 16);
+        v_off = (uint32_t)(pv.row * D * 2 + pv.ch * 16);
+    }
+    // sub-tile m of a sequence with nbk key blocks takes these offsets when all its columns exist
+    static FP_HD bool whole(int m, int nbk) { return (m + 1) * TG::SUMC <= nbk; }
+};
+
 // ---------------------------------------------------------------------------
 // Work units. Unit u of the grid runs one 256-row slice of one kept-list row,
 // or, when the row's tiles are split, one part of that slice's tile sequence:

@@ -251,10 +251,31 @@ __device__ __forceinline__ void issue_kv(const AttnArgs& a, int b, int L, int g,
 // Summary sub-tile m: the K tile holds the bf16 hi parts of its pooled keys
 // in rows 0 .. SUMC-1 and the lo parts in rows SUMC .. BLK-1, so one tile load
 // brings both and the two halves of QK^T accumulate into one logit.
+// so (with fast): per-lane offsets for whole sub-tiles, kept in registers.
 template <int BLK, int NW>
 __device__ __forceinline__ void issue_summary(const AttnArgs& a, const SeqDesc& s, int g, int m,
-                                              lds_u8* kbuf, lds_u8* vbuf, int wave, int lane) {
+                                              lds_u8* kbuf, lds_u8* vbuf, int wave, int lane,
+                                              const SumOffs<BLK, NW>& so, bool fast) {
     using TG = TileGeom<BLK, false>;
+    using SO = SumOffs<BLK, NW>;
+    if (fast && SO::whole(m, s.nbk)) {
+        const long long r0 = kbar_row(s, a.Hkv, g, TG::SUMC * m) * (D * 2);
+        if (!a.scores) {
+            const uint8_t* kb = (const uint8_t*)a.kbar_hi + r0;
+#pragma unroll
+            for (int k = 0; k < SO::NPK; ++k)
+                if (SO::has_k(k, wave))
+                    __builtin_amdgcn_global_load_lds((const void*)(kb + so.k_off[k]),
+                                                     (lds_void*)(kbuf + (k * NW + wave) * PIECE), 16, 0, 0);
+        }
+        const uint8_t* vb = (const uint8_t*)a.vbar_bf + r0 + so.v_off;
+#pragma unroll
+        for (int k = 0; k < SO::NPV; ++k)
+            if (SO::has_v(k, wave))
+                __builtin_amdgcn_global_load_lds((const void*)(vb + (k * NW + wave) * PIECE),
+                                                 (lds_void*)(vbuf + (k * NW + wave) * PIECE), 16, 0, 0);
+        return;
+    }
     // recompute the per-lane piece addresses here instead of keeping them
     // live across the tile loop (registers are the scarce resource)
     asm volatile("" : "+v"(lane));
@@ -480,6 +501,14 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_tile_kernel(Geo geo, AttnArgs
         kvo.k.init_paged(a.ka.st, lshift, wave, lane);
         kvo.v.init_paged(a.va.st, lshift, wave, lane);
     }
+    // whole summary sub-tiles load through offsets computed once (not in split
+    // parts or the paged fp8 kernel, whose registers are already full); the
+    // lo array must lie within 2 GiB after the hi array for 32-bit offsets
+    SumOffs<BLK, NW> so;
+    constexpr bool SUM_OFFS = !SPLIT && !(PAGED && FP8);
+    const unsigned long long lo_delta = (unsigned long long)((const char*)a.kbar_lo - (const char*)a.kbar_hi);
+    const bool sum_fast = SUM_OFFS && !a.dense && lo_delta < (1ull << 31);
+    if (sum_fast) so.init((uint32_t)lo_delta, wave, lane);
     // the first tile; a split row's part learns its first tile from the kept bitmap
     if (!SPLIT) issue_kv<BLK, FP8, PAGED, NW>(a, b, s.L, gk, j0, kA, vA, wave, lane, kvo, nullptr);
     // paged: stage the page ids for the later tiles (visible after the
@@ -579,7 +608,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_tile_kernel(Geo geo, AttnArgs
                 vsn = load_scale(vsp, (code * BLK) >> 7);
             }
         } else {
-            issue_summary<BLK, NW>(a, s, gk, -1 - code, kb, vb, wave, lane);
+            issue_summary<BLK, NW>(a, s, gk, -1 - code, kb, vb, wave, lane, so, sum_fast);
         }
     };
     // causal mask inside the diagonal tile: keys after the row's token
@@ -777,19 +806,19 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_tile_kernel(Geo geo, AttnArgs
     // Summary phase: realign so the loop below always starts on buffer A.
     if (in_b && nxt != TILE_NONE) {
         const int cn = next_sum(nxt);
-        if (cn != TILE_NONE) issue_summary<BLK, NW>(a, s, gk, -1 - cn, kA, vA, wave, lane);
+        if (cn != TILE_NONE) issue_summary<BLK, NW>(a, s, gk, -1 - cn, kA, vA, wave, lane, so, sum_fast);
         compute_summary(nxt, kB, vB);
         __syncthreads();
         nxt = cn;
     }
     while (nxt != TILE_NONE) {
         const int cb = next_sum(nxt);
-        if (cb != TILE_NONE) issue_summary<BLK, NW>(a, s, gk, -1 - cb, kB, vB, wave, lane);
+        if (cb != TILE_NONE) issue_summary<BLK, NW>(a, s, gk, -1 - cb, kB, vB, wave, lane, so, sum_fast);
         compute_summary(nxt, kA, vA);
         __syncthreads();
         if (cb == TILE_NONE) break;
         const int cn = next_sum(cb);
-        if (cn != TILE_NONE) issue_summary<BLK, NW>(a, s, gk, -1 - cn, kA, vA, wave, lane);
+        if (cn != TILE_NONE) issue_summary<BLK, NW>(a, s, gk, -1 - cn, kA, vA, wave, lane, so, sum_fast);
         compute_summary(cb, kB, vB);
         __syncthreads();
         nxt = cn;

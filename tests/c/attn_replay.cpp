@@ -339,6 +339,23 @@ static void replay(const Launch& L, bool split_small) {
                                       src.off);
                                 CHECK(t * PIECE + 16 * lane + 16 <= (w == 0 ? TG::KTILE : TG::VTILE),
                                       "summary LDS piece");
+                                if (SumOffs<BLK, NW>::whole(m, s.nbk)) {
+                                    // whole sub-tile: the per-lane offsets of the load
+                                    // path read the same bytes (lo array lo_delta bytes
+                                    // after the hi array, as the library lays them out)
+                                    using SO = SumOffs<BLK, NW>;
+                                    const long long lo_delta = (L.pooled_rows * D * 2 + 255) / 256 * 256;
+                                    SO so;
+                                    so.init((uint32_t)lo_delta, wave, lane);
+                                    const long long r0 = kbar_row(s, L.Hkv, gk, TG::SUMC * m) * D * 2;
+                                    const int k = t0 / NW;
+                                    const long long fast = w == 0 ? (SO::has_k(k, wave) ? r0 + so.k_off[k] : -1)
+                                                                  : (SO::has_v(k, wave) ? r0 + so.v_off + (long long)t * PIECE
+                                                                                        : -1);
+                                    const long long slow = (src.which == 1 ? lo_delta : 0) + src.off * 2;
+                                    CHECK(fast == slow, "summary offsets: sub-tile %d piece %d lane %d: %lld vs %lld", m,
+                                          t, lane, fast, slow);
+                                }
                             }
                         }
                 }
@@ -672,6 +689,17 @@ int main(int argc, char** argv) {
         }
         replay_all<8>(L, fp8);
     }
+    // launches whose rows see whole summary sub-tiles (all their pooled
+    // columns inside the sequence: the per-lane offset load path), first too
+    for (int blk : {64, 128})
+        for (int fp8 = 0; fp8 < 2; ++fp8) {
+            const int S = blk == 64 ? 2600 : 8400;
+            snprintf(name, sizeof name, "fixed whole summary sub-tiles S=%d 4/1 blk=%d %s", S, blk, fp8 ? "fp8" : "bf16");
+            g_case = name;
+            const Launch L = fixed_launch(1, S, 4, 1, blk, fp8, 0.0, seed++, false);
+            replay_all<8>(L, fp8);
+            replay_all<4>(L, fp8);
+        }
     // fixed shapes: tiny and ragged lengths, GQA ratios, densities from
     // "sink and diagonal only" to "everything kept", fused q/k/v strides;
     // among them the launch that once faulted: S = 4173, 8/2 heads, block 128

@@ -62,6 +62,10 @@ MUTANTS = [
      "z = (int)((long long)T * (split + 1) / nsplit) + (split + 1 < nsplit);"),
     ("split units give two workgroups the same part", "return UnitMap{8 * (k8 / per) + xcd, rem % slices, rem / slices};",
      "return UnitMap{8 * (k8 / per) + xcd, rem % slices, rem % nsplit};"),
+    ("whole summary sub-tiles read lo rows from the hi array",
+     "k_off[k] = has_k(k, wave) ? (part ? lo_delta : 0u)", "k_off[k] = has_k(k, wave) ? (part ? 0u : 0u)"),
+    ("whole summary sub-tiles read V without the row rotation",
+     "const PieceLoc pv = piece_loc(VSTR, 0, lane, 16);", "const PieceLoc pv = piece_loc(KSTR, 0, lane, 16);"),
     ("fp8 V key permutation dropped from the contiguous loads",
      "const int key = PERM ? vt_slot(pl.row) : pl.row;\n            off[k] = has(k, wave) ? (uint32_t)",
      "const int key = pl.row;\n            off[k] = has(k, wave) ? (uint32_t)"),
