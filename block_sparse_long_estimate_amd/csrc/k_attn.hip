@@ -490,7 +490,15 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_tile_kernel(Geo geo, AttnArgs
     // kept list of the row: from the CSR, or every block j <= i when dense
     const int rp0 = a.dense ? 0 : a.row_ptr[r];
     const int nnz = a.dense ? i + 1 : a.row_ptr[r + 1] - rp0;
-    const int j0 = a.dense ? 0 : a.col_idx[rp0];
+    // kept codes are clamped to the row's blocks: a caller's list cannot move a tile load off the row
+    const int j0 = a.dense ? 0 : min(max(a.col_idx[rp0], 0), i);
+    // bf16: the kept blocks of the row, in their order (the CSR list), code t
+    // in lane t mod 64 of kc, loaded 64 at a time, so the next kept code is one
+    // lane read rather than a scan of the LDS bitmap (fp8 has no register to
+    // spare for it and scans). kt: the current tile's index in the list.
+    constexpr bool LIST_CODES = !FP8;
+    int kt = 0;
+    int kc = (LIST_CODES && !a.dense && lane < nnz) ? a.col_idx[rp0 + lane] : 0;
     KVOffs<BLK, FP8, NW> kvo;
     if (!PAGED) {
         kvo.k.init(a.ka.st, wave, lane);
@@ -571,6 +579,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_tile_kernel(Geo geo, AttnArgs
     float svm = 0.f;
     for (int e = tid; e < nnz; e += NT) {
         const int j = a.dense ? e : a.col_idx[rp0 + e];
+        if ((unsigned)j > (unsigned)i) continue;      // not a block of this row: ignored
         atomicOr(&kept[j >> 5], 1u << (j & 31));
         if (FP8) svm = fmaxf(svm, vsp[(j * BLK) >> 7]);
     }
@@ -752,14 +761,24 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_tile_kernel(Geo geo, AttnArgs
             }
             return;
         }
-        code0 = sr.first < nnz ? a.col_idx[rp0 + sr.first] : nth_summary<TG::SUMC>(kbits, i, sr.first - nnz, no_corr);
+        code0 = sr.first < nnz ? (a.dense ? sr.first : min(max(a.col_idx[rp0 + sr.first], 0), i))
+                               : nth_summary<TG::SUMC>(kbits, i, sr.first - nnz, no_corr);
         code0 = __builtin_amdgcn_readfirstlane(code0);
+        kt = __builtin_amdgcn_readfirstlane(sr.first);
+        if (LIST_CODES && !a.dense && kt >= 64) kc = (kt - (kt & 63) + lane < nnz) ? a.col_idx[rp0 + kt - (kt & 63) + lane] : 0;
         issue(code0, kA, vA, ksA, vsA);
         __syncthreads();                              // the part's first tile landed
     }
     // the code after `code` in the sequence (kept block or summary sub-tile)
     auto next_tile = [&](int code) __attribute__((always_inline)) {
         if (SPLIT && --remaining <= 0) return TILE_NONE;
+        if (LIST_CODES && code >= 0) {
+            ++kt;
+            if (kt >= nnz) return next_summary<TG::SUMC>(kbits, i, 0, no_corr);
+            if (a.dense) return kt;                   // dense: every block j <= i, in order
+            if ((kt & 63) == 0) kc = (kt + lane < nnz) ? a.col_idx[rp0 + kt + lane] : 0;
+            return min(max(__builtin_amdgcn_readlane(kc, kt & 63), 0), i);
+        }
         return next_code<TG::SUMC>(kbits, i, code, no_corr);
     };
     auto next_sum = [&](int code) __attribute__((always_inline)) {
