@@ -73,6 +73,25 @@ def test_dense_against_oracle_and_sparse_tau_inf(fp, cfg, kind):
     say(f"  max|err| {mx:.2e} mean {mean:.2e}")
 
 
+@pytest.mark.parametrize("S,Hq,block", [(130 * 128 + 5, 4, 128), (200 * 64 + 7, 2, 64)])
+def test_long_rows_equal_dense(fp, S, Hq, block):
+    """Rows keeping more than 64 and 128 blocks (the kernel holds a row's kept
+    list 64 codes per register and reloads it as it goes): tau = +inf through
+    the sparse path equals the dense path bit for bit, so every row visits
+    its blocks 0..i in order across the reloads."""
+    cfg = synth.config(2, S=S, Hq=Hq, Hkv=1, block=block)
+    inp = synth.gen_fixed(cfg)
+    q, k, v, sc = to_dev(inp)
+    say(f"long rows S={S} {Hq}/1 block {block}")
+    p = fp.make_problem(q, k, v, block)
+    o, lse = fp.fp_dense_prefill(p, q, k, v, **sc)
+    sp = fp.sparse_prefill(q, k, v, block, float("inf"), **sc)
+    torch.cuda.synchronize()
+    nb = -(-S // block)
+    assert int(np.diff(sp["row_ptr"].cpu().numpy()).max()) == nb
+    assert torch.equal(o, sp["o"]) and torch.equal(lse, sp["lse"]), "tau = +inf differs from dense"
+
+
 def test_dense_against_torch_sdpa(fp):
     """An independent reference: torch's scaled_dot_product_attention (causal,
     float32, CPU) on the same bf16 inputs."""

@@ -56,6 +56,7 @@ CASES = [
     (2, dict(S=1500, Hq=8, Hkv=2, tau=1.0), "none"),
     (2, dict(S=1500, Hq=8, Hkv=2, tau=1.0), "per_head"),
     (2, dict(S=1500, Hq=8, Hkv=2, tau=1.0), "block_score"),
+    (2, dict(S=8192, Hq=1, Hkv=1, tau=float("inf"), block=64), "mean"),  # a part starting at tile 64 of 128
     (4, dict(S=2088, Hq=8, Hkv=2, tau=2.0), "mean"),              # fp8
     (4, dict(S=1000, Hq=4, Hkv=1, tau=1.0, block=64), "mean"),
 ]
