@@ -155,13 +155,23 @@ __device__ __forceinline__ float e4m3_val(uint32_t c) {
 // 1 KiB of LDS (lane l -> bytes 16 l .. 16 l + 15). LDS row r holds key r
 // (PERM: key vt_slot(r)); rows past the sequence repeat its last key.
 // ---------------------------------------------------------------------------
+// A 32-bit lane offset from a uniform base, passed through an empty asm so
+// that the compiler cannot hoist a 64-bit widening of it out of the tile
+// loop (two registers per offset): the load then takes the scalar-base form.
+FP_HD uint32_t lane_off(uint32_t off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("" : "+v"(off));
+#endif
+    return off;
+}
+
 template <int STR, int BLK, int ESZ, bool PERM, int NW>
 __device__ __forceinline__ void issue_full(const TileOffs<STR, BLK, ESZ, PERM, NW>& o, const uint8_t* tile_base,
                                            lds_u8* buf, int wave) {
 #pragma unroll
     for (int k = 0; k < o.NP; ++k)
         if (o.has(k, wave))
-            __builtin_amdgcn_global_load_lds((const void*)(tile_base + o.off[k]),
+            __builtin_amdgcn_global_load_lds((const void*)(tile_base + lane_off(o.off[k])),
                                              (lds_void*)(buf + (k * NW + wave) * PIECE), 16, 0, 0);
 }
 
@@ -265,14 +275,14 @@ __device__ __forceinline__ void issue_summary(const AttnArgs& a, const SeqDesc& 
 #pragma unroll
             for (int k = 0; k < SO::NPK; ++k)
                 if (SO::has_k(k, wave))
-                    __builtin_amdgcn_global_load_lds((const void*)(kb + so.k_off[k]),
+                    __builtin_amdgcn_global_load_lds((const void*)(kb + lane_off(so.k_off[k])),
                                                      (lds_void*)(kbuf + (k * NW + wave) * PIECE), 16, 0, 0);
         }
-        const uint8_t* vb = (const uint8_t*)a.vbar_bf + r0 + so.v_off;
+        const uint8_t* vb = (const uint8_t*)a.vbar_bf + r0;
 #pragma unroll
         for (int k = 0; k < SO::NPV; ++k)
             if (SO::has_v(k, wave))
-                __builtin_amdgcn_global_load_lds((const void*)(vb + (k * NW + wave) * PIECE),
+                __builtin_amdgcn_global_load_lds((const void*)(vb + (k * NW + wave) * PIECE + lane_off(so.v_off)),
                                                  (lds_void*)(vbuf + (k * NW + wave) * PIECE), 16, 0, 0);
         return;
     }
