@@ -504,8 +504,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_tile_kernel(Geo geo, AttnArgs
     const int j0 = a.dense ? 0 : min(max(a.col_idx[rp0], 0), i);
     // bf16: the kept blocks of the row, in their order (the CSR list), code t
     // in lane t mod 64 of kc, loaded 64 at a time, so the next kept code is one
-    // lane read rather than a scan of the LDS bitmap (fp8 has no register to
-    // spare for it and scans). kt: the current tile's index in the list.
+    // lane read rather than a scan of the LDS bitmap (the fp8 kernel measured
+    // no gain from it and scans). kt: the current tile's index in the list.
     constexpr bool LIST_CODES = !FP8;
     int kt = 0;
     int kc = (LIST_CODES && !a.dense && lane < nnz) ? a.col_idx[rp0 + lane] : 0;
@@ -520,8 +520,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_tile_kernel(Geo geo, AttnArgs
         kvo.v.init_paged(a.va.st, lshift, wave, lane);
     }
     // whole summary sub-tiles load through offsets computed once (not in split
-    // parts or the paged fp8 kernel, whose registers are already full); the
-    // lo array must lie within 2 GiB after the hi array for 32-bit offsets
+    // parts, whose registers are full, nor in the paged fp8 kernel, which sits
+    // at the register limit with them); the lo array must lie within 2 GiB
+    // after the hi array for 32-bit offsets
     SumOffs<BLK, NW> so;
     constexpr bool SUM_OFFS = !SPLIT && !(PAGED && FP8);
     const unsigned long long lo_delta = (unsigned long long)((const char*)a.kbar_lo - (const char*)a.kbar_hi);
