@@ -45,7 +45,10 @@
  *     Fixed shape: k and v token strides x block x element size < 2 GiB.
  *   - Inputs are post-RoPE and finite (non-finite inputs: undefined results).
  *   - Kept-block lists are CSR over rows ordered (sequence b, KV head g, query
- *     block i ascending); columns ascending, absolute key-block indices.
+ *     block i ascending); columns strictly ascending absolute key-block
+ *     indices within [0, i]. A caller's list that breaks this gives
+ *     unspecified results, but the attention never loads a tile outside the
+ *     row's blocks 0 .. i.
  */
 #ifndef FP_PREFILL_H
 #define FP_PREFILL_H
