@@ -2,7 +2,8 @@
 fp_sparse_prefill on the same kept lists: the same kernels run on the
 library's static per-GPU scratch array instead of a caller workspace, so o
 and lse must be bit-identical. Two calls in a row, the second on a smaller
-problem (the array keeps the first call's contents), then fp8."""
+problem (the array keeps the first call's contents), then a problem whose
+rows reach whole summary sub-tiles, then fp8."""
 import sys
 
 import pytest
@@ -30,6 +31,8 @@ def test_noalloc_equals_workspace_entry_point(fp):
     dev = torch.device("cuda:0")
     cases = [(synth.config(2, S=4096 + 77, Hq=8, Hkv=2, tau=2.0), "bf16"),
              (synth.config(2, S=1024 + 5, Hq=4, Hkv=1, tau=1.0, seed=9), "bf16"),
+             # rows past 64 blocks: whole summary sub-tiles (per-lane offsets into the array)
+             (synth.config(2, S=65 * 128 + 7, Hq=8, Hkv=2, tau=2.0, seed=5), "bf16"),
              (synth.config(4, S=2048 + 40, Hq=8, Hkv=2, tau=2.0), "fp8")]
     for cfg, kind in cases:
         say(f"noalloc S={cfg.S} {cfg.Hq}/{cfg.Hkv} tau={cfg.tau} {kind}")
