@@ -857,6 +857,10 @@ def main():
                        "ms_estimate_select": round(f8["ms_estimate_select"], 4),
                        "estimate_select_gbs": round(f8["estimate_gbs"], 1),
                        "traffic": measured_traffic(cfg.S, args.tau, "fp8"),
+                       "roofline": {"bound": "mfma", "kernel": "attn_tile_kernel<128, fp8> (fp_sparse_prefill)",
+                                    "achieved": round(f8["attn_kept_tflops"], 2), "peak": PEAK_TFLOPS["fp8"],
+                                    "unit": "TFLOP/s", "frac": round(f8["attn_kept_tflops"] / PEAK_TFLOPS["fp8"], 4),
+                                    "traffic": measured_traffic(cfg.S, args.tau, "fp8")},
                        "bf16_over_fp8_attention_time": round(bf["ms_attention_median"] / f8["ms_attention_median"], 3),
                        "bf16_over_fp8_context": "1.74x on H20 (47.26 / 27.19, the pages' speedups over "
                                                 "FlashAttention-2 in fp8 and bf16), other hardware"}
